@@ -1,0 +1,100 @@
+"""Seeded synthetic inputs and the named workloads for the KDA operator.
+
+This module holds no arithmetic of the method: it only draws random tensors
+and describes shapes. Both the FP64 oracle (through the tests) and the GPU
+path are fed from it.
+
+Inputs follow the measurement configuration of "KDA Memory with Recompute:
+FLA vs cuDNN Frontend FROST" (section "Sources and measurement
+configuration"): Q, K, V, raw gate, raw beta and the output gradient dO drawn
+N(0,1) in float32 and rounded (round-to-nearest-even) to the workload dtype;
+FP32 A_log and dt_bias initialised to zero; equal-length sequences packed with
+boundaries (cu_seqlens).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    seqlens: tuple  # lengths of the packed sequences
+    H: int
+    D: int  # K = V = D
+    dtype: str  # "f32" or "bf16"
+    chunk: int
+    seed: int
+    A_log: float = 0.0
+    dt_bias: float = 0.0
+
+    @property
+    def T(self) -> int:
+        return int(sum(self.seqlens))
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def cu_seqlens(self) -> list[int]:
+        cu = [0]
+        for n in self.seqlens:
+            cu.append(cu[-1] + int(n))
+        return cu
+
+
+# The five workloads: a tiny fp32 case, the small fp32 preset (10 packed
+# sequences of 512), the 8K x H64 bf16 case the headline throughput is quoted
+# on, the 8 x 8K packed varlen case and the 128K x H96 long-context case.
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", (256,), 2, 64, "f32", 64, seed=1),
+    "small_f32": Workload("small_f32", (512,) * 10, 12, 64, "f32", 16, seed=2),
+    "t8k_h64_bf16": Workload("t8k_h64_bf16", (8192,), 64, 128, "bf16", 64, seed=3),
+    "varlen8x8k_h16_bf16": Workload("varlen8x8k_h16_bf16", (8192,) * 8, 16, 128, "bf16", 64, seed=4),
+    "t128k_h96_bf16": Workload("t128k_h96_bf16", (131072,), 96, 128, "bf16", 64, seed=5),
+}
+
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "raw_g": 3, "raw_beta": 4, "dO": 5}
+
+
+def _randn(shape, seed: int, tensor_id: int, device, dtype) -> torch.Tensor:
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 1000003 + tensor_id * 7919 + 17)
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    return x.to(dtype)
+
+
+def make_inputs(seqlens, H: int, K: int, V: int, dtype=torch.float32, seed: int = 0,
+                device="cpu", A_log: float = 0.0, dt_bias: float = 0.0,
+                with_dO: bool = True) -> dict:
+    """Draw one problem. Returns torch tensors on ``device``:
+    q,k,raw_g [T,H,K]; v,dO [T,H,V]; raw_beta [T,H] (all ``dtype``);
+    A_log [H], dt_bias [H,K] (float32, constant fill); cu_seqlens int32 [N+1]
+    on ``device`` plus ``cu_seqlens_host`` (a Python list).
+    """
+    seqlens = [int(n) for n in seqlens]
+    T = sum(seqlens)
+    cu = [0]
+    for n in seqlens:
+        cu.append(cu[-1] + n)
+    out = {
+        "q": _randn((T, H, K), seed, TENSOR_IDS["q"], device, dtype),
+        "k": _randn((T, H, K), seed, TENSOR_IDS["k"], device, dtype),
+        "v": _randn((T, H, V), seed, TENSOR_IDS["v"], device, dtype),
+        "raw_g": _randn((T, H, K), seed, TENSOR_IDS["raw_g"], device, dtype),
+        "raw_beta": _randn((T, H), seed, TENSOR_IDS["raw_beta"], device, dtype),
+        "A_log": torch.full((H,), float(A_log), dtype=torch.float32, device=device),
+        "dt_bias": torch.full((H, K), float(dt_bias), dtype=torch.float32, device=device),
+        "cu_seqlens": torch.tensor(cu, dtype=torch.int32, device=device),
+        "cu_seqlens_host": cu,
+    }
+    if with_dO:
+        out["dO"] = _randn((T, H, V), seed, TENSOR_IDS["dO"], device, dtype)
+    return out
+
+
+def workload_inputs(w: Workload, device="cpu", with_dO: bool = True) -> dict:
+    return make_inputs(w.seqlens, w.H, w.D, w.D, w.torch_dtype, w.seed, device,
+                       w.A_log, w.dt_bias, with_dO)

@@ -1,0 +1,124 @@
+"""FP64 CPU oracle for the KDA operator (test infrastructure only).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It shares no code with the GPU path
+(``recompute_kda_chunked_amd``) and never imports it.
+
+``kda_oracle.c`` holds the token-by-token recurrence and its hand-derived
+reverse sweep (see its header for the equations and the passages of the pages
+they follow). This module only marshals numpy arrays into it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_BUILD = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD, "libkda_oracle.so")
+
+GATE_SIGMOID_BOUND = 0  # g = L * sigmoid(exp(A_log) * (raw_g + dt_bias))
+GATE_SOFTPLUS_CLAMP = 1  # g = max(L, -exp(A_log) * softplus(raw_g + dt_bias))
+
+
+def build(extra_flags: tuple[str, ...] = (), out_path: str | None = None) -> str:
+    """Compile the oracle with gcc (OpenMP, -O2). Returns the library path.
+
+    ``extra_flags`` lets a test build a deliberately broken variant of the
+    oracle (``-DKDA_ORACLE_MUTANT=n``) into ``out_path``.
+    """
+    out = out_path or _LIB_PATH
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           *extra_flags, "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_lib_cache: dict[str, ctypes.CDLL] = {}
+
+
+def _load(path: str | None = None) -> ctypes.CDLL:
+    path = path or _LIB_PATH
+    if path in _lib_cache:
+        return _lib_cache[path]
+    if not os.path.exists(path):
+        if path != _LIB_PATH:
+            raise FileNotFoundError(path)
+        build()
+    lib = ctypes.CDLL(path)
+    f = lib.kda_oracle
+    dp = ctypes.POINTER(ctypes.c_double)
+    f.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                  ctypes.c_double, ctypes.c_int] + [dp] * 8 + [dp] * 8 + [ctypes.c_int]
+    f.restype = ctypes.c_int
+    _lib_cache[path] = lib
+    return lib
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # a torch tensor: upcast exactly to float64 on the host
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def kda(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, dO=None,
+        scale: float = 1.0, lower_bound: float = -5.0, eps: float = 1e-6,
+        gate_mode: int = GATE_SIGMOID_BOUND, n_threads: int = 0,
+        lib_path: str | None = None) -> dict:
+    """Run the oracle. Shapes: q,k,raw_g [T,H,K]; v [T,H,V]; raw_beta [T,H];
+    A_log [H]; dt_bias [H,K]; cu_seqlens [N+1] (defaults to one sequence);
+    dO [T,H,V] or None (forward only).
+
+    Returns a dict of float64 arrays: ``o`` and, when dO is given, ``dq, dk,
+    dv, draw_g, draw_beta, dA_log, ddt_bias``.
+    """
+    q, k, v, raw_g, raw_beta = map(_f64, (q, k, v, raw_g, raw_beta))
+    A_log, dt_bias = _f64(A_log), _f64(dt_bias)
+    T, H, K = q.shape
+    V = v.shape[2]
+    if k.shape != (T, H, K) or raw_g.shape != (T, H, K) or v.shape[:2] != (T, H):
+        raise ValueError("shape mismatch among q, k, v, raw_g")
+    if raw_beta.shape != (T, H) or A_log.shape != (H,) or dt_bias.shape != (H, K):
+        raise ValueError("shape mismatch among raw_beta, A_log, dt_bias")
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64))
+    if cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must be non-decreasing from 0 to T")
+    n = len(cu) - 1
+    o = np.zeros((T, H, V))
+    out = {"o": o}
+    grads = [None] * 8
+    if dO is not None:
+        dO = _f64(dO)
+        if dO.shape != (T, H, V):
+            raise ValueError("dO shape mismatch")
+        out.update(dq=np.zeros((T, H, K)), dk=np.zeros((T, H, K)), dv=np.zeros((T, H, V)),
+                   draw_g=np.zeros((T, H, K)), draw_beta=np.zeros((T, H)),
+                   dA_log=np.zeros(H), ddt_bias=np.zeros((H, K)))
+        grads = [out[n_] for n_ in ("dq", "dk", "dv", "draw_g", "draw_beta", "dA_log", "ddt_bias")]
+    lib = _load(lib_path)
+    rc = lib.kda_oracle(n, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, K, V,
+                        float(scale), float(lower_bound), float(eps), int(gate_mode),
+                        _ptr(q), _ptr(k), _ptr(v), _ptr(raw_g), _ptr(raw_beta), _ptr(A_log),
+                        _ptr(dt_bias), _ptr(dO), _ptr(o), *[_ptr(g) for g in grads[:7]],
+                        int(n_threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle failed with status %d" % rc)
+    return out
