@@ -1,0 +1,148 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) Kimi Delta Attention chunked operator:
+ * a forward pass and a backward pass that recomputes its intermediates
+ * instead of saving them.
+ *
+ * Operator ("KDA Memory with Recompute: FLA vs cuDNN Frontend FROST",
+ * section "Sources and measurement configuration"; per-chunk operations in
+ * "KDA at the production shape..." section 2.1 and section 1.1):
+ *   per packed sequence and head, with the state S (K x V) starting at zero,
+ *     qh = scale * q / sqrt(|q|^2 + eps),  kh = k / sqrt(|k|^2 + eps)
+ *     beta = sigmoid(raw_beta)
+ *     g = L * sigmoid(exp(A_log[h]) * (raw_g + dt_bias[h,:]))   (L = gate_lower_bound)
+ *     S_t = (I - beta_t kh_t kh_t^T) Diag(exp(g_t)) S_{t-1} + beta_t kh_t v_t^T
+ *     o_t = S_t^T qh_t
+ *   no initial state, no final state; the state restarts at every sequence
+ *   boundary of cu_seqlens. The backward returns the gradients of all seven
+ *   inputs (q, k, v, raw_g, raw_beta, A_log, dt_bias) of sum(o * dO).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, row-major with
+ *     the innermost dimension contiguous: q, k, raw_g [T, H, K]; v, o, dO
+ *     [T, H, V]; raw_beta [T, H]; A_log [H] (fp32); dt_bias [H, K] (fp32);
+ *     cu_seqlens [n_seqs + 1] (int32, device copy). Pointers must be 16-byte
+ *     aligned.
+ *   - dtype selects the element type of q, k, v, raw_g, raw_beta, dO, o and
+ *     of dq, dk, dv, draw_g, draw_beta (fp32 or bf16). dA_log and ddt_bias
+ *     are always fp32.
+ *   - `stream` is a hipStream_t (passed as void*; NULL is the null stream).
+ *     All work is enqueued on it asynchronously; no call synchronises the
+ *     host with the device. Outputs are overwritten, never accumulated.
+ *   - The library allocates no device memory and keeps no state between
+ *     calls: scratch comes from the caller's `workspace` (size from the
+ *     *_workspace_bytes query for the same problem). Calls are reentrant and
+ *     thread-safe; calls sharing a workspace must be stream-ordered.
+ *   - All argument validation happens on the host before any HIP call.
+ *     Return value: KDA_OK or one of the error codes below. NaN/Inf inputs
+ *     propagate; they are not checked.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID = 1,     /* null pointer, non-positive size, bad cu_seqlens_host */
+  KDA_ERR_UNSUPPORTED = 2, /* K/V/chunk/dtype/gate combination not built */
+  KDA_ERR_WORKSPACE = 3,   /* workspace smaller than the *_workspace_bytes query */
+  KDA_ERR_HIP = 4          /* a HIP launch failed; kda_status_string names it */
+};
+
+enum { KDA_F32 = 0, KDA_BF16 = 1 };
+
+/* Gate maps. Only KDA_GATE_SIGMOID_BOUND is built; the other value is
+   reserved and rejected with KDA_ERR_UNSUPPORTED. */
+enum { KDA_GATE_SIGMOID_BOUND = 0, KDA_GATE_SOFTPLUS_CLAMP = 1 };
+
+typedef struct {
+  int32_t n_seqs;          /* N >= 1 packed sequences (empty sequences allowed) */
+  int64_t total_tokens;    /* T = cu_seqlens_host[N] >= 1 */
+  int32_t H, K, V;         /* heads, key dim, value dim; built: K == V in {64, 128} */
+  int32_t chunk;           /* chunk length C in {16, 32, 64}; tiling only, the
+                              result does not depend on it beyond rounding */
+  int32_t dtype;           /* KDA_F32 or KDA_BF16 */
+  int32_t gate_mode;       /* KDA_GATE_SIGMOID_BOUND */
+  float scale;             /* multiplies qh; 1.0 for the plain o_t = S_t^T qh_t */
+  float gate_lower_bound;  /* L < 0, e.g. -5 */
+  float l2_eps;            /* eps of the Q/K L2 normalisation, e.g. 1e-6 */
+  int32_t seg_chunks;      /* backward streaming segment in chunks; 0 = automatic */
+  const int32_t *cu_seqlens_host; /* host copy of cu_seqlens [N+1]: non-decreasing
+                                     from 0 to T; used for planning only */
+} kda_problem;
+
+/* Bytes of device workspace kda_fwd / kda_bwd need for this problem
+   (0 when the problem is invalid or unsupported; call kda_check_problem for
+   the reason). */
+size_t kda_fwd_workspace_bytes(const kda_problem *p);
+size_t kda_bwd_workspace_bytes(const kda_problem *p);
+
+/* Host-side validation only: KDA_OK, KDA_ERR_INVALID or KDA_ERR_UNSUPPORTED. */
+int kda_check_problem(const kda_problem *p);
+
+/* Prologue only (the step that normalises Q/K, applies the beta sigmoid,
+   the bounded gate and its chunk-local cumulative sum), exposed for testing.
+   Outputs, all fp32 and caller-owned: qh, kh [T,H,K]; beta [T,H];
+   gcum [T,H,K] = cumulative sum of g from the start of each chunk (chunks
+   of length p->chunk counted from each sequence start). The workspace holds
+   the chunk table (kda_prologue_workspace_bytes). */
+size_t kda_prologue_workspace_bytes(const kda_problem *p);
+int kda_prologue(const kda_problem *p, const void *q, const void *k,
+                 const void *raw_g, const void *raw_beta, const float *A_log,
+                 const float *dt_bias, const int32_t *cu_seqlens, float *qh,
+                 float *kh, float *beta, float *gcum, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* Forward: writes o [T,H,V] (dtype). Saves nothing for the backward. */
+int kda_fwd(const kda_problem *p, const void *q, const void *k, const void *v,
+            const void *raw_g, const void *raw_beta, const float *A_log,
+            const float *dt_bias, const int32_t *cu_seqlens, void *o,
+            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward: recomputes every intermediate from the inputs, streaming over
+   segments of chunks, and writes dq, dk, draw_g [T,H,K], dv [T,H,V],
+   draw_beta [T,H] (dtype) and dA_log [H], ddt_bias [H,K] (fp32). The
+   gate-parameter gradients are reduced in a fixed order (bitwise
+   reproducible run to run). */
+int kda_bwd(const kda_problem *p, const void *q, const void *k, const void *v,
+            const void *raw_g, const void *raw_beta, const float *A_log,
+            const float *dt_bias, const int32_t *cu_seqlens, const void *dO,
+            void *dq, void *dk, void *dv, void *draw_g, void *draw_beta,
+            float *dA_log, float *ddt_bias, void *workspace,
+            size_t workspace_bytes, void *stream);
+
+/* Optional per-kernel timing, for measurement tools. Between
+   kda_profile_begin() and kda_profile_end(), every kernel the calling thread
+   launches through this library is bracketed by two HIP events recorded on
+   its own stream. kda_profile_end() waits for those events and writes, per
+   kernel kind (index = KDA_KERNEL_*), the number of launches and their
+   summed duration in milliseconds into `launches` / `total_ms` (arrays of
+   `n` entries, caller-owned; n >= KDA_KERNEL_COUNT recommended). Returns
+   KDA_OK or KDA_ERR_HIP. Timing adds two event records per launch. */
+enum {
+  KDA_KERNEL_CHUNK_TABLE = 0,
+  KDA_KERNEL_PROLOGUE = 1,
+  KDA_KERNEL_CHUNK_LOCAL = 2,
+  KDA_KERNEL_SCAN_FWD = 3,
+  KDA_KERNEL_SCAN_BWD = 4,
+  KDA_KERNEL_CHUNK_GRAD = 5,
+  KDA_KERNEL_GATE_REDUCE = 6,
+  KDA_KERNEL_COUNT = 7
+};
+int kda_profile_begin(void);
+int kda_profile_end(int32_t *launches, double *total_ms, int n);
+const char *kda_kernel_name(int kind);
+
+/* Human-readable text for a status code, including the HIP error of the
+   last failed launch on this thread for KDA_ERR_HIP. */
+const char *kda_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

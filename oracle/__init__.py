@@ -26,15 +26,12 @@ GATE_SOFTPLUS_CLAMP = 1  # g = max(L, -exp(A_log) * softplus(raw_g + dt_bias))
 
 
 def build(extra_flags: tuple[str, ...] = (), out_path: str | None = None) -> str:
-    """Compile the oracle with gcc (OpenMP, -O2). Returns the library path.
-
-    ``extra_flags`` lets a test build a deliberately broken variant of the
-    oracle (``-DKDA_ORACLE_MUTANT=n``) into ``out_path``.
-    """
+    """Compile the oracle with gcc (OpenMP, -O3, no host-specific ISA so the
+    library runs on any x86-64 host). Returns the library path."""
     out = out_path or _LIB_PATH
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+    cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
            *extra_flags, "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
@@ -121,4 +118,34 @@ def kda(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, dO=None,
                         int(n_threads))
     if rc != 0:
         raise RuntimeError("kda_oracle failed with status %d" % rc)
+    return out
+
+
+def prologue(q, k, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, chunk: int = 64,
+             scale: float = 1.0, lower_bound: float = -5.0, eps: float = 1e-6,
+             gate_mode: int = GATE_SIGMOID_BOUND) -> dict:
+    """The prologue alone: qh, kh [T,H,K], beta [T,H] and gcum [T,H,K] (the
+    cumulative gate restarted every ``chunk`` tokens of each sequence)."""
+    q, k, raw_g, raw_beta = map(_f64, (q, k, raw_g, raw_beta))
+    A_log, dt_bias = _f64(A_log), _f64(dt_bias)
+    T, H, K = q.shape
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64))
+    out = dict(qh=np.zeros((T, H, K)), kh=np.zeros((T, H, K)), beta=np.zeros((T, H)),
+               gcum=np.zeros((T, H, K)))
+    lib = _load()
+    f = lib.kda_oracle_prologue
+    dp = ctypes.POINTER(ctypes.c_double)
+    f.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_int,
+                  ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                  ctypes.c_int] + [dp] * 10
+    rc = f(len(cu) - 1, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, K, float(scale),
+           float(lower_bound), float(eps), int(gate_mode), int(chunk), _ptr(q), _ptr(k),
+           _ptr(raw_g), _ptr(raw_beta), _ptr(A_log), _ptr(dt_bias), _ptr(out["qh"]),
+           _ptr(out["kh"]), _ptr(out["beta"]), _ptr(out["gcum"]))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_prologue failed")
     return out

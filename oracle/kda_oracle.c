@@ -335,3 +335,39 @@ int kda_oracle(int n_seqs, const int64_t *cu_seqlens, int H, int K, int V,
   free(pb);
   return err;
 }
+
+/* Prologue alone, for checking the prologue step: qh, kh [T,H,K], beta [T,H]
+   and gcum [T,H,K], the cumulative sum of g restarted every `chunk` tokens
+   from each sequence start. Returns 0, or 1 on bad arguments. */
+int kda_oracle_prologue(int n_seqs, const int64_t *cu_seqlens, int H, int K,
+                        double scale, double lower_bound, double eps,
+                        int gate_mode, int chunk, const double *q,
+                        const double *k, const double *raw_g,
+                        const double *raw_beta, const double *A_log,
+                        const double *dt_bias, double *qh, double *kh,
+                        double *beta, double *gcum) {
+  if (n_seqs < 0 || H <= 0 || K <= 0 || chunk <= 0 || !cu_seqlens) return 1;
+  prob_t p = {H, K, 1, scale, lower_bound, eps, gate_mode, q, k, NULL, raw_g,
+              raw_beta, A_log, dt_bias, NULL, NULL, NULL, NULL, NULL, NULL,
+              NULL};
+  double *buf = calloc((size_t)5 * K, sizeof(double));
+  if (!buf) return 1;
+  tok_t w = {0, 0, 0, buf, buf + K, buf + 2 * K, buf + 3 * K, buf + 4 * K};
+  for (int n = 0; n < n_seqs; ++n) {
+    for (int h = 0; h < H; ++h) {
+      for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
+        const size_t th = (size_t)t * H + h;
+        const int64_t j = (t - cu_seqlens[n]) % chunk;
+        prologue(&p, t, h, &w);
+        beta[th] = w.beta;
+        for (int i = 0; i < K; ++i) {
+          qh[th * K + i] = w.qh[i];
+          kh[th * K + i] = w.kh[i];
+          gcum[th * K + i] = (j == 0 ? 0.0 : gcum[(th - H) * K + i]) + w.g[i];
+        }
+      }
+    }
+  }
+  free(buf);
+  return 0;
+}

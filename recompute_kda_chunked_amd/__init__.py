@@ -1,0 +1,9 @@
+"""MI355X (gfx950) Kimi Delta Attention chunked operator with a recompute backward.
+
+The operator runs as hand-written HIP kernels behind the C ABI of
+``include/kda.h`` (``_build/libkda.so``); this package is its Python binding.
+"""
+from .ops import KDAFunction, KdaError, Problem, kda, kda_backward, kda_forward, kda_prologue
+
+__all__ = ["KDAFunction", "KdaError", "Problem", "kda", "kda_backward", "kda_forward",
+           "kda_prologue"]

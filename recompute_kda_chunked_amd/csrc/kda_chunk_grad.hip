@@ -1,0 +1,557 @@
+// Token-parallel gradient kernel: one block per (chunk, head) of a segment,
+// full K and V per block, so every contraction over the value or key
+// dimension finishes on chip and each gradient is written once, in its final
+// dtype (the tensor-lifetime rule the FROST page credits for its memory
+// advantage: no full-sequence fp32 stage buffers, no overlapping old/new
+// gradient arrays; "KDA Memory with Recompute...", sections "What are FP32
+// stage buffers..." and "Why the larger FROST state series still wins").
+//
+// Inputs per chunk: the raw q, k, v, raw gate, raw beta and dO; from the
+// recompute scans the entering state h_n and leaving-state gradient dh'_n,
+// Vn and dVn; from the chunk-local kernel T^T, P, U and -W. Reverse-mode
+// differentiation of the chunk operations (notation of the chunk-local
+// kernel; Kb = beta*kh*e^G, Bv = beta*v, qg = qh*e^G, kg = kh*e^{G_c-G}):
+//   dBv  = T^T dVn          dv   = beta * dBv
+//   dKb  = -dBv h^T          (= T^T dW with dW = -dVn h^T)
+//   dqg  = dO h^T            dkg  = Vn dh'^T
+//   dAqk = tril(dO Vn^T)     dAkk = stril(-dBv U^T - dKb W^T)
+//   dbeta = rowsum(dBv*v) + rowsum(dKb*kh*e^G) + rowsum(dAkk*P)
+// and for each gated product X[r,s] = sum_k a_rk c_sk e^{G_rk - G_sk} with
+// upstream dX ((beta_r dAkk, kh, kh) and (dAqk, qh, kh)):
+//   da_r += sum_s dX[r,s] c_s e^{G_r-G_s},  dc_s += sum_r dX[r,s] a_r e^{G_r-G_s}
+//   dG_r += a_r * (first sum),              dG_s -= c_s * (second sum)
+// plus dqh += dqg e^G, dkh += dkg e^{G_c-G} + beta dKb e^G, the matching dG
+// terms, dG_c += sum_r dkg*kg + gamma * rowsum(h * dh'). dg is the reverse
+// cumulative sum of dG within the chunk; then the prologue is differentiated
+// (L2 normalisation, sigmoid, gate map). Gate-parameter gradients leave as
+// per-chunk partials for a fixed-order reduction.
+#include "kda_prologue.h"
+
+namespace kda {
+
+template <typename OpT>
+__device__ __forceinline__ float frag_at(const typename Mma<OpT>::frag& f, int j);
+template <>
+__device__ __forceinline__ float frag_at<bf16>(const bf16x8& f, int j) { return static_cast<float>(f[j]); }
+template <>
+__device__ __forceinline__ float frag_at<float>(const float& f, int) { return f; }
+
+typedef __attribute__((ext_vector_type(4))) double f64x4;
+
+// Arithmetic of the gated-product VJP and of dG. Each gated pair (r, s)
+// enters dG twice, +X at row r and -X at row s, and only the pairs that span
+// a row survive the reverse cumulative sum; the rest must cancel. For bf16
+// problems the pair products run on bf16 MFMA and both sides use identically
+// rounded operand values, so the cancellation is exact up to fp32
+// accumulation. For fp32 problems (tolerance 1e-5) the products run on fp64
+// MFMA (v_mfma_f64_16x16x4_f64, exact products of fp32 operands) and dG is
+// kept in fp64.
+template <typename OpT>
+struct Vjp;
+template <>
+struct Vjp<bf16> {
+  typedef float T;
+  typedef f32x4 acc;
+  typedef bf16x8 frag;
+  static constexpr int KS = 32, KPL = 8;
+  static __device__ __forceinline__ acc zero() { return zero4(); }
+  static __device__ __forceinline__ acc mma(frag a, frag b, acc c) { return Mma<bf16>::mma(a, b, c); }
+  static __device__ __forceinline__ frag load(const bf16* p) { return Mma<bf16>::load(p); }
+  template <class F>
+  static __device__ __forceinline__ frag make(F f) { return Mma<bf16>::make(f); }
+  static __device__ __forceinline__ T rnd(T x) { return to_f(static_cast<bf16>(x)); }
+  static __device__ __forceinline__ T ex(T x) { return __expf(x); }
+  static __device__ __forceinline__ acc fix(acc x) { return x; }
+};
+template <>
+struct Vjp<float> {
+  typedef double T;
+  typedef f64x4 acc;
+  typedef double frag;
+  static constexpr int KS = 4, KPL = 1;
+  static __device__ __forceinline__ acc zero() { return acc{0.0, 0.0, 0.0, 0.0}; }
+  static __device__ __forceinline__ acc mma(frag a, frag b, acc c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag load(const float* p) { return static_cast<double>(*p); }
+  template <class F>
+  static __device__ __forceinline__ frag make(F f) { return f(0); }
+  static __device__ __forceinline__ T rnd(T x) { return x; }
+  static __device__ __forceinline__ T ex(T x) { return exp(x); }
+  // The f64 16x16 accumulator holds row 4r + g in register r of lane group g;
+  // move it to the common layout (row 4g + r): the value for row 4g + r sits
+  // in lane (i, r), register g.
+  static __device__ __forceinline__ acc fix(acc x) {
+    const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+    acc out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int src = i + 16 * r;
+      const double v0 = __shfl(x[0], src, kWave), v1 = __shfl(x[1], src, kWave);
+      const double v2 = __shfl(x[2], src, kWave), v3 = __shfl(x[3], src, kWave);
+      out[r] = g == 0 ? v0 : (g == 1 ? v1 : (g == 2 ? v2 : v3));
+    }
+    return out;
+  }
+};
+
+template <typename TI, typename OpT, int D, int C>
+__global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI* dO,
+                                                    int seg_begin, ChunkOps ops, SegStates st,
+                                                    TI* dq, TI* dk, TI* dv, TI* dg, TI* dbeta,
+                                                    float* partials) {
+  using M = Mma<OpT>;
+  constexpr int K = D, V = D, NB = C / 16, KPL = M::KPL, KS = M::KS;
+  constexpr int KBW = K / 64;        // key blocks per wave
+  constexpr int LDG = C + 4;         // GT [K][LDG] fp32
+  constexpr int LDQ = C + 8;         // qT, kT [K][LDQ]
+  constexpr int LDA = D + 8;         // [C][LDA] operand buffers
+  constexpr int LDX = C + 8;         // [C][LDX] dX buffers
+  constexpr int SZ1 = 4 * C * LDA * (int)sizeof(OpT), SZ2 = 4 * C * LDX * (int)sizeof(OpT);
+  __shared__ float GT[K * LDG];
+  __shared__ __attribute__((aligned(16))) TI qT[K * LDQ];
+  __shared__ __attribute__((aligned(16))) TI kT[K * LDQ];
+  __shared__ __attribute__((aligned(16))) unsigned char uni[SZ1 > SZ2 ? SZ1 : SZ2];
+  __shared__ float rq[C], rqs[C], rk[C], be[C];
+  __shared__ float dbp[4][C];
+  __shared__ float rowp[2][4][C];
+  __shared__ float ptot[4 * D];
+  __shared__ float red[256];
+
+  OpT* dBv_s = reinterpret_cast<OpT*>(uni);
+  OpT* dO_s = dBv_s + C * LDA;
+  OpT* Vn_s = dO_s + C * LDA;
+  OpT* dKb_s = Vn_s + C * LDA;
+  OpT* dXq = reinterpret_cast<OpT*>(uni);
+  OpT* dXk = dXq + C * LDX;
+  OpT* dXqT = dXk + C * LDX;
+  OpT* dXkT = dXqT + C * LDX;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
+  const int lc = blockIdx.x / d.H, h = blockIdx.x % d.H;
+  const int cglob = seg_begin + lc;
+  const ChunkLoc L = locate<C>(in, d.N, cglob);
+  const size_t idx = static_cast<size_t>(lc) * d.H + h;
+  const size_t ts = static_cast<size_t>(d.H) * D;
+  const size_t hoff = static_cast<size_t>(h) * D;
+  const TI* qr = static_cast<const TI*>(in.q) + L.t0 * ts + hoff;
+  const TI* kr = static_cast<const TI*>(in.k) + L.t0 * ts + hoff;
+  const TI* vr = static_cast<const TI*>(in.v) + L.t0 * ts + hoff;
+
+  // ---- S1: prologue, transposed raw q/k, cumulative gate G^T
+  auto Gf = [&](int r, int kk) -> float& { return GT[kk * LDG + r]; };
+  prologue_rows<TI, D, C, 4>(d, in, h, L, rq, rqs, rk, be, Gf);
+  for (int e = tid; e < C * D; e += 256) {
+    const int r = e / D, kk = e % D;
+    const bool v = r < L.len;
+    qT[kk * LDQ + r] = v ? qr[r * ts + kk] : static_cast<TI>(0.f);
+    kT[kk * LDQ + r] = v ? kr[r * ts + kk] : static_cast<TI>(0.f);
+  }
+  for (int e = tid; e < 4 * C; e += 256) {
+    dbp[e / C][e % C] = 0.f;
+    rowp[0][e / C][e % C] = 0.f;
+    rowp[1][e / C][e % C] = 0.f;
+  }
+  __syncthreads();
+  cumsum_rows<D, C, 256>(Gf, ptot);
+
+  // ---- S2: dBv = T^T dVn (tiles of dBv^T: value rows, chunk-row columns)
+  {
+    const OpT* dVnT = static_cast<const OpT*>(st.dVnT) + idx * V * C;
+    const OpT* TT = static_cast<const OpT*>(ops.TT) + idx * C * C;
+    TI* dvo = dv + L.t0 * ts + hoff;
+    for (int t = w; t < (V / 16) * NB; t += 4) {
+      const int mv = t / NB, nr = t % NB;
+      const int s_lo = (16 * nr) / KS * KS;  // T^T[r][s] = 0 for s < r
+      const f32x4 acc = tile_nt<OpT>(zero4(), dVnT + 16 * mv * C, C, TT + 16 * nr * C, C, s_lo, C, lane);
+      const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
+      OpT* dst = dBv_s + r * LDA + vv;
+      float part = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(acc[rr]);
+      if (r < L.len) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          dvo[r * ts + vv + rr] = from_f<TI>(be[r] * acc[rr]);
+          part += acc[rr] * to_f(vr[r * ts + vv + rr]);
+        }
+      }
+      part = sum_groups(part);
+      if (g == 0) dbp[w][r] += part;
+    }
+  }
+  // ---- S3: dO and Vn tiles into LDS
+  {
+    const TI* dOr = dO + L.t0 * ts + hoff;
+    const OpT* Vn = static_cast<const OpT*>(st.Vn) + idx * C * V;
+    for (int e = tid; e < C * V; e += 256) {
+      const int r = e / V, vv = e % V;
+      dO_s[r * LDA + vv] = r < L.len ? from_f<OpT>(to_f(dOr[r * ts + vv])) : from_f<OpT>(0.f);
+      Vn_s[r * LDA + vv] = Vn[e];
+    }
+  }
+  __syncthreads();
+
+  // ---- S4: products with the states; wave w owns key blocks kb = w + 4*jk
+  using VJ = Vjp<OpT>;
+  using TG = typename VJ::T;
+  static_assert(sizeof(TG) == 4 || sizeof(uni) >= sizeof(double) * K * LDG, "dG buffer");
+  f32x4 aq[KBW][NB], ak[KBW][NB];
+  TG aG[KBW][NB][4];
+#pragma unroll
+  for (int jk = 0; jk < KBW; ++jk)
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+      aq[jk][m] = ak[jk][m] = zero4();
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) aG[jk][m][rr] = 0;
+    }
+  {
+    const OpT* hm = static_cast<const OpT*>(st.h) + idx * K * V;
+    const OpT* dhm = static_cast<const OpT*>(st.dh) + idx * K * V;
+#pragma unroll
+    for (int jk = 0; jk < KBW; ++jk) {
+      const int kb = w + 4 * jk, kk = 16 * kb + i;
+      f32x4 rKb[NB], rQg[NB], rKg[NB];
+#pragma unroll
+      for (int m = 0; m < NB; ++m) rKb[m] = rQg[m] = rKg[m] = zero4();
+      float hdh = 0.f;
+      const OpT* bh = hm + kk * V + g * KPL;
+      const OpT* bdh = dhm + kk * V + g * KPL;
+      for (int v0 = 0; v0 < V; v0 += KS) {
+        const auto fh = M::load(bh + v0);
+        const auto fdh = M::load(bdh + v0);
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) hdh += frag_at<OpT>(fh, j) * frag_at<OpT>(fdh, j);
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+          const int ro = (16 * m + i) * LDA + v0 + g * KPL;
+          rKb[m] = M::mma(M::load(dBv_s + ro), fh, rKb[m]);
+          rQg[m] = M::mma(M::load(dO_s + ro), fh, rQg[m]);
+          rKg[m] = M::mma(M::load(Vn_s + ro), fdh, rKg[m]);
+        }
+      }
+      hdh = sum_groups(hdh);
+      const float Gc = GT[kk * LDG + C - 1];
+      TG colsum = 0;
+#pragma unroll
+      for (int m = 0; m < NB; ++m) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 16 * m + 4 * g + rr;
+          const float Gv = GT[kk * LDG + r];
+          const float eG = kexp<OpT>(Gv), eGc = kexp<OpT>(Gc - Gv);
+          const float qh = to_f(qT[kk * LDQ + r]) * rqs[r];
+          const float kh = to_f(kT[kk * LDQ + r]) * rk[r];
+          const float dqg = rQg[m][rr], dkg = rKg[m][rr], dKb = -rKb[m][rr];
+          const float b = be[r];
+          aq[jk][m][rr] += dqg * eG;
+          ak[jk][m][rr] += dkg * eGc + b * dKb * eG;
+          // -kg*dkg here and +kg*dkg in the G_c row cancel in the reverse
+          // cumulative sum: both use the same product value
+          const TG kgdkg = static_cast<TG>(dkg) * kh * eGc;
+          aG[jk][m][rr] += static_cast<TG>(dqg) * qh * eG - kgdkg + static_cast<TG>(dKb) * b * kh * eG;
+          colsum += kgdkg;
+          dKb_s[r * LDA + kk] = from_f<OpT>(dKb);
+          const float pb = sum16(dKb * kh * eG);
+          if (i == 0) dbp[w][r] += pb;
+        }
+      }
+      colsum += __shfl_xor(colsum, 16, kWave);
+      colsum += __shfl_xor(colsum, 32, kWave);
+      if (g == 3) aG[jk][NB - 1][3] += colsum + static_cast<TG>(kexp<OpT>(Gc)) * hdh;  // row C-1 holds G_c
+    }
+  }
+  __syncthreads();
+
+  // ---- S5: dAqk and dAkk, lower 16x16 blocks (m rows, ns columns)
+  constexpr int NPAIR = NB * (NB + 1) / 2, PPW = (NPAIR + 3) / 4;
+  f32x4 xq[PPW], xk[PPW];
+  {
+    const OpT* Ug = static_cast<const OpT*>(ops.U) + idx * C * V;
+    const OpT* Wng = static_cast<const OpT*>(ops.Wn) + idx * C * K;
+    const OpT* Pg = static_cast<const OpT*>(ops.P) + idx * C * C;
+#pragma unroll
+    for (int jp = 0; jp < PPW; ++jp) {
+      const int p = w + 4 * jp;
+      xq[jp] = xk[jp] = zero4();
+      if (p >= NPAIR) break;
+      int m = 0, ns = p;
+      while (ns > m) { ns -= m + 1; ++m; }
+      const f32x4 aqk = tile_nt<OpT>(zero4(), dO_s + 16 * m * LDA, LDA, Vn_s + 16 * ns * LDA, LDA, 0, V, lane);
+      const f32x4 a1 = tile_nt<OpT>(zero4(), dBv_s + 16 * m * LDA, LDA, Ug + 16 * ns * V, V, 0, V, lane);
+      const f32x4 a2 = tile_nt<OpT>(zero4(), dKb_s + 16 * m * LDA, LDA, Wng + 16 * ns * K, K, 0, K, lane);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = 16 * m + 4 * g + rr, s = 16 * ns + i;
+        xq[jp][rr] = (s <= r) ? aqk[rr] : 0.f;
+        const float dakk = (s < r) ? (a2[rr] - a1[rr]) : 0.f;
+        xk[jp][rr] = be[r] * dakk;
+        const float pb = sum16(dakk * to_f(Pg[r * C + s]));
+        if (i == 0) dbp[w][r] += pb;
+      }
+    }
+  }
+  __syncthreads();  // operand buffers are dead; the dX buffers reuse their space
+  for (int e = tid; e < 4 * C * LDX; e += 256) dXq[e] = from_f<OpT>(0.f);
+  __syncthreads();
+#pragma unroll
+  for (int jp = 0; jp < PPW; ++jp) {
+    const int p = w + 4 * jp;
+    if (p >= NPAIR) break;
+    int m = 0, ns = p;
+    while (ns > m) { ns -= m + 1; ++m; }
+    const int s = 16 * ns + i, r0 = 16 * m + 4 * g;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      dXq[(r0 + rr) * LDX + s] = from_f<OpT>(xq[jp][rr]);
+      dXk[(r0 + rr) * LDX + s] = from_f<OpT>(xk[jp][rr]);
+      dXqT[s * LDX + r0 + rr] = from_f<OpT>(xq[jp][rr]);
+      dXkT[s * LDX + r0 + rr] = from_f<OpT>(xk[jp][rr]);
+    }
+  }
+  __syncthreads();
+
+  // ---- S6: VJP of the gated products
+  // Operands are generated from the raw inputs and G^T. For each block pair
+  // (I, J <= I) the decay exp(G_r - G_s) is split around the first row b of
+  // block I (as in the forward), so every generated factor is finite.
+#pragma unroll
+  for (int jk = 0; jk < KBW; ++jk) {
+    const int kb = w + 4 * jk, kk = 16 * kb + i;
+    const float* Gk = GT + kk * LDG;
+    const TI* qk = qT + kk * LDQ;
+    const TI* kq = kT + kk * LDQ;
+    auto khat = [&](int r) { return static_cast<TG>(to_f(kq[r])) * static_cast<TG>(rk[r]); };
+    auto qhat = [&](int r) { return static_cast<TG>(to_f(qk[r])) * static_cast<TG>(rqs[r]); };
+    auto dec = [&](int r, int s_) { return VJ::ex(static_cast<TG>(Gk[r]) - static_cast<TG>(Gk[s_])); };
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      const int b0 = 16 * I;
+      // row side: rows r of block I, reduction over s < 16(I + 1):
+      //   raw[r] = sum_s dX[r][s] * kh_s exp(G_b - G_s)
+      typename VJ::acc rq_ = VJ::zero(), rk_ = VJ::zero();
+      const int s_hi = 16 * (I + 1);
+      for (int s0 = 0; s0 < (s_hi + VJ::KS - 1) / VJ::KS * VJ::KS; s0 += VJ::KS) {
+        const auto fb = VJ::make([&](int j) {
+          const int s_ = s0 + g * VJ::KPL + j;
+          return s_ < s_hi ? khat(s_) * dec(b0, s_) : TG(0);
+        });
+        const int ao = (16 * I + i) * LDX + s0 + g * VJ::KPL;
+        rq_ = VJ::mma(VJ::load(dXq + ao), fb, rq_);
+        rk_ = VJ::mma(VJ::load(dXk + ao), fb, rk_);
+      }
+      rq_ = VJ::fix(rq_);
+      rk_ = VJ::fix(rk_);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = b0 + 4 * g + rr;
+        const TG f = dec(r, b0);
+        // dG takes the column side's operand values for this pair, rounded as
+        // that side's MFMA operands are (see Vjp)
+        const TG Aq = VJ::rnd(qhat(r) * f), Ak = VJ::rnd(khat(r) * f);
+        aq[jk][I][rr] += static_cast<float>(rq_[rr] * f);
+        ak[jk][I][rr] += static_cast<float>(rk_[rr] * f);
+        aG[jk][I][rr] += Aq * rq_[rr] + Ak * rk_[rr];
+      }
+    }
+    // column side: rows s of block J, reduction over r in blocks I >= J; the
+    // 32-long reduction index u covers (beta*dAkk, kh) for u < 16 and
+    // (dAqk, qh) above:  y[s] = sum_r dX[r][s] * a_r exp(G_r - G_b)
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
+      TG cc[4] = {0, 0, 0, 0}, gs[4] = {0, 0, 0, 0};
+      for (int I = J; I < NB; ++I) {
+        const int b0 = 16 * I;
+        typename VJ::acc y = VJ::zero();
+        for (int u0 = 0; u0 < 32; u0 += VJ::KS) {
+          const int u = u0 + g * VJ::KPL;
+          const OpT* ap = (u < 16 ? dXkT : dXqT) + (16 * J + i) * LDX + b0 + (u & 15);
+          const auto fb = VJ::make([&](int j) {
+            const int uu = u + j, r = b0 + (uu & 15);
+            return (uu < 16 ? khat(r) : qhat(r)) * dec(r, b0);
+          });
+          y = VJ::mma(VJ::load(ap), fb, y);
+        }
+        y = VJ::fix(y);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int s_ = 16 * J + 4 * g + rr;
+          const TG f = dec(b0, s_);
+          cc[rr] += y[rr] * f;
+          gs[rr] += VJ::rnd(khat(s_) * f) * y[rr];  // the row side's B operand value
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        ak[jk][J][rr] += static_cast<float>(cc[rr]);
+        aG[jk][J][rr] -= gs[rr];
+      }
+    }
+  }
+
+  // ---- S7: row reductions for the L2-norm VJP, reverse cumulative sum of dG
+#pragma unroll
+  for (int jk = 0; jk < KBW; ++jk) {
+    const int kk = 16 * (w + 4 * jk) + i;
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = 16 * m + 4 * g + rr;
+        const float pq = sum16(to_f(qT[kk * LDQ + r]) * rq[r] * aq[jk][m][rr]);
+        const float pk = sum16(to_f(kT[kk * LDQ + r]) * rk[r] * ak[jk][m][rr]);
+        if (i == 0) {
+          rowp[0][w][r] += pq;
+          rowp[1][w][r] += pk;
+        }
+      }
+    }
+  }
+  __syncthreads();  // all reads of GT and of the dX buffers are done
+  // dG^T in LDS, in the VJP precision (fp32: the GT buffer; fp64: the
+  // operand region, free now)
+  TG* dGT = sizeof(TG) == 4 ? reinterpret_cast<TG*>(GT) : reinterpret_cast<TG*>(uni);
+#pragma unroll
+  for (int jk = 0; jk < KBW; ++jk) {
+    const int kk = 16 * (w + 4 * jk) + i;
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) dGT[kk * LDG + 16 * m + 4 * g + rr] = aG[jk][m][rr];
+  }
+  __syncthreads();
+  {
+    // reverse inclusive cumulative sum over rows, per channel (fixed order)
+    constexpr int parts = 256 / D, rp = C / parts;
+    __shared__ TG ptg[4 * D];
+    const int col = tid % D, part = tid / D;
+    TG run = 0;
+    for (int j = rp - 1; j >= 0; --j) {
+      const int r = part * rp + j;
+      run += dGT[col * LDG + r];
+      dGT[col * LDG + r] = run;
+    }
+    ptg[part * D + col] = run;
+    __syncthreads();
+    TG off = 0;
+    for (int p = part + 1; p < parts; ++p) off += ptg[p * D + col];
+    for (int j = 0; j < rp; ++j) dGT[col * LDG + part * rp + j] += off;
+    __syncthreads();
+  }
+
+  // ---- S8: prologue VJP and outputs
+  {
+    TI* dqo = dq + L.t0 * ts + hoff;
+    TI* dko = dk + L.t0 * ts + hoff;
+#pragma unroll
+    for (int jk = 0; jk < KBW; ++jk) {
+      const int kk = 16 * (w + 4 * jk) + i;
+#pragma unroll
+      for (int m = 0; m < NB; ++m) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 16 * m + 4 * g + rr;
+          if (r < L.len) {
+            const float qd = rowp[0][0][r] + rowp[0][1][r] + rowp[0][2][r] + rowp[0][3][r];
+            const float kd = rowp[1][0][r] + rowp[1][1][r] + rowp[1][2][r] + rowp[1][3][r];
+            const float qbar = to_f(qT[kk * LDQ + r]) * rq[r];
+            const float khat = to_f(kT[kk * LDQ + r]) * rk[r];
+            dqo[r * ts + kk] = from_f<TI>(rqs[r] * (aq[jk][m][rr] - qbar * qd));
+            dko[r * ts + kk] = from_f<TI>(rk[r] * (ak[jk][m][rr] - khat * kd));
+          }
+        }
+      }
+    }
+    const float ea = expf(in.A_log[h]);
+    const float* db = in.dt_bias + hoff;
+    const TI* xr = static_cast<const TI*>(in.g) + L.t0 * ts + hoff;
+    TI* dgo = dg + L.t0 * ts + hoff;
+    float pdt = 0.f, pA = 0.f;
+    for (int e = tid; e < C * D; e += 256) {
+      const int r = e / D, kk = e % D;
+      if (r < L.len) {
+        const float z = ea * (to_f(xr[r * ts + kk]) + db[kk]);
+        const float sz = sigmoidf(z);
+        const float dz = static_cast<float>(dGT[kk * LDG + r]) * d.lb * sz * (1.f - sz);
+        const float dx = dz * ea;
+        dgo[r * ts + kk] = from_f<TI>(dx);
+        pdt += dx;
+        pA += dz * z;
+      }
+    }
+    // tid % D is this thread's channel for every e above
+    ptot[(tid / D) * D + tid % D] = pdt;
+    red[tid] = pA;
+    for (int r = tid; r < L.len; r += 256) {
+      const float db_ = dbp[0][r] + dbp[1][r] + dbp[2][r] + dbp[3][r];
+      dbeta[(L.t0 + r) * d.H + h] = from_f<TI>(db_ * be[r] * (1.f - be[r]));
+    }
+    __syncthreads();
+    float* part = partials + (static_cast<size_t>(cglob) * d.H + h) * (K + 1);
+    if (tid < D) {
+      float s = 0.f;
+      for (int p = 0; p < 256 / D; ++p) s += ptot[p * D + tid];
+      part[tid] = s;
+    }
+    if (tid == 0) {
+      float s = 0.f;
+      for (int j = 0; j < 256; ++j) s += red[j];
+      part[K] = s;
+    }
+  }
+}
+
+template <typename TI, int D, int C>
+static hipError_t launch_cg(const Dims& d, const Inputs& in, const void* dO, int seg_begin,
+                            int seg_chunks, const ChunkOps& ops, const SegStates& st, void* dq,
+                            void* dk, void* dv, void* dg, void* dbeta, float* partials,
+                            hipStream_t s) {
+  hipLaunchKernelGGL((k_chunk_grad<TI, TI, D, C>), dim3(seg_chunks * d.H), dim3(256), 0, s, d,
+                     in, static_cast<const TI*>(dO), seg_begin, ops, st, static_cast<TI*>(dq),
+                     static_cast<TI*>(dk), static_cast<TI*>(dv), static_cast<TI*>(dg),
+                     static_cast<TI*>(dbeta), partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_grad(int dtype, int D, int C, const Dims& d, const Inputs& in,
+                             const void* dO, int seg_begin, int seg_chunks,
+                             const ChunkOps& ops, const SegStates& st, void* dq, void* dk,
+                             void* dv, void* dg, void* dbeta, float* partials,
+                             hipStream_t s) {
+#define KDA_CG(TI, DD, CC)                                                                  \
+  if (D == DD && C == CC)                                                                   \
+    return launch_cg<TI, DD, CC>(d, in, dO, seg_begin, seg_chunks, ops, st, dq, dk, dv, dg, \
+                                 dbeta, partials, s);
+  if (dtype == 0) {
+    KDA_CG(float, 64, 16) KDA_CG(float, 64, 32) KDA_CG(float, 64, 64)
+    KDA_CG(float, 128, 16) KDA_CG(float, 128, 32)
+  } else {
+    KDA_CG(bf16, 64, 32) KDA_CG(bf16, 64, 64) KDA_CG(bf16, 128, 32) KDA_CG(bf16, 128, 64)
+  }
+#undef KDA_CG
+  return hipErrorInvalidValue;
+}
+
+// dA_log[h] and ddt_bias[h, :] from per-chunk partials, summed over chunks in
+// increasing order (bitwise reproducible).
+__global__ void __launch_bounds__(256) k_gate_reduce(int D, int H, int n_chunks,
+                                                     const float* partials, float* dA_log,
+                                                     float* ddt_bias) {
+  const int h = blockIdx.x;
+  for (int k = threadIdx.x; k <= D; k += blockDim.x) {
+    float s = 0.f;
+    for (int c = 0; c < n_chunks; ++c) s += partials[(static_cast<size_t>(c) * H + h) * (D + 1) + k];
+    if (k < D) ddt_bias[static_cast<size_t>(h) * D + k] = s;
+    else dA_log[h] = s;
+  }
+}
+
+hipError_t launch_gate_reduce(int D, int H, int n_chunks, const float* partials,
+                              float* dA_log, float* ddt_bias, hipStream_t s) {
+  hipLaunchKernelGGL(k_gate_reduce, dim3(H), dim3(256), 0, s, D, H, n_chunks, partials, dA_log,
+                     ddt_bias);
+  return hipGetLastError();
+}
+
+}  // namespace kda

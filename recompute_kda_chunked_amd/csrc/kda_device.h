@@ -1,0 +1,130 @@
+// Device helpers for the gfx950 KDA kernels: element conversion, 64-lane
+// wavefront reductions and 16x16 MFMA tile products.
+//
+// Tile convention used by every kernel: a 16x16 output tile Y is held by one
+// wavefront as an f32x4 per lane; lane l = 16*g + i holds Y[4*g + r][i] for
+// r = 0..3 (the CDNA 16x16 accumulator layout). Products are written "NT":
+//   Y[m][n] = sum_kk A[m][kk] * B[n][kk]
+// with both operands stored kk-contiguous, so each lane reads its k-slots
+// (8 consecutive bf16, or 1 fp32) with one vector load.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return static_cast<float>(x); }
+
+template <typename T>
+__device__ __forceinline__ T from_f(float x);
+template <>
+__device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f<bf16>(float x) { return static_cast<bf16>(x); }
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+// Sum over the 16 lanes that share g (the lanes of one tile row group).
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+// Sum over the four lane groups g (lanes i, i+16, i+32, i+48).
+__device__ __forceinline__ float sum_groups(float x) {
+  x += __shfl_xor(x, 16, kWave);
+  x += __shfl_xor(x, 32, kWave);
+  return x;
+}
+
+__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// ---------------------------------------------------------------- MFMA traits
+
+template <typename OpT>
+struct Mma;
+
+// bf16 operands, fp32 accumulate: v_mfma_f32_16x16x32_bf16 (gfx950).
+// Lane (i, g) supplies k-slots 8g..8g+7 of row i for A and of column i for B.
+template <>
+struct Mma<bf16> {
+  static constexpr int KS = 32;  // reduction length per instruction
+  static constexpr int KPL = 8;  // k-slots per lane
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag load(const bf16* p) {
+    return *reinterpret_cast<const frag*>(p);
+  }
+  template <class F>
+  static __device__ __forceinline__ frag make(F f) {
+    frag r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = static_cast<bf16>(f(j));
+    return r;
+  }
+};
+
+// fp32 operands: v_mfma_f32_16x16x4_f32. Lane (i, g) supplies k-slot g.
+template <>
+struct Mma<float> {
+  static constexpr int KS = 4;
+  static constexpr int KPL = 1;
+  typedef float frag;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag load(const float* p) { return *p; }
+  template <class F>
+  static __device__ __forceinline__ frag make(F f) { return f(0); }
+};
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// acc += sum_{kk in [k_lo, k_hi)} A[i][kk] * B[i'][kk] for one 16x16 tile.
+// A and B point at the first row of the tile; lda/ldb are row strides in
+// elements. k_lo and k_hi - k_lo are multiples of Mma<OpT>::KS.
+template <typename OpT>
+__device__ __forceinline__ f32x4 tile_nt(f32x4 acc, const OpT* A, int lda, const OpT* B,
+                                         int ldb, int k_lo, int k_hi, int lane) {
+  using M = Mma<OpT>;
+  const int i = lane & 15, g = lane >> 4;
+  const OpT* a = A + i * lda + g * M::KPL;
+  const OpT* b = B + i * ldb + g * M::KPL;
+  for (int k0 = k_lo; k0 < k_hi; k0 += M::KS) acc = M::mma(M::load(a + k0), M::load(b + k0), acc);
+  return acc;
+}
+
+// Round a reduction bound up to the instruction's reduction length.
+template <typename OpT>
+__device__ __forceinline__ constexpr int kround(int x) {
+  return (x + Mma<OpT>::KS - 1) / Mma<OpT>::KS * Mma<OpT>::KS;
+}
+
+// Sequence lookup: the sequence n containing global chunk c (coff[n] <= c <
+// coff[n+1]); empty sequences have coff[n] == coff[n+1] and are skipped.
+__device__ __forceinline__ int find_seq(const int32_t* coff, int N, int c) {
+  int lo = 0, hi = N;  // answer in [0, N)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (coff[mid] <= c) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace kda

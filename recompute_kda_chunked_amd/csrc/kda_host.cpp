@@ -1,0 +1,405 @@
+// Host side of the C ABI declared in include/kda.h: validation, planning of
+// chunks and streaming segments, workspace carving and kernel launches.
+//
+// Recompute policy ("KDA Memory with Recompute: FLA vs cuDNN Frontend
+// FROST", sections "Both sides really use recomputation" and "Takeaway"):
+// the forward keeps nothing for the backward. The backward rebuilds every
+// intermediate from the inputs, one segment of chunks at a time, from the
+// last segment to the first, so the workspace is bounded by the segment size
+// rather than by the sequence length:
+//   checkpoint pass  chunk-local + state scan over segments 0..S-2, keeping
+//                    only the state that enters each segment
+//   per segment      chunk-local (recompute w, u, qg, kg, Aqk, T)
+//                    state scan from the segment's checkpoint (records h, Vn)
+//                    reverse state-gradient scan (records dh', dVn)
+//                    token-parallel gradients (final dtype, written once)
+//   finally          fixed-order reduction of the gate-parameter partials
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+using namespace kda;
+
+namespace {
+
+thread_local char g_msg[256];
+
+bool supported(int dtype, int D, int C) {
+  if (dtype == KDA_F32)
+    return (D == 64 && (C == 16 || C == 32 || C == 64)) || (D == 128 && (C == 16 || C == 32));
+  if (dtype == KDA_BF16) return (D == 64 || D == 128) && (C == 32 || C == 64);
+  return false;
+}
+
+int check_problem(const kda_problem* p) {
+  if (!p || !p->cu_seqlens_host) return KDA_ERR_INVALID;
+  if (p->n_seqs < 1 || p->H < 1 || p->K < 1 || p->V < 1 || p->total_tokens < 1)
+    return KDA_ERR_INVALID;
+  if (p->total_tokens > 0x7fffffffLL) return KDA_ERR_INVALID;
+  const int32_t* cu = p->cu_seqlens_host;
+  if (cu[0] != 0) return KDA_ERR_INVALID;
+  for (int n = 0; n < p->n_seqs; ++n)
+    if (cu[n + 1] < cu[n]) return KDA_ERR_INVALID;
+  if (cu[p->n_seqs] != p->total_tokens) return KDA_ERR_INVALID;
+  if (!(p->gate_lower_bound < 0.f) || !std::isfinite(p->gate_lower_bound)) return KDA_ERR_INVALID;
+  if (!(p->l2_eps >= 0.f) || !std::isfinite(p->l2_eps) || !std::isfinite(p->scale))
+    return KDA_ERR_INVALID;
+  if (p->seg_chunks < 0 || p->chunk < 1) return KDA_ERR_INVALID;
+  if (p->dtype != KDA_F32 && p->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (p->gate_mode != KDA_GATE_SIGMOID_BOUND) return KDA_ERR_UNSUPPORTED;
+  if (p->K != p->V) return KDA_ERR_UNSUPPORTED;
+  if (!supported(p->dtype, p->K, p->chunk)) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int N, H, D, C, dtype;
+  int64_t T;
+  int NC;        // chunks over all sequences
+  int seg, NS;   // chunks per segment, number of segments
+  size_t esz;    // operand element size
+};
+
+size_t fwd_ops_per(const Plan& P) {  // bytes per (chunk, head), forward operands
+  const size_t C = P.C, K = P.D;
+  return (4 * C * K + C * C) * P.esz + K * 4;
+}
+size_t bwd_ops_per(const Plan& P) {  // backward operands + recorded states
+  const size_t C = P.C, K = P.D;
+  return (6 * C * K + 3 * C * C) * P.esz + K * 4 + (2 * K * K + 2 * C * K) * P.esz;
+}
+
+size_t budget_bytes() {
+  const char* e = std::getenv("KDA_WS_BUDGET_MB");
+  long mb = e ? std::atol(e) : 1024;
+  if (mb < 1) mb = 1;
+  return static_cast<size_t>(mb) << 20;
+}
+
+Plan make_plan(const kda_problem* p, bool bwd) {
+  Plan P{};
+  P.N = p->n_seqs;
+  P.H = p->H;
+  P.D = p->K;
+  P.C = p->chunk;
+  P.dtype = p->dtype;
+  P.T = p->total_tokens;
+  P.esz = p->dtype == KDA_BF16 ? 2 : 4;
+  int64_t nc = 0;
+  for (int n = 0; n < P.N; ++n)
+    nc += (p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n] + P.C - 1) / P.C;
+  P.NC = static_cast<int>(nc);
+  const size_t per = (bwd ? bwd_ops_per(P) : fwd_ops_per(P)) * P.H;
+  int seg = p->seg_chunks;
+  if (seg <= 0) {
+    const size_t fit = budget_bytes() / per;
+    seg = static_cast<int>(fit < 1 ? 1 : (fit > static_cast<size_t>(P.NC) ? P.NC : fit));
+  }
+  if (seg > P.NC) seg = P.NC;
+  if (seg < 1) seg = 1;
+  P.seg = seg;
+  P.NS = (P.NC + seg - 1) / seg;
+  return P;
+}
+
+// Carve a ChunkOps (forward or backward layout) for `seg` chunks from *cur.
+ChunkOps carve_ops(const Plan& P, bool bwd, unsigned char*& cur) {
+  const size_t n = static_cast<size_t>(P.seg) * P.H;
+  const size_t C = P.C, K = P.D, e = P.esz;
+  ChunkOps o{};
+  auto take = [&](size_t bytes) { void* r = cur; cur += up(bytes); return r; };
+  o.Wn = take(n * C * K * e);
+  o.kgT = take(n * K * C * e);
+  o.gam = static_cast<float*>(take(n * K * 4));
+  if (!bwd) {
+    o.UT = take(n * K * C * e);
+    o.qg = take(n * C * K * e);
+    o.Aqk = take(n * C * C * e);
+  } else {
+    o.AqkT = take(n * C * C * e);
+    o.kg = take(n * C * K * e);
+    o.qgT = take(n * K * C * e);
+    o.WnT = take(n * K * C * e);
+    o.U = take(n * C * K * e);
+    o.TT = take(n * C * C * e);
+    o.P = take(n * C * C * e);
+  }
+  return o;
+}
+
+size_t ops_bytes(const Plan& P, bool bwd) {
+  unsigned char* cur = nullptr;
+  carve_ops(P, bwd, cur);
+  return reinterpret_cast<size_t>(cur);
+}
+
+size_t states_bytes(const Plan& P) {
+  const size_t n = static_cast<size_t>(P.seg) * P.H, C = P.C, K = P.D, e = P.esz;
+  return up(n * K * K * e) * 2 + up(n * C * K * e) * 2;
+}
+
+size_t state_slot(const Plan& P) { return up(static_cast<size_t>(P.H) * P.D * P.D * 4); }
+
+size_t fwd_bytes(const Plan& P) {
+  return up((P.N + 1) * 4) + 2 * state_slot(P) + ops_bytes(P, false);
+}
+
+size_t bwd_bytes(const Plan& P) {
+  const size_t ops = ops_bytes(P, true) > ops_bytes(P, false) ? ops_bytes(P, true) : ops_bytes(P, false);
+  return up((P.N + 1) * 4) + up(static_cast<size_t>(P.NC) * P.H * (P.D + 1) * 4) +
+         static_cast<size_t>(P.NS + 1) * state_slot(P) + 2 * state_slot(P) + ops + states_bytes(P);
+}
+
+int hip_fail(hipError_t e) {
+  std::snprintf(g_msg, sizeof g_msg, "HIP launch failed: %s", hipGetErrorString(e));
+  return KDA_ERR_HIP;
+}
+
+// Per-kernel timing (kda_profile_begin / kda_profile_end): event pairs
+// recorded on the launch stream around each launch of the calling thread.
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+thread_local bool g_prof_on = false;
+thread_local std::vector<ProfRec> g_prof;
+
+struct ProfScope {
+  int kind;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  ProfScope(int k, hipStream_t st) : kind(k), s(st) {
+    if (g_prof_on && hipEventCreate(&a) == hipSuccess) hipEventRecord(a, s);
+  }
+  void done() {
+    if (!a) return;
+    hipEvent_t b = nullptr;
+    if (hipEventCreate(&b) == hipSuccess) {
+      hipEventRecord(b, s);
+      g_prof.push_back({kind, a, b});
+    } else {
+      hipEventDestroy(a);
+    }
+    a = nullptr;
+  }
+};
+
+#define KDA_TRY(kind, expr)                    \
+  do {                                         \
+    ProfScope ps_(kind, s);                    \
+    const hipError_t e_ = (expr);              \
+    ps_.done();                                \
+    if (e_ != hipSuccess) return hip_fail(e_); \
+  } while (0)
+
+Dims make_dims(const kda_problem* p) {
+  Dims d;
+  d.N = p->n_seqs;
+  d.H = p->H;
+  d.scale = p->scale;
+  d.lb = p->gate_lower_bound;
+  d.eps = p->l2_eps;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_check_problem(const kda_problem* p) { return check_problem(p); }
+
+size_t kda_fwd_workspace_bytes(const kda_problem* p) {
+  if (check_problem(p) != KDA_OK) return 0;
+  return fwd_bytes(make_plan(p, false));
+}
+
+size_t kda_bwd_workspace_bytes(const kda_problem* p) {
+  if (check_problem(p) != KDA_OK) return 0;
+  return bwd_bytes(make_plan(p, true));
+}
+
+size_t kda_prologue_workspace_bytes(const kda_problem* p) {
+  if (check_problem(p) != KDA_OK) return 0;
+  return up((p->n_seqs + 1) * 4);
+}
+
+int kda_prologue(const kda_problem* p, const void* q, const void* k, const void* raw_g,
+                 const void* raw_beta, const float* A_log, const float* dt_bias,
+                 const int32_t* cu_seqlens, float* qh, float* kh, float* beta, float* gcum,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_problem(p);
+  if (st != KDA_OK) return st;
+  if (!q || !k || !raw_g || !raw_beta || !A_log || !dt_bias || !cu_seqlens || !qh || !kh ||
+      !beta || !gcum || !workspace)
+    return KDA_ERR_INVALID;
+  if (workspace_bytes < kda_prologue_workspace_bytes(p)) return KDA_ERR_WORKSPACE;
+  const Plan P = make_plan(p, false);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* coff = static_cast<int32_t*>(workspace);
+  Inputs in{q, k, nullptr, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, coff};
+  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
+  if (P.NC > 0)
+    KDA_TRY(KDA_KERNEL_PROLOGUE, launch_prologue(P.dtype, P.D, P.C, make_dims(p), in, P.NC, qh, kh, beta, gcum, s));
+  return KDA_OK;
+}
+
+int kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
+            const void* raw_g, const void* raw_beta, const float* A_log, const float* dt_bias,
+            const int32_t* cu_seqlens, void* o, void* workspace, size_t workspace_bytes,
+            void* stream) {
+  const int st = check_problem(p);
+  if (st != KDA_OK) return st;
+  if (!q || !k || !v || !raw_g || !raw_beta || !A_log || !dt_bias || !cu_seqlens || !o ||
+      !workspace)
+    return KDA_ERR_INVALID;
+  const Plan P = make_plan(p, false);
+  if (workspace_bytes < fwd_bytes(P)) return KDA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* cur = static_cast<unsigned char*>(workspace);
+  int32_t* coff = reinterpret_cast<int32_t*>(cur);
+  cur += up((P.N + 1) * 4);
+  float* carry[2];
+  carry[0] = reinterpret_cast<float*>(cur);
+  cur += state_slot(P);
+  carry[1] = reinterpret_cast<float*>(cur);
+  cur += state_slot(P);
+  const ChunkOps ops = carve_ops(P, false, cur);
+  const Dims d = make_dims(p);
+  const Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, coff};
+  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
+  for (int sg = 0; sg < P.NS; ++sg) {
+    const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, launch_chunk_local(P.dtype, P.D, P.C, false, d, in, c0, c1 - c0, ops, s));
+    KDA_TRY(KDA_KERNEL_SCAN_FWD, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops, o, nullptr, carry[sg & 1],
+                            carry[(sg + 1) & 1], s));
+  }
+  return KDA_OK;
+}
+
+int kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
+            const void* raw_g, const void* raw_beta, const float* A_log, const float* dt_bias,
+            const int32_t* cu_seqlens, const void* dO, void* dq, void* dk, void* dv,
+            void* draw_g, void* draw_beta, float* dA_log, float* ddt_bias, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  const int st = check_problem(p);
+  if (st != KDA_OK) return st;
+  if (!q || !k || !v || !raw_g || !raw_beta || !A_log || !dt_bias || !cu_seqlens || !dO ||
+      !dq || !dk || !dv || !draw_g || !draw_beta || !dA_log || !ddt_bias || !workspace)
+    return KDA_ERR_INVALID;
+  const Plan P = make_plan(p, true);
+  if (workspace_bytes < bwd_bytes(P)) return KDA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* cur = static_cast<unsigned char*>(workspace);
+  int32_t* coff = reinterpret_cast<int32_t*>(cur);
+  cur += up((P.N + 1) * 4);
+  float* partials = reinterpret_cast<float*>(cur);
+  cur += up(static_cast<size_t>(P.NC) * P.H * (P.D + 1) * 4);
+  float* ckpt = reinterpret_cast<float*>(cur);  // NS + 1 slots
+  const size_t slot = state_slot(P) / 4;
+  cur += static_cast<size_t>(P.NS + 1) * state_slot(P);
+  float* dcarry[2];
+  dcarry[0] = reinterpret_cast<float*>(cur);
+  cur += state_slot(P);
+  dcarry[1] = reinterpret_cast<float*>(cur);
+  cur += state_slot(P);
+  unsigned char* ops_base = cur;
+  unsigned char* c2 = ops_base;
+  const ChunkOps ops_b = carve_ops(P, true, c2);
+  unsigned char* c3 = ops_base;
+  const ChunkOps ops_f = carve_ops(P, false, c3);  // overlays ops_b (checkpoint pass only)
+  cur = ops_base + (ops_bytes(P, true) > ops_bytes(P, false) ? ops_bytes(P, true) : ops_bytes(P, false));
+  SegStates sts{};
+  {
+    const size_t n = static_cast<size_t>(P.seg) * P.H, C = P.C, K = P.D, e = P.esz;
+    sts.h = cur;
+    cur += up(n * K * K * e);
+    sts.dh = cur;
+    cur += up(n * K * K * e);
+    sts.Vn = cur;
+    cur += up(n * C * K * e);
+    sts.dVnT = cur;
+    cur += up(n * C * K * e);
+  }
+  const Dims d = make_dims(p);
+  const Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, coff};
+  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
+  // checkpoint pass: the state entering each segment
+  for (int sg = 0; sg + 1 < P.NS; ++sg) {
+    const int c0 = sg * P.seg, c1 = c0 + P.seg;
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, launch_chunk_local(P.dtype, P.D, P.C, false, d, in, c0, c1 - c0, ops_f, s));
+    KDA_TRY(KDA_KERNEL_SCAN_FWD, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_f, nullptr, nullptr,
+                            ckpt + sg * slot, ckpt + (sg + 1) * slot, s));
+  }
+  for (int sg = P.NS - 1; sg >= 0; --sg) {
+    const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, launch_chunk_local(P.dtype, P.D, P.C, true, d, in, c0, c1 - c0, ops_b, s));
+    KDA_TRY(KDA_KERNEL_SCAN_FWD, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_b, nullptr, &sts,
+                            ckpt + sg * slot, ckpt + (sg + 1) * slot, s));
+    KDA_TRY(KDA_KERNEL_SCAN_BWD, launch_scan_bwd(P.dtype, P.D, P.C, d, in, dO, c0, c1, ops_b, sts,
+                            dcarry[(sg + 1) & 1], dcarry[sg & 1], s));
+    KDA_TRY(KDA_KERNEL_CHUNK_GRAD, launch_chunk_grad(P.dtype, P.D, P.C, d, in, dO, c0, c1 - c0, ops_b, sts, dq, dk, dv,
+                              draw_g, draw_beta, partials, s));
+  }
+  KDA_TRY(KDA_KERNEL_GATE_REDUCE, launch_gate_reduce(P.D, P.H, P.NC, partials, dA_log, ddt_bias, s));
+  return KDA_OK;
+}
+
+int kda_profile_begin(void) {
+  for (auto& r : g_prof) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+  g_prof_on = true;
+  return KDA_OK;
+}
+
+int kda_profile_end(int32_t* launches, double* total_ms, int n) {
+  g_prof_on = false;
+  for (int k = 0; k < n; ++k) {
+    if (launches) launches[k] = 0;
+    if (total_ms) total_ms[k] = 0.0;
+  }
+  int st = KDA_OK;
+  for (auto& r : g_prof) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      st = KDA_ERR_HIP;
+    if (r.kind >= 0 && r.kind < n) {
+      if (launches) launches[r.kind] += 1;
+      if (total_ms) total_ms[r.kind] += ms;
+    }
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+  return st;
+}
+
+const char* kda_kernel_name(int kind) {
+  static const char* names[KDA_KERNEL_COUNT] = {"chunk_table", "prologue", "chunk_local",
+                                                "scan_fwd", "scan_bwd", "chunk_grad",
+                                                "gate_reduce"};
+  return (kind >= 0 && kind < KDA_KERNEL_COUNT) ? names[kind] : "unknown";
+}
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported K/V/chunk/dtype/gate combination";
+    case KDA_ERR_WORKSPACE: return "workspace too small";
+    case KDA_ERR_HIP: return g_msg[0] ? g_msg : "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Internal interface between the host orchestration (kda_host.cpp) and the
+// kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Problem-wide constants every kernel needs.
+struct Dims {
+  int N, H;
+  float scale, lb, eps;
+};
+
+// Raw operator inputs (device pointers, dtype per the problem).
+struct Inputs {
+  const void *q, *k, *v, *g, *beta;
+  const float *A_log, *dt_bias;
+  const int32_t *cu;    // cu_seqlens [N+1]
+  const int32_t *coff;  // chunk offsets [N+1]
+};
+
+// Per-(chunk, head) operands produced by the chunk-local kernel for one
+// segment; element (lc, h) of each array is at index lc * H + h where lc is
+// the chunk index relative to the segment start. Operand element type is
+// bf16 for bf16 problems and fp32 for fp32 problems.
+struct ChunkOps {
+  void *Wn;    // [C][K]  -W  (W = T (beta * kh * e^G))
+  void *UT;    // [V][C]  U^T (U = T (beta * v))
+  void *qg;    // [C][K]  qh * e^G                       (forward only)
+  void *kgT;   // [K][C]  (kh * e^{G_c - G})^T
+  void *Aqk;   // [C][C]  gated q.k, lower incl. diagonal (forward only)
+  float *gam;  // [K]     e^{G_c}
+  // backward extras
+  void *AqkT;  // [C][C]
+  void *kg;    // [C][K]
+  void *qgT;   // [K][C]
+  void *WnT;   // [K][C]
+  void *U;     // [C][V]
+  void *TT;    // [C][C]  T^T
+  void *P;     // [C][C]  gated k.k without beta, strictly lower
+};
+
+// States recorded by the backward scans for one segment, element (lc, h) at
+// lc * H + h: entering state h_n and leaving-state gradient dh'_n as [K][V],
+// Vn as [C][V], dVn^T as [V][C] (operand element type).
+struct SegStates {
+  void *h, *dh, *Vn, *dVnT;
+};
+
+// Launchers (defined next to their kernels). Each returns hipSuccess or the
+// launch error. `dtype` is 0 (fp32) or 1 (bf16); D = K = V; C = chunk.
+hipError_t launch_chunk_table(const int32_t* cu, int N, int C, int32_t* coff, hipStream_t s);
+hipError_t launch_prologue(int dtype, int D, int C, const Dims& d, const Inputs& in,
+                           int64_t n_chunks, float* qh, float* kh, float* beta, float* gcum,
+                           hipStream_t s);
+hipError_t launch_chunk_local(int dtype, int D, int C, bool bwd, const Dims& d,
+                              const Inputs& in, int seg_begin, int seg_chunks,
+                              const ChunkOps& ops, hipStream_t s);
+// Forward-direction scan over one segment. out_o != nullptr writes O;
+// st != nullptr records h and Vn for the backward. carry_in/out: fp32
+// [H][K][V] state of the sequence crossing the segment boundaries.
+hipError_t launch_scan_fwd(int dtype, int D, int C, const Dims& d, const Inputs& in,
+                           int seg_begin, int seg_end, const ChunkOps& ops, void* out_o,
+                           const SegStates* st, const float* carry_in, float* carry_out,
+                           hipStream_t s);
+// Reverse (state-gradient) scan over one segment; records dh' and dVn^T.
+hipError_t launch_scan_bwd(int dtype, int D, int C, const Dims& d, const Inputs& in,
+                           const void* dO, int seg_begin, int seg_end, const ChunkOps& ops,
+                           const SegStates& st, const float* carry_in, float* carry_out,
+                           hipStream_t s);
+// Token-parallel gradients for one segment; writes dq, dk, dv, draw_g,
+// draw_beta for its tokens and gate-parameter partials [chunk][H][K+1].
+hipError_t launch_chunk_grad(int dtype, int D, int C, const Dims& d, const Inputs& in,
+                             const void* dO, int seg_begin, int seg_chunks,
+                             const ChunkOps& ops, const SegStates& st, void* dq, void* dk,
+                             void* dv, void* dg, void* dbeta, float* partials,
+                             hipStream_t s);
+hipError_t launch_gate_reduce(int D, int H, int n_chunks, const float* partials,
+                              float* dA_log, float* ddt_bias, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,141 @@
+// Prologue of the KDA operator for one chunk of one head, shared by the
+// chunk-local, gradient and standalone prologue kernels.
+//
+// Follows the input description of "KDA Memory with Recompute: FLA vs cuDNN
+// Frontend FROST" (section "Sources and measurement configuration"): Q/K L2
+// normalisation inside the operator, beta = sigmoid(raw beta), a gate bounded
+// below by L and driven by FP32 A_log / dt_bias. The gate map is
+//   g = L * sigmoid(exp(A_log[h]) * (raw_g + dt_bias[h,:]))
+// (a smooth map onto (L, 0); the pages do not print the formula). The
+// chunk-local cumulative sum of g is taken in fp32, as the FLA forward keeps
+// its gate cumulative sum (FROST page, "Where FLA's memory goes").
+#pragma once
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <typename OpT>
+__device__ __forceinline__ float kexp(float x);
+// fp32 problems use the accurate exponential; bf16 problems the hardware
+// base-2 exponential (v_exp_f32) with a change of base.
+template <>
+__device__ __forceinline__ float kexp<float>(float x) { return expf(x); }
+template <>
+__device__ __forceinline__ float kexp<bf16>(float x) { return __expf(x); }
+
+// Location of chunk c (global index) of a packed batch.
+struct ChunkLoc {
+  int n;       // sequence
+  int64_t t0;  // first token
+  int len;     // valid rows (1..C)
+  bool first;  // first chunk of its sequence
+  bool last;   // last chunk of its sequence
+};
+
+template <int C>
+__device__ __forceinline__ ChunkLoc locate(const Inputs& in, int N, int c) {
+  ChunkLoc L;
+  L.n = find_seq(in.coff, N, c);
+  const int j = c - in.coff[L.n];
+  L.t0 = static_cast<int64_t>(in.cu[L.n]) + static_cast<int64_t>(j) * C;
+  const int64_t rem = static_cast<int64_t>(in.cu[L.n + 1]) - L.t0;
+  L.len = rem < C ? static_cast<int>(rem) : C;
+  L.first = (j == 0);
+  L.last = (c == in.coff[L.n + 1] - 1);
+  return L;
+}
+
+// Row part of the prologue. Every wave takes rows r = w, w + NW, ...; for each
+// row it writes the per-row scalars and the gate value of each channel to
+// G(r, k) (a functor returning a float reference into LDS). Rows r >= len are
+// padding: q = k = 0, beta = 0, g = 0, so they contribute nothing anywhere.
+//   rq[r]  = 1/sqrt(|q|^2 + eps)  (so qbar = q * rq)
+//   rqs[r] = scale * rq           (so qh = q * rqs)
+//   rk[r]  = 1/sqrt(|k|^2 + eps)  (kh = k * rk)
+//   be[r]  = sigmoid(raw_beta)
+template <typename TI, int D, int C, int NW, class GRef>
+__device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, int h,
+                                              const ChunkLoc& L, float* rq, float* rqs,
+                                              float* rk, float* be, GRef G) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const size_t ts = static_cast<size_t>(d.H) * D;
+  const TI* q = static_cast<const TI*>(in.q) + L.t0 * ts + static_cast<size_t>(h) * D;
+  const TI* k = static_cast<const TI*>(in.k) + L.t0 * ts + static_cast<size_t>(h) * D;
+  const TI* x = static_cast<const TI*>(in.g) + L.t0 * ts + static_cast<size_t>(h) * D;
+  const TI* rb = static_cast<const TI*>(in.beta) + L.t0 * d.H + h;
+  const float ea = expf(in.A_log[h]);
+  const float* db = in.dt_bias + static_cast<size_t>(h) * D;
+  for (int r = w; r < C; r += NW) {
+    const bool valid = r < L.len;
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+      const int kk = lane + 64 * j;
+      float qv = 0.f, kv = 0.f, gv = 0.f;
+      if (valid) {
+        qv = to_f(q[r * ts + kk]);
+        kv = to_f(k[r * ts + kk]);
+        const float z = ea * (to_f(x[r * ts + kk]) + db[kk]);
+        gv = d.lb * sigmoidf(z);
+      }
+      sq += qv * qv;
+      sk += kv * kv;
+      G(r, kk) = gv;
+    }
+    sq = wave_sum(sq);
+    sk = wave_sum(sk);
+    if (lane == 0) {
+      const float a = valid ? 1.0f / sqrtf(sq + d.eps) : 0.f;
+      const float b = valid ? 1.0f / sqrtf(sk + d.eps) : 0.f;
+      rq[r] = a;
+      rqs[r] = d.scale * a;
+      rk[r] = b;
+      be[r] = valid ? sigmoidf(to_f(rb[static_cast<size_t>(r) * d.H])) : 0.f;
+    }
+  }
+}
+
+// In-place inclusive cumulative sum over the C rows of every channel k of
+// G(r, k), by all threads of the block (fixed order, deterministic).
+// part_tot: LDS scratch of at least (blockDim / D) * D floats.
+template <int D, int C, int NT, class GRef>
+__device__ __forceinline__ void cumsum_rows(GRef G, float* part_tot) {
+  constexpr int parts = NT / D;
+  constexpr int rp = C / parts;
+  static_assert(NT % D == 0 && C % parts == 0, "cumsum layout");
+  const int tid = threadIdx.x;
+  const int col = tid % D, part = tid / D;
+  float run = 0.f;
+#pragma unroll 4
+  for (int i = 0; i < rp; ++i) {
+    const int r = part * rp + i;
+    run += G(r, col);
+    G(r, col) = run;
+  }
+  part_tot[part * D + col] = run;
+  __syncthreads();
+  float off = 0.f;
+  for (int p = 0; p < part; ++p) off += part_tot[p * D + col];
+  if (part > 0) {
+#pragma unroll 4
+    for (int i = 0; i < rp; ++i) G(part * rp + i, col) += off;
+  }
+  __syncthreads();
+}
+
+// Load KPL consecutive elements of TI as floats (KPL = 8 or 1).
+template <typename TI, int KPL>
+__device__ __forceinline__ void load_row_f(const TI* p, float* out) {
+  if constexpr (KPL == 8 && sizeof(TI) == 2) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = static_cast<float>(v[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) out[j] = to_f(p[j]);
+  }
+}
+
+}  // namespace kda

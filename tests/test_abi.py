@@ -1,0 +1,96 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/kda.h declares, and rejects bad problems on the host before any HIP
+call (null pointers, bad sizes, bad cu_seqlens, unsupported shapes,
+workspace too small)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from recompute_kda_chunked_amd import _lib
+from recompute_kda_chunked_amd.ops import Problem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from recompute_kda_chunked_amd import build
+        build.build()
+    return _lib.load()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def good(**kw):
+    args = dict(T=300, H=4, K=128, V=128, dtype=_lib.KDA_BF16, cu_host=[0, 100, 100, 300], chunk=64)
+    args.update(kw)
+    return Problem(**args)
+
+
+def test_valid_problem_and_workspace_sizes(lib):
+    p = good()
+    assert p.check() == _lib.KDA_OK
+    assert p.fwd_ws() > 0 and p.bwd_ws() > 0
+    # the backward workspace shrinks with the streaming segment
+    small = good(seg_chunks=1)
+    assert small.check() == _lib.KDA_OK
+    assert small.bwd_ws() < p.bwd_ws()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu_host=[0, 100, 50, 300]), _lib.KDA_ERR_INVALID),      # decreasing
+    (dict(cu_host=[1, 100, 300]), _lib.KDA_ERR_INVALID),          # does not start at 0
+    (dict(cu_host=[0, 100, 299]), _lib.KDA_ERR_INVALID),          # does not end at T
+    (dict(H=0), _lib.KDA_ERR_INVALID),
+    (dict(T=0, cu_host=[0, 0]), _lib.KDA_ERR_INVALID),
+    (dict(lower_bound=1.0), _lib.KDA_ERR_INVALID),
+    (dict(eps=-1.0), _lib.KDA_ERR_INVALID),
+    (dict(seg_chunks=-2), _lib.KDA_ERR_INVALID),
+    (dict(K=96, V=96), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(K=128, V=64), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=16), _lib.KDA_ERR_UNSUPPORTED),                    # bf16 needs C >= 32
+    (dict(chunk=48), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(gate_mode=_lib.KDA_GATE_SOFTPLUS_CLAMP), _lib.KDA_ERR_UNSUPPORTED),
+])
+def test_bad_problems_are_rejected(lib, kw, code):
+    p = good(**kw)
+    assert p.check() == code
+    assert p.fwd_ws() == 0 and p.bwd_ws() == 0
+    nul = ctypes.c_void_p(0)
+    assert lib.kda_fwd(p.ref, *([nul] * 9), nul, ctypes.c_size_t(0), nul) == code
+
+
+def test_null_pointers_and_small_workspace_rejected_before_any_launch(lib):
+    p = good()
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    assert lib.kda_fwd(p.ref, *([nul] * 9), nul, ctypes.c_size_t(0), nul) == _lib.KDA_ERR_INVALID
+    args = [fake] * 9
+    assert lib.kda_fwd(p.ref, *args, fake, ctypes.c_size_t(p.fwd_ws() - 1), nul) == _lib.KDA_ERR_WORKSPACE
+    args = [fake] * 16
+    assert lib.kda_bwd(p.ref, *args, fake, ctypes.c_size_t(p.bwd_ws() - 1), nul) == _lib.KDA_ERR_WORKSPACE
+    args[4] = nul
+    assert lib.kda_bwd(p.ref, *args, fake, ctypes.c_size_t(p.bwd_ws()), nul) == _lib.KDA_ERR_INVALID
+    assert lib.kda_check_problem(None) == _lib.KDA_ERR_INVALID
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert len(_lib.status_text(lib, code)) > 0

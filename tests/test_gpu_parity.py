@@ -1,0 +1,204 @@
+"""GPU parity of the HIP path against the FP64 oracle (needs an MI355X).
+
+Tolerances (normalised L2 error, ||x - ref|| / ||ref|| over a whole tensor):
+fp32 problems 1e-5 for O and every gradient; bf16 problems 5e-3 for O and
+2e-2 for every gradient (bf16 inputs, fp32 accumulation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import oracle
+from recompute_kda_chunked_amd import kda_backward, kda_forward, kda_prologue
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("q", "k", "v", "raw_g", "raw_beta", "A_log", "dt_bias")
+GRADS = ("dq", "dk", "dv", "draw_g", "draw_beta", "dA_log", "ddt_bias")
+TOL = {torch.float32: (1e-5, 1e-5), torch.bfloat16: (5e-3, 2e-2)}
+
+
+def announce(msg):
+    print("\n[case] " + msg, flush=True)
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    if nb == 0:
+        return float(np.max(np.abs(a))) if a.size else 0.0
+    return float(np.linalg.norm(a - b) / nb)
+
+
+def gpu_run(x, chunk, seg_chunks=0, scale=1.0, with_bwd=True):
+    args = [x[n] for n in NAMES]
+    kw = dict(cu_seqlens_host=x["cu_seqlens_host"], chunk=chunk, seg_chunks=seg_chunks,
+              scale=scale)
+    out = {"o": kda_forward(*args, x["cu_seqlens"], **kw)}
+    if with_bwd:
+        out.update(zip(GRADS, kda_backward(*args, x["dO"], x["cu_seqlens"], **kw)))
+    torch.cuda.synchronize()
+    return out
+
+
+def to_np(t):
+    return t.detach().double().cpu().numpy()
+
+
+def check(got, ref, dtype, heads=None, label=""):
+    tol_o, tol_g = TOL[dtype]
+    errs = {}
+    for name, r in ref.items():
+        a = to_np(got[name])
+        if heads is not None:
+            a = a[heads] if name in ("dA_log", "ddt_bias") else a[:, heads]
+        errs[name] = rel(a, r)
+    print(label, " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
+    for name, e in errs.items():
+        tol = tol_o if name == "o" else tol_g
+        assert np.isfinite(e) and e <= tol, (name, e, tol)
+    return errs
+
+
+def oracle_run(x, heads=None, scale=1.0, with_bwd=True):
+    sel = (lambda t: t) if heads is None else (lambda t: t[:, heads])
+    args = [sel(x[n]) for n in ("q", "k", "v", "raw_g", "raw_beta")]
+    A = x["A_log"] if heads is None else x["A_log"][heads]
+    B = x["dt_bias"] if heads is None else x["dt_bias"][heads]
+    return oracle.kda(*args, A, B, cu_seqlens=x["cu_seqlens_host"],
+                      dO=sel(x["dO"]) if with_bwd else None, scale=scale)
+
+
+# ------------------------------------------------------------------ small, full comparison
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "small_f32"])
+def test_fp32_workloads_full(name):
+    w = kda_inputs.WORKLOADS[name]
+    announce("%s full vs oracle" % name)
+    x = kda_inputs.workload_inputs(w, device="cuda")
+    check(gpu_run(x, w.chunk), oracle_run(x), torch.float32, label=name)
+
+
+RAGGED = [1, 17, 63, 64, 65, 200]
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_fp32_ragged_varlen_every_chunk_size(chunk):
+    announce("fp32 ragged D64 chunk %d" % chunk)
+    x = kda_inputs.make_inputs(RAGGED, 3, 64, 64, torch.float32, seed=11, device="cuda",
+                               A_log=0.3, dt_bias=0.2)
+    check(gpu_run(x, chunk), oracle_run(x), torch.float32, label="C%d" % chunk)
+
+
+@pytest.mark.parametrize("D,chunk", [(128, 64), (128, 32), (64, 64), (64, 32)])
+def test_bf16_ragged_varlen(D, chunk):
+    announce("bf16 ragged D%d chunk %d" % (D, chunk))
+    x = kda_inputs.make_inputs(RAGGED + [130], 2, D, D, torch.bfloat16, seed=12, device="cuda")
+    check(gpu_run(x, chunk), oracle_run(x), torch.bfloat16, label="bf16 D%d C%d" % (D, chunk))
+
+
+def test_fp32_d128_and_segment_streaming():
+    announce("fp32 D128 chunk 32, one-chunk segments")
+    x = kda_inputs.make_inputs([70, 1, 130], 2, 128, 128, torch.float32, seed=13, device="cuda")
+    ref = oracle_run(x)
+    check(gpu_run(x, 32), ref, torch.float32, label="seg auto")
+    check(gpu_run(x, 32, seg_chunks=1), ref, torch.float32, label="seg 1")
+    check(gpu_run(x, 32, seg_chunks=3), ref, torch.float32, label="seg 3")
+
+
+def test_slow_decay_long_memory():
+    announce("slow decay dt_bias=-8, fp32 and bf16")
+    for dt, D, C in ((torch.float32, 64, 64), (torch.bfloat16, 128, 64)):
+        x = kda_inputs.make_inputs([700, 300], 2, D, D, dt, seed=14, device="cuda", dt_bias=-8.0)
+        check(gpu_run(x, C, seg_chunks=3), oracle_run(x), dt, label=str(dt))
+
+
+def test_scale_argument():
+    announce("scale 1/sqrt(K)")
+    x = kda_inputs.make_inputs([90, 33], 2, 64, 64, torch.float32, seed=15, device="cuda")
+    s = 64 ** -0.5
+    check(gpu_run(x, 32, scale=s), oracle_run(x, scale=s), torch.float32, label="scale")
+
+
+# ------------------------------------------------------------------ special inputs
+
+
+def test_beta_zero_gives_exact_zeros():
+    announce("beta = 0")
+    x = kda_inputs.make_inputs([100, 28], 2, 64, 64, torch.float32, seed=16, device="cuda")
+    x["raw_beta"].fill_(-1e4)
+    got = gpu_run(x, 64)
+    for name in ("o",) + GRADS:
+        assert torch.count_nonzero(got[name]).item() == 0, name
+
+
+def test_gate_at_bound_stays_finite():
+    # Single write at token 0, then beta = 0 and every channel decaying at the
+    # bound: the chunk's cumulative gate runs down to -5 * 63. Any unsafe split
+    # of exp(G_r - G_s) overflows here.
+    announce("gate at the -5 bound, single write")
+    for dt, D in ((torch.float32, 64), (torch.bfloat16, 128)):
+        x = kda_inputs.make_inputs([128], 1, D, D, dt, seed=17, device="cuda")
+        x["raw_beta"].fill_(-1e4)
+        x["raw_beta"][0] = 40.0
+        x["q"].copy_(x["k"][0:1].expand_as(x["q"]))
+        x["raw_g"].fill_(40.0)
+        x["raw_g"][:, :, ::2] = -1e4  # half the channels hold, half decay at -5
+        got = gpu_run(x, 64)
+        for name in ("o",) + GRADS:
+            assert torch.isfinite(got[name]).all(), (dt, name)
+        ref = oracle_run(x)
+        check(got, ref, dt, label="bound " + str(dt))
+
+
+# ------------------------------------------------------------------ structure
+
+
+def test_prologue_step():
+    announce("prologue step")
+    x = kda_inputs.make_inputs(RAGGED, 3, 128, 128, torch.bfloat16, seed=18, device="cuda",
+                               A_log=-0.4, dt_bias=0.7)
+    qh, kh, be, gc = kda_prologue(x["q"], x["k"], x["raw_g"], x["raw_beta"], x["A_log"],
+                                  x["dt_bias"], x["cu_seqlens"],
+                                  cu_seqlens_host=x["cu_seqlens_host"], chunk=64)
+    torch.cuda.synchronize()
+    ref = oracle.prologue(x["q"], x["k"], x["raw_g"], x["raw_beta"], x["A_log"], x["dt_bias"],
+                          x["cu_seqlens_host"], chunk=64)
+    for name, t in (("qh", qh), ("kh", kh), ("beta", be), ("gcum", gc)):
+        e = rel(to_np(t), ref[name])
+        print("prologue", name, "%.2e" % e, flush=True)
+        assert e <= 1e-6, (name, e)
+
+
+def test_bitwise_deterministic():
+    announce("run-to-run determinism")
+    x = kda_inputs.make_inputs([300, 77], 4, 128, 128, torch.bfloat16, seed=19, device="cuda")
+    a = gpu_run(x, 64, seg_chunks=2)
+    b = gpu_run(x, 64, seg_chunks=2)
+    for name in a:
+        assert torch.equal(a[name], b[name]), name
+
+
+def test_chunk_size_invariance_bf16():
+    announce("C32 vs C64, bf16")
+    x = kda_inputs.make_inputs([257, 64], 2, 128, 128, torch.bfloat16, seed=20, device="cuda")
+    ref = oracle_run(x)
+    check(gpu_run(x, 32), ref, torch.bfloat16, label="C32")
+    check(gpu_run(x, 64), ref, torch.bfloat16, label="C64")
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled heads)
+
+
+@pytest.mark.parametrize("name,heads", [("t8k_h64_bf16", [0, 29, 63]),
+                                        ("varlen8x8k_h16_bf16", [3, 15])])
+def test_bf16_workloads_sampled_heads(name, heads):
+    w = kda_inputs.WORKLOADS[name]
+    announce("%s sampled heads %s" % (name, heads))
+    x = kda_inputs.workload_inputs(w, device="cuda")
+    got = gpu_run(x, w.chunk)
+    ref = oracle_run(x, heads=heads)
+    check(got, ref, torch.bfloat16, heads=heads, label=name)

@@ -303,3 +303,20 @@ def test_long_sequence_crosses_oracle_checkpoint_blocks():
     assert rel(r["o"], chunked_ref.chunk_fwd(**p, chunk=64)) < 1e-12
     for name in ("dq", "dk", "dv", "draw_g", "draw_beta", "dA_log", "ddt_bias"):
         assert rel(r[name], ref[name]) < 1e-11, name
+
+
+def test_prologue_entry_matches_its_definition():
+    # gcum restarts every chunk from each sequence start; qh,kh unit-norm
+    # (up to eps) rows; beta in (0, 1); g in (L, 0) so gcum is decreasing.
+    p, _ = rand_problem(20, [5, 40, 0, 17], 2, 6, 4)
+    r = oracle.prologue(p["q"], p["k"], p["raw_g"], p["raw_beta"], p["A_log"], p["dt_bias"],
+                        p["cu_seqlens"], chunk=16)
+    qh, kh, g = _prologue_np(p)
+    assert np.allclose(r["qh"], qh, rtol=1e-14) and np.allclose(r["kh"], kh, rtol=1e-14)
+    assert np.allclose(r["beta"], 1 / (1 + np.exp(-p["raw_beta"])), rtol=1e-14)
+    cu = p["cu_seqlens"]
+    for n in range(len(cu) - 1):
+        for t in range(cu[n], cu[n + 1]):
+            c0 = cu[n] + (t - cu[n]) // 16 * 16
+            assert np.allclose(r["gcum"][t], g[c0:t + 1].sum(0), rtol=1e-13, atol=1e-15)
+    assert np.all(g < 0) and np.all(g > L_BOUND)
