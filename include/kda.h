@@ -120,10 +120,12 @@ int kda_bwd(const kda_problem *p, const void *q, const void *k, const void *v,
    kda_profile_begin() and kda_profile_end(), every kernel the calling thread
    launches through this library is bracketed by two HIP events recorded on
    its own stream. kda_profile_end() waits for those events and writes, per
-   kernel kind (index = KDA_KERNEL_*), the number of launches and their
-   summed duration in milliseconds into `launches` / `total_ms` (arrays of
-   `n` entries, caller-owned; n >= KDA_KERNEL_COUNT recommended). Returns
-   KDA_OK or KDA_ERR_HIP. Timing adds two event records per launch. */
+   kernel kind (index = KDA_KERNEL_*), the number of launches, their summed
+   duration in milliseconds and the summed number of (chunk, head) units the
+   launches processed into `launches` / `total_ms` / `units` (arrays of `n`
+   entries, caller-owned, each may be NULL; n >= KDA_KERNEL_COUNT
+   recommended). Returns KDA_OK or KDA_ERR_HIP. Timing adds two event
+   records per launch. */
 enum {
   KDA_KERNEL_CHUNK_TABLE = 0,
   KDA_KERNEL_PROLOGUE = 1,
@@ -135,7 +137,7 @@ enum {
   KDA_KERNEL_COUNT = 7
 };
 int kda_profile_begin(void);
-int kda_profile_end(int32_t *launches, double *total_ms, int n);
+int kda_profile_end(int32_t *launches, double *total_ms, int64_t *units, int n);
 const char *kda_kernel_name(int kind);
 
 /* Human-readable text for a status code, including the HIP error of the

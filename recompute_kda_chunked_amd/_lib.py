@@ -72,7 +72,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kda_profile_begin.argtypes = []
     lib.kda_profile_begin.restype = ctypes.c_int
     lib.kda_profile_end.argtypes = [ctypes.POINTER(ctypes.c_int32),
-                                    ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+                                    ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
     lib.kda_profile_end.restype = ctypes.c_int
     lib.kda_kernel_name.argtypes = [ctypes.c_int]
     lib.kda_kernel_name.restype = ctypes.c_char_p
@@ -92,12 +93,15 @@ def profile_begin() -> None:
 
 
 def profile_end() -> dict:
-    """{kernel name: (launches, total ms)} since profile_begin() on this thread."""
+    """{kernel name: (launches, total ms, (chunk, head) units)} since
+    profile_begin() on this thread."""
     lib = load()
     n = KERNEL_COUNT
     launches = (ctypes.c_int32 * n)()
     ms = (ctypes.c_double * n)()
-    st = lib.kda_profile_end(launches, ms, n)
+    units = (ctypes.c_int64 * n)()
+    st = lib.kda_profile_end(launches, ms, units, n)
     if st != KDA_OK:
         raise RuntimeError("kda_profile_end: " + status_text(lib, st))
-    return {lib.kda_kernel_name(k).decode(): (int(launches[k]), float(ms[k])) for k in range(n)}
+    return {lib.kda_kernel_name(k).decode(): (int(launches[k]), float(ms[k]), int(units[k]))
+            for k in range(n)}

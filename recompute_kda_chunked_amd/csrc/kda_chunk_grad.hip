@@ -95,28 +95,44 @@ struct Vjp<float> {
   }
 };
 
+// SPLIT * D / 16 waves: wave w owns key block kb = w % (D/16) (16 channels)
+// and row group half = w / (D/16) (one of SPLIT contiguous runs of the
+// chunk's 16-row blocks) for every per-element accumulator, and shares the
+// chunk-level products with the other waves.
+template <int D>
+constexpr int grad_split() { return D >= 128 ? 1 : 2; }
+
 template <typename TI, typename OpT, int D, int C>
-__global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI* dO,
+__global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, Inputs in, const TI* dO,
                                                     int seg_begin, ChunkOps ops, SegStates st,
                                                     TI* dq, TI* dk, TI* dv, TI* dg, TI* dbeta,
                                                     float* partials) {
   using M = Mma<OpT>;
+  using VJ = Vjp<OpT>;
+  using TG = typename VJ::T;
   constexpr int K = D, V = D, NB = C / 16, KPL = M::KPL, KS = M::KS;
-  constexpr int KBW = K / 64;        // key blocks per wave
+  constexpr int SPLIT = grad_split<D>();
+  constexpr int NKB = D / 16, NW = SPLIT * NKB, NT = NW * 64;
+  constexpr int MR = (NB + SPLIT - 1) / SPLIT;  // row blocks per wave
   constexpr int LDG = C + 4;         // GT [K][LDG] fp32
   constexpr int LDQ = C + 8;         // qT, kT [K][LDQ]
   constexpr int LDA = D + 8;         // [C][LDA] operand buffers
   constexpr int LDX = C + 8;         // [C][LDX] dX buffers
   constexpr int SZ1 = 4 * C * LDA * (int)sizeof(OpT), SZ2 = 4 * C * LDX * (int)sizeof(OpT);
+  constexpr int SZU = SZ1 > SZ2 ? SZ1 : SZ2;
+  // after the VJP the operand region holds dG^T (fp64 problems), then the
+  // scratch of the reverse cumulative sum and of the partial reductions
+  constexpr int OFF_S = sizeof(TG) == 4 ? 0 : (int)sizeof(double) * K * LDG;
+  static_assert(OFF_S + (int)sizeof(TG) * NT + 4 * NT <= SZU, "LDS scratch must fit");
   __shared__ float GT[K * LDG];
   __shared__ __attribute__((aligned(16))) TI qT[K * LDQ];
   __shared__ __attribute__((aligned(16))) TI kT[K * LDQ];
-  __shared__ __attribute__((aligned(16))) unsigned char uni[SZ1 > SZ2 ? SZ1 : SZ2];
+  __shared__ __attribute__((aligned(16))) unsigned char uni[SZU];
   __shared__ float rq[C], rqs[C], rk[C], be[C];
-  __shared__ float dbp[4][C];
-  __shared__ float rowp[2][4][C];
-  __shared__ float ptot[4 * D];
-  __shared__ float red[256];
+  __shared__ float dbp[NW][C];
+  __shared__ float rowp[2][NKB][C];
+  __shared__ float ptot[NT];
+  __shared__ TG csum[SPLIT][NKB][16];
 
   OpT* dBv_s = reinterpret_cast<OpT*>(uni);
   OpT* dO_s = dBv_s + C * LDA;
@@ -128,6 +144,7 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
   OpT* dXkT = dXqT + C * LDX;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
+  const int kb = w % NKB, half = w / NKB, kk = 16 * kb + i;
   const int lc = blockIdx.x / d.H, h = blockIdx.x % d.H;
   const int cglob = seg_begin + lc;
   const ChunkLoc L = locate<C>(in, d.N, cglob);
@@ -137,44 +154,45 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
   const TI* qr = static_cast<const TI*>(in.q) + L.t0 * ts + hoff;
   const TI* kr = static_cast<const TI*>(in.k) + L.t0 * ts + hoff;
   const TI* vr = static_cast<const TI*>(in.v) + L.t0 * ts + hoff;
+  auto row_block = [&](int jm) { return half * MR + jm; };  // valid while < NB
 
   // ---- S1: prologue, transposed raw q/k, cumulative gate G^T
-  auto Gf = [&](int r, int kk) -> float& { return GT[kk * LDG + r]; };
-  prologue_rows<TI, D, C, 4>(d, in, h, L, rq, rqs, rk, be, Gf);
-  for (int e = tid; e < C * D; e += 256) {
-    const int r = e / D, kk = e % D;
+  auto Gf = [&](int r, int kk_) -> float& { return GT[kk_ * LDG + r]; };
+  prologue_rows<TI, D, C, NW>(d, in, h, L, rq, rqs, rk, be, Gf);
+  for (int e = tid; e < C * D; e += NT) {
+    const int r = e / D, kc = e % D;
     const bool v = r < L.len;
-    qT[kk * LDQ + r] = v ? qr[r * ts + kk] : static_cast<TI>(0.f);
-    kT[kk * LDQ + r] = v ? kr[r * ts + kk] : static_cast<TI>(0.f);
+    qT[kc * LDQ + r] = v ? qr[r * ts + kc] : static_cast<TI>(0.f);
+    kT[kc * LDQ + r] = v ? kr[r * ts + kc] : static_cast<TI>(0.f);
   }
-  for (int e = tid; e < 4 * C; e += 256) {
-    dbp[e / C][e % C] = 0.f;
-    rowp[0][e / C][e % C] = 0.f;
-    rowp[1][e / C][e % C] = 0.f;
-  }
+  for (int e = tid; e < NW * C; e += NT) dbp[e / C][e % C] = 0.f;
+  for (int e = tid; e < 2 * NKB * C; e += NT) (&rowp[0][0][0])[e] = 0.f;
   __syncthreads();
-  cumsum_rows<D, C, 256>(Gf, ptot);
+  cumsum_rows<D, C, NT>(Gf, ptot);
 
   // ---- S2: dBv = T^T dVn (tiles of dBv^T: value rows, chunk-row columns)
   {
     const OpT* dVnT = static_cast<const OpT*>(st.dVnT) + idx * V * C;
     const OpT* TT = static_cast<const OpT*>(ops.TT) + idx * C * C;
     TI* dvo = dv + L.t0 * ts + hoff;
-    for (int t = w; t < (V / 16) * NB; t += 4) {
+    for (int t = w; t < (V / 16) * NB; t += NW) {
       const int mv = t / NB, nr = t % NB;
       const int s_lo = (16 * nr) / KS * KS;  // T^T[r][s] = 0 for s < r
-      const f32x4 acc = tile_nt<OpT>(zero4(), dVnT + 16 * mv * C, C, TT + 16 * nr * C, C, s_lo, C, lane);
       const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
+      float vin[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) vin[rr] = r < L.len ? to_f(vr[r * ts + vv + rr]) : 0.f;
+      const f32x4 acc = tile_nt<OpT>(zero4(), dVnT + 16 * mv * C, C, TT + 16 * nr * C, C, s_lo, C, lane);
       OpT* dst = dBv_s + r * LDA + vv;
       float part = 0.f;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(acc[rr]);
+      for (int rr = 0; rr < 4; ++rr) {
+        dst[rr] = from_f<OpT>(acc[rr]);
+        part += acc[rr] * vin[rr];
+      }
       if (r < L.len) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          dvo[r * ts + vv + rr] = from_f<TI>(be[r] * acc[rr]);
-          part += acc[rr] * to_f(vr[r * ts + vv + rr]);
-        }
+        for (int rr = 0; rr < 4; ++rr) dvo[r * ts + vv + rr] = from_f<TI>(be[r] * acc[rr]);
       }
       part = sum_groups(part);
       if (g == 0) dbp[w][r] += part;
@@ -184,7 +202,7 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
   {
     const TI* dOr = dO + L.t0 * ts + hoff;
     const OpT* Vn = static_cast<const OpT*>(st.Vn) + idx * C * V;
-    for (int e = tid; e < C * V; e += 256) {
+    for (int e = tid; e < C * V; e += NT) {
       const int r = e / V, vv = e % V;
       dO_s[r * LDA + vv] = r < L.len ? from_f<OpT>(to_f(dOr[r * ts + vv])) : from_f<OpT>(0.f);
       Vn_s[r * LDA + vv] = Vn[e];
@@ -192,80 +210,78 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
   }
   __syncthreads();
 
-  // ---- S4: products with the states; wave w owns key blocks kb = w + 4*jk
-  using VJ = Vjp<OpT>;
-  using TG = typename VJ::T;
-  static_assert(sizeof(TG) == 4 || sizeof(uni) >= sizeof(double) * K * LDG, "dG buffer");
-  f32x4 aq[KBW][NB], ak[KBW][NB];
-  TG aG[KBW][NB][4];
+  // ---- S4: products with the states for the wave's (key block, row blocks)
+  f32x4 aq[MR], ak[MR];
+  TG aG[MR][4];
 #pragma unroll
-  for (int jk = 0; jk < KBW; ++jk)
+  for (int jm = 0; jm < MR; ++jm) {
+    aq[jm] = ak[jm] = zero4();
 #pragma unroll
-    for (int m = 0; m < NB; ++m) {
-      aq[jk][m] = ak[jk][m] = zero4();
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) aG[jk][m][rr] = 0;
-    }
+    for (int rr = 0; rr < 4; ++rr) aG[jm][rr] = 0;
+  }
+  TG hdh = 0;
   {
     const OpT* hm = static_cast<const OpT*>(st.h) + idx * K * V;
     const OpT* dhm = static_cast<const OpT*>(st.dh) + idx * K * V;
-#pragma unroll
-    for (int jk = 0; jk < KBW; ++jk) {
-      const int kb = w + 4 * jk, kk = 16 * kb + i;
-      f32x4 rKb[NB], rQg[NB], rKg[NB];
-#pragma unroll
-      for (int m = 0; m < NB; ++m) rKb[m] = rQg[m] = rKg[m] = zero4();
-      float hdh = 0.f;
+    // the wave's rows of h and dh' as B fragments, loaded once
+    constexpr int NVS = V / KS;
+    typename M::frag fh[NVS], fdh[NVS];
+    float hd = 0.f;
+    {
       const OpT* bh = hm + kk * V + g * KPL;
       const OpT* bdh = dhm + kk * V + g * KPL;
-      for (int v0 = 0; v0 < V; v0 += KS) {
-        const auto fh = M::load(bh + v0);
-        const auto fdh = M::load(bdh + v0);
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) hdh += frag_at<OpT>(fh, j) * frag_at<OpT>(fdh, j);
+      for (int j = 0; j < NVS; ++j) {
+        fh[j] = M::load(bh + j * KS);
+        fdh[j] = M::load(bdh + j * KS);
 #pragma unroll
-        for (int m = 0; m < NB; ++m) {
-          const int ro = (16 * m + i) * LDA + v0 + g * KPL;
-          rKb[m] = M::mma(M::load(dBv_s + ro), fh, rKb[m]);
-          rQg[m] = M::mma(M::load(dO_s + ro), fh, rQg[m]);
-          rKg[m] = M::mma(M::load(Vn_s + ro), fdh, rKg[m]);
-        }
+        for (int jj = 0; jj < KPL; ++jj) hd += frag_at<OpT>(fh[j], jj) * frag_at<OpT>(fdh[j], jj);
       }
-      hdh = sum_groups(hdh);
-      const float Gc = GT[kk * LDG + C - 1];
-      TG colsum = 0;
-#pragma unroll
-      for (int m = 0; m < NB; ++m) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = 16 * m + 4 * g + rr;
-          const float Gv = GT[kk * LDG + r];
-          const float eG = kexp<OpT>(Gv), eGc = kexp<OpT>(Gc - Gv);
-          const float qh = to_f(qT[kk * LDQ + r]) * rqs[r];
-          const float kh = to_f(kT[kk * LDQ + r]) * rk[r];
-          const float dqg = rQg[m][rr], dkg = rKg[m][rr], dKb = -rKb[m][rr];
-          const float b = be[r];
-          aq[jk][m][rr] += dqg * eG;
-          ak[jk][m][rr] += dkg * eGc + b * dKb * eG;
-          // -kg*dkg here and +kg*dkg in the G_c row cancel in the reverse
-          // cumulative sum: both use the same product value
-          const TG kgdkg = static_cast<TG>(dkg) * kh * eGc;
-          aG[jk][m][rr] += static_cast<TG>(dqg) * qh * eG - kgdkg + static_cast<TG>(dKb) * b * kh * eG;
-          colsum += kgdkg;
-          dKb_s[r * LDA + kk] = from_f<OpT>(dKb);
-          const float pb = sum16(dKb * kh * eG);
-          if (i == 0) dbp[w][r] += pb;
-        }
-      }
-      colsum += __shfl_xor(colsum, 16, kWave);
-      colsum += __shfl_xor(colsum, 32, kWave);
-      if (g == 3) aG[jk][NB - 1][3] += colsum + static_cast<TG>(kexp<OpT>(Gc)) * hdh;  // row C-1 holds G_c
     }
+    hdh = static_cast<TG>(sum_groups(hd));
+    const float Gc = GT[kk * LDG + C - 1];
+    TG colsum = 0;
+#pragma unroll
+    for (int jm = 0; jm < MR; ++jm) {
+      const int m = row_block(jm);
+      if (m >= NB) break;
+      f32x4 rKb = zero4(), rQg = zero4(), rKg = zero4();
+#pragma unroll
+      for (int j = 0; j < NVS; ++j) {
+        const int ro = (16 * m + i) * LDA + j * KS + g * KPL;
+        rKb = M::mma(M::load(dBv_s + ro), fh[j], rKb);
+        rQg = M::mma(M::load(dO_s + ro), fh[j], rQg);
+        rKg = M::mma(M::load(Vn_s + ro), fdh[j], rKg);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = 16 * m + 4 * g + rr;
+        const float Gv = GT[kk * LDG + r];
+        const float eG = kexp<OpT>(Gv), eGc = kexp<OpT>(Gc - Gv);
+        const float qh = to_f(qT[kk * LDQ + r]) * rqs[r];
+        const float kh = to_f(kT[kk * LDQ + r]) * rk[r];
+        const float dqg = rQg[rr], dkg = rKg[rr], dKb = -rKb[rr];
+        const float b = be[r];
+        aq[jm][rr] += dqg * eG;
+        ak[jm][rr] += dkg * eGc + b * dKb * eG;
+        // -kg*dkg here and +kg*dkg in the G_c row cancel in the reverse
+        // cumulative sum: both use the same product value
+        const TG kgdkg = static_cast<TG>(dkg) * kh * eGc;
+        aG[jm][rr] += static_cast<TG>(dqg) * qh * eG - kgdkg + static_cast<TG>(dKb) * b * kh * eG;
+        colsum += kgdkg;
+        dKb_s[r * LDA + kk] = from_f<OpT>(dKb);
+        const float pb = sum16(dKb * kh * eG);
+        if (i == 0) dbp[w][r] += pb;
+      }
+    }
+    colsum += __shfl_xor(colsum, 16, kWave);
+    colsum += __shfl_xor(colsum, 32, kWave);
+    if (g == 0) csum[half][kb][i] = colsum;
   }
   __syncthreads();
 
   // ---- S5: dAqk and dAkk, lower 16x16 blocks (m rows, ns columns)
-  constexpr int NPAIR = NB * (NB + 1) / 2, PPW = (NPAIR + 3) / 4;
+  constexpr int NPAIR = NB * (NB + 1) / 2, PPW = (NPAIR + NW - 1) / NW;
   f32x4 xq[PPW], xk[PPW];
   {
     const OpT* Ug = static_cast<const OpT*>(ops.U) + idx * C * V;
@@ -273,7 +289,7 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
     const OpT* Pg = static_cast<const OpT*>(ops.P) + idx * C * C;
 #pragma unroll
     for (int jp = 0; jp < PPW; ++jp) {
-      const int p = w + 4 * jp;
+      const int p = w + NW * jp;
       xq[jp] = xk[jp] = zero4();
       if (p >= NPAIR) break;
       int m = 0, ns = p;
@@ -283,31 +299,31 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
       const f32x4 a2 = tile_nt<OpT>(zero4(), dKb_s + 16 * m * LDA, LDA, Wng + 16 * ns * K, K, 0, K, lane);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int r = 16 * m + 4 * g + rr, s = 16 * ns + i;
-        xq[jp][rr] = (s <= r) ? aqk[rr] : 0.f;
-        const float dakk = (s < r) ? (a2[rr] - a1[rr]) : 0.f;
+        const int r = 16 * m + 4 * g + rr, s_ = 16 * ns + i;
+        xq[jp][rr] = (s_ <= r) ? aqk[rr] : 0.f;
+        const float dakk = (s_ < r) ? (a2[rr] - a1[rr]) : 0.f;
         xk[jp][rr] = be[r] * dakk;
-        const float pb = sum16(dakk * to_f(Pg[r * C + s]));
+        const float pb = sum16(dakk * to_f(Pg[r * C + s_]));
         if (i == 0) dbp[w][r] += pb;
       }
     }
   }
   __syncthreads();  // operand buffers are dead; the dX buffers reuse their space
-  for (int e = tid; e < 4 * C * LDX; e += 256) dXq[e] = from_f<OpT>(0.f);
+  for (int e = tid; e < 4 * C * LDX; e += NT) dXq[e] = from_f<OpT>(0.f);
   __syncthreads();
 #pragma unroll
   for (int jp = 0; jp < PPW; ++jp) {
-    const int p = w + 4 * jp;
+    const int p = w + NW * jp;
     if (p >= NPAIR) break;
     int m = 0, ns = p;
     while (ns > m) { ns -= m + 1; ++m; }
-    const int s = 16 * ns + i, r0 = 16 * m + 4 * g;
+    const int s_ = 16 * ns + i, r0 = 16 * m + 4 * g;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      dXq[(r0 + rr) * LDX + s] = from_f<OpT>(xq[jp][rr]);
-      dXk[(r0 + rr) * LDX + s] = from_f<OpT>(xk[jp][rr]);
-      dXqT[s * LDX + r0 + rr] = from_f<OpT>(xq[jp][rr]);
-      dXkT[s * LDX + r0 + rr] = from_f<OpT>(xk[jp][rr]);
+      dXq[(r0 + rr) * LDX + s_] = from_f<OpT>(xq[jp][rr]);
+      dXk[(r0 + rr) * LDX + s_] = from_f<OpT>(xk[jp][rr]);
+      dXqT[s_ * LDX + r0 + rr] = from_f<OpT>(xq[jp][rr]);
+      dXkT[s_ * LDX + r0 + rr] = from_f<OpT>(xk[jp][rr]);
     }
   }
   __syncthreads();
@@ -316,9 +332,7 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
   // Operands are generated from the raw inputs and G^T. For each block pair
   // (I, J <= I) the decay exp(G_r - G_s) is split around the first row b of
   // block I (as in the forward), so every generated factor is finite.
-#pragma unroll
-  for (int jk = 0; jk < KBW; ++jk) {
-    const int kb = w + 4 * jk, kk = 16 * kb + i;
+  {
     const float* Gk = GT + kk * LDG;
     const TI* qk = qT + kk * LDQ;
     const TI* kq = kT + kk * LDQ;
@@ -326,12 +340,15 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
     auto qhat = [&](int r) { return static_cast<TG>(to_f(qk[r])) * static_cast<TG>(rqs[r]); };
     auto dec = [&](int r, int s_) { return VJ::ex(static_cast<TG>(Gk[r]) - static_cast<TG>(Gk[s_])); };
 #pragma unroll
-    for (int I = 0; I < NB; ++I) {
+    for (int jm = 0; jm < MR; ++jm) {
+      const int I = row_block(jm);
+      if (I >= NB) break;
       const int b0 = 16 * I;
       // row side: rows r of block I, reduction over s < 16(I + 1):
       //   raw[r] = sum_s dX[r][s] * kh_s exp(G_b - G_s)
       typename VJ::acc rq_ = VJ::zero(), rk_ = VJ::zero();
       const int s_hi = 16 * (I + 1);
+#pragma unroll 1
       for (int s0 = 0; s0 < (s_hi + VJ::KS - 1) / VJ::KS * VJ::KS; s0 += VJ::KS) {
         const auto fb = VJ::make([&](int j) {
           const int s_ = s0 + g * VJ::KPL + j;
@@ -350,26 +367,26 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
         // dG takes the column side's operand values for this pair, rounded as
         // that side's MFMA operands are (see Vjp)
         const TG Aq = VJ::rnd(qhat(r) * f), Ak = VJ::rnd(khat(r) * f);
-        aq[jk][I][rr] += static_cast<float>(rq_[rr] * f);
-        ak[jk][I][rr] += static_cast<float>(rk_[rr] * f);
-        aG[jk][I][rr] += Aq * rq_[rr] + Ak * rk_[rr];
+        aq[jm][rr] += static_cast<float>(rq_[rr] * f);
+        ak[jm][rr] += static_cast<float>(rk_[rr] * f);
+        aG[jm][rr] += Aq * rq_[rr] + Ak * rk_[rr];
       }
-    }
-    // column side: rows s of block J, reduction over r in blocks I >= J; the
-    // 32-long reduction index u covers (beta*dAkk, kh) for u < 16 and
-    // (dAqk, qh) above:  y[s] = sum_r dX[r][s] * a_r exp(G_r - G_b)
-#pragma unroll
-    for (int J = 0; J < NB; ++J) {
+      // column side: rows s of block J = I here, reduction over r in blocks
+      // I2 >= J; the 32-long reduction index u covers (beta*dAkk, kh) for
+      // u < 16 and (dAqk, qh) above:  y[s] = sum_r dX[r][s] * a_r exp(G_r - G_b)
+      const int J = I;
       TG cc[4] = {0, 0, 0, 0}, gs[4] = {0, 0, 0, 0};
-      for (int I = J; I < NB; ++I) {
-        const int b0 = 16 * I;
+#pragma unroll 1
+      for (int I2 = J; I2 < NB; ++I2) {
+        const int c0 = 16 * I2;
         typename VJ::acc y = VJ::zero();
+#pragma unroll 1
         for (int u0 = 0; u0 < 32; u0 += VJ::KS) {
           const int u = u0 + g * VJ::KPL;
-          const OpT* ap = (u < 16 ? dXkT : dXqT) + (16 * J + i) * LDX + b0 + (u & 15);
+          const OpT* ap = (u < 16 ? dXkT : dXqT) + (16 * J + i) * LDX + c0 + (u & 15);
           const auto fb = VJ::make([&](int j) {
-            const int uu = u + j, r = b0 + (uu & 15);
-            return (uu < 16 ? khat(r) : qhat(r)) * dec(r, b0);
+            const int uu = u + j, r = c0 + (uu & 15);
+            return (uu < 16 ? khat(r) : qhat(r)) * dec(r, c0);
           });
           y = VJ::mma(VJ::load(ap), fb, y);
         }
@@ -377,54 +394,61 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int s_ = 16 * J + 4 * g + rr;
-          const TG f = dec(b0, s_);
+          const TG f = dec(c0, s_);
           cc[rr] += y[rr] * f;
           gs[rr] += VJ::rnd(khat(s_) * f) * y[rr];  // the row side's B operand value
         }
       }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        ak[jk][J][rr] += static_cast<float>(cc[rr]);
-        aG[jk][J][rr] -= gs[rr];
+        ak[jm][rr] += static_cast<float>(cc[rr]);
+        aG[jm][rr] -= gs[rr];
       }
     }
   }
 
-  // ---- S7: row reductions for the L2-norm VJP, reverse cumulative sum of dG
+  // ---- S7: row reductions for the L2-norm VJP; G_c terms; reverse cumsum of dG
 #pragma unroll
-  for (int jk = 0; jk < KBW; ++jk) {
-    const int kk = 16 * (w + 4 * jk) + i;
+  for (int jm = 0; jm < MR; ++jm) {
+    const int m = row_block(jm);
+    if (m >= NB) break;
 #pragma unroll
-    for (int m = 0; m < NB; ++m) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r = 16 * m + 4 * g + rr;
-        const float pq = sum16(to_f(qT[kk * LDQ + r]) * rq[r] * aq[jk][m][rr]);
-        const float pk = sum16(to_f(kT[kk * LDQ + r]) * rk[r] * ak[jk][m][rr]);
-        if (i == 0) {
-          rowp[0][w][r] += pq;
-          rowp[1][w][r] += pk;
-        }
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = 16 * m + 4 * g + rr;
+      const float pq = sum16(to_f(qT[kk * LDQ + r]) * rq[r] * aq[jm][rr]);
+      const float pk = sum16(to_f(kT[kk * LDQ + r]) * rk[r] * ak[jm][rr]);
+      if (i == 0) {
+        rowp[0][kb][r] = pq;
+        rowp[1][kb][r] = pk;
       }
     }
+    // row C-1 holds G_c: add sum_r kg*dkg over all row groups and gamma * (h . dh')
+    if (m == NB - 1 && g == 3) {
+      const float Gc = GT[kk * LDG + C - 1];
+      TG cs = 0;
+#pragma unroll
+      for (int hh = 0; hh < SPLIT; ++hh) cs += csum[hh][kb][i];
+      aG[jm][3] += cs + static_cast<TG>(kexp<OpT>(Gc)) * hdh;
+    }
   }
-  __syncthreads();  // all reads of GT and of the dX buffers are done
+  __syncthreads();  // all reads of GT as the cumulative gate are done
   // dG^T in LDS, in the VJP precision (fp32: the GT buffer; fp64: the
   // operand region, free now)
   TG* dGT = sizeof(TG) == 4 ? reinterpret_cast<TG*>(GT) : reinterpret_cast<TG*>(uni);
+  TG* ptg = reinterpret_cast<TG*>(uni + OFF_S);
+  float* red = reinterpret_cast<float*>(uni + OFF_S + sizeof(TG) * NT);
 #pragma unroll
-  for (int jk = 0; jk < KBW; ++jk) {
-    const int kk = 16 * (w + 4 * jk) + i;
+  for (int jm = 0; jm < MR; ++jm) {
+    const int m = row_block(jm);
+    if (m >= NB) break;
 #pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) dGT[kk * LDG + 16 * m + 4 * g + rr] = aG[jk][m][rr];
+    for (int rr = 0; rr < 4; ++rr) dGT[kk * LDG + 16 * m + 4 * g + rr] = aG[jm][rr];
   }
   __syncthreads();
   {
     // reverse inclusive cumulative sum over rows, per channel (fixed order)
-    constexpr int parts = 256 / D, rp = C / parts;
-    __shared__ TG ptg[4 * D];
+    constexpr int parts = NT / D, rp = C / parts;
+    static_assert(C % parts == 0, "reverse cumulative sum layout");
     const int col = tid % D, part = tid / D;
     TG run = 0;
     for (int j = rp - 1; j >= 0; --j) {
@@ -435,7 +459,7 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
     ptg[part * D + col] = run;
     __syncthreads();
     TG off = 0;
-    for (int p = part + 1; p < parts; ++p) off += ptg[p * D + col];
+    for (int p2 = part + 1; p2 < parts; ++p2) off += ptg[p2 * D + col];
     for (int j = 0; j < rp; ++j) dGT[col * LDG + part * rp + j] += off;
     __syncthreads();
   }
@@ -445,21 +469,22 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
     TI* dqo = dq + L.t0 * ts + hoff;
     TI* dko = dk + L.t0 * ts + hoff;
 #pragma unroll
-    for (int jk = 0; jk < KBW; ++jk) {
-      const int kk = 16 * (w + 4 * jk) + i;
+    for (int jm = 0; jm < MR; ++jm) {
+      const int m = row_block(jm);
+      if (m >= NB) break;
 #pragma unroll
-      for (int m = 0; m < NB; ++m) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = 16 * m + 4 * g + rr;
-          if (r < L.len) {
-            const float qd = rowp[0][0][r] + rowp[0][1][r] + rowp[0][2][r] + rowp[0][3][r];
-            const float kd = rowp[1][0][r] + rowp[1][1][r] + rowp[1][2][r] + rowp[1][3][r];
-            const float qbar = to_f(qT[kk * LDQ + r]) * rq[r];
-            const float khat = to_f(kT[kk * LDQ + r]) * rk[r];
-            dqo[r * ts + kk] = from_f<TI>(rqs[r] * (aq[jk][m][rr] - qbar * qd));
-            dko[r * ts + kk] = from_f<TI>(rk[r] * (ak[jk][m][rr] - khat * kd));
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = 16 * m + 4 * g + rr;
+        if (r < L.len) {
+          float qd = 0.f, kd = 0.f;
+          for (int k2 = 0; k2 < NKB; ++k2) {
+            qd += rowp[0][k2][r];
+            kd += rowp[1][k2][r];
           }
+          const float qbar = to_f(qT[kk * LDQ + r]) * rq[r];
+          const float khat_ = to_f(kT[kk * LDQ + r]) * rk[r];
+          dqo[r * ts + kk] = from_f<TI>(rqs[r] * (aq[jm][rr] - qbar * qd));
+          dko[r * ts + kk] = from_f<TI>(rk[r] * (ak[jm][rr] - khat_ * kd));
         }
       }
     }
@@ -468,36 +493,45 @@ __global__ void __launch_bounds__(256) k_chunk_grad(Dims d, Inputs in, const TI*
     const TI* xr = static_cast<const TI*>(in.g) + L.t0 * ts + hoff;
     TI* dgo = dg + L.t0 * ts + hoff;
     float pdt = 0.f, pA = 0.f;
-    for (int e = tid; e < C * D; e += 256) {
-      const int r = e / D, kk = e % D;
-      if (r < L.len) {
-        const float z = ea * (to_f(xr[r * ts + kk]) + db[kk]);
+    constexpr int PER = (C * D + NT - 1) / NT;
+    float xin[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = tid + NT * j, r = e / D, kc = e % D;
+      xin[j] = (e < C * D && r < L.len) ? to_f(xr[r * ts + kc]) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = tid + NT * j, r = e / D, kc = e % D;
+      if (e < C * D && r < L.len) {
+        const float z = ea * (xin[j] + db[kc]);
         const float sz = sigmoidf(z);
-        const float dz = static_cast<float>(dGT[kk * LDG + r]) * d.lb * sz * (1.f - sz);
+        const float dz = static_cast<float>(dGT[kc * LDG + r]) * d.lb * sz * (1.f - sz);
         const float dx = dz * ea;
-        dgo[r * ts + kk] = from_f<TI>(dx);
+        dgo[r * ts + kc] = from_f<TI>(dx);
         pdt += dx;
         pA += dz * z;
       }
     }
     // tid % D is this thread's channel for every e above
-    ptot[(tid / D) * D + tid % D] = pdt;
+    ptot[tid] = pdt;
     red[tid] = pA;
-    for (int r = tid; r < L.len; r += 256) {
-      const float db_ = dbp[0][r] + dbp[1][r] + dbp[2][r] + dbp[3][r];
+    for (int r = tid; r < L.len; r += NT) {
+      float db_ = 0.f;
+      for (int w2 = 0; w2 < NW; ++w2) db_ += dbp[w2][r];
       dbeta[(L.t0 + r) * d.H + h] = from_f<TI>(db_ * be[r] * (1.f - be[r]));
     }
     __syncthreads();
     float* part = partials + (static_cast<size_t>(cglob) * d.H + h) * (K + 1);
     if (tid < D) {
-      float s = 0.f;
-      for (int p = 0; p < 256 / D; ++p) s += ptot[p * D + tid];
-      part[tid] = s;
+      float s2 = 0.f;
+      for (int p2 = 0; p2 < NT / D; ++p2) s2 += ptot[p2 * D + tid];
+      part[tid] = s2;
     }
     if (tid == 0) {
-      float s = 0.f;
-      for (int j = 0; j < 256; ++j) s += red[j];
-      part[K] = s;
+      float s2 = 0.f;
+      for (int j = 0; j < NT; ++j) s2 += red[j];
+      part[K] = s2;
     }
   }
 }
@@ -507,7 +541,7 @@ static hipError_t launch_cg(const Dims& d, const Inputs& in, const void* dO, int
                             int seg_chunks, const ChunkOps& ops, const SegStates& st, void* dq,
                             void* dk, void* dv, void* dg, void* dbeta, float* partials,
                             hipStream_t s) {
-  hipLaunchKernelGGL((k_chunk_grad<TI, TI, D, C>), dim3(seg_chunks * d.H), dim3(256), 0, s, d,
+  hipLaunchKernelGGL((k_chunk_grad<TI, TI, D, C>), dim3(seg_chunks * d.H), dim3(D * 4 * grad_split<D>()), 0, s, d,
                      in, static_cast<const TI*>(dO), seg_begin, ops, st, static_cast<TI*>(dq),
                      static_cast<TI*>(dk), static_cast<TI*>(dv), static_cast<TI*>(dg),
                      static_cast<TI*>(dbeta), partials);

@@ -126,31 +126,46 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
     }
     float* gam = ops.gam + idx * K;
     for (int kk = tid; kk < K; kk += 256) gam[kk] = kexp<OpT>(Gs[(C - 1) * LDG + kk]);
+    // Element-wise outputs. All global loads of a loop are issued before its
+    // stores (the output and input pointers may alias as far as the compiler
+    // knows, which would otherwise serialise every load behind a store).
+    constexpr int PER = C * K / 256;
     // row-major [C][K] outputs: qg (forward) or kg (backward)
-    OpT* rowm = static_cast<OpT*>(BWD ? ops.kg : ops.qg) + idx * C * K;
-    for (int e = tid; e < C * K; e += 256) {
-      const int r = e / K, kk = e % K;
-      float val = 0.f;
-      if (r < L.len) {
-        const float gr = Gs[r * LDG + kk];
-        val = BWD ? to_f(kr[r * ts + kk]) * rk[r] * kexp<OpT>(Gs[(C - 1) * LDG + kk] - gr)
-                  : to_f(qr[r * ts + kk]) * rqs[r] * kexp<OpT>(gr);
+    {
+      float src[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int e = tid + 256 * j, r = e / K, kk = e % K;
+        src[j] = r < L.len ? to_f((BWD ? kr : qr)[r * ts + kk]) : 0.f;
       }
-      rowm[e] = from_f<OpT>(val);
+      OpT* rowm = static_cast<OpT*>(BWD ? ops.kg : ops.qg) + idx * C * K;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int e = tid + 256 * j, r = e / K, kk = e % K;
+        const float gr = Gs[r * LDG + kk];
+        const float val = BWD ? src[j] * rk[r] * kexp<OpT>(Gs[(C - 1) * LDG + kk] - gr)
+                              : src[j] * rqs[r] * kexp<OpT>(gr);
+        rowm[e] = from_f<OpT>(val);
+      }
     }
     // transposed [K][C] outputs: kgT always, qgT for the backward
-    OpT* kgT = static_cast<OpT*>(ops.kgT) + idx * K * C;
-    OpT* qgT = BWD ? static_cast<OpT*>(ops.qgT) + idx * K * C : nullptr;
-    for (int e = tid; e < K * C; e += 256) {
-      const int kk = e / C, r = e % C;
-      float vk = 0.f, vq = 0.f;
-      if (r < L.len) {
-        const float gr = Gs[r * LDG + kk];
-        vk = to_f(kr[r * ts + kk]) * rk[r] * kexp<OpT>(Gs[(C - 1) * LDG + kk] - gr);
-        if (BWD) vq = to_f(qr[r * ts + kk]) * rqs[r] * kexp<OpT>(gr);
+    {
+      float ks[PER], qs[BWD ? PER : 1];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int e = tid + 256 * j, kk = e / C, r = e % C;
+        ks[j] = r < L.len ? to_f(kr[r * ts + kk]) : 0.f;
+        if (BWD) qs[j] = r < L.len ? to_f(qr[r * ts + kk]) : 0.f;
       }
-      kgT[e] = from_f<OpT>(vk);
-      if (BWD) qgT[e] = from_f<OpT>(vq);
+      OpT* kgT = static_cast<OpT*>(ops.kgT) + idx * K * C;
+      OpT* qgT = BWD ? static_cast<OpT*>(ops.qgT) + idx * K * C : nullptr;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int e = tid + 256 * j, kk = e / C, r = e % C;
+        const float gr = Gs[r * LDG + kk];
+        kgT[e] = from_f<OpT>(ks[j] * rk[r] * kexp<OpT>(Gs[(C - 1) * LDG + kk] - gr));
+        if (BWD) qgT[e] = from_f<OpT>(qs[j] * rqs[r] * kexp<OpT>(gr));
+      }
     }
   }
   __syncthreads();
@@ -174,24 +189,39 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
     for (int r = 0; r < 16; ++r) Ts[(16 * I + r) * LDM + 16 * I + j] = tcol[r];
   }
   __syncthreads();
-  // off-diagonal blocks, one block row at a time:
-  //   T[I, J] = -T[I, I] * sum_{J <= M < I} A[I, M] T[M, J]
-  for (int I = 1; I < NB; ++I) {
-    const int ncol = 16 * I;
-    for (int e = tid; e < 16 * ncol; e += 256) {
-      const int r = e / ncol, cc = e % ncol;
-      const int R = 16 * I + r;
-      float s = 0.f;
-      for (int m = (cc / 16) * 16; m < ncol; ++m) s += Ms[R * LDM + m] * Ts[m * LDM + cc];
-      Sx[r * C + cc] = be[R] * s;
+  // Off-diagonal blocks on fp32 MFMA (v_mfma_f32_16x16x4_f32), level by
+  // level d = I - J (blocks of one level are independent):
+  //   S[I, J] = sum_{J <= M < I} A[I, M] T[M, J],   T[I, J] = -T[I, I] S[I, J]
+  // with A[r, s] = beta_r P[r, s]. Sx holds one 16x16 S block per block of
+  // the level.
+  for (int dl = 1; dl < NB; ++dl) {
+    for (int b = w; b < NB - dl; b += 4) {
+      const int J = b, I = J + dl;
+      f32x4 acc = zero4();
+      const float bI = be[16 * I + i];
+      for (int Mb = J; Mb < I; ++Mb) {
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const float a = bI * Ms[(16 * I + i) * LDM + 16 * Mb + k0 + g];
+          const float t = Ts[(16 * Mb + k0 + g) * LDM + 16 * J + i];
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, t, acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) Sx[b * 256 + (4 * g + rr) * 16 + i] = acc[rr];
     }
     __syncthreads();
-    for (int e = tid; e < 16 * ncol; e += 256) {
-      const int r = e / ncol, cc = e % ncol;
-      const int R = 16 * I + r;
-      float s = 0.f;
-      for (int r2 = 0; r2 <= r; ++r2) s += Ts[R * LDM + 16 * I + r2] * Sx[r2 * C + cc];
-      Ts[R * LDM + cc] = -s;
+    for (int b = w; b < NB - dl; b += 4) {
+      const int J = b, I = J + dl;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4) {
+        const float a = Ts[(16 * I + i) * LDM + 16 * I + k0 + g];
+        const float sx = Sx[b * 256 + (k0 + g) * 16 + i];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sx, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) Ts[(16 * I + 4 * g + rr) * LDM + 16 * J + i] = -acc[rr];
     }
     __syncthreads();
   }
@@ -208,62 +238,68 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
 
   // ---- W = T Kb and U = T Bv (MFMA). Kb^T / Bv^T fragments are generated:
   // lane (i, g) holds column i (a channel) and k-slots s = s0 + g*KPL + j.
+  // The raw k / v values a wave needs are loaded up front (strided reads of
+  // the chunk tile, all in flight together).
+  constexpr int NSF = C / KS;  // fragments along the chunk
+  constexpr int NMW = (K / 16 + 3) / 4;
   OpT* Wn = static_cast<OpT*>(ops.Wn) + idx * C * K;
-  for (int mk = w; mk < K / 16; mk += 4) {
-    f32x4 acc[NB], acc2[NB];
+  {
+    float raw[NMW][NSF][KPL], vraw[NMW][NSF][KPL];
 #pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] = acc2[n] = zero4();
-    const int kk = 16 * mk + i;
-    for (int s0 = 0; s0 < C; s0 += KS) {
-      const auto gen = M::make([&](int j) {
-        const int s = s0 + g * KPL + j;
-        return s < L.len ? be[s] * rk[s] * to_f(kr[s * ts + kk]) * kexp<OpT>(Gs[s * LDG + kk])
-                         : 0.f;
-      });
+    for (int jm = 0; jm < NMW; ++jm) {
+      const int kk = 16 * (w + 4 * jm) + i;
+#pragma unroll
+      for (int f = 0; f < NSF; ++f)
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const int s_ = f * KS + g * KPL + j;
+          const bool ok = s_ < L.len && w + 4 * jm < K / 16;
+          raw[jm][f][j] = ok ? to_f(kr[s_ * ts + kk]) : 0.f;
+          vraw[jm][f][j] = ok ? to_f(vr[s_ * ts + kk]) : 0.f;
+        }
+    }
+#pragma unroll
+    for (int jm = 0; jm < NMW; ++jm) {
+      const int mk = w + 4 * jm;
+      if (mk >= K / 16) break;
+      const int kk = 16 * mk + i;
+      f32x4 acc[NB], acc2[NB], accu[NB];
+#pragma unroll
+      for (int n = 0; n < NB; ++n) acc[n] = acc2[n] = accu[n] = zero4();
+#pragma unroll
+      for (int f = 0; f < NSF; ++f) {
+        const int s0 = f * KS;
+        const auto gk = M::make([&](int j) {
+          const int s_ = s0 + g * KPL + j;
+          return be[s_] * rk[s_] * raw[jm][f][j] * kexp<OpT>(Gs[s_ * LDG + kk]);
+        });
+        const auto gv = M::make([&](int j) { return be[s0 + g * KPL + j] * vraw[jm][f][j]; });
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          const auto tb = M::load(Tb + (16 * n + i) * LDT + s0 + g * KPL);
+          acc[n] = M::mma(gk, tb, acc[n]);              // W^T tile (k rows, r cols)
+          if (BWD) acc2[n] = M::mma(tb, gk, acc2[n]);   // W tile (r rows, k cols)
+          if (BWD) accu[n] = M::mma(gv, tb, accu[n]);   // U^T tile: U[16n + i][16mk + 4g + rr]
+          else accu[n] = M::mma(tb, gv, accu[n]);       // U tile: U[16n + 4g + rr][16mk + i]
+        }
+      }
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        const auto tb = M::load(Tb + (16 * n + i) * LDT + s0 + g * KPL);
-        acc[n] = M::mma(gen, tb, acc[n]);      // W^T tile (k rows, r cols)
-        if (BWD) acc2[n] = M::mma(tb, gen, acc2[n]);  // W tile (r rows, k cols)
+        // acc[n][rr] = W[16n + i][16mk + 4g + rr]
+        OpT* dst = Wn + (16 * n + i) * K + 16 * mk + 4 * g;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(-acc[n][rr]);
+        if (BWD) {
+          // acc2[n][rr] = W[16n + 4g + rr][16mk + i]  ->  WnT[k][r..r+3]
+          OpT* dT = static_cast<OpT*>(ops.WnT) + idx * K * C + (16 * mk + i) * C + 16 * n + 4 * g;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) dT[rr] = from_f<OpT>(-acc2[n][rr]);
+        }
+        OpT* du = BWD ? static_cast<OpT*>(ops.U) + idx * C * V + (16 * n + i) * V + 16 * mk + 4 * g
+                      : static_cast<OpT*>(ops.UT) + idx * V * C + (16 * mk + i) * C + 16 * n + 4 * g;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) du[rr] = from_f<OpT>(accu[n][rr]);
       }
-    }
-#pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      // acc[n][rr] = W[16n + i][16mk + 4g + rr]
-      OpT* dst = Wn + (16 * n + i) * K + 16 * mk + 4 * g;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(-acc[n][rr]);
-      if (BWD) {
-        // acc2[n][rr] = W[16n + 4g + rr][16mk + i]  ->  WnT[k][r..r+3]
-        OpT* dT = static_cast<OpT*>(ops.WnT) + idx * K * C + (16 * mk + i) * C + 16 * n + 4 * g;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dT[rr] = from_f<OpT>(-acc2[n][rr]);
-      }
-    }
-  }
-  for (int mv = w; mv < V / 16; mv += 4) {
-    f32x4 acc[NB];
-#pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] = zero4();
-    const int vv = 16 * mv + i;
-    for (int s0 = 0; s0 < C; s0 += KS) {
-      const auto gen = M::make([&](int j) {
-        const int s = s0 + g * KPL + j;
-        return s < L.len ? be[s] * to_f(vr[s * ts + vv]) : 0.f;
-      });
-#pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const auto tb = M::load(Tb + (16 * n + i) * LDT + s0 + g * KPL);
-        if (BWD) acc[n] = M::mma(gen, tb, acc[n]);  // U^T tile: U[16n + i][16mv + 4g + rr]
-        else acc[n] = M::mma(tb, gen, acc[n]);      // U tile: U[16n + 4g + rr][16mv + i]
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      OpT* dst = BWD ? static_cast<OpT*>(ops.U) + idx * C * V + (16 * n + i) * V + 16 * mv + 4 * g
-                     : static_cast<OpT*>(ops.UT) + idx * V * C + (16 * mv + i) * C + 16 * n + 4 * g;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(acc[n][rr]);
     }
   }
 }

@@ -167,6 +167,7 @@ int hip_fail(hipError_t e) {
 // recorded on the launch stream around each launch of the calling thread.
 struct ProfRec {
   int kind;
+  int64_t units;
   hipEvent_t a, b;
 };
 thread_local bool g_prof_on = false;
@@ -174,9 +175,10 @@ thread_local std::vector<ProfRec> g_prof;
 
 struct ProfScope {
   int kind;
+  int64_t units;
   hipStream_t s;
   hipEvent_t a = nullptr;
-  ProfScope(int k, hipStream_t st) : kind(k), s(st) {
+  ProfScope(int k, int64_t u, hipStream_t st) : kind(k), units(u), s(st) {
     if (g_prof_on && hipEventCreate(&a) == hipSuccess) hipEventRecord(a, s);
   }
   void done() {
@@ -184,7 +186,7 @@ struct ProfScope {
     hipEvent_t b = nullptr;
     if (hipEventCreate(&b) == hipSuccess) {
       hipEventRecord(b, s);
-      g_prof.push_back({kind, a, b});
+      g_prof.push_back({kind, units, a, b});
     } else {
       hipEventDestroy(a);
     }
@@ -192,9 +194,9 @@ struct ProfScope {
   }
 };
 
-#define KDA_TRY(kind, expr)                    \
+#define KDA_TRY(kind, units, expr)             \
   do {                                         \
-    ProfScope ps_(kind, s);                    \
+    ProfScope ps_(kind, units, s);             \
     const hipError_t e_ = (expr);              \
     ps_.done();                                \
     if (e_ != hipSuccess) return hip_fail(e_); \
@@ -245,9 +247,9 @@ int kda_prologue(const kda_problem* p, const void* q, const void* k, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* coff = static_cast<int32_t*>(workspace);
   Inputs in{q, k, nullptr, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, coff};
-  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
+  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
   if (P.NC > 0)
-    KDA_TRY(KDA_KERNEL_PROLOGUE, launch_prologue(P.dtype, P.D, P.C, make_dims(p), in, P.NC, qh, kh, beta, gcum, s));
+    KDA_TRY(KDA_KERNEL_PROLOGUE, static_cast<int64_t>(P.NC) * P.H, launch_prologue(P.dtype, P.D, P.C, make_dims(p), in, P.NC, qh, kh, beta, gcum, s));
   return KDA_OK;
 }
 
@@ -274,11 +276,11 @@ int kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
   const ChunkOps ops = carve_ops(P, false, cur);
   const Dims d = make_dims(p);
   const Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, coff};
-  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
+  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
   for (int sg = 0; sg < P.NS; ++sg) {
     const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
-    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, launch_chunk_local(P.dtype, P.D, P.C, false, d, in, c0, c1 - c0, ops, s));
-    KDA_TRY(KDA_KERNEL_SCAN_FWD, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops, o, nullptr, carry[sg & 1],
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, false, d, in, c0, c1 - c0, ops, s));
+    KDA_TRY(KDA_KERNEL_SCAN_FWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops, o, nullptr, carry[sg & 1],
                             carry[(sg + 1) & 1], s));
   }
   return KDA_OK;
@@ -330,25 +332,25 @@ int kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
   }
   const Dims d = make_dims(p);
   const Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, coff};
-  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
+  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
   // checkpoint pass: the state entering each segment
   for (int sg = 0; sg + 1 < P.NS; ++sg) {
     const int c0 = sg * P.seg, c1 = c0 + P.seg;
-    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, launch_chunk_local(P.dtype, P.D, P.C, false, d, in, c0, c1 - c0, ops_f, s));
-    KDA_TRY(KDA_KERNEL_SCAN_FWD, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_f, nullptr, nullptr,
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, false, d, in, c0, c1 - c0, ops_f, s));
+    KDA_TRY(KDA_KERNEL_SCAN_FWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_f, nullptr, nullptr,
                             ckpt + sg * slot, ckpt + (sg + 1) * slot, s));
   }
   for (int sg = P.NS - 1; sg >= 0; --sg) {
     const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
-    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, launch_chunk_local(P.dtype, P.D, P.C, true, d, in, c0, c1 - c0, ops_b, s));
-    KDA_TRY(KDA_KERNEL_SCAN_FWD, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_b, nullptr, &sts,
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, true, d, in, c0, c1 - c0, ops_b, s));
+    KDA_TRY(KDA_KERNEL_SCAN_FWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_b, nullptr, &sts,
                             ckpt + sg * slot, ckpt + (sg + 1) * slot, s));
-    KDA_TRY(KDA_KERNEL_SCAN_BWD, launch_scan_bwd(P.dtype, P.D, P.C, d, in, dO, c0, c1, ops_b, sts,
+    KDA_TRY(KDA_KERNEL_SCAN_BWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_bwd(P.dtype, P.D, P.C, d, in, dO, c0, c1, ops_b, sts,
                             dcarry[(sg + 1) & 1], dcarry[sg & 1], s));
-    KDA_TRY(KDA_KERNEL_CHUNK_GRAD, launch_chunk_grad(P.dtype, P.D, P.C, d, in, dO, c0, c1 - c0, ops_b, sts, dq, dk, dv,
+    KDA_TRY(KDA_KERNEL_CHUNK_GRAD, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_grad(P.dtype, P.D, P.C, d, in, dO, c0, c1 - c0, ops_b, sts, dq, dk, dv,
                               draw_g, draw_beta, partials, s));
   }
-  KDA_TRY(KDA_KERNEL_GATE_REDUCE, launch_gate_reduce(P.D, P.H, P.NC, partials, dA_log, ddt_bias, s));
+  KDA_TRY(KDA_KERNEL_GATE_REDUCE, 0, launch_gate_reduce(P.D, P.H, P.NC, partials, dA_log, ddt_bias, s));
   return KDA_OK;
 }
 
@@ -362,11 +364,12 @@ int kda_profile_begin(void) {
   return KDA_OK;
 }
 
-int kda_profile_end(int32_t* launches, double* total_ms, int n) {
+int kda_profile_end(int32_t* launches, double* total_ms, int64_t* units, int n) {
   g_prof_on = false;
   for (int k = 0; k < n; ++k) {
     if (launches) launches[k] = 0;
     if (total_ms) total_ms[k] = 0.0;
+    if (units) units[k] = 0;
   }
   int st = KDA_OK;
   for (auto& r : g_prof) {
@@ -376,6 +379,7 @@ int kda_profile_end(int32_t* launches, double* total_ms, int n) {
     if (r.kind >= 0 && r.kind < n) {
       if (launches) launches[r.kind] += 1;
       if (total_ms) total_ms[r.kind] += ms;
+      if (units) units[r.kind] += r.units;
     }
     hipEventDestroy(r.a);
     hipEventDestroy(r.b);

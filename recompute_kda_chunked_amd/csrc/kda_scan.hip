@@ -1,4 +1,5 @@
-// Inter-chunk state scans: one block per (sequence, head, value tile).
+// Inter-chunk state scans: one block (4 waves) per (sequence, head, value
+// tile).
 //
 // Forward direction ("KDA at the production shape..." section 1.1: the state
 // stays on chip for the whole chunk loop; per chunk v_new = u - w h, the
@@ -11,7 +12,14 @@
 // Value columns of the state evolve independently, so the value dimension is
 // split into tiles of BV columns, one block each (the V-tiling of the FLA
 // state kernel, section 1.1). The fp32 state lives in registers as 16x16
-// MFMA accumulator tiles; an operand copy sits in LDS for the next chunk.
+// MFMA accumulator tiles; a bf16 (or fp32) operand copy sits in LDS.
+//
+// Work split: wave w owns row block m = w of the chunk (Vn, O or dVn tiles,
+// all value blocks of the tile) and MKW row blocks of the state. The serial
+// chunk loop is software-pipelined: the per-chunk operands a wave needs
+// (rows of W, qg, Aqk, kg^T, U, gamma, dO, ...) for chunk c+1 are loaded into
+// registers while chunk c is computed, so the global-load latency stays off
+// the recurrence.
 //
 // Block-to-XCD mapping: blocks are dealt round-robin to the 8 XCDs, so the
 // NVT value tiles of one (sequence, head) get block ids that are equal mod 8
@@ -31,19 +39,86 @@ __device__ __forceinline__ bool scan_program(const Dims& d, int& n, int& h, int&
   return true;
 }
 
+// Tile geometry shared by both scans.
+template <typename OpT, int D, int C, int BV>
+struct ScanGeo {
+  using M = Mma<OpT>;
+  static constexpr int K = D, V = D, NB = C / 16, NVT = V / BV, BVT = BV / 16;
+  static constexpr int NHT = (K / 16) * BVT;  // state tiles
+  static constexpr int HPW = NHT / 4;          // state tiles per wave
+  static constexpr int MKW = HPW / BVT;        // state row blocks per wave
+  static constexpr int NKF = K / M::KS;        // fragments along K
+  static constexpr int NCF = C / M::KS;        // fragments along C
+  static constexpr int LDH = K + 8, LDC = C + 8;
+  static_assert(NHT % 4 == 0 && HPW % BVT == 0, "state tiles must split over 4 waves");
+};
+
+// Operands of one chunk for one wave of the forward scan.
+template <typename OpT, int D, int C, int BV>
+struct FwdOps {
+  using G = ScanGeo<OpT, D, C, BV>;
+  using F = typename G::M::frag;
+  F w[G::NKF];                // W rows of block m (negated: -W)
+  F q[G::NKF];                // qg rows of block m (output only)
+  F a[G::NCF];                // Aqk rows of block m (output only)
+  float u[G::BVT][4];         // U at the Vn tile positions
+  F kt[G::MKW][G::NCF];       // kg^T rows of the wave's state row blocks
+  float gm[G::MKW][4];        // gamma at the wave's state rows
+};
+
+template <typename OpT, int D, int C, int BV, bool OUT_O, bool REC>
+__device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const ChunkOps& ops,
+                                             size_t idx, int v0, int w, int i, int g) {
+  using G = ScanGeo<OpT, D, C, BV>;
+  using M = typename G::M;
+  constexpr int K = G::K, V = G::V;
+  if (w < G::NB) {
+    const int m = w;
+    const OpT* Wn = static_cast<const OpT*>(ops.Wn) + idx * C * K + (16 * m + i) * K + g * M::KPL;
+#pragma unroll
+    for (int j = 0; j < G::NKF; ++j) f.w[j] = M::load(Wn + j * M::KS);
+    if (OUT_O) {
+      const OpT* qg = static_cast<const OpT*>(ops.qg) + idx * C * K + (16 * m + i) * K + g * M::KPL;
+#pragma unroll
+      for (int j = 0; j < G::NKF; ++j) f.q[j] = M::load(qg + j * M::KS);
+      const OpT* aq = static_cast<const OpT*>(ops.Aqk) + idx * C * C + (16 * m + i) * C + g * M::KPL;
+#pragma unroll
+      for (int j = 0; j < G::NCF; ++j) f.a[j] = M::load(aq + j * M::KS);
+    }
+#pragma unroll
+    for (int nv = 0; nv < G::BVT; ++nv) {
+      if (REC) {
+        const OpT* U = static_cast<const OpT*>(ops.U) + idx * C * V;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) f.u[nv][rr] = to_f(U[(16 * m + 4 * g + rr) * V + v0 + 16 * nv + i]);
+      } else {
+        const OpT* src = static_cast<const OpT*>(ops.UT) + idx * V * C + (v0 + 16 * nv + i) * C + 16 * m + 4 * g;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) f.u[nv][rr] = to_f(src[rr]);
+      }
+    }
+  }
+  const OpT* kgT = static_cast<const OpT*>(ops.kgT) + idx * K * C;
+  const float* gam = ops.gam + idx * K;
+#pragma unroll
+  for (int jm = 0; jm < G::MKW; ++jm) {
+    const int mk = w * G::MKW + jm;
+#pragma unroll
+    for (int j = 0; j < G::NCF; ++j) f.kt[jm][j] = M::load(kgT + (16 * mk + i) * C + j * M::KS + g * M::KPL);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) f.gm[jm][rr] = gam[16 * mk + 4 * g + rr];
+  }
+}
+
 template <typename TI, typename OpT, int D, int C, int BV, bool OUT_O, bool REC>
 __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_begin,
                                                   int seg_end, ChunkOps ops, TI* o,
                                                   SegStates st, const float* carry_in,
                                                   float* carry_out) {
-  using M = Mma<OpT>;
-  constexpr int K = D, V = D, NB = C / 16, NVT = V / BV, KPL = M::KPL, KS = M::KS;
-  constexpr int BVT = BV / 16;
-  constexpr int NHT = (K / 16) * BVT, HPW = NHT / 4;  // state tiles, per wave
-  constexpr int NVN = NB * BVT;                         // Vn tiles
-  constexpr int VPW = (NVN + 3) / 4;
-  constexpr int LDH = K + 8, LDC = C + 8;
-  static_assert(NHT % 4 == 0, "state tiles must split over 4 waves");
+  using G = ScanGeo<OpT, D, C, BV>;
+  using M = typename G::M;
+  constexpr int K = G::K, V = G::V, NB = G::NB, NVT = G::NVT, BVT = G::BVT;
+  constexpr int HPW = G::HPW, MKW = G::MKW, LDH = G::LDH, LDC = G::LDC, KS = M::KS, KPL = M::KPL;
   __shared__ __attribute__((aligned(16))) OpT hT_s[BV * LDH];
   __shared__ __attribute__((aligned(16))) OpT VnT_s[BV * LDC];
 
@@ -55,11 +130,12 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
   const int v0 = vt * BV;
   const size_t ts = static_cast<size_t>(d.H) * V;
 
+  // state tile j of this wave: row block mk = w*MKW + j/BVT, value block nv = j%BVT
   f32x4 hs[HPW];
   const bool fresh = (cb == in.coff[n]);
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
-    const int t = w * HPW + j, mk = t / BVT, nv = t % BVT;
+    const int mk = w * MKW + j / BVT, nv = j % BVT;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int kk = 16 * mk + 4 * g + rr, vv = v0 + 16 * nv + i;
@@ -69,111 +145,157 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
   auto put_state = [&]() {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
-      const int t = w * HPW + j, mk = t / BVT, nv = t % BVT;
+      const int mk = w * MKW + j / BVT, nv = j % BVT;
       OpT* dst = hT_s + (16 * nv + i) * LDH + 16 * mk + 4 * g;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(hs[j][rr]);
     }
   };
   put_state();
+
+  FwdOps<OpT, D, C, BV> cur, nxt;
+  load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(cur, ops, static_cast<size_t>(cb - seg_begin) * d.H + h,
+                                          v0, w, i, g);
   __syncthreads();
 
   for (int c = cb; c < ce; ++c) {
     const size_t idx = static_cast<size_t>(c - seg_begin) * d.H + h;
-    const OpT* Wn = static_cast<const OpT*>(ops.Wn) + idx * C * K;
-    const OpT* kgT = static_cast<const OpT*>(ops.kgT) + idx * K * C;
-    const float* gam = ops.gam + idx * K;
+    if (c + 1 < ce)
+      load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(nxt, ops, idx + d.H, v0, w, i, g);
     if (REC) {
       // entering state h_n as [K][V]
       OpT* hd = static_cast<OpT*>(st.h) + idx * K * V;
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
-        const int t = w * HPW + j, mk = t / BVT, nv = t % BVT;
+        const int mk = w * MKW + j / BVT, nv = j % BVT;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
           hd[(16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = from_f<OpT>(hs[j][rr]);
       }
     }
-    // Vn = U - W h (and the inter part of O), tiles (row block m, value block nv)
-    f32x4 accO[VPW];
+    // Vn = U - W h and the inter part qg h of O: row block m = w, all value blocks
+    f32x4 accO[BVT];
+    if (w < NB) {
+      const int m = w;
 #pragma unroll
-    for (int j = 0; j < VPW; ++j) {
-      const int t = w + 4 * j;
-      if (t >= NVN) break;
-      const int m = t / BVT, nv = t % BVT;
-      f32x4 accV;
-      if (REC) {
-        const OpT* U = static_cast<const OpT*>(ops.U) + idx * C * V;
+      for (int nv = 0; nv < BVT; ++nv) {
+        f32x4 accV = {cur.u[nv][0], cur.u[nv][1], cur.u[nv][2], cur.u[nv][3]};
+        accO[nv] = zero4();
+        const OpT* bh = hT_s + (16 * nv + i) * LDH + g * KPL;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) accV[rr] = to_f(U[(16 * m + 4 * g + rr) * V + v0 + 16 * nv + i]);
-      } else {
-        const OpT* UT = static_cast<const OpT*>(ops.UT) + idx * V * C;
-        const OpT* src = UT + (v0 + 16 * nv + i) * C + 16 * m + 4 * g;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) accV[rr] = to_f(src[rr]);
-      }
-      accO[j] = zero4();
-      const OpT* aw = Wn + (16 * m + i) * K + g * KPL;
-      const OpT* bh = hT_s + (16 * nv + i) * LDH + g * KPL;
-      if (OUT_O) {
-        const OpT* aq = static_cast<const OpT*>(ops.qg) + idx * C * K + (16 * m + i) * K + g * KPL;
-        for (int k0 = 0; k0 < K; k0 += KS) {
-          const auto b = M::load(bh + k0);
-          accV = M::mma(M::load(aw + k0), b, accV);
-          accO[j] = M::mma(M::load(aq + k0), b, accO[j]);
+        for (int j = 0; j < G::NKF; ++j) {
+          const auto b = M::load(bh + j * KS);
+          accV = M::mma(cur.w[j], b, accV);
+          if (OUT_O) accO[nv] = M::mma(cur.q[j], b, accO[nv]);
         }
-      } else {
-        for (int k0 = 0; k0 < K; k0 += KS) accV = M::mma(M::load(aw + k0), M::load(bh + k0), accV);
-      }
-      OpT* dst = VnT_s + (16 * nv + i) * LDC + 16 * m + 4 * g;
+        OpT* dst = VnT_s + (16 * nv + i) * LDC + 16 * m + 4 * g;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(accV[rr]);
-      if (REC) {
-        OpT* vn = static_cast<OpT*>(st.Vn) + idx * C * V;
+        for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(accV[rr]);
+        if (REC) {
+          OpT* vn = static_cast<OpT*>(st.Vn) + idx * C * V;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          vn[(16 * m + 4 * g + rr) * V + v0 + 16 * nv + i] = from_f<OpT>(accV[rr]);
+          for (int rr = 0; rr < 4; ++rr)
+            vn[(16 * m + 4 * g + rr) * V + v0 + 16 * nv + i] = from_f<OpT>(accV[rr]);
+        }
       }
     }
     __syncthreads();
-    if (OUT_O) {
+    if (OUT_O && w < NB) {
+      const int m = w;
       const int64_t t0 = static_cast<int64_t>(in.cu[n]) + static_cast<int64_t>(c - in.coff[n]) * C;
       const int len = static_cast<int>(min(static_cast<int64_t>(C), in.cu[n + 1] - t0));
-      const OpT* Aqk = static_cast<const OpT*>(ops.Aqk) + idx * C * C;
+      const int nf = (16 * (m + 1) + KS - 1) / KS;  // Aqk[r][s] = 0 for s > r
 #pragma unroll
-      for (int j = 0; j < VPW; ++j) {
-        const int t = w + 4 * j;
-        if (t >= NVN) break;
-        const int m = t / BVT, nv = t % BVT;
-        accO[j] = tile_nt<OpT>(accO[j], Aqk + 16 * m * C, C, VnT_s + 16 * nv * LDC, LDC, 0,
-                               kround<OpT>(16 * (m + 1)), lane);
+      for (int nv = 0; nv < BVT; ++nv) {
+        const OpT* bv = VnT_s + (16 * nv + i) * LDC + g * KPL;
+#pragma unroll
+        for (int j = 0; j < G::NCF; ++j)
+          if (j < nf) accO[nv] = M::mma(cur.a[j], M::load(bv + j * KS), accO[nv]);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int r = 16 * m + 4 * g + rr;
-          if (r < len) o[(t0 + r) * ts + static_cast<size_t>(h) * V + v0 + 16 * nv + i] = from_f<TI>(accO[j][rr]);
+          if (r < len) o[(t0 + r) * ts + static_cast<size_t>(h) * V + v0 + 16 * nv + i] = from_f<TI>(accO[nv][rr]);
         }
       }
     }
     // h <- Diag(gamma) h + kg^T Vn
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
-      const int t = w * HPW + j, mk = t / BVT, nv = t % BVT;
+      const int jm = j / BVT, nv = j % BVT;
       f32x4 acc;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) acc[rr] = gam[16 * mk + 4 * g + rr] * hs[j][rr];
-      hs[j] = tile_nt<OpT>(acc, kgT + 16 * mk * C, C, VnT_s + 16 * nv * LDC, LDC, 0, C, lane);
+      for (int rr = 0; rr < 4; ++rr) acc[rr] = cur.gm[jm][rr] * hs[j][rr];
+      const OpT* bv = VnT_s + (16 * nv + i) * LDC + g * KPL;
+#pragma unroll
+      for (int jj = 0; jj < G::NCF; ++jj) acc = M::mma(cur.kt[jm][jj], M::load(bv + jj * KS), acc);
+      hs[j] = acc;
     }
+    // hT_s was last read before the barrier above; the barrier below also
+    // keeps the next chunk's VnT_s writes behind this chunk's VnT_s reads
     put_state();
     __syncthreads();
+    if (c + 1 < ce) cur = nxt;
   }
   if (ce < in.coff[n + 1]) {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
-      const int t = w * HPW + j, mk = t / BVT, nv = t % BVT;
+      const int mk = w * MKW + j / BVT, nv = j % BVT;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
         carry_out[(static_cast<size_t>(h) * K + 16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = hs[j][rr];
     }
+  }
+}
+
+// Operands of one chunk for one wave of the reverse scan.
+template <typename TI, typename OpT, int D, int C, int BV>
+struct BwdOps {
+  using G = ScanGeo<OpT, D, C, BV>;
+  using F = typename G::M::frag;
+  static constexpr int NDO = C * BV / 256;  // dO elements per thread
+  F at[G::NCF];               // Aqk^T rows of block m
+  F kg[G::NKF];               // kg rows of block m
+  F qt[G::MKW][G::NCF];       // qg^T rows of the wave's state row blocks
+  F wt[G::MKW][G::NCF];       // -W^T rows of the wave's state row blocks
+  float gm[G::MKW][4];
+  float dOv[NDO];             // dO tile elements this thread stages into LDS
+};
+
+template <typename TI, typename OpT, int D, int C, int BV>
+__device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const ChunkOps& ops,
+                                             size_t idx, const TI* dO, int64_t t0, int len,
+                                             size_t ts, int h, int v0, int tid, int w, int i,
+                                             int g) {
+  using G = ScanGeo<OpT, D, C, BV>;
+  using M = typename G::M;
+  constexpr int K = G::K, V = G::V;
+  if (w < G::NB) {
+    const int m = w;
+    const OpT* at = static_cast<const OpT*>(ops.AqkT) + idx * C * C + (16 * m + i) * C + g * M::KPL;
+#pragma unroll
+    for (int j = 0; j < G::NCF; ++j) f.at[j] = M::load(at + j * M::KS);
+    const OpT* kg = static_cast<const OpT*>(ops.kg) + idx * C * K + (16 * m + i) * K + g * M::KPL;
+#pragma unroll
+    for (int j = 0; j < G::NKF; ++j) f.kg[j] = M::load(kg + j * M::KS);
+  }
+  const OpT* qgT = static_cast<const OpT*>(ops.qgT) + idx * K * C;
+  const OpT* WnT = static_cast<const OpT*>(ops.WnT) + idx * K * C;
+  const float* gam = ops.gam + idx * K;
+#pragma unroll
+  for (int jm = 0; jm < G::MKW; ++jm) {
+    const int mk = w * G::MKW + jm;
+#pragma unroll
+    for (int j = 0; j < G::NCF; ++j) {
+      f.qt[jm][j] = M::load(qgT + (16 * mk + i) * C + j * M::KS + g * M::KPL);
+      f.wt[jm][j] = M::load(WnT + (16 * mk + i) * C + j * M::KS + g * M::KPL);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) f.gm[jm][rr] = gam[16 * mk + 4 * g + rr];
+  }
+#pragma unroll
+  for (int j = 0; j < BwdOps<TI, OpT, D, C, BV>::NDO; ++j) {
+    const int e = tid + 256 * j, r = e / BV, vv = e % BV;
+    f.dOv[j] = r < len ? to_f(dO[(t0 + r) * ts + static_cast<size_t>(h) * V + v0 + vv]) : 0.f;
   }
 }
 
@@ -182,12 +304,12 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
                                                   int seg_begin, int seg_end, ChunkOps ops,
                                                   SegStates st, const float* carry_in,
                                                   float* carry_out) {
-  using M = Mma<OpT>;
-  constexpr int K = D, V = D, NB = C / 16, NVT = V / BV;
-  constexpr int BVT = BV / 16;
-  constexpr int NHT = (K / 16) * BVT, HPW = NHT / 4;
-  constexpr int NVN = NB * BVT;
-  constexpr int LDH = K + 8, LDC = C + 8;
+  using G = ScanGeo<OpT, D, C, BV>;
+  using M = typename G::M;
+  using Ops = BwdOps<TI, OpT, D, C, BV>;
+  constexpr int K = G::K, V = G::V, NB = G::NB, NVT = G::NVT, BVT = G::BVT;
+  constexpr int HPW = G::HPW, MKW = G::MKW, LDH = G::LDH, LDC = G::LDC, KS = M::KS, KPL = M::KPL;
+  static_assert(C * BV % 256 == 0, "dO tile split");
   __shared__ __attribute__((aligned(16))) OpT dhT_s[BV * LDH];
   __shared__ __attribute__((aligned(16))) OpT dVnT_s[BV * LDC];
   __shared__ __attribute__((aligned(16))) OpT dOT_s[BV * LDC];
@@ -199,12 +321,18 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
   const int v0 = vt * BV;
   const size_t ts = static_cast<size_t>(d.H) * V;
+  auto chunk_t0 = [&](int c) {
+    return static_cast<int64_t>(in.cu[n]) + static_cast<int64_t>(c - in.coff[n]) * C;
+  };
+  auto chunk_len = [&](int64_t t0) {
+    return static_cast<int>(min(static_cast<int64_t>(C), in.cu[n + 1] - t0));
+  };
 
   f32x4 hs[HPW];  // dh' (gradient of the state leaving the current chunk)
   const bool fresh = (ce == in.coff[n + 1]);
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
-    const int t = w * HPW + j, mk = t / BVT, nv = t % BVT;
+    const int mk = w * MKW + j / BVT, nv = j % BVT;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int kk = 16 * mk + 4 * g + rr, vv = v0 + 16 * nv + i;
@@ -214,7 +342,7 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
   auto put_state = [&]() {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
-      const int t = w * HPW + j, mk = t / BVT, nv = t % BVT;
+      const int mk = w * MKW + j / BVT, nv = j % BVT;
       OpT* dst = dhT_s + (16 * nv + i) * LDH + 16 * mk + 4 * g;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(hs[j][rr]);
@@ -222,64 +350,82 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
   };
   put_state();
 
+  Ops cur, nxt;
+  {
+    const int64_t t0 = chunk_t0(ce - 1);
+    load_bwd_ops<TI, OpT, D, C, BV>(cur, ops, static_cast<size_t>(ce - 1 - seg_begin) * d.H + h, dO,
+                                    t0, chunk_len(t0), ts, h, v0, tid, w, i, g);
+  }
   for (int c = ce - 1; c >= cb; --c) {
     const size_t idx = static_cast<size_t>(c - seg_begin) * d.H + h;
-    const int64_t t0 = static_cast<int64_t>(in.cu[n]) + static_cast<int64_t>(c - in.coff[n]) * C;
-    const int len = static_cast<int>(min(static_cast<int64_t>(C), in.cu[n + 1] - t0));
+    if (c - 1 >= cb) {
+      const int64_t t1 = chunk_t0(c - 1);
+      load_bwd_ops<TI, OpT, D, C, BV>(nxt, ops, idx - d.H, dO, t1, chunk_len(t1), ts, h, v0, tid,
+                                      w, i, g);
+    }
     // dO tile, transposed into LDS ([BV][C]); padded rows are zero
-    for (int e = tid; e < C * BV; e += 256) {
-      const int r = e / BV, vv = e % BV;
-      dOT_s[vv * LDC + r] = r < len ? from_f<OpT>(to_f(dO[(t0 + r) * ts + static_cast<size_t>(h) * V + v0 + vv]))
-                                    : from_f<OpT>(0.f);
+#pragma unroll
+    for (int j = 0; j < Ops::NDO; ++j) {
+      const int e = tid + 256 * j, r = e / BV, vv = e % BV;
+      dOT_s[vv * LDC + r] = from_f<OpT>(cur.dOv[j]);
     }
     {
       OpT* hd = static_cast<OpT*>(st.dh) + idx * K * V;
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
-        const int t = w * HPW + j, mk = t / BVT, nv = t % BVT;
+        const int mk = w * MKW + j / BVT, nv = j % BVT;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
           hd[(16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = from_f<OpT>(hs[j][rr]);
       }
     }
     __syncthreads();
-    const OpT* AqkT = static_cast<const OpT*>(ops.AqkT) + idx * C * C;
-    const OpT* kg = static_cast<const OpT*>(ops.kg) + idx * C * K;
-    for (int t = w; t < NVN; t += 4) {
-      const int m = t / BVT, nv = t % BVT;
-      f32x4 acc = zero4();
-      // Aqk^T[r][s] is zero for s < r: start the reduction at the block's row
-      const int s_lo = (16 * m) / M::KS * M::KS;
-      acc = tile_nt<OpT>(acc, AqkT + 16 * m * C, C, dOT_s + 16 * nv * LDC, LDC, s_lo, C, lane);
-      acc = tile_nt<OpT>(acc, kg + 16 * m * K, K, dhT_s + 16 * nv * LDH, LDH, 0, K, lane);
-      OpT* dst = dVnT_s + (16 * nv + i) * LDC + 16 * m + 4 * g;
-      OpT* gd = static_cast<OpT*>(st.dVnT) + idx * V * C + (v0 + 16 * nv + i) * C + 16 * m + 4 * g;
+    if (w < NB) {
+      const int m = w;
+      const int f_lo = (16 * m) / KS;  // Aqk^T[r][s] = 0 for s < r
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        dst[rr] = from_f<OpT>(acc[rr]);
-        gd[rr] = from_f<OpT>(acc[rr]);
+      for (int nv = 0; nv < BVT; ++nv) {
+        f32x4 acc = zero4();
+        const OpT* bo = dOT_s + (16 * nv + i) * LDC + g * KPL;
+#pragma unroll
+        for (int j = 0; j < G::NCF; ++j)
+          if (j >= f_lo) acc = M::mma(cur.at[j], M::load(bo + j * KS), acc);
+        const OpT* bd = dhT_s + (16 * nv + i) * LDH + g * KPL;
+#pragma unroll
+        for (int j = 0; j < G::NKF; ++j) acc = M::mma(cur.kg[j], M::load(bd + j * KS), acc);
+        OpT* dst = dVnT_s + (16 * nv + i) * LDC + 16 * m + 4 * g;
+        OpT* gd = static_cast<OpT*>(st.dVnT) + idx * V * C + (v0 + 16 * nv + i) * C + 16 * m + 4 * g;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          dst[rr] = from_f<OpT>(acc[rr]);
+          gd[rr] = from_f<OpT>(acc[rr]);
+        }
       }
     }
     __syncthreads();
-    const OpT* qgT = static_cast<const OpT*>(ops.qgT) + idx * K * C;
-    const OpT* WnT = static_cast<const OpT*>(ops.WnT) + idx * K * C;
-    const float* gam = ops.gam + idx * K;
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
-      const int t = w * HPW + j, mk = t / BVT, nv = t % BVT;
+      const int jm = j / BVT, nv = j % BVT;
       f32x4 acc;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) acc[rr] = gam[16 * mk + 4 * g + rr] * hs[j][rr];
-      acc = tile_nt<OpT>(acc, qgT + 16 * mk * C, C, dOT_s + 16 * nv * LDC, LDC, 0, C, lane);
-      hs[j] = tile_nt<OpT>(acc, WnT + 16 * mk * C, C, dVnT_s + 16 * nv * LDC, LDC, 0, C, lane);
+      for (int rr = 0; rr < 4; ++rr) acc[rr] = cur.gm[jm][rr] * hs[j][rr];
+      const OpT* bo = dOT_s + (16 * nv + i) * LDC + g * KPL;
+      const OpT* bv = dVnT_s + (16 * nv + i) * LDC + g * KPL;
+#pragma unroll
+      for (int jj = 0; jj < G::NCF; ++jj) {
+        acc = M::mma(cur.qt[jm][jj], M::load(bo + jj * KS), acc);
+        acc = M::mma(cur.wt[jm][jj], M::load(bv + jj * KS), acc);
+      }
+      hs[j] = acc;
     }
-    __syncthreads();  // every wave is done reading dhT_s / dOT_s of this chunk
+    __syncthreads();  // every wave is done reading dhT_s / dOT_s / dVnT_s of this chunk
     put_state();
+    if (c - 1 >= cb) cur = nxt;
   }
   if (cb > in.coff[n]) {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
-      const int t = w * HPW + j, mk = t / BVT, nv = t % BVT;
+      const int mk = w * MKW + j / BVT, nv = j % BVT;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
         carry_out[(static_cast<size_t>(h) * K + 16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = hs[j][rr];
