@@ -30,6 +30,69 @@
 
 namespace kda {
 
+// A [D][C] tile (channel rows, chunk-row columns) staged in LDS: written as
+// packed row pairs by the element-wise pass, read as MFMA operand fragments
+// (KPL consecutive chunk rows of one channel) or drained to memory as
+// contiguous vectors.
+template <typename OpT, int D, int C>
+struct TileT;
+
+// bf16: unpadded rows of C elements; the 16-byte units of a row are permuted
+// by an XOR of channel bits so that both the packed-pair writes (16 lanes on
+// channels 8 apart) and the fragment reads (8 lanes on consecutive channels)
+// spread over the LDS banks.
+template <int D, int C>
+struct TileT<bf16, D, C> {
+  static_assert(C == 32 || C == 64, "bf16 tiles hold 32 or 64 chunk rows");
+  static constexpr int NU = C / 8;                // 16-byte units per row
+  static constexpr int R = C == 64 ? 0 : 1;       // log2(rows per 32 banks)
+  static constexpr int kElems = D * C;
+  static constexpr int kBytes = kElems * 2;
+  static __device__ __forceinline__ int swz(int kk) { return ((kk >> R) ^ (kk >> 3)) & (NU - 1); }
+  static __device__ __forceinline__ int off(int kk, int s) {
+    return kk * C + 8 * ((s >> 3) ^ swz(kk)) + (s & 7);
+  }
+  // rows s and s + 1 (s even) of channel kk
+  static __device__ __forceinline__ void put2(bf16* t, int kk, int s, float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    bf16x2 v;
+    v[0] = static_cast<bf16>(a);
+    v[1] = static_cast<bf16>(b);
+    *reinterpret_cast<bf16x2*>(t + off(kk, s)) = v;
+  }
+  // rows s .. s + 7 (s a multiple of 8) of channel kk
+  static __device__ __forceinline__ bf16x8 frag(const bf16* t, int kk, int s) {
+    return *reinterpret_cast<const bf16x8*>(t + off(kk, s));
+  }
+  static __device__ __forceinline__ void drain(const bf16* t, bf16* dst, int tid) {
+    for (int e = tid; e < D * NU; e += 256) {
+      const int kk = e / NU, u = e % NU;
+      *reinterpret_cast<bf16x8*>(dst + kk * C + 8 * u) =
+          *reinterpret_cast<const bf16x8*>(t + kk * C + 8 * (u ^ swz(kk)));
+    }
+  }
+};
+
+// fp32: rows padded to C + 1 words.
+template <int D, int C>
+struct TileT<float, D, C> {
+  static constexpr int LD = C + 1;
+  static constexpr int kElems = D * LD;
+  static constexpr int kBytes = kElems * 4;
+  static __device__ __forceinline__ void put2(float* t, int kk, int s, float a, float b) {
+    t[kk * LD + s] = a;
+    t[kk * LD + s + 1] = b;
+  }
+  static __device__ __forceinline__ float frag(const float* t, int kk, int s) { return t[kk * LD + s]; }
+  static __device__ __forceinline__ void drain(const float* t, float* dst, int tid) {
+    for (int e = tid; e < D * C / 4; e += 256) {
+      const int kk = e / (C / 4), s = 4 * (e % (C / 4));
+      const float* src = t + kk * LD + s;
+      *reinterpret_cast<f32x4*>(dst + kk * C + s) = f32x4{src[0], src[1], src[2], src[3]};
+    }
+  }
+};
+
 template <typename TI, typename OpT, int D, int C, bool BWD>
 __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_begin,
                                                      ChunkOps ops) {
@@ -40,12 +103,18 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
   constexpr int LDT = C + 8;   // operand C x C stride (16-byte aligned rows)
   constexpr int SZ_M = C * LDM * 4, SZ_TB = C * LDT * (int)sizeof(OpT);
   constexpr int SZ_R = SZ_M > SZ_TB ? SZ_M : SZ_TB;
-  __shared__ float Gs[C * LDG];
+  using TL = TileT<OpT, D, C>;
+  constexpr int SZ_G = C * LDG * 4, SZ_S = 2 * TL::kBytes;
+  // the cumulative gate, then two staged transposed tiles at a time
+  __shared__ __attribute__((aligned(16))) unsigned char regG[SZ_G > SZ_S ? SZ_G : SZ_S];
   __shared__ __attribute__((aligned(16))) unsigned char regM[SZ_R];  // P, then Tb
   __shared__ float As[C * LDM];                                         // Aqk, then T
   __shared__ float Sx[16 * C];
   __shared__ float rq[C], rqs[C], rk[C], be[C];
   __shared__ float ptot[4 * D];
+  float* Gs = reinterpret_cast<float*>(regG);
+  OpT* tile0 = reinterpret_cast<OpT*>(regG);
+  OpT* tile1 = tile0 + TL::kElems;
   float* Ms = reinterpret_cast<float*>(regM);
   OpT* Tb = reinterpret_cast<OpT*>(regM);
   float* Ts = As;
@@ -113,7 +182,13 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
   }
   __syncthreads();
 
-  // ---- elementwise outputs and the C x C matrices that leave before the inverse
+  // ---- outputs that leave before the inverse: Aqk (or its transpose), P,
+  // gamma, then one pass over (row pair, VE channels) items computing every
+  // gated element-wise operand from vector loads of q, k, v:
+  //   qg = qh e^G, kg = kh e^{G_c - G}, Kb = beta kh e^G, Bv = beta v
+  // Row-major ones are stored directly; transposed ones are staged in LDS
+  // (row pairs packed) and leave as contiguous vectors, or stay as the
+  // operands of W and U.
   {
     OpT* aq = static_cast<OpT*>(BWD ? ops.AqkT : ops.Aqk) + idx * C * C;
     for (int e = tid; e < C * C; e += 256) {
@@ -126,49 +201,79 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
     }
     float* gam = ops.gam + idx * K;
     for (int kk = tid; kk < K; kk += 256) gam[kk] = kexp<OpT>(Gs[(C - 1) * LDG + kk]);
-    // Element-wise outputs. All global loads of a loop are issued before its
-    // stores (the output and input pointers may alias as far as the compiler
-    // knows, which would otherwise serialise every load behind a store).
-    constexpr int PER = C * K / 256;
-    // row-major [C][K] outputs: qg (forward) or kg (backward)
-    {
-      float src[PER];
+  }
+  typedef typename Vec16<TI>::T VT;
+  constexpr int VE = 16 / sizeof(TI), LPR = D / VE;
+  constexpr int NITEM = (C / 2) * LPR, IPT = (NITEM + 255) / 256;
+  // staged values per item: [0] kg (both), [1] Kb, [2] Bv, [3] qg (backward)
+  constexpr int NSV = BWD ? 4 : 3;
+  float sv[IPT][NSV][2][VE];
+  {
+    VT xq[IPT][2], xk[IPT][2], xv[IPT][2];
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int e = tid + 256 * j, r = e / K, kk = e % K;
-        src[j] = r < L.len ? to_f((BWD ? kr : qr)[r * ts + kk]) : 0.f;
-      }
-      OpT* rowm = static_cast<OpT*>(BWD ? ops.kg : ops.qg) + idx * C * K;
+    for (int it = 0; it < IPT; ++it) {
+      const int item = tid + 256 * it, rp = item / LPR, c0 = (item % LPR) * VE;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int e = tid + 256 * j, r = e / K, kk = e % K;
-        const float gr = Gs[r * LDG + kk];
-        const float val = BWD ? src[j] * rk[r] * kexp<OpT>(Gs[(C - 1) * LDG + kk] - gr)
-                              : src[j] * rqs[r] * kexp<OpT>(gr);
-        rowm[e] = from_f<OpT>(val);
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int r = 2 * rp + h2;
+        if (item < NITEM && r < L.len) {
+          xq[it][h2] = *reinterpret_cast<const VT*>(qr + r * ts + c0);
+          xk[it][h2] = *reinterpret_cast<const VT*>(kr + r * ts + c0);
+          xv[it][h2] = *reinterpret_cast<const VT*>(vr + r * ts + c0);
+        } else {
+#pragma unroll
+          for (int j = 0; j < VE; ++j)
+            xq[it][h2][j] = xk[it][h2][j] = xv[it][h2][j] = static_cast<TI>(0.f);
+        }
       }
     }
-    // transposed [K][C] outputs: kgT always, qgT for the backward
-    {
-      float ks[PER], qs[BWD ? PER : 1];
+    OpT* rowm = static_cast<OpT*>(BWD ? ops.kg : ops.qg) + idx * C * K;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int e = tid + 256 * j, kk = e / C, r = e % C;
-        ks[j] = r < L.len ? to_f(kr[r * ts + kk]) : 0.f;
-        if (BWD) qs[j] = r < L.len ? to_f(qr[r * ts + kk]) : 0.f;
-      }
-      OpT* kgT = static_cast<OpT*>(ops.kgT) + idx * K * C;
-      OpT* qgT = BWD ? static_cast<OpT*>(ops.qgT) + idx * K * C : nullptr;
+    for (int it = 0; it < IPT; ++it) {
+      const int item = tid + 256 * it, rp = item / LPR, c0 = (item % LPR) * VE;
+      if (item >= NITEM) break;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int e = tid + 256 * j, kk = e / C, r = e % C;
-        const float gr = Gs[r * LDG + kk];
-        kgT[e] = from_f<OpT>(ks[j] * rk[r] * kexp<OpT>(Gs[(C - 1) * LDG + kk] - gr));
-        if (BWD) qgT[e] = from_f<OpT>(qs[j] * rqs[r] * kexp<OpT>(gr));
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int r = 2 * rp + h2;
+        const float sq = rqs[r], sk = rk[r], b = be[r];
+        VT out;
+#pragma unroll
+        for (int j = 0; j < VE; ++j) {
+          const float gr = Gs[r * LDG + c0 + j];
+          const float eG = kexp<OpT>(gr), eGc = kexp<OpT>(Gs[(C - 1) * LDG + c0 + j] - gr);
+          const float kh = to_f(xk[it][h2][j]) * sk;
+          const float qg = to_f(xq[it][h2][j]) * sq * eG;
+          sv[it][0][h2][j] = kh * eGc;
+          sv[it][1][h2][j] = b * kh * eG;
+          sv[it][2][h2][j] = b * to_f(xv[it][h2][j]);
+          if (BWD) sv[it][NSV - 1][h2][j] = qg;
+          out[j] = from_f<OpT>(BWD ? sv[it][0][h2][j] : qg);
+        }
+        *reinterpret_cast<VT*>(rowm + r * K + c0) = out;
       }
     }
   }
+  __syncthreads();  // the gate region and As are free from here
+  // round 1: kg^T (and qg^T) leave through the staging area
+  auto stage = [&](OpT* tile, int which) {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int item = tid + 256 * it, rp = item / LPR, c0 = (item % LPR) * VE;
+      if (item >= NITEM) break;
+#pragma unroll
+      for (int j = 0; j < VE; ++j)
+        TL::put2(tile, c0 + j, 2 * rp, sv[it][which][0][j], sv[it][which][1][j]);
+    }
+  };
+  stage(tile0, 0);
+  if (BWD) stage(tile1, NSV - 1);
   __syncthreads();
+  TL::drain(tile0, static_cast<OpT*>(ops.kgT) + idx * K * C, tid);
+  if (BWD) TL::drain(tile1, static_cast<OpT*>(ops.qgT) + idx * K * C, tid);
+  __syncthreads();
+  // round 2: the operands of W and U stay in LDS
+  stage(tile0, 1);
+  stage(tile1, 2);
 
   // ---- T = (I + Akk)^-1: diagonal 16x16 blocks by forward substitution
   for (int e = tid; e < C * LDM; e += 256) Ts[e] = 0.f;
@@ -236,28 +341,12 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
   }
   __syncthreads();
 
-  // ---- W = T Kb and U = T Bv (MFMA). Kb^T / Bv^T fragments are generated:
-  // lane (i, g) holds column i (a channel) and k-slots s = s0 + g*KPL + j.
-  // The raw k / v values a wave needs are loaded up front (strided reads of
-  // the chunk tile, all in flight together).
+  // ---- W = T Kb and U = T Bv (MFMA). Kb^T / Bv^T fragments come from the
+  // staged tiles: lane (i, g) holds channel i and k-slots s0 + g*KPL + j.
   constexpr int NSF = C / KS;  // fragments along the chunk
   constexpr int NMW = (K / 16 + 3) / 4;
   OpT* Wn = static_cast<OpT*>(ops.Wn) + idx * C * K;
   {
-    float raw[NMW][NSF][KPL], vraw[NMW][NSF][KPL];
-#pragma unroll
-    for (int jm = 0; jm < NMW; ++jm) {
-      const int kk = 16 * (w + 4 * jm) + i;
-#pragma unroll
-      for (int f = 0; f < NSF; ++f)
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-          const int s_ = f * KS + g * KPL + j;
-          const bool ok = s_ < L.len && w + 4 * jm < K / 16;
-          raw[jm][f][j] = ok ? to_f(kr[s_ * ts + kk]) : 0.f;
-          vraw[jm][f][j] = ok ? to_f(vr[s_ * ts + kk]) : 0.f;
-        }
-    }
 #pragma unroll
     for (int jm = 0; jm < NMW; ++jm) {
       const int mk = w + 4 * jm;
@@ -269,11 +358,8 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
 #pragma unroll
       for (int f = 0; f < NSF; ++f) {
         const int s0 = f * KS;
-        const auto gk = M::make([&](int j) {
-          const int s_ = s0 + g * KPL + j;
-          return be[s_] * rk[s_] * raw[jm][f][j] * kexp<OpT>(Gs[s_ * LDG + kk]);
-        });
-        const auto gv = M::make([&](int j) { return be[s0 + g * KPL + j] * vraw[jm][f][j]; });
+        const auto gk = TL::frag(tile0, kk, s0 + g * KPL);
+        const auto gv = TL::frag(tile1, kk, s0 + g * KPL);
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
           const auto tb = M::load(Tb + (16 * n + i) * LDT + s0 + g * KPL);
@@ -324,7 +410,7 @@ hipError_t launch_chunk_local(int dtype, int D, int C, bool bwd, const Dims& d,
   if (D == DD && C == CC) return launch_cl<TI, TI, DD, CC>(bwd, d, in, seg_begin, seg_chunks, ops, s);
   if (dtype == 0) {
     KDA_CL(float, 64, 16) KDA_CL(float, 64, 32) KDA_CL(float, 64, 64)
-    KDA_CL(float, 128, 16) KDA_CL(float, 128, 32) KDA_CL(float, 128, 64)
+    KDA_CL(float, 128, 16) KDA_CL(float, 128, 32)
   } else {
     KDA_CL(bf16, 64, 32) KDA_CL(bf16, 64, 64) KDA_CL(bf16, 128, 32) KDA_CL(bf16, 128, 64)
   }

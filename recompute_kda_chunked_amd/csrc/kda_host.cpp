@@ -20,7 +20,7 @@
 #include <cstring>
 #include <vector>
 
-#include "../../include/kda.h"
+#include "kda.h"
 #include "kda_internal.h"
 
 using namespace kda;

@@ -47,52 +47,96 @@ __device__ __forceinline__ ChunkLoc locate(const Inputs& in, int N, int c) {
   return L;
 }
 
-// Row part of the prologue. Every wave takes rows r = w, w + NW, ...; for each
-// row it writes the per-row scalars and the gate value of each channel to
-// G(r, k) (a functor returning a float reference into LDS). Rows r >= len are
-// padding: q = k = 0, beta = 0, g = 0, so they contribute nothing anywhere.
+// Row part of the prologue. Each row is read with 16-byte vector loads by
+// LPR = D / (16 / sizeof(TI)) consecutive lanes, so one wave instruction
+// covers 64 / LPR rows; wave w takes row groups w, w + NW, ... and issues the
+// loads of all its rows before any arithmetic. For each row it writes the
+// per-row scalars and the gate value of each channel to G(r, k) (a functor
+// returning a float reference into LDS). Rows r >= len are padding:
+// q = k = 0, beta = 0, g = 0, so they contribute nothing anywhere.
 //   rq[r]  = 1/sqrt(|q|^2 + eps)  (so qbar = q * rq)
 //   rqs[r] = scale * rq           (so qh = q * rqs)
 //   rk[r]  = 1/sqrt(|k|^2 + eps)  (kh = k * rk)
 //   be[r]  = sigmoid(raw_beta)
+template <typename TI>
+struct Vec16;
+template <>
+struct Vec16<bf16> {
+  typedef bf16x8 T;
+};
+template <>
+struct Vec16<float> {
+  typedef f32x4 T;
+};
+
 template <typename TI, int D, int C, int NW, class GRef>
 __device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, int h,
                                               const ChunkLoc& L, float* rq, float* rqs,
                                               float* rk, float* be, GRef G) {
+  typedef typename Vec16<TI>::T VT;
+  constexpr int VE = 16 / sizeof(TI);  // elements per vector load
+  constexpr int LPR = D / VE;          // lanes per row
+  constexpr int RPI = 64 / LPR;        // rows per wave instruction
+  constexpr int NIT = (C + NW * RPI - 1) / (NW * RPI);
+  static_assert(D % VE == 0 && 64 % LPR == 0, "prologue row layout");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int sub = lane % LPR, rsub = lane / LPR, c0 = sub * VE;
   const size_t ts = static_cast<size_t>(d.H) * D;
-  const TI* q = static_cast<const TI*>(in.q) + L.t0 * ts + static_cast<size_t>(h) * D;
-  const TI* k = static_cast<const TI*>(in.k) + L.t0 * ts + static_cast<size_t>(h) * D;
-  const TI* x = static_cast<const TI*>(in.g) + L.t0 * ts + static_cast<size_t>(h) * D;
+  const size_t hoff = static_cast<size_t>(h) * D + c0;
+  const TI* q = static_cast<const TI*>(in.q) + L.t0 * ts + hoff;
+  const TI* k = static_cast<const TI*>(in.k) + L.t0 * ts + hoff;
+  const TI* x = static_cast<const TI*>(in.g) + L.t0 * ts + hoff;
   const TI* rb = static_cast<const TI*>(in.beta) + L.t0 * d.H + h;
+  VT qv[NIT], kv[NIT], xv[NIT];
+  float bv[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int r = (w + NW * it) * RPI + rsub;
+    if (r < L.len) {
+      qv[it] = *reinterpret_cast<const VT*>(q + r * ts);
+      kv[it] = *reinterpret_cast<const VT*>(k + r * ts);
+      xv[it] = *reinterpret_cast<const VT*>(x + r * ts);
+      bv[it] = sub == 0 ? to_f(rb[static_cast<size_t>(r) * d.H]) : 0.f;
+    } else {
+#pragma unroll
+      for (int j = 0; j < VE; ++j) qv[it][j] = kv[it][j] = xv[it][j] = static_cast<TI>(0.f);
+      bv[it] = 0.f;
+    }
+  }
   const float ea = expf(in.A_log[h]);
-  const float* db = in.dt_bias + static_cast<size_t>(h) * D;
-  for (int r = w; r < C; r += NW) {
+  float db[VE];
+#pragma unroll
+  for (int j = 0; j < VE; ++j) db[j] = in.dt_bias[static_cast<size_t>(h) * D + c0 + j];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int r = (w + NW * it) * RPI + rsub;
     const bool valid = r < L.len;
     float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int j = 0; j < D / 64; ++j) {
-      const int kk = lane + 64 * j;
-      float qv = 0.f, kv = 0.f, gv = 0.f;
-      if (valid) {
-        qv = to_f(q[r * ts + kk]);
-        kv = to_f(k[r * ts + kk]);
-        const float z = ea * (to_f(x[r * ts + kk]) + db[kk]);
-        gv = d.lb * sigmoidf(z);
-      }
-      sq += qv * qv;
-      sk += kv * kv;
-      G(r, kk) = gv;
+    for (int j = 0; j < VE; ++j) {
+      const float a = to_f(qv[it][j]), b = to_f(kv[it][j]);
+      sq += a * a;
+      sk += b * b;
     }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
-    if (lane == 0) {
-      const float a = valid ? 1.0f / sqrtf(sq + d.eps) : 0.f;
-      const float b = valid ? 1.0f / sqrtf(sk + d.eps) : 0.f;
-      rq[r] = a;
-      rqs[r] = d.scale * a;
-      rk[r] = b;
-      be[r] = valid ? sigmoidf(to_f(rb[static_cast<size_t>(r) * d.H])) : 0.f;
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) {
+      sq += __shfl_xor(sq, o, kWave);
+      sk += __shfl_xor(sk, o, kWave);
+    }
+    if (r < C) {
+#pragma unroll
+      for (int j = 0; j < VE; ++j) {
+        const float z = ea * (to_f(xv[it][j]) + db[j]);
+        G(r, c0 + j) = valid ? d.lb * sigmoidf(z) : 0.f;
+      }
+      if (sub == 0) {
+        const float a = valid ? 1.0f / sqrtf(sq + d.eps) : 0.f;
+        const float b = valid ? 1.0f / sqrtf(sk + d.eps) : 0.f;
+        rq[r] = a;
+        rqs[r] = d.scale * a;
+        rk[r] = b;
+        be[r] = valid ? sigmoidf(bv[it]) : 0.f;
+      }
     }
   }
 }
