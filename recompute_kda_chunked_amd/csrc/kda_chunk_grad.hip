@@ -170,42 +170,91 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   __syncthreads();
   cumsum_rows<D, C, NT>(Gf, ptot);
 
-  // ---- S2: dBv = T^T dVn (tiles of dBv^T: value rows, chunk-row columns)
+  // ---- S2: dBv = T^T dVn (tiles of dBv^T: value rows, chunk-row columns),
+  // ---- S3: dO and Vn tiles into LDS.
+  // Every global load of both phases is issued before their first store
+  // (loads and stores share one completion counter, so a load issued after
+  // a store would also wait for the store).
   {
+    static_assert(sizeof(TI) == sizeof(OpT), "inputs and operands share a type");
+    typedef typename Vec16<TI>::T VT;
+    constexpr int VE = 16 / sizeof(TI), NVR = V / VE, NV = C * NVR, VPT = (NV + NT - 1) / NT;
+    constexpr int T2 = (V / 16) * NB, TPW = (T2 + NW - 1) / NW, NKS = C / KS;
     const OpT* dVnT = static_cast<const OpT*>(st.dVnT) + idx * V * C;
     const OpT* TT = static_cast<const OpT*>(ops.TT) + idx * C * C;
-    TI* dvo = dv + L.t0 * ts + hoff;
-    for (int t = w; t < (V / 16) * NB; t += NW) {
-      const int mv = t / NB, nr = t % NB;
-      const int s_lo = (16 * nr) / KS * KS;  // T^T[r][s] = 0 for s < r
-      const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
-      float vin[4];
+    const TI* dOr = dO + L.t0 * ts + hoff;
+    const OpT* Vn = static_cast<const OpT*>(st.Vn) + idx * C * V;
+    VT xo[VPT], xn[VPT];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) vin[rr] = r < L.len ? to_f(vr[r * ts + vv + rr]) : 0.f;
-      const f32x4 acc = tile_nt<OpT>(zero4(), dVnT + 16 * mv * C, C, TT + 16 * nr * C, C, s_lo, C, lane);
+    for (int j = 0; j < VPT; ++j) {
+      const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
+      if (e < NV) {
+        xn[j] = *reinterpret_cast<const VT*>(Vn + r * V + c);
+        if (r < L.len) {
+          xo[j] = *reinterpret_cast<const VT*>(dOr + r * ts + c);
+        } else {
+#pragma unroll
+          for (int q2 = 0; q2 < VE; ++q2) xo[j][q2] = static_cast<TI>(0.f);
+        }
+      }
+    }
+    typename M::frag fa[TPW][NKS], fb[TPW][NKS];
+    float vin[TPW][4];
+#pragma unroll
+    for (int jt = 0; jt < TPW; ++jt) {
+      const int t = w + NW * jt;
+      if (t >= T2) break;
+      const int mv = t / NB, nr = t % NB;
+      const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
+      // the whole reduction is taken (T^T[r][s] is stored as 0 for s < r)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        fa[jt][ks] = M::load(dVnT + (16 * mv + i) * C + ks * KS + g * KPL);
+        fb[jt][ks] = M::load(TT + (16 * nr + i) * C + ks * KS + g * KPL);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) vin[jt][rr] = r < L.len ? to_f(vr[r * ts + vv + rr]) : 0.f;
+    }
+    f32x4 dvv[TPW];
+#pragma unroll
+    for (int jt = 0; jt < TPW; ++jt) {
+      const int t = w + NW * jt;
+      if (t >= T2) break;
+      const int mv = t / NB, nr = t % NB;
+      const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) acc = M::mma(fa[jt][ks], fb[jt][ks], acc);
       OpT* dst = dBv_s + r * LDA + vv;
       float part = 0.f;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         dst[rr] = from_f<OpT>(acc[rr]);
-        part += acc[rr] * vin[rr];
-      }
-      if (r < L.len) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dvo[r * ts + vv + rr] = from_f<TI>(be[r] * acc[rr]);
+        part += acc[rr] * vin[jt][rr];
+        dvv[jt][rr] = be[r] * acc[rr];
       }
       part = sum_groups(part);
       if (g == 0) dbp[w][r] += part;
     }
-  }
-  // ---- S3: dO and Vn tiles into LDS
-  {
-    const TI* dOr = dO + L.t0 * ts + hoff;
-    const OpT* Vn = static_cast<const OpT*>(st.Vn) + idx * C * V;
-    for (int e = tid; e < C * V; e += NT) {
-      const int r = e / V, vv = e % V;
-      dO_s[r * LDA + vv] = r < L.len ? from_f<OpT>(to_f(dOr[r * ts + vv])) : from_f<OpT>(0.f);
-      Vn_s[r * LDA + vv] = Vn[e];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
+      if (e < NV) {
+        *reinterpret_cast<VT*>(dO_s + r * LDA + c) = xo[j];
+        *reinterpret_cast<VT*>(Vn_s + r * LDA + c) = xn[j];
+      }
+    }
+    TI* dvo = dv + L.t0 * ts + hoff;
+#pragma unroll
+    for (int jt = 0; jt < TPW; ++jt) {
+      const int t = w + NW * jt;
+      if (t >= T2) break;
+      const int mv = t / NB, nr = t % NB;
+      const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
+      if (r < L.len) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) dvo[r * ts + vv + rr] = from_f<TI>(dvv[jt][rr]);
+      }
     }
   }
   __syncthreads();
@@ -408,6 +457,21 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   }
 
   // ---- S7: row reductions for the L2-norm VJP; G_c terms; reverse cumsum of dG
+  // (the raw gate and dt_bias that S8 needs are loaded first, so their
+  // latency overlaps this phase and no load follows a store in S8)
+  constexpr int PER = (C * D + NT - 1) / NT;
+  static_assert(NT % D == 0, "one channel per thread in the gate VJP");
+  float xin[PER];
+  const float dbias = in.dt_bias[hoff + tid % D];
+  const float ea = expf(in.A_log[h]);
+  {
+    const TI* xr = static_cast<const TI*>(in.g) + L.t0 * ts + hoff;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = tid + NT * j, r = e / D, kc = e % D;
+      xin[j] = (e < C * D && r < L.len) ? to_f(xr[r * ts + kc]) : 0.f;
+    }
+  }
 #pragma unroll
   for (int jm = 0; jm < MR; ++jm) {
     const int m = row_block(jm);
@@ -488,23 +552,13 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         }
       }
     }
-    const float ea = expf(in.A_log[h]);
-    const float* db = in.dt_bias + hoff;
-    const TI* xr = static_cast<const TI*>(in.g) + L.t0 * ts + hoff;
     TI* dgo = dg + L.t0 * ts + hoff;
     float pdt = 0.f, pA = 0.f;
-    constexpr int PER = (C * D + NT - 1) / NT;
-    float xin[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = tid + NT * j, r = e / D, kc = e % D;
-      xin[j] = (e < C * D && r < L.len) ? to_f(xr[r * ts + kc]) : 0.f;
-    }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int e = tid + NT * j, r = e / D, kc = e % D;
       if (e < C * D && r < L.len) {
-        const float z = ea * (xin[j] + db[kc]);
+        const float z = ea * (xin[j] + dbias);
         const float sz = sigmoidf(z);
         const float dz = static_cast<float>(dGT[kc * LDG + r]) * d.lb * sz * (1.f - sz);
         const float dx = dz * ea;

@@ -189,19 +189,6 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
   // Row-major ones are stored directly; transposed ones are staged in LDS
   // (row pairs packed) and leave as contiguous vectors, or stay as the
   // operands of W and U.
-  {
-    OpT* aq = static_cast<OpT*>(BWD ? ops.AqkT : ops.Aqk) + idx * C * C;
-    for (int e = tid; e < C * C; e += 256) {
-      const int a = e / C, b = e % C;
-      aq[e] = from_f<OpT>(BWD ? As[b * LDM + a] : As[a * LDM + b]);
-    }
-    if (BWD) {
-      OpT* P = static_cast<OpT*>(ops.P) + idx * C * C;
-      for (int e = tid; e < C * C; e += 256) P[e] = from_f<OpT>(Ms[(e / C) * LDM + e % C]);
-    }
-    float* gam = ops.gam + idx * K;
-    for (int kk = tid; kk < K; kk += 256) gam[kk] = kexp<OpT>(Gs[(C - 1) * LDG + kk]);
-  }
   typedef typename Vec16<TI>::T VT;
   constexpr int VE = 16 / sizeof(TI), LPR = D / VE;
   constexpr int NITEM = (C / 2) * LPR, IPT = (NITEM + 255) / 256;
@@ -226,6 +213,21 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
             xq[it][h2][j] = xk[it][h2][j] = xv[it][h2][j] = static_cast<TI>(0.f);
         }
       }
+    }
+    // stores of this phase follow all of its loads (loads and stores share one
+    // completion counter)
+    {
+      OpT* aq = static_cast<OpT*>(BWD ? ops.AqkT : ops.Aqk) + idx * C * C;
+      for (int e = tid; e < C * C; e += 256) {
+        const int a = e / C, b = e % C;
+        aq[e] = from_f<OpT>(BWD ? As[b * LDM + a] : As[a * LDM + b]);
+      }
+      if (BWD) {
+        OpT* P = static_cast<OpT*>(ops.P) + idx * C * C;
+        for (int e = tid; e < C * C; e += 256) P[e] = from_f<OpT>(Ms[(e / C) * LDM + e % C]);
+      }
+      float* gam = ops.gam + idx * K;
+      for (int kk = tid; kk < K; kk += 256) gam[kk] = kexp<OpT>(Gs[(C - 1) * LDG + kk]);
     }
     OpT* rowm = static_cast<OpT*>(BWD ? ops.kg : ops.qg) + idx * C * K;
 #pragma unroll
