@@ -64,8 +64,10 @@ typedef struct {
   int32_t n_seqs;          /* N >= 1 packed sequences (empty sequences allowed) */
   int64_t total_tokens;    /* T = cu_seqlens_host[N] >= 1 */
   int32_t H, K, V;         /* heads, key dim, value dim; built: K == V in {64, 128} */
-  int32_t chunk;           /* chunk length C in {16, 32, 64}; tiling only, the
-                              result does not depend on it beyond rounding */
+  int32_t chunk;           /* chunk length C; tiling only, the result does not
+                              depend on it beyond rounding. Built: fp32 K=64:
+                              16, 32, 64; fp32 K=128: 16, 32; bf16 K=64 or
+                              128: 32, 64 (others: KDA_ERR_UNSUPPORTED) */
   int32_t dtype;           /* KDA_F32 or KDA_BF16 */
   int32_t gate_mode;       /* KDA_GATE_SIGMOID_BOUND */
   float scale;             /* multiplies qh; 1.0 for the plain o_t = S_t^T qh_t */
