@@ -17,9 +17,11 @@
 // Work split: wave w owns row block m = w of the chunk (Vn, O or dVn tiles,
 // all value blocks of the tile) and MKW row blocks of the state. The serial
 // chunk loop is software-pipelined: the per-chunk operands a wave needs
-// (rows of W, qg, Aqk, kg^T, U, gamma, dO, ...) for chunk c+1 are loaded into
-// registers while chunk c is computed, so the global-load latency stays off
-// the recurrence.
+// (rows of W, qg, Aqk, kg^T, U, gamma, dO, ...) for chunk c+2 are loaded into
+// registers while chunk c is computed (three rotating register sets), so the
+// global-load latency, longer than one chunk step, stays off the recurrence.
+// The prefetched values stay raw until use: converting them at load time
+// would make the wave wait for the loads right away.
 //
 // Block-to-XCD mapping: blocks are dealt round-robin to the 8 XCDs, so the
 // NVT value tiles of one (sequence, head) get block ids that are equal mod 8
@@ -61,9 +63,10 @@ struct FwdOps {
   F w[G::NKF];                // W rows of block m (negated: -W)
   F q[G::NKF];                // qg rows of block m (output only)
   F a[G::NCF];                // Aqk rows of block m (output only)
-  float u[G::BVT][4];         // U at the Vn tile positions
+  OpT u[G::BVT][4];           // U at the Vn tile positions (raw: converted at use, so
+                              // the prefetch does not wait for its loads)
   F kt[G::MKW][G::NCF];       // kg^T rows of the wave's state row blocks
-  float gm[G::MKW][4];        // gamma at the wave's state rows
+  f32x4 gm[G::MKW];           // gamma at the wave's state rows
 };
 
 template <typename OpT, int D, int C, int BV, bool OUT_O, bool REC>
@@ -90,11 +93,11 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
       if (REC) {
         const OpT* U = static_cast<const OpT*>(ops.U) + idx * C * V;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) f.u[nv][rr] = to_f(U[(16 * m + 4 * g + rr) * V + v0 + 16 * nv + i]);
+        for (int rr = 0; rr < 4; ++rr) f.u[nv][rr] = U[(16 * m + 4 * g + rr) * V + v0 + 16 * nv + i];
       } else {
         const OpT* src = static_cast<const OpT*>(ops.UT) + idx * V * C + (v0 + 16 * nv + i) * C + 16 * m + 4 * g;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) f.u[nv][rr] = to_f(src[rr]);
+        for (int rr = 0; rr < 4; ++rr) f.u[nv][rr] = src[rr];
       }
     }
   }
@@ -105,8 +108,7 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
     const int mk = w * G::MKW + jm;
 #pragma unroll
     for (int j = 0; j < G::NCF; ++j) f.kt[jm][j] = M::load(kgT + (16 * mk + i) * C + j * M::KS + g * M::KPL);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) f.gm[jm][rr] = gam[16 * mk + 4 * g + rr];
+    f.gm[jm] = *reinterpret_cast<const f32x4*>(gam + 16 * mk + 4 * g);
   }
 }
 
@@ -153,15 +155,19 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
   };
   put_state();
 
-  FwdOps<OpT, D, C, BV> cur, nxt;
-  load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(cur, ops, static_cast<size_t>(cb - seg_begin) * d.H + h,
-                                          v0, w, i, g);
+  // Three operand sets rotate so that chunk c + 2 is being loaded while
+  // chunk c is computed (the loop is unrolled by three, no register copies).
+  using Ops = FwdOps<OpT, D, C, BV>;
+  Ops s0, s1, s2;
+  const size_t idx0 = static_cast<size_t>(cb - seg_begin) * d.H + h;
+  load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(s0, ops, idx0, v0, w, i, g);
+  if (cb + 1 < ce) load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(s1, ops, idx0 + d.H, v0, w, i, g);
   __syncthreads();
 
-  for (int c = cb; c < ce; ++c) {
+  auto step = [&](int c, const Ops& cur, Ops& fill) {
     const size_t idx = static_cast<size_t>(c - seg_begin) * d.H + h;
-    if (c + 1 < ce)
-      load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(nxt, ops, idx + d.H, v0, w, i, g);
+    if (c + 2 < ce)
+      load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(fill, ops, idx + 2 * d.H, v0, w, i, g);
     if (REC) {
       // entering state h_n as [K][V]
       OpT* hd = static_cast<OpT*>(st.h) + idx * K * V;
@@ -179,7 +185,7 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
       const int m = w;
 #pragma unroll
       for (int nv = 0; nv < BVT; ++nv) {
-        f32x4 accV = {cur.u[nv][0], cur.u[nv][1], cur.u[nv][2], cur.u[nv][3]};
+        f32x4 accV = {to_f(cur.u[nv][0]), to_f(cur.u[nv][1]), to_f(cur.u[nv][2]), to_f(cur.u[nv][3])};
         accO[nv] = zero4();
         const OpT* bh = hT_s + (16 * nv + i) * LDH + g * KPL;
 #pragma unroll
@@ -234,7 +240,11 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
     // keeps the next chunk's VnT_s writes behind this chunk's VnT_s reads
     put_state();
     __syncthreads();
-    if (c + 1 < ce) cur = nxt;
+  };
+  for (int c = cb; c < ce; c += 3) {
+    step(c, s0, s2);
+    if (c + 1 < ce) step(c + 1, s1, s0);
+    if (c + 2 < ce) step(c + 2, s2, s1);
   }
   if (ce < in.coff[n + 1]) {
 #pragma unroll
@@ -257,8 +267,8 @@ struct BwdOps {
   F kg[G::NKF];               // kg rows of block m
   F qt[G::MKW][G::NCF];       // qg^T rows of the wave's state row blocks
   F wt[G::MKW][G::NCF];       // -W^T rows of the wave's state row blocks
-  float gm[G::MKW][4];
-  float dOv[NDO];             // dO tile elements this thread stages into LDS
+  f32x4 gm[G::MKW];
+  TI dOv[NDO];                // dO tile elements this thread stages into LDS (raw)
 };
 
 template <typename TI, typename OpT, int D, int C, int BV>
@@ -289,13 +299,12 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
       f.qt[jm][j] = M::load(qgT + (16 * mk + i) * C + j * M::KS + g * M::KPL);
       f.wt[jm][j] = M::load(WnT + (16 * mk + i) * C + j * M::KS + g * M::KPL);
     }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) f.gm[jm][rr] = gam[16 * mk + 4 * g + rr];
+    f.gm[jm] = *reinterpret_cast<const f32x4*>(gam + 16 * mk + 4 * g);
   }
 #pragma unroll
   for (int j = 0; j < BwdOps<TI, OpT, D, C, BV>::NDO; ++j) {
     const int e = tid + 256 * j, r = e / BV, vv = e % BV;
-    f.dOv[j] = r < len ? to_f(dO[(t0 + r) * ts + static_cast<size_t>(h) * V + v0 + vv]) : 0.f;
+    f.dOv[j] = r < len ? dO[(t0 + r) * ts + static_cast<size_t>(h) * V + v0 + vv] : static_cast<TI>(0.f);
   }
 }
 
@@ -350,24 +359,23 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
   };
   put_state();
 
-  Ops cur, nxt;
-  {
-    const int64_t t0 = chunk_t0(ce - 1);
-    load_bwd_ops<TI, OpT, D, C, BV>(cur, ops, static_cast<size_t>(ce - 1 - seg_begin) * d.H + h, dO,
-                                    t0, chunk_len(t0), ts, h, v0, tid, w, i, g);
-  }
-  for (int c = ce - 1; c >= cb; --c) {
+  // three rotating operand sets: chunk c - 2 loads while chunk c is computed
+  Ops s0, s1, s2;
+  auto load = [&](Ops& f, int c) {
+    const int64_t t0 = chunk_t0(c);
+    load_bwd_ops<TI, OpT, D, C, BV>(f, ops, static_cast<size_t>(c - seg_begin) * d.H + h, dO, t0,
+                                    chunk_len(t0), ts, h, v0, tid, w, i, g);
+  };
+  load(s0, ce - 1);
+  if (ce - 2 >= cb) load(s1, ce - 2);
+  auto step = [&](int c, const Ops& cur, Ops& fill) {
     const size_t idx = static_cast<size_t>(c - seg_begin) * d.H + h;
-    if (c - 1 >= cb) {
-      const int64_t t1 = chunk_t0(c - 1);
-      load_bwd_ops<TI, OpT, D, C, BV>(nxt, ops, idx - d.H, dO, t1, chunk_len(t1), ts, h, v0, tid,
-                                      w, i, g);
-    }
+    if (c - 2 >= cb) load(fill, c - 2);
     // dO tile, transposed into LDS ([BV][C]); padded rows are zero
 #pragma unroll
     for (int j = 0; j < Ops::NDO; ++j) {
       const int e = tid + 256 * j, r = e / BV, vv = e % BV;
-      dOT_s[vv * LDC + r] = from_f<OpT>(cur.dOv[j]);
+      dOT_s[vv * LDC + r] = static_cast<OpT>(cur.dOv[j]);
     }
     {
       OpT* hd = static_cast<OpT*>(st.dh) + idx * K * V;
@@ -420,7 +428,11 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
     }
     __syncthreads();  // every wave is done reading dhT_s / dOT_s / dVnT_s of this chunk
     put_state();
-    if (c - 1 >= cb) cur = nxt;
+  };
+  for (int c = ce - 1; c >= cb; c -= 3) {
+    step(c, s0, s2);
+    if (c - 1 >= cb) step(c - 1, s1, s0);
+    if (c - 2 >= cb) step(c - 2, s2, s1);
   }
   if (cb > in.coff[n]) {
 #pragma unroll
@@ -433,10 +445,9 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
   }
 }
 
-// Value-tile width: the forward scan keeps 32 columns per block (its
-// per-chunk operand reads are shared by fewer blocks); the reverse scan runs
-// 16-column tiles, twice the blocks, which measured faster.
-constexpr int kBvFwd = 32, kBvBwd = 16;
+// Value-tile width of both scans: 32 columns, N*H*V/32 blocks of 4 waves
+// (one wave per SIMD, so the rotating operand sets may use AGPRs as well).
+constexpr int kBvFwd = 32, kBvBwd = 32;
 
 template <typename TI, int D, int C>
 static hipError_t launch_sf(const Dims& d, const Inputs& in, int seg_begin, int seg_end,
