@@ -55,6 +55,26 @@ struct ScanGeo {
   static_assert(NHT % 4 == 0 && HPW % BVT == 0, "state tiles must split over 4 waves");
 };
 
+// Raw element bits held in a full register. A 16-bit load that fills only
+// half a register would depend on the register's old contents (and make the
+// wave wait for earlier loads); these loads zero-extend instead.
+template <typename T>
+__device__ __forceinline__ uint32_t load_bits(const T* p);
+template <>
+__device__ __forceinline__ uint32_t load_bits<bf16>(const bf16* p) {
+  return *reinterpret_cast<const uint16_t*>(p);
+}
+template <>
+__device__ __forceinline__ uint32_t load_bits<float>(const float* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
+template <typename T>
+__device__ __forceinline__ float bits_to_f(uint32_t b);
+template <>
+__device__ __forceinline__ float bits_to_f<bf16>(uint32_t b) { return __uint_as_float(b << 16); }
+template <>
+__device__ __forceinline__ float bits_to_f<float>(uint32_t b) { return __uint_as_float(b); }
+
 // Operands of one chunk for one wave of the forward scan.
 template <typename OpT, int D, int C, int BV>
 struct FwdOps {
@@ -63,8 +83,8 @@ struct FwdOps {
   F w[G::NKF];                // W rows of block m (negated: -W)
   F q[G::NKF];                // qg rows of block m (output only)
   F a[G::NCF];                // Aqk rows of block m (output only)
-  OpT u[G::BVT][4];           // U at the Vn tile positions (raw: converted at use, so
-                              // the prefetch does not wait for its loads)
+  uint32_t u[G::BVT][4];      // U at the Vn tile positions, raw bits (converted at
+                              // use, so the prefetch does not wait for its loads)
   F kt[G::MKW][G::NCF];       // kg^T rows of the wave's state row blocks
   f32x4 gm[G::MKW];           // gamma at the wave's state rows
 };
@@ -93,11 +113,20 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
       if (REC) {
         const OpT* U = static_cast<const OpT*>(ops.U) + idx * C * V;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) f.u[nv][rr] = U[(16 * m + 4 * g + rr) * V + v0 + 16 * nv + i];
+        for (int rr = 0; rr < 4; ++rr) f.u[nv][rr] = load_bits<OpT>(U + (16 * m + 4 * g + rr) * V + v0 + 16 * nv + i);
       } else {
         const OpT* src = static_cast<const OpT*>(ops.UT) + idx * V * C + (v0 + 16 * nv + i) * C + 16 * m + 4 * g;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) f.u[nv][rr] = src[rr];
+        if constexpr (sizeof(OpT) == 2) {  // four bf16 packed in u[nv][0..1]
+          const uint2 x = *reinterpret_cast<const uint2*>(src);
+          f.u[nv][0] = x.x;
+          f.u[nv][1] = x.y;
+        } else {
+          const uint4 x = *reinterpret_cast<const uint4*>(src);
+          f.u[nv][0] = x.x;
+          f.u[nv][1] = x.y;
+          f.u[nv][2] = x.z;
+          f.u[nv][3] = x.w;
+        }
       }
     }
   }
@@ -126,7 +155,11 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
 
   int n, h, vt;
   if (!scan_program<NVT>(d, n, h, vt)) return;
-  const int cb = max(in.coff[n], seg_begin), ce = min(in.coff[n + 1], seg_end);
+  // sequence bounds read once: the loop's stores could alias them as far as
+  // the compiler knows, and a reload would wait for every prefetch in flight
+  const int coff0 = in.coff[n], coff1 = in.coff[n + 1];
+  const int64_t tok0 = in.cu[n], tok1 = in.cu[n + 1];
+  const int cb = max(coff0, seg_begin), ce = min(coff1, seg_end);
   if (cb >= ce) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
   const int v0 = vt * BV;
@@ -134,7 +167,7 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
 
   // state tile j of this wave: row block mk = w*MKW + j/BVT, value block nv = j%BVT
   f32x4 hs[HPW];
-  const bool fresh = (cb == in.coff[n]);
+  const bool fresh = (cb == coff0);
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const int mk = w * MKW + j / BVT, nv = j % BVT;
@@ -185,7 +218,16 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
       const int m = w;
 #pragma unroll
       for (int nv = 0; nv < BVT; ++nv) {
-        f32x4 accV = {to_f(cur.u[nv][0]), to_f(cur.u[nv][1]), to_f(cur.u[nv][2]), to_f(cur.u[nv][3])};
+        f32x4 accV;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          if (REC || sizeof(OpT) == 4) {
+            accV[rr] = bits_to_f<OpT>(cur.u[nv][rr]);
+          } else {
+            const uint32_t wd = cur.u[nv][rr >> 1];
+            accV[rr] = __uint_as_float((rr & 1) ? (wd & 0xffff0000u) : (wd << 16));
+          }
+        }
         accO[nv] = zero4();
         const OpT* bh = hT_s + (16 * nv + i) * LDH + g * KPL;
 #pragma unroll
@@ -208,8 +250,8 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
     __syncthreads();
     if (OUT_O && w < NB) {
       const int m = w;
-      const int64_t t0 = static_cast<int64_t>(in.cu[n]) + static_cast<int64_t>(c - in.coff[n]) * C;
-      const int len = static_cast<int>(min(static_cast<int64_t>(C), in.cu[n + 1] - t0));
+      const int64_t t0 = tok0 + static_cast<int64_t>(c - coff0) * C;
+      const int len = static_cast<int>(min(static_cast<int64_t>(C), tok1 - t0));
       const int nf = (16 * (m + 1) + KS - 1) / KS;  // Aqk[r][s] = 0 for s > r
 #pragma unroll
       for (int nv = 0; nv < BVT; ++nv) {
@@ -246,7 +288,7 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
     if (c + 1 < ce) step(c + 1, s1, s0);
     if (c + 2 < ce) step(c + 2, s2, s1);
   }
-  if (ce < in.coff[n + 1]) {
+  if (ce < coff1) {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       const int mk = w * MKW + j / BVT, nv = j % BVT;
@@ -268,7 +310,7 @@ struct BwdOps {
   F qt[G::MKW][G::NCF];       // qg^T rows of the wave's state row blocks
   F wt[G::MKW][G::NCF];       // -W^T rows of the wave's state row blocks
   f32x4 gm[G::MKW];
-  TI dOv[NDO];                // dO tile elements this thread stages into LDS (raw)
+  uint32_t dOv[NDO];          // dO tile elements this thread stages into LDS (raw bits)
 };
 
 template <typename TI, typename OpT, int D, int C, int BV>
@@ -304,7 +346,7 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
 #pragma unroll
   for (int j = 0; j < BwdOps<TI, OpT, D, C, BV>::NDO; ++j) {
     const int e = tid + 256 * j, r = e / BV, vv = e % BV;
-    f.dOv[j] = r < len ? dO[(t0 + r) * ts + static_cast<size_t>(h) * V + v0 + vv] : static_cast<TI>(0.f);
+    f.dOv[j] = r < len ? load_bits<TI>(dO + (t0 + r) * ts + static_cast<size_t>(h) * V + v0 + vv) : 0u;
   }
 }
 
@@ -325,20 +367,24 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
 
   int n, h, vt;
   if (!scan_program<NVT>(d, n, h, vt)) return;
-  const int cb = max(in.coff[n], seg_begin), ce = min(in.coff[n + 1], seg_end);
+  // sequence bounds read once: the loop's stores could alias them as far as
+  // the compiler knows, and a reload would wait for every prefetch in flight
+  const int coff0 = in.coff[n], coff1 = in.coff[n + 1];
+  const int64_t tok0 = in.cu[n], tok1 = in.cu[n + 1];
+  const int cb = max(coff0, seg_begin), ce = min(coff1, seg_end);
   if (cb >= ce) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
   const int v0 = vt * BV;
   const size_t ts = static_cast<size_t>(d.H) * V;
   auto chunk_t0 = [&](int c) {
-    return static_cast<int64_t>(in.cu[n]) + static_cast<int64_t>(c - in.coff[n]) * C;
+    return tok0 + static_cast<int64_t>(c - coff0) * C;
   };
   auto chunk_len = [&](int64_t t0) {
-    return static_cast<int>(min(static_cast<int64_t>(C), in.cu[n + 1] - t0));
+    return static_cast<int>(min(static_cast<int64_t>(C), tok1 - t0));
   };
 
   f32x4 hs[HPW];  // dh' (gradient of the state leaving the current chunk)
-  const bool fresh = (ce == in.coff[n + 1]);
+  const bool fresh = (ce == coff1);
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const int mk = w * MKW + j / BVT, nv = j % BVT;
@@ -375,7 +421,7 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
 #pragma unroll
     for (int j = 0; j < Ops::NDO; ++j) {
       const int e = tid + 256 * j, r = e / BV, vv = e % BV;
-      dOT_s[vv * LDC + r] = static_cast<OpT>(cur.dOv[j]);
+      dOT_s[vv * LDC + r] = from_f<OpT>(bits_to_f<TI>(cur.dOv[j]));
     }
     {
       OpT* hd = static_cast<OpT*>(st.dh) + idx * K * V;
@@ -434,7 +480,7 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
     if (c - 1 >= cb) step(c - 1, s1, s0);
     if (c - 2 >= cb) step(c - 2, s2, s1);
   }
-  if (cb > in.coff[n]) {
+  if (cb > coff0) {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       const int mk = w * MKW + j / BVT, nv = j % BVT;
