@@ -61,6 +61,7 @@ struct Vjp<bf16> {
   static __device__ __forceinline__ frag make(F f) { return Mma<bf16>::make(f); }
   static __device__ __forceinline__ T rnd(T x) { return to_f(static_cast<bf16>(x)); }
   static __device__ __forceinline__ T ex(T x) { return __expf(x); }
+  static __device__ __forceinline__ T sig(T x) { return sigmoidf(x); }
   static __device__ __forceinline__ acc fix(acc x) { return x; }
 };
 template <>
@@ -78,6 +79,7 @@ struct Vjp<float> {
   static __device__ __forceinline__ frag make(F f) { return f(0); }
   static __device__ __forceinline__ T rnd(T x) { return x; }
   static __device__ __forceinline__ T ex(T x) { return exp(x); }
+  static __device__ __forceinline__ T sig(T x) { return 1.0 / (1.0 + exp(-x)); }
   // The f64 16x16 accumulator holds row 4r + g in register r of lane group g;
   // move it to the common layout (row 4g + r): the value for row 4g + r sits
   // in lane (i, r), register g.
@@ -106,10 +108,12 @@ template <typename TI, typename OpT, int D, int C>
 __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, Inputs in, const TI* dO,
                                                     int seg_begin, ChunkOps ops, SegStates st,
                                                     TI* dq, TI* dk, TI* dv, TI* dg, TI* dbeta,
-                                                    float* partials) {
+                                                    double* partials) {
   using M = Mma<OpT>;
   using VJ = Vjp<OpT>;
   using TG = typename VJ::T;
+  typedef typename GateT<OpT>::T GV;  // cumulative gate (fp64 for fp32 problems)
+  static_assert(sizeof(GV) == sizeof(TG), "dG reuses the cumulative-gate buffer");
   constexpr int K = D, V = D, NB = C / 16, KPL = M::KPL, KS = M::KS;
   constexpr int SPLIT = grad_split<D>();
   constexpr int NKB = D / 16, NW = SPLIT * NKB, NT = NW * 64;
@@ -120,18 +124,19 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   constexpr int LDX = C + 8;         // [C][LDX] dX buffers
   constexpr int SZ1 = 4 * C * LDA * (int)sizeof(OpT), SZ2 = 4 * C * LDX * (int)sizeof(OpT);
   constexpr int SZU = SZ1 > SZ2 ? SZ1 : SZ2;
-  // after the VJP the operand region holds dG^T (fp64 problems), then the
-  // scratch of the reverse cumulative sum and of the partial reductions
-  constexpr int OFF_S = sizeof(TG) == 4 ? 0 : (int)sizeof(double) * K * LDG;
+  // after the VJP the operand region holds the scratch of the reverse
+  // cumulative sum and of the partial reductions
+  constexpr int OFF_S = 0;
   static_assert(OFF_S + (int)sizeof(TG) * NT + 4 * NT <= SZU, "LDS scratch must fit");
-  __shared__ float GT[K * LDG];
+  __shared__ GV GT[K * LDG];
   __shared__ __attribute__((aligned(16))) TI qT[K * LDQ];
   __shared__ __attribute__((aligned(16))) TI kT[K * LDQ];
   __shared__ __attribute__((aligned(16))) unsigned char uni[SZU];
   __shared__ float rq[C], rqs[C], rk[C], be[C];
   __shared__ float dbp[NW][C];
   __shared__ float rowp[2][NKB][C];
-  __shared__ float ptot[NT];
+  __shared__ float rsum[2][C];  // rowp summed over key blocks
+  __shared__ GV ptot[NT];
   __shared__ TG csum[SPLIT][NKB][16];
 
   OpT* dBv_s = reinterpret_cast<OpT*>(uni);
@@ -157,7 +162,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   auto row_block = [&](int jm) { return half * MR + jm; };  // valid while < NB
 
   // ---- S1: prologue, transposed raw q/k, cumulative gate G^T
-  auto Gf = [&](int r, int kk_) -> float& { return GT[kk_ * LDG + r]; };
+  auto Gf = [&](int r, int kk_) -> GV& { return GT[kk_ * LDG + r]; };
   prologue_rows<TI, D, C, NW>(d, in, h, L, rq, rqs, rk, be, Gf);
   for (int e = tid; e < C * D; e += NT) {
     const int r = e / D, kc = e % D;
@@ -288,7 +293,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       }
     }
     hdh = static_cast<TG>(sum_groups(hd));
-    const float Gc = GT[kk * LDG + C - 1];
+    const GV Gc = GT[kk * LDG + C - 1];
     TG colsum = 0;
 #pragma unroll
     for (int jm = 0; jm < MR; ++jm) {
@@ -305,7 +310,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int r = 16 * m + 4 * g + rr;
-        const float Gv = GT[kk * LDG + r];
+        const GV Gv = GT[kk * LDG + r];
         const float eG = kexp<OpT>(Gv), eGc = kexp<OpT>(Gc - Gv);
         const float qh = to_f(qT[kk * LDQ + r]) * rqs[r];
         const float kh = to_f(kT[kk * LDQ + r]) * rk[r];
@@ -382,7 +387,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // (I, J <= I) the decay exp(G_r - G_s) is split around the first row b of
   // block I (as in the forward), so every generated factor is finite.
   {
-    const float* Gk = GT + kk * LDG;
+    const GV* Gk = GT + kk * LDG;
     const TI* qk = qT + kk * LDQ;
     const TI* kq = kT + kk * LDQ;
     auto khat = [&](int r) { return static_cast<TG>(to_f(kq[r])) * static_cast<TG>(rk[r]); };
@@ -488,7 +493,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     }
     // row C-1 holds G_c: add sum_r kg*dkg over all row groups and gamma * (h . dh')
     if (m == NB - 1 && g == 3) {
-      const float Gc = GT[kk * LDG + C - 1];
+      const GV Gc = GT[kk * LDG + C - 1];
       TG cs = 0;
 #pragma unroll
       for (int hh = 0; hh < SPLIT; ++hh) cs += csum[hh][kb][i];
@@ -496,11 +501,10 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     }
   }
   __syncthreads();  // all reads of GT as the cumulative gate are done
-  // dG^T in LDS, in the VJP precision (fp32: the GT buffer; fp64: the
-  // operand region, free now)
-  TG* dGT = sizeof(TG) == 4 ? reinterpret_cast<TG*>(GT) : reinterpret_cast<TG*>(uni);
+  // dG^T in LDS, in the VJP precision, over the cumulative gate (same type)
+  TG* dGT = reinterpret_cast<TG*>(GT);
   TG* ptg = reinterpret_cast<TG*>(uni + OFF_S);
-  float* red = reinterpret_cast<float*>(uni + OFF_S + sizeof(TG) * NT);
+  TG* red = reinterpret_cast<TG*>(uni + OFF_S + sizeof(TG) * NT);
 #pragma unroll
   for (int jm = 0; jm < MR; ++jm) {
     const int m = row_block(jm);
@@ -514,17 +518,27 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     constexpr int parts = NT / D, rp = C / parts;
     static_assert(C % parts == 0, "reverse cumulative sum layout");
     const int col = tid % D, part = tid / D;
+    TG v[rp];
+#pragma unroll
+    for (int j = 0; j < rp; ++j) v[j] = dGT[col * LDG + part * rp + j];
     TG run = 0;
+#pragma unroll
     for (int j = rp - 1; j >= 0; --j) {
-      const int r = part * rp + j;
-      run += dGT[col * LDG + r];
-      dGT[col * LDG + r] = run;
+      run += v[j];
+      v[j] = run;
     }
     ptg[part * D + col] = run;
     __syncthreads();
     TG off = 0;
     for (int p2 = part + 1; p2 < parts; ++p2) off += ptg[p2 * D + col];
-    for (int j = 0; j < rp; ++j) dGT[col * LDG + part * rp + j] += off;
+#pragma unroll
+    for (int j = 0; j < rp; ++j) dGT[col * LDG + part * rp + j] = v[j] + off;
+    if (tid < 2 * C) {
+      const int which = tid / C, r = tid % C;
+      float acc = 0.f;
+      for (int k2 = 0; k2 < NKB; ++k2) acc += rowp[which][k2][r];
+      rsum[which][r] = acc;
+    }
     __syncthreads();
   }
 
@@ -540,11 +554,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       for (int rr = 0; rr < 4; ++rr) {
         const int r = 16 * m + 4 * g + rr;
         if (r < L.len) {
-          float qd = 0.f, kd = 0.f;
-          for (int k2 = 0; k2 < NKB; ++k2) {
-            qd += rowp[0][k2][r];
-            kd += rowp[1][k2][r];
-          }
+          const float qd = rsum[0][r], kd = rsum[1][r];
           const float qbar = to_f(qT[kk * LDQ + r]) * rq[r];
           const float khat_ = to_f(kT[kk * LDQ + r]) * rk[r];
           dqo[r * ts + kk] = from_f<TI>(rqs[r] * (aq[jm][rr] - qbar * qd));
@@ -552,40 +562,45 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         }
       }
     }
+    // the gate map's VJP and the gate-parameter sums run in the VJP precision
+    // (fp64 for fp32 problems: the dA_log sum cancels heavily)
     TI* dgo = dg + L.t0 * ts + hoff;
-    float pdt = 0.f, pA = 0.f;
+    TG pdt = 0, pA = 0;
+    const TG eat = static_cast<TG>(ea);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int e = tid + NT * j, r = e / D, kc = e % D;
       if (e < C * D && r < L.len) {
-        const float z = ea * (xin[j] + dbias);
-        const float sz = sigmoidf(z);
-        const float dz = static_cast<float>(dGT[kc * LDG + r]) * d.lb * sz * (1.f - sz);
-        const float dx = dz * ea;
-        dgo[r * ts + kc] = from_f<TI>(dx);
+        const TG z = eat * (static_cast<TG>(xin[j]) + static_cast<TG>(dbias));
+        const TG sz = VJ::sig(z);
+        const TG dz = static_cast<TG>(dGT[kc * LDG + r]) * static_cast<TG>(d.lb) * sz * (1 - sz);
+        const TG dx = dz * eat;
+        dgo[r * ts + kc] = from_f<TI>(static_cast<float>(dx));
         pdt += dx;
         pA += dz * z;
       }
     }
     // tid % D is this thread's channel for every e above
-    ptot[tid] = pdt;
-    red[tid] = pA;
+    ptg[tid] = pdt;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) pA += __shfl_xor(pA, o, kWave);
+    if (lane == 0) red[w] = pA;
     for (int r = tid; r < L.len; r += NT) {
       float db_ = 0.f;
       for (int w2 = 0; w2 < NW; ++w2) db_ += dbp[w2][r];
       dbeta[(L.t0 + r) * d.H + h] = from_f<TI>(db_ * be[r] * (1.f - be[r]));
     }
     __syncthreads();
-    float* part = partials + (static_cast<size_t>(cglob) * d.H + h) * (K + 1);
+    double* part = partials + (static_cast<size_t>(cglob) * d.H + h) * (K + 1);
     if (tid < D) {
-      float s2 = 0.f;
-      for (int p2 = 0; p2 < NT / D; ++p2) s2 += ptot[p2 * D + tid];
-      part[tid] = s2;
+      TG s2 = 0;
+      for (int p2 = 0; p2 < NT / D; ++p2) s2 += ptg[p2 * D + tid];
+      part[tid] = static_cast<double>(s2);
     }
     if (tid == 0) {
-      float s2 = 0.f;
-      for (int j = 0; j < NT; ++j) s2 += red[j];
-      part[K] = s2;
+      TG s2 = 0;
+      for (int j = 0; j < NW; ++j) s2 += red[j];
+      part[K] = static_cast<double>(s2);
     }
   }
 }
@@ -593,7 +608,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 template <typename TI, int D, int C>
 static hipError_t launch_cg(const Dims& d, const Inputs& in, const void* dO, int seg_begin,
                             int seg_chunks, const ChunkOps& ops, const SegStates& st, void* dq,
-                            void* dk, void* dv, void* dg, void* dbeta, float* partials,
+                            void* dk, void* dv, void* dg, void* dbeta, double* partials,
                             hipStream_t s) {
   hipLaunchKernelGGL((k_chunk_grad<TI, TI, D, C>), dim3(seg_chunks * d.H), dim3(D * 4 * grad_split<D>()), 0, s, d,
                      in, static_cast<const TI*>(dO), seg_begin, ops, st, static_cast<TI*>(dq),
@@ -605,7 +620,7 @@ static hipError_t launch_cg(const Dims& d, const Inputs& in, const void* dO, int
 hipError_t launch_chunk_grad(int dtype, int D, int C, const Dims& d, const Inputs& in,
                              const void* dO, int seg_begin, int seg_chunks,
                              const ChunkOps& ops, const SegStates& st, void* dq, void* dk,
-                             void* dv, void* dg, void* dbeta, float* partials,
+                             void* dv, void* dg, void* dbeta, double* partials,
                              hipStream_t s) {
 #define KDA_CG(TI, DD, CC)                                                                  \
   if (D == DD && C == CC)                                                                   \
@@ -621,24 +636,33 @@ hipError_t launch_chunk_grad(int dtype, int D, int C, const Dims& d, const Input
   return hipErrorInvalidValue;
 }
 
-// dA_log[h] and ddt_bias[h, :] from per-chunk partials, summed over chunks in
-// increasing order (bitwise reproducible).
+// dA_log[h] and ddt_bias[h, :] from per-chunk partials (fp64). Block (h, kg)
+// covers 64 columns of head h; its four waves sum interleaved chunk subsets
+// in order and the four results are added in wave order (deterministic).
 __global__ void __launch_bounds__(256) k_gate_reduce(int D, int H, int n_chunks,
-                                                     const float* partials, float* dA_log,
+                                                     const double* partials, float* dA_log,
                                                      float* ddt_bias) {
-  const int h = blockIdx.x;
-  for (int k = threadIdx.x; k <= D; k += blockDim.x) {
-    float s = 0.f;
-    for (int c = 0; c < n_chunks; ++c) s += partials[(static_cast<size_t>(c) * H + h) * (D + 1) + k];
-    if (k < D) ddt_bias[static_cast<size_t>(h) * D + k] = s;
-    else dA_log[h] = s;
+  __shared__ double red[4][64];
+  const int h = blockIdx.x, l = threadIdx.x & 63, part = threadIdx.x >> 6;
+  const int k = blockIdx.y * 64 + l;
+  double s = 0.0;
+  if (k <= D) {
+#pragma unroll 8
+    for (int c = part; c < n_chunks; c += 4) s += partials[(static_cast<size_t>(c) * H + h) * (D + 1) + k];
+  }
+  red[part][l] = s;
+  __syncthreads();
+  if (part == 0 && k <= D) {
+    const double t = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
+    if (k < D) ddt_bias[static_cast<size_t>(h) * D + k] = static_cast<float>(t);
+    else dA_log[h] = static_cast<float>(t);
   }
 }
 
-hipError_t launch_gate_reduce(int D, int H, int n_chunks, const float* partials,
+hipError_t launch_gate_reduce(int D, int H, int n_chunks, const double* partials,
                               float* dA_log, float* ddt_bias, hipStream_t s) {
-  hipLaunchKernelGGL(k_gate_reduce, dim3(H), dim3(256), 0, s, D, H, n_chunks, partials, dA_log,
-                     ddt_bias);
+  hipLaunchKernelGGL(k_gate_reduce, dim3(H, (D + 1 + 63) / 64), dim3(256), 0, s, D, H, n_chunks,
+                     partials, dA_log, ddt_bias);
   return hipGetLastError();
 }
 

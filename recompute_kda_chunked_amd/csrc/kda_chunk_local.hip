@@ -104,15 +104,16 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
   constexpr int SZ_M = C * LDM * 4, SZ_TB = C * LDT * (int)sizeof(OpT);
   constexpr int SZ_R = SZ_M > SZ_TB ? SZ_M : SZ_TB;
   using TL = TileT<OpT, D, C>;
-  constexpr int SZ_G = C * LDG * 4, SZ_S = 2 * TL::kBytes;
+  typedef typename GateT<OpT>::T GV;
+  constexpr int SZ_G = C * LDG * (int)sizeof(GV), SZ_S = 2 * TL::kBytes;
   // the cumulative gate, then two staged transposed tiles at a time
   __shared__ __attribute__((aligned(16))) unsigned char regG[SZ_G > SZ_S ? SZ_G : SZ_S];
   __shared__ __attribute__((aligned(16))) unsigned char regM[SZ_R];  // P, then Tb
   __shared__ float As[C * LDM];                                         // Aqk, then T
   __shared__ float Sx[16 * C];
   __shared__ float rq[C], rqs[C], rk[C], be[C];
-  __shared__ float ptot[4 * D];
-  float* Gs = reinterpret_cast<float*>(regG);
+  __shared__ GV ptot[4 * D];
+  GV* Gs = reinterpret_cast<GV*>(regG);
   OpT* tile0 = reinterpret_cast<OpT*>(regG);
   OpT* tile1 = tile0 + TL::kElems;
   float* Ms = reinterpret_cast<float*>(regM);
@@ -133,7 +134,7 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
     Ms[e] = 0.f;
     As[e] = 0.f;
   }
-  auto G = [&](int r, int kk) -> float& { return Gs[r * LDG + kk]; };
+  auto G = [&](int r, int kk) -> GV& { return Gs[r * LDG + kk]; };
   prologue_rows<TI, D, C, 4>(d, in, h, L, rq, rqs, rk, be, G);
   __syncthreads();
   cumsum_rows<D, C, 256>(G, ptot);
@@ -162,7 +163,7 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
       }
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
-        const float gb = Gs[16 * I * LDG + kk + j];
+        const GV gb = Gs[16 * I * LDG + kk + j];
         ea[j] = kexp<OpT>(Gs[ra * LDG + kk + j] - gb);
         eb[j] = kexp<OpT>(gb - Gs[rb * LDG + kk + j]);
       }
@@ -241,7 +242,7 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
         VT out;
 #pragma unroll
         for (int j = 0; j < VE; ++j) {
-          const float gr = Gs[r * LDG + c0 + j];
+          const GV gr = Gs[r * LDG + c0 + j];
           const float eG = kexp<OpT>(gr), eGc = kexp<OpT>(Gs[(C - 1) * LDG + c0 + j] - gr);
           const float kh = to_f(xk[it][h2][j]) * sk;
           const float qg = to_f(xq[it][h2][j]) * sq * eG;

@@ -154,7 +154,7 @@ size_t fwd_bytes(const Plan& P) {
 
 size_t bwd_bytes(const Plan& P) {
   const size_t ops = ops_bytes(P, true) > ops_bytes(P, false) ? ops_bytes(P, true) : ops_bytes(P, false);
-  return up((P.N + 1) * 4) + up(static_cast<size_t>(P.NC) * P.H * (P.D + 1) * 4) +
+  return up((P.N + 1) * 4) + up(static_cast<size_t>(P.NC) * P.H * (P.D + 1) * 8) +
          static_cast<size_t>(P.NS + 1) * state_slot(P) + 2 * state_slot(P) + ops + states_bytes(P);
 }
 
@@ -302,8 +302,8 @@ int kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
   unsigned char* cur = static_cast<unsigned char*>(workspace);
   int32_t* coff = reinterpret_cast<int32_t*>(cur);
   cur += up((P.N + 1) * 4);
-  float* partials = reinterpret_cast<float*>(cur);
-  cur += up(static_cast<size_t>(P.NC) * P.H * (P.D + 1) * 4);
+  double* partials = reinterpret_cast<double*>(cur);
+  cur += up(static_cast<size_t>(P.NC) * P.H * (P.D + 1) * 8);
   float* ckpt = reinterpret_cast<float*>(cur);  // NS + 1 slots
   const size_t slot = state_slot(P) / 4;
   cur += static_cast<size_t>(P.NS + 1) * state_slot(P);

@@ -76,9 +76,9 @@ hipError_t launch_scan_bwd(int dtype, int D, int C, const Dims& d, const Inputs&
 hipError_t launch_chunk_grad(int dtype, int D, int C, const Dims& d, const Inputs& in,
                              const void* dO, int seg_begin, int seg_chunks,
                              const ChunkOps& ops, const SegStates& st, void* dq, void* dk,
-                             void* dv, void* dg, void* dbeta, float* partials,
+                             void* dv, void* dg, void* dbeta, double* partials,
                              hipStream_t s);
-hipError_t launch_gate_reduce(int D, int H, int n_chunks, const float* partials,
+hipError_t launch_gate_reduce(int D, int H, int n_chunks, const double* partials,
                               float* dA_log, float* ddt_bias, hipStream_t s);
 
 }  // namespace kda

@@ -16,14 +16,34 @@
 
 namespace kda {
 
+// Type of the cumulative gate G. For fp32 problems it is fp64: within a
+// 64-row chunk |G| reaches ~160 at the bound, where one fp32 ulp (1.5e-5)
+// would already exceed the fp32 tolerance once it becomes the relative error
+// of every exp(G_r - G_s). bf16 problems keep it in fp32.
 template <typename OpT>
-__device__ __forceinline__ float kexp(float x);
-// fp32 problems use the accurate exponential; bf16 problems the hardware
-// base-2 exponential (v_exp_f32) with a change of base.
+struct GateT {
+  typedef float T;
+};
 template <>
-__device__ __forceinline__ float kexp<float>(float x) { return expf(x); }
+struct GateT<float> {
+  typedef double T;
+};
+
+template <typename OpT>
+__device__ __forceinline__ float kexp(typename GateT<OpT>::T x);
+// fp32 problems: the fp64 exponential, rounded once; bf16 problems: the
+// hardware base-2 exponential (v_exp_f32) with a change of base.
+template <>
+__device__ __forceinline__ float kexp<float>(double x) { return static_cast<float>(exp(x)); }
 template <>
 __device__ __forceinline__ float kexp<bf16>(float x) { return __expf(x); }
+
+template <typename T>
+__device__ __forceinline__ T sigmoid_t(T x);
+template <>
+__device__ __forceinline__ float sigmoid_t<float>(float x) { return sigmoidf(x); }
+template <>
+__device__ __forceinline__ double sigmoid_t<double>(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 // Location of chunk c (global index) of a packed batch.
 struct ChunkLoc {
@@ -103,7 +123,8 @@ __device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, i
       bv[it] = 0.f;
     }
   }
-  const float ea = expf(in.A_log[h]);
+  typedef typename GateT<TI>::T GV;
+  const GV ea = exp(static_cast<GV>(in.A_log[h]));
   float db[VE];
 #pragma unroll
   for (int j = 0; j < VE; ++j) db[j] = in.dt_bias[static_cast<size_t>(h) * D + c0 + j];
@@ -126,8 +147,9 @@ __device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, i
     if (r < C) {
 #pragma unroll
       for (int j = 0; j < VE; ++j) {
-        const float z = ea * (to_f(xv[it][j]) + db[j]);
-        G(r, c0 + j) = valid ? d.lb * sigmoidf(z) : 0.f;
+        // the gate map in the cumulative gate's precision
+        const GV z = static_cast<GV>(ea) * (static_cast<GV>(to_f(xv[it][j])) + static_cast<GV>(db[j]));
+        G(r, c0 + j) = valid ? static_cast<GV>(d.lb) * sigmoid_t<GV>(z) : GV(0);
       }
       if (sub == 0) {
         const float a = valid ? 1.0f / sqrtf(sq + d.eps) : 0.f;
@@ -143,29 +165,31 @@ __device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, i
 
 // In-place inclusive cumulative sum over the C rows of every channel k of
 // G(r, k), by all threads of the block (fixed order, deterministic).
-// part_tot: LDS scratch of at least (blockDim / D) * D floats.
-template <int D, int C, int NT, class GRef>
-__device__ __forceinline__ void cumsum_rows(GRef G, float* part_tot) {
+// part_tot: LDS scratch of at least (blockDim / D) * D values of G's type.
+template <int D, int C, int NT, class GRef, typename PT>
+__device__ __forceinline__ void cumsum_rows(GRef G, PT* part_tot) {
   constexpr int parts = NT / D;
   constexpr int rp = C / parts;
   static_assert(NT % D == 0 && C % parts == 0, "cumsum layout");
   const int tid = threadIdx.x;
   const int col = tid % D, part = tid / D;
-  float run = 0.f;
-#pragma unroll 4
+  // all reads of the thread's run first (independent LDS loads in flight
+  // together), then the running sum in registers
+  PT v[rp];
+#pragma unroll
+  for (int i = 0; i < rp; ++i) v[i] = G(part * rp + i, col);
+  PT run = 0;
+#pragma unroll
   for (int i = 0; i < rp; ++i) {
-    const int r = part * rp + i;
-    run += G(r, col);
-    G(r, col) = run;
+    run += v[i];
+    v[i] = run;
   }
   part_tot[part * D + col] = run;
   __syncthreads();
-  float off = 0.f;
+  PT off = 0;
   for (int p = 0; p < part; ++p) off += part_tot[p * D + col];
-  if (part > 0) {
-#pragma unroll 4
-    for (int i = 0; i < rp; ++i) G(part * rp + i, col) += off;
-  }
+#pragma unroll
+  for (int i = 0; i < rp; ++i) G(part * rp + i, col) = v[i] + off;
   __syncthreads();
 }
 

@@ -42,13 +42,14 @@ hipError_t launch_chunk_table(const int32_t* cu, int N, int C, int32_t* coff, hi
 template <typename TI, int D, int C>
 __global__ void __launch_bounds__(256) k_prologue(Dims d, Inputs in, float* qh, float* kh,
                                                   float* beta, float* gcum) {
+  typedef typename GateT<TI>::T GV;
   constexpr int LDG = D + 4;
-  __shared__ float Gs[C * LDG];
+  __shared__ GV Gs[C * LDG];
   __shared__ float rq[C], rqs[C], rk[C], be[C];
-  __shared__ float ptot[4 * D];
+  __shared__ GV ptot[4 * D];
   const int c = blockIdx.x / d.H, h = blockIdx.x % d.H;
   const ChunkLoc L = locate<C>(in, d.N, c);
-  auto G = [&](int r, int kk) -> float& { return Gs[r * LDG + kk]; };
+  auto G = [&](int r, int kk) -> GV& { return Gs[r * LDG + kk]; };
   prologue_rows<TI, D, C, 4>(d, in, h, L, rq, rqs, rk, be, G);
   __syncthreads();
   cumsum_rows<D, C, 256>(G, ptot);
@@ -60,7 +61,7 @@ __global__ void __launch_bounds__(256) k_prologue(Dims d, Inputs in, float* qh, 
     const size_t o = (L.t0 + r) * ts + static_cast<size_t>(h) * D + kk;
     qh[o] = to_f(q[r * ts + kk]) * rqs[r];
     kh[o] = to_f(k[r * ts + kk]) * rk[r];
-    gcum[o] = Gs[r * LDG + kk];
+    gcum[o] = static_cast<float>(Gs[r * LDG + kk]);
   }
   for (int r = threadIdx.x; r < L.len; r += 256) beta[(L.t0 + r) * d.H + h] = be[r];
 }
