@@ -164,11 +164,34 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // ---- S1: prologue, transposed raw q/k, cumulative gate G^T
   auto Gf = [&](int r, int kk_) -> GV& { return GT[kk_ * LDG + r]; };
   prologue_rows<TI, D, C, NW>(d, in, h, L, rq, rqs, rk, be, Gf);
-  for (int e = tid; e < C * D; e += NT) {
-    const int r = e / D, kc = e % D;
-    const bool v = r < L.len;
-    qT[kc * LDQ + r] = v ? qr[r * ts + kc] : static_cast<TI>(0.f);
-    kT[kc * LDQ + r] = v ? kr[r * ts + kc] : static_cast<TI>(0.f);
+  {
+    // raw q, k transposed into LDS: 16-byte row loads (all issued first),
+    // element writes
+    typedef typename Vec16<TI>::T VT;
+    constexpr int VE = 16 / sizeof(TI), NVR = D / VE, NV = C * NVR, VPT = (NV + NT - 1) / NT;
+    VT xq[VPT], xk[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
+      if (e < NV && r < L.len) {
+        xq[j] = *reinterpret_cast<const VT*>(qr + r * ts + c);
+        xk[j] = *reinterpret_cast<const VT*>(kr + r * ts + c);
+      } else {
+#pragma unroll
+        for (int q2 = 0; q2 < VE; ++q2) xq[j][q2] = xk[j][q2] = static_cast<TI>(0.f);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
+      if (e < NV) {
+#pragma unroll
+        for (int q2 = 0; q2 < VE; ++q2) {
+          qT[(c + q2) * LDQ + r] = xq[j][q2];
+          kT[(c + q2) * LDQ + r] = xk[j][q2];
+        }
+      }
+    }
   }
   for (int e = tid; e < NW * C; e += NT) dbp[e / C][e % C] = 0.f;
   for (int e = tid; e < 2 * NKB * C; e += NT) (&rowp[0][0][0])[e] = 0.f;
@@ -204,7 +227,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       }
     }
     typename M::frag fa[TPW][NKS], fb[TPW][NKS];
-    float vin[TPW][4];
+    uint32_t vin[TPW][4];  // raw bits, row clamped (masked at use)
 #pragma unroll
     for (int jt = 0; jt < TPW; ++jt) {
       const int t = w + NW * jt;
@@ -218,7 +241,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         fb[jt][ks] = M::load(TT + (16 * nr + i) * C + ks * KS + g * KPL);
       }
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) vin[jt][rr] = r < L.len ? to_f(vr[r * ts + vv + rr]) : 0.f;
+      for (int rr = 0; rr < 4; ++rr) vin[jt][rr] = load_bits<TI>(vr + (r < L.len ? r : L.len - 1) * ts + vv + rr);
     }
     f32x4 dvv[TPW];
 #pragma unroll
@@ -235,7 +258,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         dst[rr] = from_f<OpT>(acc[rr]);
-        part += acc[rr] * vin[jt][rr];
+        part += r < L.len ? acc[rr] * bits_to_f<TI>(vin[jt][rr]) : 0.f;
         dvv[jt][rr] = be[r] * acc[rr];
       }
       part = sum_groups(part);
@@ -348,16 +371,32 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       if (p >= NPAIR) break;
       int m = 0, ns = p;
       while (ns > m) { ns -= m + 1; ++m; }
+      // global operands of this pair first (U and -W rows of block ns, P)
+      constexpr int NKV = V / KS;
+      typename M::frag fu[NKV], fw[NKV];
+      uint32_t pv[4];  // raw: converted at use
+#pragma unroll
+      for (int j = 0; j < NKV; ++j) {
+        fu[j] = M::load(Ug + (16 * ns + i) * V + j * KS + g * KPL);
+        fw[j] = M::load(Wng + (16 * ns + i) * K + j * KS + g * KPL);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) pv[rr] = load_bits<OpT>(Pg + (16 * m + 4 * g + rr) * C + 16 * ns + i);
       const f32x4 aqk = tile_nt<OpT>(zero4(), dO_s + 16 * m * LDA, LDA, Vn_s + 16 * ns * LDA, LDA, 0, V, lane);
-      const f32x4 a1 = tile_nt<OpT>(zero4(), dBv_s + 16 * m * LDA, LDA, Ug + 16 * ns * V, V, 0, V, lane);
-      const f32x4 a2 = tile_nt<OpT>(zero4(), dKb_s + 16 * m * LDA, LDA, Wng + 16 * ns * K, K, 0, K, lane);
+      f32x4 a1 = zero4(), a2 = zero4();
+#pragma unroll
+      for (int j = 0; j < NKV; ++j) {
+        const int ao = (16 * m + i) * LDA + j * KS + g * KPL;
+        a1 = M::mma(M::load(dBv_s + ao), fu[j], a1);
+        a2 = M::mma(M::load(dKb_s + ao), fw[j], a2);
+      }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int r = 16 * m + 4 * g + rr, s_ = 16 * ns + i;
         xq[jp][rr] = (s_ <= r) ? aqk[rr] : 0.f;
         const float dakk = (s_ < r) ? (a2[rr] - a1[rr]) : 0.f;
         xk[jp][rr] = be[r] * dakk;
-        const float pb = sum16(dakk * to_f(Pg[r * C + s_]));
+        const float pb = sum16(dakk * bits_to_f<OpT>(pv[rr]));
         if (i == 0) dbp[w][r] += pb;
       }
     }
@@ -466,7 +505,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // latency overlaps this phase and no load follows a store in S8)
   constexpr int PER = (C * D + NT - 1) / NT;
   static_assert(NT % D == 0, "one channel per thread in the gate VJP");
-  float xin[PER];
+  uint32_t xin[PER];  // raw bits: converted at use, so the loads stay in flight
   const float dbias = in.dt_bias[hoff + tid % D];
   const float ea = expf(in.A_log[h]);
   {
@@ -474,7 +513,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int e = tid + NT * j, r = e / D, kc = e % D;
-      xin[j] = (e < C * D && r < L.len) ? to_f(xr[r * ts + kc]) : 0.f;
+      const int rc = r < L.len ? r : L.len - 1;  // clamped row, masked at use
+      xin[j] = load_bits<TI>(xr + rc * ts + kc);
     }
   }
 #pragma unroll
@@ -542,8 +582,27 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     __syncthreads();
   }
 
-  // ---- S8: prologue VJP and outputs
+  // ---- S8: prologue VJP and outputs. The gate map's VJP consumes the raw
+  // gate loads before the first store of the phase (a load waited for after
+  // a store would also wait for the store).
   {
+    // the gate map's VJP and the gate-parameter sums run in the VJP precision
+    // (fp64 for fp32 problems: the dA_log sum cancels heavily)
+    TG pdt = 0, pA = 0;
+    const TG eat = static_cast<TG>(ea);
+    float dxv[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = tid + NT * j, r = e / D, kc = e % D;
+      const bool ok = e < C * D && r < L.len;
+      const TG z = eat * (static_cast<TG>(bits_to_f<TI>(xin[j])) + static_cast<TG>(dbias));
+      const TG sz = VJ::sig(z);
+      const TG dz = ok ? static_cast<TG>(dGT[kc * LDG + (r < C ? r : 0)]) * static_cast<TG>(d.lb) * sz * (1 - sz) : TG(0);
+      const TG dx = dz * eat;
+      dxv[j] = static_cast<float>(dx);
+      pdt += dx;
+      pA += dz * z;
+    }
     TI* dqo = dq + L.t0 * ts + hoff;
     TI* dko = dk + L.t0 * ts + hoff;
 #pragma unroll
@@ -562,23 +621,11 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         }
       }
     }
-    // the gate map's VJP and the gate-parameter sums run in the VJP precision
-    // (fp64 for fp32 problems: the dA_log sum cancels heavily)
     TI* dgo = dg + L.t0 * ts + hoff;
-    TG pdt = 0, pA = 0;
-    const TG eat = static_cast<TG>(ea);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int e = tid + NT * j, r = e / D, kc = e % D;
-      if (e < C * D && r < L.len) {
-        const TG z = eat * (static_cast<TG>(xin[j]) + static_cast<TG>(dbias));
-        const TG sz = VJ::sig(z);
-        const TG dz = static_cast<TG>(dGT[kc * LDG + r]) * static_cast<TG>(d.lb) * sz * (1 - sz);
-        const TG dx = dz * eat;
-        dgo[r * ts + kc] = from_f<TI>(static_cast<float>(dx));
-        pdt += dx;
-        pA += dz * z;
-      }
+      if (e < C * D && r < L.len) dgo[r * ts + kc] = from_f<TI>(dxv[j]);
     }
     // tid % D is this thread's channel for every e above
     ptg[tid] = pdt;

@@ -144,33 +144,37 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
     int I = 0, J = p;
     while (J > I) { J -= I + 1; ++I; }
     const int ra = 16 * I + i, rb = 16 * J + i;
-    const bool va = ra < L.len, vb = rb < L.len;
+    // Raw rows for every k-step, all in flight together. Rows past the chunk's
+    // end read the last valid row; their scales rqs / rk are zero.
+    const int rac = ra < L.len ? ra : L.len - 1, rbc = rb < L.len ? rb : L.len - 1;
+    constexpr int NKS = K / KS;
+    typename M::frag xa[NKS], xk[NKS], xb[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int kk = ks * KS + g * KPL;
+      xa[ks] = M::load(qr + rac * ts + kk);
+      xk[ks] = M::load(kr + rac * ts + kk);
+      xb[ks] = M::load(kr + rbc * ts + kk);
+    }
+    auto el = [](const typename M::frag& f, int j) -> float {
+      if constexpr (KPL == 1) return to_f(f);
+      else return to_f(f[j]);
+    };
+    const float sq = rqs[ra], sk = rk[ra], sb = rk[rb];
     f32x4 accP = zero4(), accQ = zero4();
-    for (int k0 = 0; k0 < K; k0 += KS) {
-      const int kk = k0 + g * KPL;
-      float qa[KPL], ka[KPL], kb[KPL], ea[KPL], eb[KPL];
-      if (va) {
-        load_row_f<TI, KPL>(qr + ra * ts + kk, qa);
-        load_row_f<TI, KPL>(kr + ra * ts + kk, ka);
-      } else {
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) qa[j] = ka[j] = 0.f;
-      }
-      if (vb) load_row_f<TI, KPL>(kr + rb * ts + kk, kb);
-      else {
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) kb[j] = 0.f;
-      }
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int kk = ks * KS + g * KPL;
+      float ea[KPL], eb[KPL];
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
         const GV gb = Gs[16 * I * LDG + kk + j];
         ea[j] = kexp<OpT>(Gs[ra * LDG + kk + j] - gb);
         eb[j] = kexp<OpT>(gb - Gs[rb * LDG + kk + j]);
       }
-      const float sq = rqs[ra], sk = rk[ra], sb = rk[rb];
-      const auto fq = M::make([&](int j) { return qa[j] * sq * ea[j]; });
-      const auto fk = M::make([&](int j) { return ka[j] * sk * ea[j]; });
-      const auto fb = M::make([&](int j) { return kb[j] * sb * eb[j]; });
+      const auto fq = M::make([&](int j) { return el(xa[ks], j) * sq * ea[j]; });
+      const auto fk = M::make([&](int j) { return el(xk[ks], j) * sk * ea[j]; });
+      const auto fb = M::make([&](int j) { return el(xb[ks], j) * sb * eb[j]; });
       accP = M::mma(fk, fb, accP);
       accQ = M::mma(fq, fb, accQ);
     }
@@ -203,16 +207,13 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
       const int item = tid + 256 * it, rp = item / LPR, c0 = (item % LPR) * VE;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const int r = 2 * rp + h2;
-        if (item < NITEM && r < L.len) {
-          xq[it][h2] = *reinterpret_cast<const VT*>(qr + r * ts + c0);
-          xk[it][h2] = *reinterpret_cast<const VT*>(kr + r * ts + c0);
-          xv[it][h2] = *reinterpret_cast<const VT*>(vr + r * ts + c0);
-        } else {
-#pragma unroll
-          for (int j = 0; j < VE; ++j)
-            xq[it][h2][j] = xk[it][h2][j] = xv[it][h2][j] = static_cast<TI>(0.f);
-        }
+        // rows past the chunk's end read the last valid row (no branch);
+        // their scales rqs, rk and beta are zero
+        const int r = 2 * rp + h2, rc = (item < NITEM && r < L.len) ? r : L.len - 1;
+        const int cc = item < NITEM ? c0 : 0;
+        xq[it][h2] = *reinterpret_cast<const VT*>(qr + rc * ts + cc);
+        xk[it][h2] = *reinterpret_cast<const VT*>(kr + rc * ts + cc);
+        xv[it][h2] = *reinterpret_cast<const VT*>(vr + rc * ts + cc);
       }
     }
     // stores of this phase follow all of its loads (loads and stores share one

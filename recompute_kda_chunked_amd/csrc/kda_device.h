@@ -31,6 +31,26 @@ __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16 from_f<bf16>(float x) { return static_cast<bf16>(x); }
 
+// Raw element bits held in a full register. A 16-bit load that fills only
+// half a register would depend on the register's old contents (and make the
+// wave wait for earlier loads); these loads zero-extend instead.
+template <typename T>
+__device__ __forceinline__ uint32_t load_bits(const T* p);
+template <>
+__device__ __forceinline__ uint32_t load_bits<bf16>(const bf16* p) {
+  return *reinterpret_cast<const uint16_t*>(p);
+}
+template <>
+__device__ __forceinline__ uint32_t load_bits<float>(const float* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
+template <typename T>
+__device__ __forceinline__ float bits_to_f(uint32_t b);
+template <>
+__device__ __forceinline__ float bits_to_f<bf16>(uint32_t b) { return __uint_as_float(b << 16); }
+template <>
+__device__ __forceinline__ float bits_to_f<float>(uint32_t b) { return __uint_as_float(b); }
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
@@ -51,7 +71,8 @@ __device__ __forceinline__ float sum_groups(float x) {
   return x;
 }
 
-__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// 1 / (1 + e^-x) with the hardware reciprocal (about 1 ulp).
+__device__ __forceinline__ float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // ---------------------------------------------------------------- MFMA traits
 

@@ -107,21 +107,19 @@ __device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, i
   const TI* k = static_cast<const TI*>(in.k) + L.t0 * ts + hoff;
   const TI* x = static_cast<const TI*>(in.g) + L.t0 * ts + hoff;
   const TI* rb = static_cast<const TI*>(in.beta) + L.t0 * d.H + h;
+  // Rows past the chunk's end load the last valid row instead (always in
+  // bounds, no branch) and are masked at use: a load under a branch, or one
+  // converted on arrival, would make the wave wait for it right away.
   VT qv[NIT], kv[NIT], xv[NIT];
-  float bv[NIT];
+  uint32_t bv[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int r = (w + NW * it) * RPI + rsub;
-    if (r < L.len) {
-      qv[it] = *reinterpret_cast<const VT*>(q + r * ts);
-      kv[it] = *reinterpret_cast<const VT*>(k + r * ts);
-      xv[it] = *reinterpret_cast<const VT*>(x + r * ts);
-      bv[it] = sub == 0 ? to_f(rb[static_cast<size_t>(r) * d.H]) : 0.f;
-    } else {
-#pragma unroll
-      for (int j = 0; j < VE; ++j) qv[it][j] = kv[it][j] = xv[it][j] = static_cast<TI>(0.f);
-      bv[it] = 0.f;
-    }
+    const int rc = r < L.len ? r : L.len - 1;
+    qv[it] = *reinterpret_cast<const VT*>(q + rc * ts);
+    kv[it] = *reinterpret_cast<const VT*>(k + rc * ts);
+    xv[it] = *reinterpret_cast<const VT*>(x + rc * ts);
+    bv[it] = load_bits<TI>(rb + static_cast<size_t>(rc) * d.H);
   }
   typedef typename GateT<TI>::T GV;
   const GV ea = exp(static_cast<GV>(in.A_log[h]));
@@ -157,7 +155,7 @@ __device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, i
         rq[r] = a;
         rqs[r] = d.scale * a;
         rk[r] = b;
-        be[r] = valid ? sigmoidf(bv[it]) : 0.f;
+        be[r] = valid ? sigmoidf(bits_to_f<TI>(bv[it])) : 0.f;
       }
     }
   }

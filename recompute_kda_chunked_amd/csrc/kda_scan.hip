@@ -55,26 +55,6 @@ struct ScanGeo {
   static_assert(NHT % 4 == 0 && HPW % BVT == 0, "state tiles must split over 4 waves");
 };
 
-// Raw element bits held in a full register. A 16-bit load that fills only
-// half a register would depend on the register's old contents (and make the
-// wave wait for earlier loads); these loads zero-extend instead.
-template <typename T>
-__device__ __forceinline__ uint32_t load_bits(const T* p);
-template <>
-__device__ __forceinline__ uint32_t load_bits<bf16>(const bf16* p) {
-  return *reinterpret_cast<const uint16_t*>(p);
-}
-template <>
-__device__ __forceinline__ uint32_t load_bits<float>(const float* p) {
-  return *reinterpret_cast<const uint32_t*>(p);
-}
-template <typename T>
-__device__ __forceinline__ float bits_to_f(uint32_t b);
-template <>
-__device__ __forceinline__ float bits_to_f<bf16>(uint32_t b) { return __uint_as_float(b << 16); }
-template <>
-__device__ __forceinline__ float bits_to_f<float>(uint32_t b) { return __uint_as_float(b); }
-
 // Operands of one chunk for one wave of the forward scan.
 template <typename OpT, int D, int C, int BV>
 struct FwdOps {
