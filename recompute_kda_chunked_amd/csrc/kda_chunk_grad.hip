@@ -161,77 +161,34 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   const TI* vr = static_cast<const TI*>(in.v) + L.t0 * ts + hoff;
   auto row_block = [&](int jm) { return half * MR + jm; };  // valid while < NB
 
-  // ---- S1: prologue, transposed raw q/k, cumulative gate G^T
-  auto Gf = [&](int r, int kk_) -> GV& { return GT[kk_ * LDG + r]; };
-  prologue_rows<TI, D, C, NW>(d, in, h, L, rq, rqs, rk, be, Gf);
+  // Global loads of S1 (raw q, k tiles) and S2/S3 (dVn^T, T^T, dO, Vn, v)
+  // are all issued here, before any arithmetic, so their latency overlaps the
+  // prologue and the cumulative sum. Rows past the chunk's end read the last
+  // valid row (no branch) and are masked where they are used.
+  static_assert(sizeof(TI) == sizeof(OpT), "inputs and operands share a type");
+  typedef typename Vec16<TI>::T VT;
+  constexpr int VE = 16 / sizeof(TI), NVR = D / VE, NV = C * NVR, VPT = (NV + NT - 1) / NT;
+  constexpr int T2 = (V / 16) * NB, TPW = (T2 + NW - 1) / NW, NKS = C / KS;
+  VT ldq[VPT], ldk[VPT], ldo[VPT], ldn[VPT];
+  typename M::frag fa[TPW][NKS], fb[TPW][NKS];
+  uint32_t vin[TPW][4];
   {
-    // raw q, k transposed into LDS: 16-byte row loads (all issued first),
-    // element writes
-    typedef typename Vec16<TI>::T VT;
-    constexpr int VE = 16 / sizeof(TI), NVR = D / VE, NV = C * NVR, VPT = (NV + NT - 1) / NT;
-    VT xq[VPT], xk[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
-      if (e < NV && r < L.len) {
-        xq[j] = *reinterpret_cast<const VT*>(qr + r * ts + c);
-        xk[j] = *reinterpret_cast<const VT*>(kr + r * ts + c);
-      } else {
-#pragma unroll
-        for (int q2 = 0; q2 < VE; ++q2) xq[j][q2] = xk[j][q2] = static_cast<TI>(0.f);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
-      if (e < NV) {
-#pragma unroll
-        for (int q2 = 0; q2 < VE; ++q2) {
-          qT[(c + q2) * LDQ + r] = xq[j][q2];
-          kT[(c + q2) * LDQ + r] = xk[j][q2];
-        }
-      }
-    }
-  }
-  for (int e = tid; e < NW * C; e += NT) dbp[e / C][e % C] = 0.f;
-  for (int e = tid; e < 2 * NKB * C; e += NT) (&rowp[0][0][0])[e] = 0.f;
-  __syncthreads();
-  cumsum_rows<D, C, NT>(Gf, ptot);
-
-  // ---- S2: dBv = T^T dVn (tiles of dBv^T: value rows, chunk-row columns),
-  // ---- S3: dO and Vn tiles into LDS.
-  // Every global load of both phases is issued before their first store
-  // (loads and stores share one completion counter, so a load issued after
-  // a store would also wait for the store).
-  {
-    static_assert(sizeof(TI) == sizeof(OpT), "inputs and operands share a type");
-    typedef typename Vec16<TI>::T VT;
-    constexpr int VE = 16 / sizeof(TI), NVR = V / VE, NV = C * NVR, VPT = (NV + NT - 1) / NT;
-    constexpr int T2 = (V / 16) * NB, TPW = (T2 + NW - 1) / NW, NKS = C / KS;
     const OpT* dVnT = static_cast<const OpT*>(st.dVnT) + idx * V * C;
     const OpT* TT = static_cast<const OpT*>(ops.TT) + idx * C * C;
     const TI* dOr = dO + L.t0 * ts + hoff;
     const OpT* Vn = static_cast<const OpT*>(st.Vn) + idx * C * V;
-    VT xo[VPT], xn[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
-      if (e < NV) {
-        xn[j] = *reinterpret_cast<const VT*>(Vn + r * V + c);
-        if (r < L.len) {
-          xo[j] = *reinterpret_cast<const VT*>(dOr + r * ts + c);
-        } else {
-#pragma unroll
-          for (int q2 = 0; q2 < VE; ++q2) xo[j][q2] = static_cast<TI>(0.f);
-        }
-      }
+      const int e0 = tid + NT * j, e = e0 < NV ? e0 : 0, r = e / NVR, c = (e % NVR) * VE;
+      const int rc = r < L.len ? r : L.len - 1;
+      ldq[j] = *reinterpret_cast<const VT*>(qr + rc * ts + c);
+      ldk[j] = *reinterpret_cast<const VT*>(kr + rc * ts + c);
+      ldo[j] = *reinterpret_cast<const VT*>(dOr + rc * ts + c);
+      ldn[j] = *reinterpret_cast<const VT*>(Vn + r * V + c);
     }
-    typename M::frag fa[TPW][NKS], fb[TPW][NKS];
-    uint32_t vin[TPW][4];  // raw bits, row clamped (masked at use)
 #pragma unroll
     for (int jt = 0; jt < TPW; ++jt) {
-      const int t = w + NW * jt;
-      if (t >= T2) break;
+      const int t0 = w + NW * jt, t = t0 < T2 ? t0 : 0;
       const int mv = t / NB, nr = t % NB;
       const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
       // the whole reduction is taken (T^T[r][s] is stored as 0 for s < r)
@@ -243,6 +200,35 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) vin[jt][rr] = load_bits<TI>(vr + (r < L.len ? r : L.len - 1) * ts + vv + rr);
     }
+  }
+
+  // ---- S1: prologue, transposed raw q/k, cumulative gate G^T
+  auto Gf = [&](int r, int kk_) -> GV& { return GT[kk_ * LDG + r]; };
+  prologue_rows<TI, D, C, NW>(d, in, h, L, rq, rqs, rk, be, Gf);
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
+    if (e < NV) {
+      const bool ok = r < L.len;
+#pragma unroll
+      for (int q2 = 0; q2 < VE; ++q2) {
+        qT[(c + q2) * LDQ + r] = ok ? ldq[j][q2] : static_cast<TI>(0.f);
+        kT[(c + q2) * LDQ + r] = ok ? ldk[j][q2] : static_cast<TI>(0.f);
+      }
+    }
+  }
+  for (int e = tid; e < NW * C; e += NT) dbp[e / C][e % C] = 0.f;
+  for (int e = tid; e < 2 * NKB * C; e += NT) (&rowp[0][0][0])[e] = 0.f;
+  __syncthreads();
+  cumsum_rows<D, C, NT>(Gf, ptot);
+
+  // ---- S2: dBv = T^T dVn (tiles of dBv^T: value rows, chunk-row columns),
+  // ---- S3: dO and Vn tiles into LDS. The h, dh' fragments S4 needs are
+  // requested before this phase's stores (loads and stores share one
+  // completion counter, so a load issued after a store would wait for it).
+  constexpr int NVS = V / KS;
+  typename M::frag fh[NVS], fdh[NVS];
+  {
     f32x4 dvv[TPW];
 #pragma unroll
     for (int jt = 0; jt < TPW; ++jt) {
@@ -268,8 +254,20 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     for (int j = 0; j < VPT; ++j) {
       const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
       if (e < NV) {
-        *reinterpret_cast<VT*>(dO_s + r * LDA + c) = xo[j];
-        *reinterpret_cast<VT*>(Vn_s + r * LDA + c) = xn[j];
+        VT zo;
+#pragma unroll
+        for (int q2 = 0; q2 < VE; ++q2) zo[q2] = r < L.len ? ldo[j][q2] : static_cast<TI>(0.f);
+        *reinterpret_cast<VT*>(dO_s + r * LDA + c) = zo;
+        *reinterpret_cast<VT*>(Vn_s + r * LDA + c) = ldn[j];
+      }
+    }
+    {
+      const OpT* bh = static_cast<const OpT*>(st.h) + idx * K * V + kk * V + g * KPL;
+      const OpT* bdh = static_cast<const OpT*>(st.dh) + idx * K * V + kk * V + g * KPL;
+#pragma unroll
+      for (int j = 0; j < NVS; ++j) {
+        fh[j] = M::load(bh + j * KS);
+        fdh[j] = M::load(bdh + j * KS);
       }
     }
     TI* dvo = dv + L.t0 * ts + hoff;
@@ -298,22 +296,12 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   }
   TG hdh = 0;
   {
-    const OpT* hm = static_cast<const OpT*>(st.h) + idx * K * V;
-    const OpT* dhm = static_cast<const OpT*>(st.dh) + idx * K * V;
-    // the wave's rows of h and dh' as B fragments, loaded once
-    constexpr int NVS = V / KS;
-    typename M::frag fh[NVS], fdh[NVS];
+    // the wave's rows of h and dh' as B fragments (loaded during S2)
     float hd = 0.f;
-    {
-      const OpT* bh = hm + kk * V + g * KPL;
-      const OpT* bdh = dhm + kk * V + g * KPL;
 #pragma unroll
-      for (int j = 0; j < NVS; ++j) {
-        fh[j] = M::load(bh + j * KS);
-        fdh[j] = M::load(bdh + j * KS);
+    for (int j = 0; j < NVS; ++j) {
 #pragma unroll
-        for (int jj = 0; jj < KPL; ++jj) hd += frag_at<OpT>(fh[j], jj) * frag_at<OpT>(fdh[j], jj);
-      }
+      for (int jj = 0; jj < KPL; ++jj) hd += frag_at<OpT>(fh[j], jj) * frag_at<OpT>(fdh[j], jj);
     }
     hdh = static_cast<TG>(sum_groups(hd));
     const GV Gc = GT[kk * LDG + C - 1];
