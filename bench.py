@@ -97,11 +97,13 @@ def profile_traffic(kernel: str, workload: str):
 
 
 def cpu_baseline(x, w) -> dict:
-    """The FP64 oracle on the first n heads of the same inputs (n = host threads)."""
+    """The FP64 oracle on the first n heads of the same inputs (n = twice the
+    host threads, at most H), all tokens, scaled to the full workload."""
     import numpy as np
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
-    nh = max(1, min(w.H, threads))
+    # two heads per thread: about 10-20 s of CPU work at the 8K and 128K sizes
+    nh = max(1, min(w.H, 2 * threads))
     sl = slice(0, nh)
     host = {n: x[n][:, sl].double().cpu().numpy() for n in ("q", "k", "v", "raw_g", "raw_beta", "dO")}
     A = x["A_log"][sl].double().cpu().numpy()
