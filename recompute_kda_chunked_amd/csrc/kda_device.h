@@ -57,12 +57,29 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Sum over the 16 lanes that share g (the lanes of one tile row group).
-__device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+// DPP lane move (a VALU operand modifier: no LDS traffic, unlike a shuffle).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 2, 4, 8, 16 or 32),
+// every lane of a group receiving the group's sum: swaps within quads
+// (quad_perm [1,0,3,2], [2,3,0,1]), then mirrors within 8 and 16 lanes
+// (row_half_mirror, row_mirror); lanes 16 apart are combined by a shuffle.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16 || N == 32, "lane group size");
+  if (N >= 2) x += dpp_mov<0xB1>(x);
+  if (N >= 4) x += dpp_mov<0x4E>(x);
+  if (N >= 8) x += dpp_mov<0x141>(x);
+  if (N >= 16) x += dpp_mov<0x140>(x);
+  if (N >= 32) x += __shfl_xor(x, 16, kWave);
   return x;
 }
+
+// Sum over the 16 lanes that share g (the lanes of one tile row group).
+__device__ __forceinline__ float sum16(float x) { return group_sum<16>(x); }
 
 // Sum over the four lane groups g (lanes i, i+16, i+32, i+48).
 __device__ __forceinline__ float sum_groups(float x) {

@@ -137,11 +137,8 @@ __device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, i
       sq += a * a;
       sk += b * b;
     }
-#pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) {
-      sq += __shfl_xor(sq, o, kWave);
-      sk += __shfl_xor(sk, o, kWave);
-    }
+    sq = group_sum<LPR>(sq);
+    sk = group_sum<LPR>(sk);
     if (r < C) {
 #pragma unroll
       for (int j = 0; j < VE; ++j) {
