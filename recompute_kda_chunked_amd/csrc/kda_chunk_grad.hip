@@ -128,11 +128,11 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // cumulative sum and of the partial reductions
   constexpr int OFF_S = 0;
   static_assert(OFF_S + (int)sizeof(TG) * NT + 4 * NT <= SZU, "LDS scratch must fit");
-  __shared__ GV GT[K * LDG];
+  __shared__ __attribute__((aligned(16))) GV GT[K * LDG];
   __shared__ __attribute__((aligned(16))) TI qT[K * LDQ];
   __shared__ __attribute__((aligned(16))) TI kT[K * LDQ];
   __shared__ __attribute__((aligned(16))) unsigned char uni[SZU];
-  __shared__ float rq[C], rqs[C], rk[C], be[C];
+  __shared__ __attribute__((aligned(16))) float rq[C], rqs[C], rk[C], be[C];
   __shared__ float dbp[NW][C];
   __shared__ float rowp[2][NKB][C];
   __shared__ float rsum[2][C];  // rowp summed over key blocks
@@ -420,6 +420,32 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     auto khat = [&](int r) { return static_cast<TG>(to_f(kq[r])) * static_cast<TG>(rk[r]); };
     auto qhat = [&](int r) { return static_cast<TG>(to_f(qk[r])) * static_cast<TG>(rqs[r]); };
     auto dec = [&](int r, int s_) { return VJ::ex(static_cast<TG>(Gk[r]) - static_cast<TG>(Gk[s_])); };
+    // Eight consecutive rows r0..r0+7 (r0 a multiple of 8) of this channel's
+    // raw q or k, its row scale and G, read as 16-byte LDS vectors (bf16
+    // operands; the fp32 path reads one row per lane).
+    struct Rows8 {
+      float x[8], sc[8], G[8];
+    };
+    auto rows8 = [&](const TI* col, const float* scale, int r0) {
+      Rows8 o;
+      if constexpr (VJ::KPL == 8) {
+        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(col + r0);
+        const f32x4 s0v = *reinterpret_cast<const f32x4*>(scale + r0);
+        const f32x4 s1v = *reinterpret_cast<const f32x4*>(scale + r0 + 4);
+        const f32x4 g0v = *reinterpret_cast<const f32x4*>(Gk + r0);
+        const f32x4 g1v = *reinterpret_cast<const f32x4*>(Gk + r0 + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o.x[j] = to_f(xv[j]);
+          o.x[j + 4] = to_f(xv[j + 4]);
+          o.sc[j] = s0v[j];
+          o.sc[j + 4] = s1v[j];
+          o.G[j] = g0v[j];
+          o.G[j + 4] = g1v[j];
+        }
+      }
+      return o;
+    };
 #pragma unroll
     for (int jm = 0; jm < MR; ++jm) {
       const int I = row_block(jm);
@@ -431,10 +457,20 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       const int s_hi = 16 * (I + 1);
 #pragma unroll 1
       for (int s0 = 0; s0 < (s_hi + VJ::KS - 1) / VJ::KS * VJ::KS; s0 += VJ::KS) {
-        const auto fb = VJ::make([&](int j) {
-          const int s_ = s0 + g * VJ::KPL + j;
-          return s_ < s_hi ? khat(s_) * dec(b0, s_) : TG(0);
-        });
+        typename VJ::frag fb;
+        if constexpr (VJ::KPL == 8) {
+          const int sb = s0 + g * 8;
+          const Rows8 v = rows8(kq, rk, sb);
+          const float gb = Gk[b0];
+          fb = VJ::make([&](int j) {
+            return sb + j < s_hi ? v.x[j] * v.sc[j] * VJ::ex(gb - v.G[j]) : TG(0);
+          });
+        } else {
+          fb = VJ::make([&](int j) {
+            const int s_ = s0 + g * VJ::KPL + j;
+            return s_ < s_hi ? khat(s_) * dec(b0, s_) : TG(0);
+          });
+        }
         const int ao = (16 * I + i) * LDX + s0 + g * VJ::KPL;
         rq_ = VJ::mma(VJ::load(dXq + ao), fb, rq_);
         rk_ = VJ::mma(VJ::load(dXk + ao), fb, rk_);
@@ -465,10 +501,19 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         for (int u0 = 0; u0 < 32; u0 += VJ::KS) {
           const int u = u0 + g * VJ::KPL;
           const OpT* ap = (u < 16 ? dXkT : dXqT) + (16 * J + i) * LDX + c0 + (u & 15);
-          const auto fb = VJ::make([&](int j) {
-            const int uu = u + j, r = c0 + (uu & 15);
-            return (uu < 16 ? khat(r) : qhat(r)) * dec(r, c0);
-          });
+          typename VJ::frag fb;
+          if constexpr (VJ::KPL == 8) {
+            // u is 0, 8, 16 or 24: rows c0 + (u & 15) .. + 7 of kh (u < 16) or qh
+            const int rb = c0 + (u & 15);
+            const Rows8 v = u < 16 ? rows8(kq, rk, rb) : rows8(qk, rqs, rb);
+            const float gc = Gk[c0];
+            fb = VJ::make([&](int j) { return v.x[j] * v.sc[j] * VJ::ex(v.G[j] - gc); });
+          } else {
+            fb = VJ::make([&](int j) {
+              const int uu = u + j, r = c0 + (uu & 15);
+              return (uu < 16 ? khat(r) : qhat(r)) * dec(r, c0);
+            });
+          }
           y = VJ::mma(VJ::load(ap), fb, y);
         }
         y = VJ::fix(y);
