@@ -50,11 +50,11 @@ def _load(path: str | None = None) -> ctypes.CDLL:
             raise FileNotFoundError(path)
         build()
     lib = ctypes.CDLL(path)
-    f = lib.kda_oracle
+    f = lib.kda_oracle_ex
     dp = ctypes.POINTER(ctypes.c_double)
     f.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
                   ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
-                  ctypes.c_double, ctypes.c_int] + [dp] * 8 + [dp] * 8 + [ctypes.c_int]
+                  ctypes.c_double, ctypes.c_int] + [dp] * 8 + [dp] * 8 + [dp] * 4 + [ctypes.c_int]
     f.restype = ctypes.c_int
     _lib_cache[path] = lib
     return lib
@@ -75,13 +75,16 @@ def _ptr(a: np.ndarray | None):
 def kda(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, dO=None,
         scale: float = 1.0, lower_bound: float = -5.0, eps: float = 1e-6,
         gate_mode: int = GATE_SIGMOID_BOUND, n_threads: int = 0,
-        lib_path: str | None = None) -> dict:
+        lib_path: str | None = None, h0=None, dht=None, final_state: bool = False) -> dict:
     """Run the oracle. Shapes: q,k,raw_g [T,H,K]; v [T,H,V]; raw_beta [T,H];
     A_log [H]; dt_bias [H,K]; cu_seqlens [N+1] (defaults to one sequence);
-    dO [T,H,V] or None (forward only).
+    dO [T,H,V] or None (forward only); h0 [N,H,K,V] or None (each sequence
+    starts from zero); dht [N,H,K,V] or None (no loss on the final state).
 
-    Returns a dict of float64 arrays: ``o`` and, when dO is given, ``dq, dk,
-    dv, draw_g, draw_beta, dA_log, ddt_bias``.
+    Returns a dict of float64 arrays: ``o``; ``ht`` (the final state of every
+    sequence) when final_state, h0 or dht is given; and, when dO is given,
+    ``dq, dk, dv, draw_g, draw_beta, dA_log, ddt_bias`` plus ``dh0`` when h0
+    is given.
     """
     q, k, v, raw_g, raw_beta = map(_f64, (q, k, v, raw_g, raw_beta))
     A_log, dt_bias = _f64(A_log), _f64(dt_bias)
@@ -110,12 +113,27 @@ def kda(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, dO=None,
                    draw_g=np.zeros((T, H, K)), draw_beta=np.zeros((T, H)),
                    dA_log=np.zeros(H), ddt_bias=np.zeros((H, K)))
         grads = [out[n_] for n_ in ("dq", "dk", "dv", "draw_g", "draw_beta", "dA_log", "ddt_bias")]
+    sshape = (n, H, K, V)
+    if h0 is not None:
+        h0 = _f64(h0)
+        if h0.shape != sshape:
+            raise ValueError("h0 must be [N,H,K,V]")
+    if dht is not None:
+        dht = _f64(dht)
+        if dht.shape != sshape:
+            raise ValueError("dht must be [N,H,K,V]")
+    ht = np.zeros(sshape) if (final_state or h0 is not None or dht is not None) else None
+    if ht is not None:
+        out["ht"] = ht
+    dh0 = np.zeros(sshape) if (dO is not None and h0 is not None) else None
+    if dh0 is not None:
+        out["dh0"] = dh0
     lib = _load(lib_path)
-    rc = lib.kda_oracle(n, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, K, V,
-                        float(scale), float(lower_bound), float(eps), int(gate_mode),
-                        _ptr(q), _ptr(k), _ptr(v), _ptr(raw_g), _ptr(raw_beta), _ptr(A_log),
-                        _ptr(dt_bias), _ptr(dO), _ptr(o), *[_ptr(g) for g in grads[:7]],
-                        int(n_threads))
+    rc = lib.kda_oracle_ex(n, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, K, V,
+                           float(scale), float(lower_bound), float(eps), int(gate_mode),
+                           _ptr(q), _ptr(k), _ptr(v), _ptr(raw_g), _ptr(raw_beta), _ptr(A_log),
+                           _ptr(dt_bias), _ptr(dO), _ptr(o), *[_ptr(g) for g in grads[:7]],
+                           _ptr(h0), _ptr(ht), _ptr(dht), _ptr(dh0), int(n_threads))
     if rc != 0:
         raise RuntimeError("kda_oracle failed with status %d" % rc)
     return out

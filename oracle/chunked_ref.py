@@ -58,16 +58,20 @@ def _chunk_mats(qh, kh, beta, G):
 
 
 def chunk_fwd(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, chunk,
-              scale=1.0, lower_bound=-5.0, eps=1e-6):
-    """Chunk-form forward. Returns O [T,H,V] (float64)."""
+              scale=1.0, lower_bound=-5.0, eps=1e-6, h0=None, return_state=False):
+    """Chunk-form forward. Returns O [T,H,V] (float64), or (O, ht) with the
+    state after every sequence's last chunk, ht [N,H,K,V], when return_state.
+    h0 [N,H,K,V]: the state each sequence enters its first chunk with (zero
+    when None)."""
     T, H, K = q.shape
     out = np.zeros((T, H, v.shape[2]))
+    ht = np.zeros((len(cu_seqlens) - 1, H, K, v.shape[2]))
     for n in range(len(cu_seqlens) - 1):
         a, b = int(cu_seqlens[n]), int(cu_seqlens[n + 1])
         for hh in range(H):
             p = _prologue(q[a:b, hh], k[a:b, hh], raw_g[a:b, hh], raw_beta[a:b, hh],
                           A_log[hh], dt_bias[hh], scale, lower_bound, eps)
-            h = np.zeros((K, v.shape[2]))
+            h = np.zeros((K, v.shape[2])) if h0 is None else np.array(h0[n, hh], dtype=np.float64)
             for c0 in range(0, b - a, chunk):
                 sl = slice(c0, min(c0 + chunk, b - a))
                 G = np.cumsum(p["g"][sl], axis=0)
@@ -79,7 +83,8 @@ def chunk_fwd(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, chunk,
                 out[a:b, hh][sl] = (p["qh"][sl] * np.exp(G)) @ h + Aqk @ Vn
                 kg = p["kh"][sl] * np.exp(G[-1][None, :] - G)
                 h = np.exp(G[-1])[:, None] * h + kg.T @ Vn
-    return out
+            ht[n, hh] = h
+    return (out, ht) if return_state else out
 
 
 def chunk_bwd(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, dO, chunk,

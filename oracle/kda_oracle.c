@@ -21,14 +21,22 @@
  *
  *   Token recurrence (the gated delta rule with a per-channel decay, as the
  *   pieces in "KDA at the production shape..." section 1.1 and the per-chunk
- *   operation table of section 2.1 describe it; no initial state, no final
- *   state, the state restarts at every packed-sequence boundary per the
- *   measurement configuration of the FROST page):
+ *   operation table of section 2.1 describe it; the state restarts at every
+ *   packed-sequence boundary per the measurement configuration of the FROST
+ *   page, from zero there, which measures no initial and no final state):
  *     St = Diag(exp(g_t)) S_{t-1}           (channel-wise decay of the state)
  *     u_t = v_t - St^T kh_t                 (delta-rule prediction error)
  *     S_t = St + beta_t kh_t u_t^T          (rank-one write)
  *     o_t = S_t^T qh_t
  *   which is S_t = (I - beta k k^T) Diag(e^g) S_{t-1} + beta k v^T.
+ *
+ *   Optional state input and output (kda_oracle_ex): each sequence n may
+ *   start from a given S_{-1} = h0[n] instead of zero, and its last state
+ *   S_{L-1} is returned as ht[n] (an empty sequence passes h0 through). The
+ *   backward then takes a gradient dht[n] of the loss with respect to ht[n]
+ *   (the reverse sweep starts from it instead of zero) and returns dh0[n],
+ *   the gradient with respect to h0[n] (the sweep's dS once it has passed
+ *   the first token). Both are [N, H, K, V].
  *
  *   Backward: reverse-mode differentiation of exactly the steps above, token
  *   by token in reverse order, then of the prologue. All seven inputs
@@ -57,6 +65,8 @@ typedef struct {
   int gate_mode;
   const double *q, *k, *v, *raw_g, *raw_beta, *A_log, *dt_bias, *dO;
   double *o, *dq, *dk, *dv, *draw_g, *draw_beta;
+  const double *h0, *dht; /* [N,H,K,V] or NULL (zero) */
+  double *ht, *dh0;       /* [N,H,K,V] or NULL (not written) */
 } prob_t;
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
@@ -129,10 +139,11 @@ typedef struct {
 
 /* Forward and (if dO) backward for one (sequence, head) task.
    dA_log_out / ddt_out receive this task's contribution. */
-static int run_task(const prob_t *p, int64_t t0, int64_t t1, int h,
+static int run_task(const prob_t *p, int n, int64_t t0, int64_t t1, int h,
                     double *dA_log_out, double *ddt_out) {
   const int K = p->K, V = p->V, H = p->H;
   const size_t KV = (size_t)K * V;
+  const size_t soff = ((size_t)n * H + h) * KV; /* this task's [K,V] state slot */
   const int64_t L = t1 - t0;
   int err = 0;
   scratch_t s;
@@ -163,7 +174,8 @@ static int run_task(const prob_t *p, int64_t t0, int64_t t1, int h,
   }
   tok_t w = {0, 0, 0, s.qh, s.kh, s.qbar, s.g, s.z};
 
-  /* ---- forward: token recurrence, S = 0 at the sequence start ---- */
+  /* ---- forward: token recurrence from S = h0 (or 0) at the sequence start ---- */
+  if (p->h0) memcpy(s.S, p->h0 + soff, sizeof(double) * KV);
   for (int64_t t = t0; t < t1; ++t) {
     if (s.ckpt && (t - t0) % CKPT == 0)
       memcpy(s.ckpt + (size_t)((t - t0) / CKPT) * KV, s.S, sizeof(double) * KV);
@@ -171,10 +183,14 @@ static int run_task(const prob_t *p, int64_t t0, int64_t t1, int h,
     step(p, &w, p->v + ((size_t)t * H + h) * V, s.S, NULL, s.u,
          p->o ? p->o + ((size_t)t * H + h) * V : s.tmp);
   }
+  if (p->ht) memcpy(p->ht + soff, s.S, sizeof(double) * KV);
   if (!p->dO) goto done;
 
-  /* ---- backward: reverse sweep, dS = 0 after the sequence end ---- */
-  memset(s.dS, 0, sizeof(double) * KV);
+  /* ---- backward: reverse sweep from dS = dht (or 0) after the sequence end ---- */
+  if (p->dht)
+    memcpy(s.dS, p->dht + soff, sizeof(double) * KV);
+  else
+    memset(s.dS, 0, sizeof(double) * KV);
   *dA_log_out = 0;
   for (int i = 0; i < K; ++i) ddt_out[i] = 0;
   const double ea = exp(p->A_log[h]);
@@ -274,6 +290,8 @@ static int run_task(const prob_t *p, int64_t t0, int64_t t1, int h,
       }
     }
   }
+  /* dS now holds the gradient with respect to the state entering the first token */
+  if (p->dh0) memcpy(p->dh0 + soff, s.dS, sizeof(double) * KV);
 done:
   free(s.S); free(s.St); free(s.dS); free(s.dSt); free(s.u); free(s.du);
   free(s.tmp); free(s.dqh); free(s.dkh); free(s.dg); free(s.qh); free(s.kh);
@@ -282,24 +300,28 @@ done:
 }
 
 /* Entry point. cu_seqlens: [n_seqs+1], non-decreasing from 0. dO == NULL runs
-   the forward only (gradient pointers are then ignored). o may be NULL when
+   the forward only (gradient pointers, dht and dh0 are then ignored). h0, ht,
+   dht, dh0: [n_seqs, H, K, V] or NULL (h0, dht NULL = zero; ht, dh0 NULL =
+   not written). o may be NULL when
    only gradients are wanted. Returns 0 on success, 1 on bad arguments or
    allocation failure. n_threads <= 0 uses the OpenMP default. */
-int kda_oracle(int n_seqs, const int64_t *cu_seqlens, int H, int K, int V,
-               double scale, double lower_bound, double eps, int gate_mode,
-               const double *q, const double *k, const double *v,
-               const double *raw_g, const double *raw_beta,
-               const double *A_log, const double *dt_bias, const double *dO,
-               double *o, double *dq, double *dk, double *dv, double *draw_g,
-               double *draw_beta, double *dA_log, double *ddt_bias,
-               int n_threads) {
+int kda_oracle_ex(int n_seqs, const int64_t *cu_seqlens, int H, int K, int V,
+                  double scale, double lower_bound, double eps, int gate_mode,
+                  const double *q, const double *k, const double *v,
+                  const double *raw_g, const double *raw_beta,
+                  const double *A_log, const double *dt_bias, const double *dO,
+                  double *o, double *dq, double *dk, double *dv, double *draw_g,
+                  double *draw_beta, double *dA_log, double *ddt_bias,
+                  const double *h0, double *ht, const double *dht, double *dh0,
+                  int n_threads) {
   if (n_seqs < 0 || H <= 0 || K <= 0 || V <= 0 || !cu_seqlens) return 1;
   if (gate_mode != 0 && gate_mode != 1) return 1;
   if (cu_seqlens[0] != 0) return 1;
   for (int n = 0; n < n_seqs; ++n)
     if (cu_seqlens[n + 1] < cu_seqlens[n]) return 1;
   prob_t p = {H, K, V, scale, lower_bound, eps, gate_mode, q, k, v, raw_g,
-              raw_beta, A_log, dt_bias, dO, o, dq, dk, dv, draw_g, draw_beta};
+              raw_beta, A_log, dt_bias, dO, o, dq, dk, dv, draw_g, draw_beta,
+              h0, dO ? dht : NULL, ht, dO ? dh0 : NULL};
   const int ntask = n_seqs * H;
   double *pa = NULL, *pb = NULL;
   if (dO) {
@@ -314,7 +336,7 @@ int kda_oracle(int n_seqs, const int64_t *cu_seqlens, int H, int K, int V,
 #endif
   for (int task = 0; task < ntask; ++task) {
     const int n = task / H, h = task % H;
-    if (run_task(&p, cu_seqlens[n], cu_seqlens[n + 1], h,
+    if (run_task(&p, n, cu_seqlens[n], cu_seqlens[n + 1], h,
                  dO ? pa + task : NULL, dO ? pb + (size_t)task * K : NULL))
       err = 1;
   }
@@ -336,6 +358,21 @@ int kda_oracle(int n_seqs, const int64_t *cu_seqlens, int H, int K, int V,
   return err;
 }
 
+/* The operator without state input or output (every sequence starts from zero). */
+int kda_oracle(int n_seqs, const int64_t *cu_seqlens, int H, int K, int V,
+               double scale, double lower_bound, double eps, int gate_mode,
+               const double *q, const double *k, const double *v,
+               const double *raw_g, const double *raw_beta,
+               const double *A_log, const double *dt_bias, const double *dO,
+               double *o, double *dq, double *dk, double *dv, double *draw_g,
+               double *draw_beta, double *dA_log, double *ddt_bias,
+               int n_threads) {
+  return kda_oracle_ex(n_seqs, cu_seqlens, H, K, V, scale, lower_bound, eps,
+                       gate_mode, q, k, v, raw_g, raw_beta, A_log, dt_bias, dO,
+                       o, dq, dk, dv, draw_g, draw_beta, dA_log, ddt_bias, NULL,
+                       NULL, NULL, NULL, n_threads);
+}
+
 /* Prologue alone, for checking the prologue step: qh, kh [T,H,K], beta [T,H]
    and gcum [T,H,K], the cumulative sum of g restarted every `chunk` tokens
    from each sequence start. Returns 0, or 1 on bad arguments. */
@@ -349,7 +386,7 @@ int kda_oracle_prologue(int n_seqs, const int64_t *cu_seqlens, int H, int K,
   if (n_seqs < 0 || H <= 0 || K <= 0 || chunk <= 0 || !cu_seqlens) return 1;
   prob_t p = {H, K, 1, scale, lower_bound, eps, gate_mode, q, k, NULL, raw_g,
               raw_beta, A_log, dt_bias, NULL, NULL, NULL, NULL, NULL, NULL,
-              NULL};
+              NULL, NULL, NULL, NULL, NULL};
   double *buf = calloc((size_t)5 * K, sizeof(double));
   if (!buf) return 1;
   tok_t w = {0, 0, 0, buf, buf + K, buf + 2 * K, buf + 3 * K, buf + 4 * K};

@@ -95,3 +95,82 @@ def test_mutant_is_caught(name, tmp_path):
     subprocess.run(["gcc", "-O1", "-fPIC", "-shared", "-std=c11", "-o", lib, str(mpath), "-lm"],
                    check=True)
     assert not _pins_pass(lib), "planted mistake %s went unnoticed" % name
+
+
+# Mistakes in the state input / output path, against the state pins: the chunk
+# form from h0, the two-part run, and a finite difference on h0.
+STATE_MUTANTS = {
+    "h0_ignored": ("if (p->h0) memcpy(s.S, p->h0 + soff, sizeof(double) * KV);", ";"),
+    "h0_wrong_sequence": ("const size_t soff = ((size_t)n * H + h) * KV;",
+                          "const size_t soff = ((size_t)0 * n + h) * KV;"),
+    "ht_not_written": ("if (p->ht) memcpy(p->ht + soff, s.S, sizeof(double) * KV);", ";"),
+    "dht_ignored": ("    memcpy(s.dS, p->dht + soff, sizeof(double) * KV);",
+                    "    memset(s.dS, 0, sizeof(double) * KV);"),
+    "dh0_before_last_decay": ("if (p->dh0) memcpy(p->dh0 + soff, s.dS, sizeof(double) * KV);",
+                              "if (p->dh0) memcpy(p->dh0 + soff, s.dSt, sizeof(double) * KV);"),
+}
+
+
+def _state_pins_pass(lib_path) -> bool:
+    rng = np.random.default_rng(5)
+    H, K, V = 2, 4, 3
+    seqlens = [7, 10]
+    T = sum(seqlens)
+    p = dict(q=rng.standard_normal((T, H, K)), k=rng.standard_normal((T, H, K)),
+             v=rng.standard_normal((T, H, V)), raw_g=rng.standard_normal((T, H, K)),
+             raw_beta=rng.standard_normal((T, H)), A_log=rng.standard_normal(H) * 0.5,
+             dt_bias=rng.standard_normal((H, K)) * 0.5,
+             cu_seqlens=np.array([0, 7, 17], dtype=np.int64))
+    h0 = rng.standard_normal((2, H, K, V))
+    dht = rng.standard_normal((2, H, K, V))
+    dO = rng.standard_normal((T, H, V))
+
+    def rel(a, b):
+        return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+    r = oracle.kda(**p, dO=dO, h0=h0, dht=dht, lib_path=lib_path)
+    o, ht = chunked_ref.chunk_fwd(**p, chunk=4, h0=h0, return_state=True)
+    if rel(r["o"], o) > 1e-12 or rel(r["ht"], ht) > 1e-12:
+        return False
+    # two-part run of the second sequence, cut after 4 of its 10 tokens
+    def sub(a, b):
+        s = {k_: (v_[a:b] if k_ in ("q", "k", "v", "raw_g", "raw_beta") else v_)
+             for k_, v_ in p.items() if k_ != "cu_seqlens"}
+        s["cu_seqlens"] = np.array([0, b - a], dtype=np.int64)
+        return s
+    mid = oracle.kda(**sub(7, 11), h0=h0[1:], lib_path=lib_path)["ht"]
+    tail = oracle.kda(**sub(11, 17), dO=dO[11:], h0=mid, dht=dht[1:], lib_path=lib_path)
+    head = oracle.kda(**sub(7, 11), dO=dO[7:11], h0=h0[1:], dht=tail["dh0"], lib_path=lib_path)
+    if rel(np.concatenate([head["dk"], tail["dk"]]), r["dk"][7:]) > 1e-11:
+        return False
+    if rel(head["dh0"][0], r["dh0"][1]) > 1e-11:
+        return False
+    # finite difference on one h0 entry, loss sum(O dO) + sum(ht dht)
+    ix = (1, 0, 2, 1)
+    step = 1e-6
+    vals = []
+    for sgn in (1, -1):
+        h = h0.copy()
+        h[ix] += sgn * step
+        s = oracle.kda(**p, h0=h, lib_path=lib_path)
+        vals.append(np.sum(s["o"] * dO) + np.sum(s["ht"] * dht))
+    fd = (vals[0] - vals[1]) / (2 * step)
+    return abs(fd - r["dh0"][ix]) <= 1e-6 * (abs(r["dh0"][ix]) + 1)
+
+
+def test_unmutated_oracle_passes_the_state_battery():
+    assert _state_pins_pass(None)
+
+
+@pytest.mark.parametrize("name", sorted(STATE_MUTANTS))
+def test_state_mutant_is_caught(name, tmp_path):
+    old, new = STATE_MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor must match exactly once"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmutant.so")
+    import subprocess
+    subprocess.run(["gcc", "-O1", "-fPIC", "-shared", "-std=c11", "-o", lib, str(mpath), "-lm"],
+                   check=True)
+    assert not _state_pins_pass(lib), "planted mistake %s went unnoticed" % name
