@@ -9,12 +9,18 @@
  *   per packed sequence and head, with the state S (K x V) starting at zero,
  *     qh = scale * q / sqrt(|q|^2 + eps),  kh = k / sqrt(|k|^2 + eps)
  *     beta = sigmoid(raw_beta)
- *     g = L * sigmoid(exp(A_log[h]) * (raw_g + dt_bias[h,:]))   (L = gate_lower_bound)
+ *     g = L * sigmoid(exp(A_log[h]) * (raw_g + dt_bias[h,:]))   (L = gate_lower_bound;
+ *         the default gate map, see gate_mode below)
  *     S_t = (I - beta_t kh_t kh_t^T) Diag(exp(g_t)) S_{t-1} + beta_t kh_t v_t^T
  *     o_t = S_t^T qh_t
- *   no initial state, no final state; the state restarts at every sequence
- *   boundary of cu_seqlens. The backward returns the gradients of all seven
- *   inputs (q, k, v, raw_g, raw_beta, A_log, dt_bias) of sum(o * dO).
+ *   the state restarts at every sequence boundary of cu_seqlens, from zero
+ *   (the measured setting of the FROST page: no initial state, no final
+ *   state). The backward returns the gradients of all seven inputs (q, k, v,
+ *   raw_g, raw_beta, A_log, dt_bias) of sum(o * dO). kda_fwd_ex / kda_bwd_ex
+ *   add an optional initial state per sequence, its final state and their
+ *   gradients, and optional forward-saved checkpoints (FROST's
+ *   checkpoint_every_n_tokens, same page, "Both sides really use
+ *   recomputation").
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller, row-major with
@@ -56,8 +62,12 @@ enum {
 
 enum { KDA_F32 = 0, KDA_BF16 = 1 };
 
-/* Gate maps. Only KDA_GATE_SIGMOID_BOUND is built; the other value is
-   reserved and rejected with KDA_ERR_UNSUPPORTED. */
+/* Gate maps (the pages fix the bound L and the FP32 A_log / dt_bias drive,
+   not the formula), with z = raw_g + dt_bias[h,:]:
+     KDA_GATE_SIGMOID_BOUND   g = L * sigmoid(exp(A_log[h]) * z)
+     KDA_GATE_SOFTPLUS_CLAMP  g = max(L, -exp(A_log[h]) * softplus(z));
+                              no gradient flows where the bound holds.
+   Other values: KDA_ERR_UNSUPPORTED. */
 enum { KDA_GATE_SIGMOID_BOUND = 0, KDA_GATE_SOFTPLUS_CLAMP = 1 };
 
 typedef struct {
@@ -69,7 +79,7 @@ typedef struct {
                               16, 32, 64; fp32 K=128: 16, 32; bf16 K=64 or
                               128: 32, 64 (others: KDA_ERR_UNSUPPORTED) */
   int32_t dtype;           /* KDA_F32 or KDA_BF16 */
-  int32_t gate_mode;       /* KDA_GATE_SIGMOID_BOUND */
+  int32_t gate_mode;       /* KDA_GATE_SIGMOID_BOUND or KDA_GATE_SOFTPLUS_CLAMP */
   float scale;             /* multiplies qh; 1.0 for the plain o_t = S_t^T qh_t */
   float gate_lower_bound;  /* L < 0, e.g. -5 */
   float l2_eps;            /* eps of the Q/K L2 normalisation, e.g. 1e-6 */
@@ -117,6 +127,58 @@ int kda_bwd(const kda_problem *p, const void *q, const void *k, const void *v,
             void *dq, void *dk, void *dv, void *draw_g, void *draw_beta,
             float *dA_log, float *ddt_bias, void *workspace,
             size_t workspace_bytes, void *stream);
+
+/* State ends and forward-saved checkpoints (all fp32, device, caller-owned;
+   every pointer may be NULL):
+     h0    [N, H, K, V]  state each sequence starts from (NULL: zero). An
+                         empty sequence passes it through to ht.
+     ht    [N, H, K, V]  kda_fwd_ex: the state after each sequence's last
+                         token (NULL: not written).
+     dht   [N, H, K, V]  kda_bwd_ex: gradient of the loss with respect to ht
+                         (NULL: zero), so the gradients are those of
+                         sum(o * dO) + sum(ht * dht).
+     dh0   [N, H, K, V]  kda_bwd_ex: gradient with respect to h0 (NULL: not
+                         written).
+     ckpt, ckpt_bytes    kda_fwd_ex writes, kda_bwd_ex reads, the state that
+                         enters every backward segment (kda_checkpoint_bytes
+                         bytes, at multiples of kda_bwd_segment_chunks
+                         chunks), so the backward skips the pass that
+                         recomputes them. Pass the same problem to both calls
+                         (set seg_chunks explicitly, or keep the workspace
+                         budget unchanged between them). ckpt_bytes smaller
+                         than kda_checkpoint_bytes: KDA_ERR_WORKSPACE.
+   The backward still recomputes w, u and h of every chunk. kda_fwd_ex reads
+   h0 and writes ht and ckpt; kda_bwd_ex reads h0, dht and ckpt (which it
+   leaves unchanged) and writes dh0. The same problem and h0 must be passed
+   to both. */
+typedef struct {
+  const float *h0;
+  float *ht;
+  const float *dht;
+  float *dh0;
+  float *ckpt;
+  size_t ckpt_bytes;
+} kda_state_io;
+
+/* Bytes of the checkpoint buffer of kda_state_io for this problem, and the
+   backward's segment length in chunks (0 when the problem is invalid). */
+size_t kda_checkpoint_bytes(const kda_problem *p);
+int32_t kda_bwd_segment_chunks(const kda_problem *p);
+
+/* kda_fwd / kda_bwd with state ends and checkpoints (io may be NULL, which
+   is kda_fwd / kda_bwd). Workspace sizes are those of kda_fwd_workspace_bytes
+   / kda_bwd_workspace_bytes. */
+int kda_fwd_ex(const kda_problem *p, const void *q, const void *k, const void *v,
+               const void *raw_g, const void *raw_beta, const float *A_log,
+               const float *dt_bias, const int32_t *cu_seqlens, void *o,
+               const kda_state_io *io, void *workspace, size_t workspace_bytes,
+               void *stream);
+int kda_bwd_ex(const kda_problem *p, const void *q, const void *k, const void *v,
+               const void *raw_g, const void *raw_beta, const float *A_log,
+               const float *dt_bias, const int32_t *cu_seqlens, const void *dO,
+               void *dq, void *dk, void *dv, void *draw_g, void *draw_beta,
+               float *dA_log, float *ddt_bias, const kda_state_io *io,
+               void *workspace, size_t workspace_bytes, void *stream);
 
 /* Optional per-kernel timing, for measurement tools. Between
    kda_profile_begin() and kda_profile_end(), every kernel the calling thread

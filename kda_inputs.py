@@ -56,7 +56,7 @@ WORKLOADS = {
     "t128k_h96_bf16": Workload("t128k_h96_bf16", (131072,), 96, 128, "bf16", 64, seed=5),
 }
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "raw_g": 3, "raw_beta": 4, "dO": 5}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "raw_g": 3, "raw_beta": 4, "dO": 5, "h0": 6, "dht": 7}
 
 
 def _randn(shape, seed: int, tensor_id: int, device, dtype) -> torch.Tensor:
@@ -93,6 +93,13 @@ def make_inputs(seqlens, H: int, K: int, V: int, dtype=torch.float32, seed: int 
     if with_dO:
         out["dO"] = _randn((T, H, V), seed, TENSOR_IDS["dO"], device, dtype)
     return out
+
+
+def make_states(n_seqs: int, H: int, K: int, V: int, seed: int = 0, device="cpu") -> dict:
+    """Initial states h0 and final-state gradients dht, fp32 [N,H,K,V] ~ N(0,1)."""
+    shape = (n_seqs, H, K, V)
+    return {"h0": _randn(shape, seed, TENSOR_IDS["h0"], device, torch.float32),
+            "dht": _randn(shape, seed, TENSOR_IDS["dht"], device, torch.float32)}
 
 
 def workload_inputs(w: Workload, device="cpu", with_dO: bool = True) -> dict:

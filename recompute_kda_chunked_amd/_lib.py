@@ -18,6 +18,7 @@ KDA_GATE_SIGMOID_BOUND, KDA_GATE_SOFTPLUS_CLAMP = 0, 1
 # Every function the header declares (checked against include/kda.h by the tests).
 EXPORTS = ("kda_fwd_workspace_bytes", "kda_bwd_workspace_bytes", "kda_check_problem",
            "kda_prologue_workspace_bytes", "kda_prologue", "kda_fwd", "kda_bwd",
+           "kda_checkpoint_bytes", "kda_bwd_segment_chunks", "kda_fwd_ex", "kda_bwd_ex",
            "kda_profile_begin", "kda_profile_end", "kda_kernel_name", "kda_status_string")
 KERNEL_COUNT = 7
 
@@ -37,6 +38,17 @@ class KdaProblem(ctypes.Structure):
         ("l2_eps", ctypes.c_float),
         ("seg_chunks", ctypes.c_int32),
         ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+class KdaStateIO(ctypes.Structure):
+    _fields_ = [
+        ("h0", ctypes.c_void_p),
+        ("ht", ctypes.c_void_p),
+        ("dht", ctypes.c_void_p),
+        ("dh0", ctypes.c_void_p),
+        ("ckpt", ctypes.c_void_p),
+        ("ckpt_bytes", ctypes.c_size_t),
     ]
 
 
@@ -69,6 +81,15 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kda_fwd.restype = ctypes.c_int
     lib.kda_bwd.argtypes = [pp] + [vp] * 16 + [vp, sz, vp]
     lib.kda_bwd.restype = ctypes.c_int
+    iop = ctypes.POINTER(KdaStateIO)
+    lib.kda_checkpoint_bytes.argtypes = [pp]
+    lib.kda_checkpoint_bytes.restype = sz
+    lib.kda_bwd_segment_chunks.argtypes = [pp]
+    lib.kda_bwd_segment_chunks.restype = ctypes.c_int32
+    lib.kda_fwd_ex.argtypes = [pp] + [vp] * 9 + [iop, vp, sz, vp]
+    lib.kda_fwd_ex.restype = ctypes.c_int
+    lib.kda_bwd_ex.argtypes = [pp] + [vp] * 16 + [iop, vp, sz, vp]
+    lib.kda_bwd_ex.restype = ctypes.c_int
     lib.kda_profile_begin.argtypes = []
     lib.kda_profile_begin.restype = ctypes.c_int
     lib.kda_profile_end.argtypes = [ctypes.POINTER(ctypes.c_int32),

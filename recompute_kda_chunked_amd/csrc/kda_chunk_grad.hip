@@ -540,7 +540,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   static_assert(NT % D == 0, "one channel per thread in the gate VJP");
   uint32_t xin[PER];  // raw bits: converted at use, so the loads stay in flight
   const float dbias = in.dt_bias[hoff + tid % D];
-  const float ea = expf(in.A_log[h]);
+  // exp(A_log) in the gate's precision, as the forward's gate map takes it
+  const TG eat = exp(static_cast<TG>(in.A_log[h]));
   {
     const TI* xr = static_cast<const TI*>(in.g) + L.t0 * ts + hoff;
 #pragma unroll
@@ -622,19 +623,31 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     // the gate map's VJP and the gate-parameter sums run in the VJP precision
     // (fp64 for fp32 problems: the dA_log sum cancels heavily)
     TG pdt = 0, pA = 0;
-    const TG eat = static_cast<TG>(ea);
     float dxv[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int e = tid + NT * j, r = e / D, kc = e % D;
       const bool ok = e < C * D && r < L.len;
-      const TG z = eat * (static_cast<TG>(bits_to_f<TI>(xin[j])) + static_cast<TG>(dbias));
-      const TG sz = VJ::sig(z);
-      const TG dz = ok ? static_cast<TG>(dGT[kc * LDG + (r < C ? r : 0)]) * static_cast<TG>(d.lb) * sz * (1 - sz) : TG(0);
-      const TG dx = dz * eat;
+      const TG xb = static_cast<TG>(bits_to_f<TI>(xin[j])) + static_cast<TG>(dbias);
+      const TG dgv = ok ? static_cast<TG>(dGT[kc * LDG + (r < C ? r : 0)]) : TG(0);
+      TG dx, dA;
+      if (d.gate_mode == 0) {
+        // g = L sigmoid(z), z = e^A (x + b): dg/dx = e^A L s (1 - s), dg/dA = z L s (1 - s)
+        const TG z = eat * xb, sz = VJ::sig(z);
+        const TG dz = dgv * static_cast<TG>(d.lb) * sz * (1 - sz);
+        dx = dz * eat;
+        dA = dz * z;
+      } else {
+        // g = -e^A softplus(x + b) above the bound: dg/dx = -e^A sigmoid(x + b),
+        // dg/dA = g; no gradient where the bound holds
+        const TG c = -eat * softplus_t<TG>(xb);
+        const bool act = c > static_cast<TG>(d.lb);
+        dx = act ? -dgv * eat * VJ::sig(xb) : TG(0);
+        dA = act ? dgv * c : TG(0);
+      }
       dxv[j] = static_cast<float>(dx);
       pdt += dx;
-      pA += dz * z;
+      pA += dA;
     }
     TI* dqo = dq + L.t0 * ts + hoff;
     TI* dko = dk + L.t0 * ts + hoff;

@@ -51,7 +51,8 @@ int check_problem(const kda_problem* p) {
     return KDA_ERR_INVALID;
   if (p->seg_chunks < 0 || p->chunk < 1) return KDA_ERR_INVALID;
   if (p->dtype != KDA_F32 && p->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-  if (p->gate_mode != KDA_GATE_SIGMOID_BOUND) return KDA_ERR_UNSUPPORTED;
+  if (p->gate_mode != KDA_GATE_SIGMOID_BOUND && p->gate_mode != KDA_GATE_SOFTPLUS_CLAMP)
+    return KDA_ERR_UNSUPPORTED;
   if (p->K != p->V) return KDA_ERR_UNSUPPORTED;
   if (!supported(p->dtype, p->K, p->chunk)) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
@@ -158,6 +159,12 @@ size_t bwd_bytes(const Plan& P) {
          static_cast<size_t>(P.NS + 1) * state_slot(P) + 2 * state_slot(P) + ops + states_bytes(P);
 }
 
+bool has_empty_sequence(const kda_problem* p) {
+  for (int n = 0; n < p->n_seqs; ++n)
+    if (p->cu_seqlens_host[n + 1] == p->cu_seqlens_host[n]) return true;
+  return false;
+}
+
 int hip_fail(hipError_t e) {
   std::snprintf(g_msg, sizeof g_msg, "HIP launch failed: %s", hipGetErrorString(e));
   return KDA_ERR_HIP;
@@ -209,6 +216,7 @@ Dims make_dims(const kda_problem* p) {
   d.scale = p->scale;
   d.lb = p->gate_lower_bound;
   d.eps = p->l2_eps;
+  d.gate_mode = p->gate_mode;
   return d;
 }
 
@@ -253,10 +261,21 @@ int kda_prologue(const kda_problem* p, const void* q, const void* k, const void*
   return KDA_OK;
 }
 
-int kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
-            const void* raw_g, const void* raw_beta, const float* A_log, const float* dt_bias,
-            const int32_t* cu_seqlens, void* o, void* workspace, size_t workspace_bytes,
-            void* stream) {
+int32_t kda_bwd_segment_chunks(const kda_problem* p) {
+  if (check_problem(p) != KDA_OK) return 0;
+  return make_plan(p, true).seg;
+}
+
+size_t kda_checkpoint_bytes(const kda_problem* p) {
+  if (check_problem(p) != KDA_OK) return 0;
+  const Plan P = make_plan(p, true);
+  return static_cast<size_t>(P.NS) * state_slot(P);
+}
+
+int kda_fwd_ex(const kda_problem* p, const void* q, const void* k, const void* v,
+               const void* raw_g, const void* raw_beta, const float* A_log,
+               const float* dt_bias, const int32_t* cu_seqlens, void* o,
+               const kda_state_io* io, void* workspace, size_t workspace_bytes, void* stream) {
   const int st = check_problem(p);
   if (st != KDA_OK) return st;
   if (!q || !k || !v || !raw_g || !raw_beta || !A_log || !dt_bias || !cu_seqlens || !o ||
@@ -264,6 +283,15 @@ int kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
     return KDA_ERR_INVALID;
   const Plan P = make_plan(p, false);
   if (workspace_bytes < fwd_bytes(P)) return KDA_ERR_WORKSPACE;
+  const kda_state_io none{};
+  if (!io) io = &none;
+  int ck_every = 0;
+  if (io->ckpt) {
+    if (io->ckpt_bytes < kda_checkpoint_bytes(p)) return KDA_ERR_WORKSPACE;
+    const Plan PB = make_plan(p, true);
+    if (PB.NS > 1) ck_every = PB.seg;  // a single segment needs no checkpoint
+  }
+  const ScanStates ss{io->h0, io->ht, ck_every ? io->ckpt : nullptr, ck_every};
   hipStream_t s = static_cast<hipStream_t>(stream);
   unsigned char* cur = static_cast<unsigned char*>(workspace);
   int32_t* coff = reinterpret_cast<int32_t*>(cur);
@@ -281,16 +309,27 @@ int kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
     const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
     KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, false, d, in, c0, c1 - c0, ops, s));
     KDA_TRY(KDA_KERNEL_SCAN_FWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops, o, nullptr, carry[sg & 1],
-                            carry[(sg + 1) & 1], s));
+                            carry[(sg + 1) & 1], ss, s));
   }
+  if (io->ht && has_empty_sequence(p))
+    KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_state_passthrough(cu_seqlens, P.N, P.H, P.D * P.D, io->h0, io->ht, s));
   return KDA_OK;
 }
 
-int kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
+int kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
             const void* raw_g, const void* raw_beta, const float* A_log, const float* dt_bias,
-            const int32_t* cu_seqlens, const void* dO, void* dq, void* dk, void* dv,
-            void* draw_g, void* draw_beta, float* dA_log, float* ddt_bias, void* workspace,
-            size_t workspace_bytes, void* stream) {
+            const int32_t* cu_seqlens, void* o, void* workspace, size_t workspace_bytes,
+            void* stream) {
+  return kda_fwd_ex(p, q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, o, nullptr,
+                    workspace, workspace_bytes, stream);
+}
+
+int kda_bwd_ex(const kda_problem* p, const void* q, const void* k, const void* v,
+               const void* raw_g, const void* raw_beta, const float* A_log,
+               const float* dt_bias, const int32_t* cu_seqlens, const void* dO, void* dq,
+               void* dk, void* dv, void* draw_g, void* draw_beta, float* dA_log,
+               float* ddt_bias, const kda_state_io* io, void* workspace,
+               size_t workspace_bytes, void* stream) {
   const int st = check_problem(p);
   if (st != KDA_OK) return st;
   if (!q || !k || !v || !raw_g || !raw_beta || !A_log || !dt_bias || !cu_seqlens || !dO ||
@@ -298,13 +337,19 @@ int kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
     return KDA_ERR_INVALID;
   const Plan P = make_plan(p, true);
   if (workspace_bytes < bwd_bytes(P)) return KDA_ERR_WORKSPACE;
+  const kda_state_io none{};
+  if (!io) io = &none;
+  if (io->ckpt && io->ckpt_bytes < kda_checkpoint_bytes(p)) return KDA_ERR_WORKSPACE;
+  const ScanStates fwd_ss{io->h0, nullptr, nullptr, 0};
+  const ScanStates bwd_ss{io->dht, io->dh0, nullptr, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   unsigned char* cur = static_cast<unsigned char*>(workspace);
   int32_t* coff = reinterpret_cast<int32_t*>(cur);
   cur += up((P.N + 1) * 4);
   double* partials = reinterpret_cast<double*>(cur);
   cur += up(static_cast<size_t>(P.NC) * P.H * (P.D + 1) * 8);
-  float* ckpt = reinterpret_cast<float*>(cur);  // NS + 1 slots
+  // state entering each segment (slot sg); the forward's checkpoints when given
+  float* ckpt = io->ckpt ? io->ckpt : reinterpret_cast<float*>(cur);
   const size_t slot = state_slot(P) / 4;
   cur += static_cast<size_t>(P.NS + 1) * state_slot(P);
   float* dcarry[2];
@@ -333,25 +378,39 @@ int kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
   const Dims d = make_dims(p);
   const Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, coff};
   KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
-  // checkpoint pass: the state entering each segment
-  for (int sg = 0; sg + 1 < P.NS; ++sg) {
+  // checkpoint pass: the state entering each segment (skipped when the
+  // forward saved them)
+  for (int sg = 0; !io->ckpt && sg + 1 < P.NS; ++sg) {
     const int c0 = sg * P.seg, c1 = c0 + P.seg;
     KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, false, d, in, c0, c1 - c0, ops_f, s));
     KDA_TRY(KDA_KERNEL_SCAN_FWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_f, nullptr, nullptr,
-                            ckpt + sg * slot, ckpt + (sg + 1) * slot, s));
+                            ckpt + sg * slot, ckpt + (sg + 1) * slot, fwd_ss, s));
   }
   for (int sg = P.NS - 1; sg >= 0; --sg) {
     const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
     KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, true, d, in, c0, c1 - c0, ops_b, s));
+    // the recording scan writes no carry: the next segment's entering state is known
     KDA_TRY(KDA_KERNEL_SCAN_FWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_b, nullptr, &sts,
-                            ckpt + sg * slot, ckpt + (sg + 1) * slot, s));
+                            ckpt + sg * slot, nullptr, fwd_ss, s));
     KDA_TRY(KDA_KERNEL_SCAN_BWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_bwd(P.dtype, P.D, P.C, d, in, dO, c0, c1, ops_b, sts,
-                            dcarry[(sg + 1) & 1], dcarry[sg & 1], s));
+                            dcarry[(sg + 1) & 1], dcarry[sg & 1], bwd_ss, s));
     KDA_TRY(KDA_KERNEL_CHUNK_GRAD, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_grad(P.dtype, P.D, P.C, d, in, dO, c0, c1 - c0, ops_b, sts, dq, dk, dv,
                               draw_g, draw_beta, partials, s));
   }
   KDA_TRY(KDA_KERNEL_GATE_REDUCE, 0, launch_gate_reduce(P.D, P.H, P.NC, partials, dA_log, ddt_bias, s));
+  if (io->dh0 && has_empty_sequence(p))
+    KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_state_passthrough(cu_seqlens, P.N, P.H, P.D * P.D, io->dht, io->dh0, s));
   return KDA_OK;
+}
+
+int kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
+            const void* raw_g, const void* raw_beta, const float* A_log, const float* dt_bias,
+            const int32_t* cu_seqlens, const void* dO, void* dq, void* dk, void* dv,
+            void* draw_g, void* draw_beta, float* dA_log, float* ddt_bias, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  return kda_bwd_ex(p, q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, dO, dq, dk, dv,
+                    draw_g, draw_beta, dA_log, ddt_bias, nullptr, workspace, workspace_bytes,
+                    stream);
 }
 
 int kda_profile_begin(void) {

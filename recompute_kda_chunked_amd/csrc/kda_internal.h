@@ -12,6 +12,7 @@ namespace kda {
 struct Dims {
   int N, H;
   float scale, lb, eps;
+  int gate_mode;  // 0: L * sigmoid(e^A (x + b)); 1: max(L, -e^A softplus(x + b))
 };
 
 // Raw operator inputs (device pointers, dtype per the problem).
@@ -50,6 +51,21 @@ struct SegStates {
   void *h, *dh, *Vn, *dVnT;
 };
 
+// Per-sequence state ends of a scan, all fp32 [N][H][K][V] (sequence n's
+// slice at n * H * K * V) or null:
+//   forward scan: init = initial states (null: zero), fin = final states
+//     out (null: not written), ck = states entering every chunk that is a
+//     multiple of ck_every and lies inside its sequence, slot c / ck_every of
+//     [slots][H][K][V] (null: none);
+//   reverse scan: init = final-state gradients (null: zero), fin = initial-
+//     state gradients out (null: not written); ck unused.
+struct ScanStates {
+  const float* init;
+  float* fin;
+  float* ck;
+  int ck_every;
+};
+
 // Launchers (defined next to their kernels). Each returns hipSuccess or the
 // launch error. `dtype` is 0 (fp32) or 1 (bf16); D = K = V; C = chunk.
 hipError_t launch_chunk_table(const int32_t* cu, int N, int C, int32_t* coff, hipStream_t s);
@@ -65,12 +81,16 @@ hipError_t launch_chunk_local(int dtype, int D, int C, bool bwd, const Dims& d,
 hipError_t launch_scan_fwd(int dtype, int D, int C, const Dims& d, const Inputs& in,
                            int seg_begin, int seg_end, const ChunkOps& ops, void* out_o,
                            const SegStates* st, const float* carry_in, float* carry_out,
-                           hipStream_t s);
+                           const ScanStates& ss, hipStream_t s);
 // Reverse (state-gradient) scan over one segment; records dh' and dVn^T.
 hipError_t launch_scan_bwd(int dtype, int D, int C, const Dims& d, const Inputs& in,
                            const void* dO, int seg_begin, int seg_end, const ChunkOps& ops,
                            const SegStates& st, const float* carry_in, float* carry_out,
-                           hipStream_t s);
+                           const ScanStates& ss, hipStream_t s);
+// dst[n] = src[n] (or zero when src is null) for every empty sequence n;
+// KV = K * V floats per (sequence, head).
+hipError_t launch_state_passthrough(const int32_t* cu, int N, int H, int KV, const float* src,
+                                    float* dst, hipStream_t s);
 // Token-parallel gradients for one segment; writes dq, dk, dv, draw_g,
 // draw_beta for its tokens and gate-parameter partials [chunk][H][K+1].
 hipError_t launch_chunk_grad(int dtype, int D, int C, const Dims& d, const Inputs& in,

@@ -4,9 +4,13 @@
 // Follows the input description of "KDA Memory with Recompute: FLA vs cuDNN
 // Frontend FROST" (section "Sources and measurement configuration"): Q/K L2
 // normalisation inside the operator, beta = sigmoid(raw beta), a gate bounded
-// below by L and driven by FP32 A_log / dt_bias. The gate map is
-//   g = L * sigmoid(exp(A_log[h]) * (raw_g + dt_bias[h,:]))
-// (a smooth map onto (L, 0); the pages do not print the formula). The
+// below by L and driven by FP32 A_log / dt_bias. The pages do not print the
+// gate formula; two maps are built (gate_mode):
+//   0: g = L * sigmoid(exp(A_log[h]) * (raw_g + dt_bias[h,:]))
+//      (a smooth map onto (L, 0), the default)
+//   1: g = max(L, -exp(A_log[h]) * softplus(raw_g + dt_bias[h,:]))
+//      (the softplus decay clamped at the bound)
+// The
 // chunk-local cumulative sum of g is taken in fp32, as the FLA forward keeps
 // its gate cumulative sum (FROST page, "Where FLA's memory goes").
 #pragma once
@@ -44,6 +48,23 @@ template <>
 __device__ __forceinline__ float sigmoid_t<float>(float x) { return sigmoidf(x); }
 template <>
 __device__ __forceinline__ double sigmoid_t<double>(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+// softplus(x) = log(1 + e^x); past the cut-off e^-x is below half an ulp of x.
+template <typename T>
+__device__ __forceinline__ T softplus_t(T x);
+template <>
+__device__ __forceinline__ float softplus_t<float>(float x) { return x > 20.f ? x : log1pf(expf(x)); }
+template <>
+__device__ __forceinline__ double softplus_t<double>(double x) { return x > 40.0 ? x : log1p(exp(x)); }
+
+// The gate map g(x + b) for gate_mode 0 or 1 (ea = exp(A_log[h]), xb = raw_g +
+// dt_bias, lb = L), in the precision of T.
+template <typename T>
+__device__ __forceinline__ T gate_map(int mode, T ea, T xb, T lb) {
+  if (mode == 0) return lb * sigmoid_t<T>(ea * xb);
+  const T c = -ea * softplus_t<T>(xb);
+  return c > lb ? c : lb;
+}
 
 // Location of chunk c (global index) of a packed batch.
 struct ChunkLoc {
@@ -143,8 +164,8 @@ __device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, i
 #pragma unroll
       for (int j = 0; j < VE; ++j) {
         // the gate map in the cumulative gate's precision
-        const GV z = static_cast<GV>(ea) * (static_cast<GV>(to_f(xv[it][j])) + static_cast<GV>(db[j]));
-        G(r, c0 + j) = valid ? static_cast<GV>(d.lb) * sigmoid_t<GV>(z) : GV(0);
+        const GV xb = static_cast<GV>(to_f(xv[it][j])) + static_cast<GV>(db[j]);
+        G(r, c0 + j) = valid ? gate_map<GV>(d.gate_mode, ea, xb, static_cast<GV>(d.lb)) : GV(0);
       }
       if (sub == 0) {
         const float a = valid ? 1.0f / sqrtf(sq + d.eps) : 0.f;

@@ -125,7 +125,7 @@ template <typename TI, typename OpT, int D, int C, int BV, bool OUT_O, bool REC>
 __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_begin,
                                                   int seg_end, ChunkOps ops, TI* o,
                                                   SegStates st, const float* carry_in,
-                                                  float* carry_out) {
+                                                  float* carry_out, ScanStates ss) {
   using G = ScanGeo<OpT, D, C, BV>;
   using M = typename G::M;
   constexpr int K = G::K, V = G::V, NB = G::NB, NVT = G::NVT, BVT = G::BVT;
@@ -145,18 +145,25 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
   const int v0 = vt * BV;
   const size_t ts = static_cast<size_t>(d.H) * V;
 
-  // state tile j of this wave: row block mk = w*MKW + j/BVT, value block nv = j%BVT
+  // state tile j of this wave: row block mk = w*MKW + j/BVT, value block nv = j%BVT.
+  // At the sequence's first chunk the state is its initial state (or zero),
+  // otherwise the carry of the previous segment.
   f32x4 hs[HPW];
   const bool fresh = (cb == coff0);
+  const float* hin = !fresh ? carry_in
+                     : (ss.init ? ss.init + static_cast<size_t>(n) * d.H * K * V : nullptr);
+  const bool zero_in = hin == nullptr;
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const int mk = w * MKW + j / BVT, nv = j % BVT;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int kk = 16 * mk + 4 * g + rr, vv = v0 + 16 * nv + i;
-      hs[j][rr] = fresh ? 0.f : carry_in[(static_cast<size_t>(h) * K + kk) * V + vv];
+      hs[j][rr] = zero_in ? 0.f : hin[(static_cast<size_t>(h) * K + kk) * V + vv];
     }
   }
+  // states at multiples of ss.ck_every chunks (the backward's segment starts)
+  int next_ck = ss.ck ? (cb + ss.ck_every - 1) / ss.ck_every * ss.ck_every : 0x7fffffff;
   auto put_state = [&]() {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
@@ -181,6 +188,19 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
     const size_t idx = static_cast<size_t>(c - seg_begin) * d.H + h;
     if (c + 2 < ce)
       load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(fill, ops, idx + 2 * d.H, v0, w, i, g);
+    if (c == next_ck) {
+      // the state entering chunk c, needed only where c is inside the sequence
+      if (c > coff0) {
+        float* dst = ss.ck + (static_cast<size_t>(c / ss.ck_every) * d.H + h) * K * V;
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          const int mk = w * MKW + j / BVT, nv = j % BVT;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) dst[(16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = hs[j][rr];
+        }
+      }
+      next_ck += ss.ck_every;
+    }
     if (REC) {
       // entering state h_n as [K][V]
       OpT* hd = static_cast<OpT*>(st.h) + idx * K * V;
@@ -268,13 +288,16 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
     if (c + 1 < ce) step(c + 1, s1, s0);
     if (c + 2 < ce) step(c + 2, s2, s1);
   }
-  if (ce < coff1) {
+  // the state leaves as the next segment's carry, or as the sequence's final state
+  float* hout = ce < coff1 ? carry_out
+                           : (ss.fin ? ss.fin + static_cast<size_t>(n) * d.H * K * V : nullptr);
+  if (hout) {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       const int mk = w * MKW + j / BVT, nv = j % BVT;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
-        carry_out[(static_cast<size_t>(h) * K + 16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = hs[j][rr];
+        hout[(static_cast<size_t>(h) * K + 16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = hs[j][rr];
     }
   }
 }
@@ -334,7 +357,7 @@ template <typename TI, typename OpT, int D, int C, int BV>
 __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* dO,
                                                   int seg_begin, int seg_end, ChunkOps ops,
                                                   SegStates st, const float* carry_in,
-                                                  float* carry_out) {
+                                                  float* carry_out, ScanStates ss) {
   using G = ScanGeo<OpT, D, C, BV>;
   using M = typename G::M;
   using Ops = BwdOps<TI, OpT, D, C, BV>;
@@ -363,15 +386,21 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
     return static_cast<int>(min(static_cast<int64_t>(C), tok1 - t0));
   };
 
-  f32x4 hs[HPW];  // dh' (gradient of the state leaving the current chunk)
+  // dh' (gradient of the state leaving the current chunk): after the
+  // sequence's last chunk it is the final state's gradient (or zero),
+  // otherwise the carry of the following segment
+  f32x4 hs[HPW];
   const bool fresh = (ce == coff1);
+  const float* hin = !fresh ? carry_in
+                     : (ss.init ? ss.init + static_cast<size_t>(n) * d.H * K * V : nullptr);
+  const bool zero_in = hin == nullptr;
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const int mk = w * MKW + j / BVT, nv = j % BVT;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int kk = 16 * mk + 4 * g + rr, vv = v0 + 16 * nv + i;
-      hs[j][rr] = fresh ? 0.f : carry_in[(static_cast<size_t>(h) * K + kk) * V + vv];
+      hs[j][rr] = zero_in ? 0.f : hin[(static_cast<size_t>(h) * K + kk) * V + vv];
     }
   }
   auto put_state = [&]() {
@@ -460,13 +489,17 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
     if (c - 1 >= cb) step(c - 1, s1, s0);
     if (c - 2 >= cb) step(c - 2, s2, s1);
   }
-  if (cb > coff0) {
+  // the gradient leaves as the previous segment's carry, or, past the
+  // sequence's first chunk, as the initial state's gradient
+  float* hout = cb > coff0 ? carry_out
+                           : (ss.fin ? ss.fin + static_cast<size_t>(n) * d.H * K * V : nullptr);
+  if (hout) {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       const int mk = w * MKW + j / BVT, nv = j % BVT;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
-        carry_out[(static_cast<size_t>(h) * K + 16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = hs[j][rr];
+        hout[(static_cast<size_t>(h) * K + 16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = hs[j][rr];
     }
   }
 }
@@ -478,32 +511,34 @@ constexpr int kBvFwd = 32, kBvBwd = 32;
 template <typename TI, int D, int C>
 static hipError_t launch_sf(const Dims& d, const Inputs& in, int seg_begin, int seg_end,
                             const ChunkOps& ops, void* o, const SegStates* st,
-                            const float* carry_in, float* carry_out, hipStream_t s) {
+                            const float* carry_in, float* carry_out, const ScanStates& ss,
+                            hipStream_t s) {
   constexpr int BV = kBvFwd, NVT = D / BV;
   const int groups = (d.N * d.H + 7) / 8;
   const dim3 grid(groups * 8 * NVT), block(256);
   SegStates z{};
   if (o)
     hipLaunchKernelGGL((k_scan_fwd<TI, TI, D, C, BV, true, false>), grid, block, 0, s, d, in,
-                       seg_begin, seg_end, ops, static_cast<TI*>(o), z, carry_in, carry_out);
+                       seg_begin, seg_end, ops, static_cast<TI*>(o), z, carry_in, carry_out, ss);
   else if (st)
     hipLaunchKernelGGL((k_scan_fwd<TI, TI, D, C, BV, false, true>), grid, block, 0, s, d, in,
-                       seg_begin, seg_end, ops, nullptr, *st, carry_in, carry_out);
+                       seg_begin, seg_end, ops, nullptr, *st, carry_in, carry_out, ss);
   else
     hipLaunchKernelGGL((k_scan_fwd<TI, TI, D, C, BV, false, false>), grid, block, 0, s, d, in,
-                       seg_begin, seg_end, ops, nullptr, z, carry_in, carry_out);
+                       seg_begin, seg_end, ops, nullptr, z, carry_in, carry_out, ss);
   return hipGetLastError();
 }
 
 template <typename TI, int D, int C>
 static hipError_t launch_sb(const Dims& d, const Inputs& in, const void* dO, int seg_begin,
                             int seg_end, const ChunkOps& ops, const SegStates& st,
-                            const float* carry_in, float* carry_out, hipStream_t s) {
+                            const float* carry_in, float* carry_out, const ScanStates& ss,
+                            hipStream_t s) {
   constexpr int BV = kBvBwd, NVT = D / BV;
   const int groups = (d.N * d.H + 7) / 8;
   hipLaunchKernelGGL((k_scan_bwd<TI, TI, D, C, BV>), dim3(groups * 8 * NVT), dim3(256), 0, s,
                      d, in, static_cast<const TI*>(dO), seg_begin, seg_end, ops, st, carry_in,
-                     carry_out);
+                     carry_out, ss);
   return hipGetLastError();
 }
 
@@ -526,15 +561,32 @@ static hipError_t launch_sb(const Dims& d, const Inputs& in, const void* dO, int
 hipError_t launch_scan_fwd(int dtype, int D, int C, const Dims& d, const Inputs& in,
                            int seg_begin, int seg_end, const ChunkOps& ops, void* out_o,
                            const SegStates* st, const float* carry_in, float* carry_out,
-                           hipStream_t s) {
-  KDA_DISPATCH(launch_sf, d, in, seg_begin, seg_end, ops, out_o, st, carry_in, carry_out, s)
+                           const ScanStates& ss, hipStream_t s) {
+  KDA_DISPATCH(launch_sf, d, in, seg_begin, seg_end, ops, out_o, st, carry_in, carry_out, ss, s)
 }
 
 hipError_t launch_scan_bwd(int dtype, int D, int C, const Dims& d, const Inputs& in,
                            const void* dO, int seg_begin, int seg_end, const ChunkOps& ops,
                            const SegStates& st, const float* carry_in, float* carry_out,
-                           hipStream_t s) {
-  KDA_DISPATCH(launch_sb, d, in, dO, seg_begin, seg_end, ops, st, carry_in, carry_out, s)
+                           const ScanStates& ss, hipStream_t s) {
+  KDA_DISPATCH(launch_sb, d, in, dO, seg_begin, seg_end, ops, st, carry_in, carry_out, ss, s)
+}
+
+// Sequences with no tokens: their outgoing state (final state, or the
+// initial state's gradient) is the incoming one, or zero. One block per
+// (sequence, head); non-empty sequences exit at once.
+__global__ void __launch_bounds__(256) k_state_passthrough(const int32_t* cu, int H, int KV,
+                                                           const float* src, float* dst) {
+  const int n = blockIdx.x / H, h = blockIdx.x % H;
+  if (cu[n] != cu[n + 1]) return;
+  const size_t off = (static_cast<size_t>(n) * H + h) * KV;
+  for (int e = threadIdx.x; e < KV; e += 256) dst[off + e] = src ? src[off + e] : 0.f;
+}
+
+hipError_t launch_state_passthrough(const int32_t* cu, int N, int H, int KV, const float* src,
+                                    float* dst, hipStream_t s) {
+  hipLaunchKernelGGL(k_state_passthrough, dim3(N * H), dim3(256), 0, s, cu, H, KV, src, dst);
+  return hipGetLastError();
 }
 
 }  // namespace kda

@@ -92,40 +92,102 @@ def _default_cu(T, device):
     return torch.tensor([0, T], dtype=torch.int32, device=device), [0, T]
 
 
+class Checkpoints:
+    """States a forward saved at the starts of the backward's segments (fp32,
+    device) and the segment length, in chunks, they were taken at."""
+
+    def __init__(self, states: torch.Tensor, seg_chunks: int):
+        self.states = states
+        self.seg_chunks = int(seg_chunks)
+
+
+def _state_io(h0=None, ht=None, dht=None, dh0=None, ckpt=None):
+    io = _lib.KdaStateIO()
+    io.h0 = h0.data_ptr() if h0 is not None else None
+    io.ht = ht.data_ptr() if ht is not None else None
+    io.dht = dht.data_ptr() if dht is not None else None
+    io.dh0 = dh0.data_ptr() if dh0 is not None else None
+    if ckpt is not None:
+        io.ckpt = ckpt.data_ptr()
+        io.ckpt_bytes = ckpt.numel() * ckpt.element_size()
+    return io
+
+
+def _check_state(name, t, shape, dev):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.float32:
+        raise KdaError("%s: expected shape %s float32, got %s %s"
+                       % (name, tuple(shape), tuple(t.shape), t.dtype))
+    if t.device != dev or not t.is_contiguous() or t.data_ptr() % 16:
+        raise KdaError("%s must be contiguous, 16-byte aligned and on %s" % (name, dev))
+
+
 def kda_forward(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, *,
                 cu_seqlens_host=None, scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6,
-                seg_chunks=0, out=None):
-    """O [T,H,V] of the KDA operator (no state saved for the backward)."""
+                seg_chunks=0, gate_mode=_lib.KDA_GATE_SIGMOID_BOUND, initial_state=None,
+                output_final_state=False, save_checkpoints=False, out=None):
+    """O [T,H,V] of the KDA operator.
+
+    initial_state: fp32 [N,H,K,V] state each sequence starts from (zero when
+    None). With output_final_state or save_checkpoints the result is
+    (O, ht, checkpoints): ht the fp32 [N,H,K,V] state after each sequence
+    (None unless output_final_state), checkpoints a Checkpoints for
+    kda_backward (None unless save_checkpoints)."""
     if cu_seqlens is None:
         cu_seqlens, cu_seqlens_host = _default_cu(q.shape[0], q.device)
     T, H, K, V, dt = _check_inputs(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens)
-    prob = Problem(T, H, K, V, dt, _cu_host(cu_seqlens, cu_seqlens_host), chunk, scale,
-                   lower_bound, eps, seg_chunks)
+    cu_host = _cu_host(cu_seqlens, cu_seqlens_host)
+    N = len(cu_host) - 1
+    _check_state("initial_state", initial_state, (N, H, K, V), q.device)
+    prob = Problem(T, H, K, V, dt, cu_host, chunk, scale, lower_bound, eps, seg_chunks,
+                   gate_mode)
     lib = _lib.load()
     _raise(lib, prob.check(), "kda_fwd")
-    o = torch.empty((T, H, V), dtype=dt, device=q.device) if out is None else out
-    ws = torch.empty(prob.fwd_ws(), dtype=torch.uint8, device=q.device)
-    st = lib.kda_fwd(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(raw_g), _ptr(raw_beta),
-                     _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(o), _ptr(ws),
-                     ctypes.c_size_t(ws.numel()), _stream(q.device))
+    dev = q.device
+    o = torch.empty((T, H, V), dtype=dt, device=dev) if out is None else out
+    ht = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    ck = None
+    if save_checkpoints:
+        nbytes = int(lib.kda_checkpoint_bytes(prob.ref))
+        ck = Checkpoints(torch.empty(max(nbytes, 256) // 4, dtype=torch.float32, device=dev),
+                         lib.kda_bwd_segment_chunks(prob.ref))
+    io = _state_io(h0=initial_state, ht=ht, ckpt=ck.states if ck is not None else None)
+    ws = torch.empty(prob.fwd_ws(), dtype=torch.uint8, device=dev)
+    st = lib.kda_fwd_ex(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(raw_g), _ptr(raw_beta),
+                        _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(o), ctypes.byref(io),
+                        _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
     _raise(lib, st, "kda_fwd")
+    if output_final_state or save_checkpoints:
+        return o, ht, ck
     return o
 
 
 def kda_backward(q, k, v, raw_g, raw_beta, A_log, dt_bias, dO, cu_seqlens=None, *,
                  cu_seqlens_host=None, scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6,
-                 seg_chunks=0):
-    """Gradients (dq, dk, dv, draw_g, draw_beta, dA_log, ddt_bias) of sum(O * dO),
-    recomputing every intermediate from the inputs."""
+                 seg_chunks=0, gate_mode=_lib.KDA_GATE_SIGMOID_BOUND, initial_state=None,
+                 d_final_state=None, checkpoints=None):
+    """Gradients (dq, dk, dv, draw_g, draw_beta, dA_log, ddt_bias) of
+    sum(O * dO) + sum(ht * d_final_state), recomputing every chunk's
+    intermediates from the inputs; dh0 is appended when initial_state is
+    given. checkpoints: the forward's Checkpoints for the same problem (the
+    backward then skips the pass that recomputes the segment states)."""
     if cu_seqlens is None:
         cu_seqlens, cu_seqlens_host = _default_cu(q.shape[0], q.device)
     T, H, K, V, dt = _check_inputs(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens,
                                    extra=[("dO", (dO, tuple(v.shape), v.dtype))])
-    prob = Problem(T, H, K, V, dt, _cu_host(cu_seqlens, cu_seqlens_host), chunk, scale,
-                   lower_bound, eps, seg_chunks)
+    cu_host = _cu_host(cu_seqlens, cu_seqlens_host)
+    N = len(cu_host) - 1
+    dev = q.device
+    _check_state("initial_state", initial_state, (N, H, K, V), dev)
+    _check_state("d_final_state", d_final_state, (N, H, K, V), dev)
+    prob = Problem(T, H, K, V, dt, cu_host, chunk, scale, lower_bound, eps, seg_chunks,
+                   gate_mode)
     lib = _lib.load()
     _raise(lib, prob.check(), "kda_bwd")
-    dev = q.device
+    if checkpoints is not None and lib.kda_bwd_segment_chunks(prob.ref) != checkpoints.seg_chunks:
+        raise KdaError("checkpoints were saved at a segment of %d chunks; this backward "
+                       "uses %d" % (checkpoints.seg_chunks, lib.kda_bwd_segment_chunks(prob.ref)))
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -133,23 +195,30 @@ def kda_backward(q, k, v, raw_g, raw_beta, A_log, dt_bias, dO, cu_seqlens=None, 
     db = torch.empty_like(raw_beta)
     dA = torch.empty((H,), dtype=torch.float32, device=dev)
     ddt = torch.empty((H, K), dtype=torch.float32, device=dev)
+    dh0 = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) \
+        if initial_state is not None else None
+    io = _state_io(h0=initial_state, dht=d_final_state, dh0=dh0,
+                   ckpt=checkpoints.states if checkpoints is not None else None)
     ws = torch.empty(prob.bwd_ws(), dtype=torch.uint8, device=dev)
-    st = lib.kda_bwd(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(raw_g), _ptr(raw_beta),
-                     _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(dO), _ptr(dq),
-                     _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dA), _ptr(ddt), _ptr(ws),
-                     ctypes.c_size_t(ws.numel()), _stream(dev))
+    st = lib.kda_bwd_ex(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(raw_g), _ptr(raw_beta),
+                        _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(dO), _ptr(dq),
+                        _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dA), _ptr(ddt),
+                        ctypes.byref(io), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
     _raise(lib, st, "kda_bwd")
+    if dh0 is not None:
+        return dq, dk, dv, dg, db, dA, ddt, dh0
     return dq, dk, dv, dg, db, dA, ddt
 
 
 def kda_prologue(q, k, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, *,
-                 cu_seqlens_host=None, scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6):
+                 cu_seqlens_host=None, scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6,
+                 gate_mode=_lib.KDA_GATE_SIGMOID_BOUND):
     """fp32 (qh, kh, beta, gcum) of the prologue step alone."""
     if cu_seqlens is None:
         cu_seqlens, cu_seqlens_host = _default_cu(q.shape[0], q.device)
     T, H, K, V, dt = _check_inputs(q, k, q, raw_g, raw_beta, A_log, dt_bias, cu_seqlens)
     prob = Problem(T, H, K, K, dt, _cu_host(cu_seqlens, cu_seqlens_host), chunk, scale,
-                   lower_bound, eps)
+                   lower_bound, eps, gate_mode=gate_mode)
     lib = _lib.load()
     _raise(lib, prob.check(), "kda_prologue")
     dev = q.device
@@ -167,29 +236,53 @@ def kda_prologue(q, k, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, *,
 
 
 class KDAFunction(torch.autograd.Function):
-    """Autograd wrapper: saves references to the caller's inputs only."""
+    """Autograd wrapper: saves references to the caller's inputs only (plus
+    the segment-start states when opts["save_checkpoints"])."""
 
     @staticmethod
-    def forward(ctx, q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, cu_host, opts):
-        ctx.save_for_backward(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens)
+    def forward(ctx, q, k, v, raw_g, raw_beta, A_log, dt_bias, h0, cu_seqlens, cu_host, opts):
+        ctx.set_materialize_grads(False)
+        ctx.save_for_backward(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, h0)
         ctx.cu_host = cu_host
-        ctx.opts = opts
-        return kda_forward(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens,
-                           cu_seqlens_host=cu_host, **opts)
+        ctx.opts = {k_: v_ for k_, v_ in opts.items()
+                    if k_ not in ("output_final_state", "save_checkpoints")}
+        final = opts.get("output_final_state", False)
+        res = kda_forward(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens,
+                          cu_seqlens_host=cu_host, initial_state=h0, output_final_state=final,
+                          save_checkpoints=opts.get("save_checkpoints", False), **ctx.opts)
+        if isinstance(res, tuple):
+            o, ht, ctx.ckpt = res
+        else:
+            o, ht, ctx.ckpt = res, None, None
+        return (o, ht) if final else o
 
     @staticmethod
-    def backward(ctx, dO):
-        q, k, v, raw_g, raw_beta, A_log, dt_bias, cu = ctx.saved_tensors
-        grads = kda_backward(q, k, v, raw_g, raw_beta, A_log, dt_bias, dO.contiguous(), cu,
-                             cu_seqlens_host=ctx.cu_host, **ctx.opts)
-        return (*grads, None, None, None)
+    def backward(ctx, dO, dht=None):
+        q, k, v, raw_g, raw_beta, A_log, dt_bias, cu, h0 = ctx.saved_tensors
+        dO = torch.zeros_like(v) if dO is None else dO.contiguous()
+        dht = None if dht is None else dht.contiguous()
+        grads = kda_backward(q, k, v, raw_g, raw_beta, A_log, dt_bias, dO, cu,
+                             cu_seqlens_host=ctx.cu_host, initial_state=h0, d_final_state=dht,
+                             checkpoints=ctx.ckpt, **ctx.opts)
+        ctx.ckpt = None
+        dh0 = grads[7] if h0 is not None else None
+        return (*grads[:7], dh0, None, None, None)
 
 
 def kda(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, *, cu_seqlens_host=None,
-        scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6, seg_chunks=0):
-    """Differentiable KDA operator; returns O [T,H,V]."""
+        scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6, seg_chunks=0,
+        gate_mode=_lib.KDA_GATE_SIGMOID_BOUND, initial_state=None, output_final_state=False,
+        save_checkpoints=False):
+    """Differentiable KDA operator; returns O [T,H,V], or (O, ht) with
+    output_final_state. initial_state (fp32 [N,H,K,V]) is differentiable.
+    save_checkpoints keeps the states at the backward's segment starts from
+    the forward to the backward (a memory/time trade: the backward skips one
+    forward-direction pass; every chunk's w, u and h are still recomputed)."""
     if cu_seqlens is None:
         cu_seqlens, cu_seqlens_host = _default_cu(q.shape[0], q.device)
     cu_host = _cu_host(cu_seqlens, cu_seqlens_host)
-    opts = dict(scale=scale, chunk=chunk, lower_bound=lower_bound, eps=eps, seg_chunks=seg_chunks)
-    return KDAFunction.apply(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, cu_host, opts)
+    opts = dict(scale=scale, chunk=chunk, lower_bound=lower_bound, eps=eps, seg_chunks=seg_chunks,
+                gate_mode=gate_mode, output_final_state=output_final_state,
+                save_checkpoints=save_checkpoints)
+    return KDAFunction.apply(q, k, v, raw_g, raw_beta, A_log, dt_bias, initial_state, cu_seqlens,
+                             cu_host, opts)

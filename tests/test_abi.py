@@ -67,7 +67,7 @@ def test_valid_problem_and_workspace_sizes(lib):
     (dict(chunk=16), _lib.KDA_ERR_UNSUPPORTED),                    # bf16 needs C >= 32
     (dict(chunk=48), _lib.KDA_ERR_UNSUPPORTED),
     (dict(dtype=7), _lib.KDA_ERR_UNSUPPORTED),
-    (dict(gate_mode=_lib.KDA_GATE_SOFTPLUS_CLAMP), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(gate_mode=2), _lib.KDA_ERR_UNSUPPORTED),
 ])
 def test_bad_problems_are_rejected(lib, kw, code):
     p = good(**kw)
@@ -94,3 +94,32 @@ def test_null_pointers_and_small_workspace_rejected_before_any_launch(lib):
 def test_status_strings(lib):
     for code in range(5):
         assert len(_lib.status_text(lib, code)) > 0
+
+
+def test_checkpoint_queries_follow_the_backward_segments(lib):
+    p = good(seg_chunks=1)  # chunks: 2 + 0 + 4 = 6 segments of one chunk
+    slot = 4 * 128 * 128 * 4
+    assert lib.kda_bwd_segment_chunks(p.ref) == 1
+    assert lib.kda_checkpoint_bytes(p.ref) == 6 * slot
+    q = good(seg_chunks=4)
+    assert lib.kda_bwd_segment_chunks(q.ref) == 4
+    assert lib.kda_checkpoint_bytes(q.ref) == 2 * slot
+    bad = good(H=0)
+    assert lib.kda_bwd_segment_chunks(bad.ref) == 0 and lib.kda_checkpoint_bytes(bad.ref) == 0
+
+
+def test_state_io_validation_before_any_launch(lib):
+    p = good(seg_chunks=1)
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    io = _lib.KdaStateIO()
+    io.ckpt = 0x2000
+    io.ckpt_bytes = lib.kda_checkpoint_bytes(p.ref) - 1
+    assert lib.kda_fwd_ex(p.ref, *([fake] * 9), ctypes.byref(io), fake,
+                          ctypes.c_size_t(p.fwd_ws()), nul) == _lib.KDA_ERR_WORKSPACE
+    assert lib.kda_bwd_ex(p.ref, *([fake] * 16), ctypes.byref(io), fake,
+                          ctypes.c_size_t(p.bwd_ws()), nul) == _lib.KDA_ERR_WORKSPACE
+    args = [fake] * 16
+    args[9] = nul  # dq
+    assert lib.kda_bwd_ex(p.ref, *args, None, fake, ctypes.c_size_t(p.bwd_ws()),
+                          nul) == _lib.KDA_ERR_INVALID
