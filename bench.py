@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--workload", default="t8k_h64_bf16")
     ap.add_argument("--seg-chunks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--checkpoints", action="store_true",
+                    help="the forward saves the states entering the backward's segments "
+                         "(the backward skips its checkpoint pass; w, u, h are still "
+                         "recomputed per chunk)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -143,8 +147,12 @@ def main() -> int:
     kw = dict(cu_seqlens_host=x["cu_seqlens_host"], chunk=w.chunk, seg_chunks=args.seg_chunks)
 
     def step():
-        o = kda_forward(*(x[n] for n in names), x["cu_seqlens"], **kw)
-        g = kda_backward(*(x[n] for n in names), x["dO"], x["cu_seqlens"], **kw)
+        if args.checkpoints:
+            o, _, ck = kda_forward(*(x[n] for n in names), x["cu_seqlens"],
+                                   save_checkpoints=True, **kw)
+        else:
+            o, ck = kda_forward(*(x[n] for n in names), x["cu_seqlens"], **kw), None
+        g = kda_backward(*(x[n] for n in names), x["dO"], x["cu_seqlens"], checkpoints=ck, **kw)
         return o, g
 
     for _ in range(args.warmup):
@@ -208,7 +216,7 @@ def main() -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "n_seqs": len(w.seqlens), "tokens": w.T, "heads": w.H,
-                   "head_dim": w.D, "chunk": w.chunk},
+                   "head_dim": w.D, "chunk": w.chunk, "fwd_checkpoints": bool(args.checkpoints)},
         "peak_alloc_gib": round(peak_alloc, 3), "peak_reserved_gib": round(peak_res, 3),
         "e2e_hbm_roof_frac": round(e2e_frac, 4), "wall_s_timed": round(wall, 3),
         "kernels": {k: {kk: round(vv, 4) if isinstance(vv, float) else vv for kk, vv in v.items()}

@@ -181,13 +181,16 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
   Ops s0, s1, s2;
   const size_t idx0 = static_cast<size_t>(cb - seg_begin) * d.H + h;
   load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(s0, ops, idx0, v0, w, i, g);
-  if (cb + 1 < ce) load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(s1, ops, idx0 + d.H, v0, w, i, g);
+  load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(s1, ops, cb + 1 < ce ? idx0 + d.H : idx0, v0, w, i, g);
   __syncthreads();
 
   auto step = [&](int c, const Ops& cur, Ops& fill) {
     const size_t idx = static_cast<size_t>(c - seg_begin) * d.H + h;
-    if (c + 2 < ce)
-      load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(fill, ops, idx + 2 * d.H, v0, w, i, g);
+    // unconditional (the last chunk again past the end): on every path the
+    // same number of loads follows each set, so the waits before a set's use
+    // can leave the two later sets in flight
+    load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(
+        fill, ops, static_cast<size_t>(min(c + 2, ce - 1) - seg_begin) * d.H + h, v0, w, i, g);
     if (c == next_ck) {
       // the state entering chunk c, needed only where c is inside the sequence
       if (c > coff0) {
@@ -346,10 +349,13 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
     }
     f.gm[jm] = *reinterpret_cast<const f32x4*>(gam + 16 * mk + 4 * g);
   }
+  // rows past the chunk's end read its last row (unconditional loads stay
+  // where they are issued; a conditional one would be moved to its use and
+  // waited for there) and are zeroed where they are used
 #pragma unroll
   for (int j = 0; j < BwdOps<TI, OpT, D, C, BV>::NDO; ++j) {
-    const int e = tid + 256 * j, r = e / BV, vv = e % BV;
-    f.dOv[j] = r < len ? load_bits<TI>(dO + (t0 + r) * ts + static_cast<size_t>(h) * V + v0 + vv) : 0u;
+    const int e = tid + 256 * j, r = e / BV, vv = e % BV, rc = r < len ? r : len - 1;
+    f.dOv[j] = load_bits<TI>(dO + (t0 + rc) * ts + static_cast<size_t>(h) * V + v0 + vv);
   }
 }
 
@@ -422,15 +428,17 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
                                     chunk_len(t0), ts, h, v0, tid, w, i, g);
   };
   load(s0, ce - 1);
-  if (ce - 2 >= cb) load(s1, ce - 2);
+  load(s1, max(ce - 2, cb));
   auto step = [&](int c, const Ops& cur, Ops& fill) {
     const size_t idx = static_cast<size_t>(c - seg_begin) * d.H + h;
-    if (c - 2 >= cb) load(fill, c - 2);
+    // unconditional (the first chunk again past the start), as in the forward scan
+    load(fill, max(c - 2, cb));
     // dO tile, transposed into LDS ([BV][C]); padded rows are zero
+    const int len = chunk_len(chunk_t0(c));
 #pragma unroll
     for (int j = 0; j < Ops::NDO; ++j) {
       const int e = tid + 256 * j, r = e / BV, vv = e % BV;
-      dOT_s[vv * LDC + r] = from_f<OpT>(bits_to_f<TI>(cur.dOv[j]));
+      dOT_s[vv * LDC + r] = from_f<OpT>(r < len ? bits_to_f<TI>(cur.dOv[j]) : 0.f);
     }
     {
       OpT* hd = static_cast<OpT*>(st.dh) + idx * K * V;
