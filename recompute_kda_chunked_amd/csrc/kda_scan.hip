@@ -75,8 +75,10 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
   using G = ScanGeo<OpT, D, C, BV>;
   using M = typename G::M;
   constexpr int K = G::K, V = G::V;
-  if (w < G::NB) {
-    const int m = w;
+  {
+    // waves past the last row block (C < 64) load that block's rows again and
+    // leave them unused: the loads stay unconditional
+    const int m = w < G::NB ? w : G::NB - 1;
     const OpT* Wn = static_cast<const OpT*>(ops.Wn) + idx * C * K + (16 * m + i) * K + g * M::KPL;
 #pragma unroll
     for (int j = 0; j < G::NKF; ++j) f.w[j] = M::load(Wn + j * M::KS);
@@ -286,11 +288,17 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
     put_state();
     __syncthreads();
   };
-  for (int c = cb; c < ce; c += 3) {
+  // whole groups of three chunks in the loop (every step issues the same
+  // loads, so each wait leaves the two newer operand sets in flight), then
+  // the last one or two chunks
+  int c = cb;
+  for (; c + 2 < ce; c += 3) {
     step(c, s0, s2);
-    if (c + 1 < ce) step(c + 1, s1, s0);
-    if (c + 2 < ce) step(c + 2, s2, s1);
+    step(c + 1, s1, s0);
+    step(c + 2, s2, s1);
   }
+  if (c < ce) step(c, s0, s2);
+  if (c + 1 < ce) step(c + 1, s1, s0);
   // the state leaves as the next segment's carry, or as the sequence's final state
   float* hout = ce < coff1 ? carry_out
                            : (ss.fin ? ss.fin + static_cast<size_t>(n) * d.H * K * V : nullptr);
@@ -327,8 +335,8 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
   using G = ScanGeo<OpT, D, C, BV>;
   using M = typename G::M;
   constexpr int K = G::K, V = G::V;
-  if (w < G::NB) {
-    const int m = w;
+  {
+    const int m = w < G::NB ? w : G::NB - 1;  // unconditional, as in the forward
     const OpT* at = static_cast<const OpT*>(ops.AqkT) + idx * C * C + (16 * m + i) * C + g * M::KPL;
 #pragma unroll
     for (int j = 0; j < G::NCF; ++j) f.at[j] = M::load(at + j * M::KS);
@@ -492,11 +500,15 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
     __syncthreads();  // every wave is done reading dhT_s / dOT_s / dVnT_s of this chunk
     put_state();
   };
-  for (int c = ce - 1; c >= cb; c -= 3) {
+  // whole groups of three chunks in the loop, then the first one or two
+  int c = ce - 1;
+  for (; c - 2 >= cb; c -= 3) {
     step(c, s0, s2);
-    if (c - 1 >= cb) step(c - 1, s1, s0);
-    if (c - 2 >= cb) step(c - 2, s2, s1);
+    step(c - 1, s1, s0);
+    step(c - 2, s2, s1);
   }
+  if (c >= cb) step(c, s0, s2);
+  if (c - 1 >= cb) step(c - 1, s1, s0);
   // the gradient leaves as the previous segment's carry, or, past the
   // sequence's first chunk, as the initial state's gradient
   float* hout = cb > coff0 ? carry_out
