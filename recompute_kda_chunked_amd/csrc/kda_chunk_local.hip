@@ -369,8 +369,7 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
           const auto tb = M::load(Tb + (16 * n + i) * LDT + s0 + g * KPL);
           acc[n] = M::mma(gk, tb, acc[n]);              // W^T tile (k rows, r cols)
           if (BWD) acc2[n] = M::mma(tb, gk, acc2[n]);   // W tile (r rows, k cols)
-          if (BWD) accu[n] = M::mma(gv, tb, accu[n]);   // U^T tile: U[16n + i][16mk + 4g + rr]
-          else accu[n] = M::mma(tb, gv, accu[n]);       // U tile: U[16n + 4g + rr][16mk + i]
+          accu[n] = M::mma(gv, tb, accu[n]);            // U^T tile: U[16n + i][16mk + 4g + rr]
         }
       }
 #pragma unroll
@@ -385,8 +384,7 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) dT[rr] = from_f<OpT>(-acc2[n][rr]);
         }
-        OpT* du = BWD ? static_cast<OpT*>(ops.U) + idx * C * V + (16 * n + i) * V + 16 * mk + 4 * g
-                      : static_cast<OpT*>(ops.UT) + idx * V * C + (16 * mk + i) * C + 16 * n + 4 * g;
+        OpT* du = static_cast<OpT*>(ops.U) + idx * C * V + (16 * n + i) * V + 16 * mk + 4 * g;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) du[rr] = from_f<OpT>(accu[n][rr]);
       }

@@ -120,8 +120,8 @@ ChunkOps carve_ops(const Plan& P, bool bwd, unsigned char*& cur) {
   o.Wn = take(n * C * K * e);
   o.kgT = take(n * K * C * e);
   o.gam = static_cast<float*>(take(n * K * 4));
+  o.U = take(n * C * K * e);
   if (!bwd) {
-    o.UT = take(n * K * C * e);
     o.qg = take(n * C * K * e);
     o.Aqk = take(n * C * C * e);
   } else {
@@ -129,7 +129,6 @@ ChunkOps carve_ops(const Plan& P, bool bwd, unsigned char*& cur) {
     o.kg = take(n * C * K * e);
     o.qgT = take(n * K * C * e);
     o.WnT = take(n * K * C * e);
-    o.U = take(n * C * K * e);
     o.TT = take(n * C * C * e);
     o.P = take(n * C * C * e);
   }

@@ -29,7 +29,7 @@ struct Inputs {
 // bf16 for bf16 problems and fp32 for fp32 problems.
 struct ChunkOps {
   void *Wn;    // [C][K]  -W  (W = T (beta * kh * e^G))
-  void *UT;    // [V][C]  U^T (U = T (beta * v))
+  void *U;     // [C][V]  U = T (beta * v)
   void *qg;    // [C][K]  qh * e^G                       (forward only)
   void *kgT;   // [K][C]  (kh * e^{G_c - G})^T
   void *Aqk;   // [C][C]  gated q.k, lower incl. diagonal (forward only)
@@ -39,7 +39,6 @@ struct ChunkOps {
   void *kg;    // [C][K]
   void *qgT;   // [K][C]
   void *WnT;   // [K][C]
-  void *U;     // [C][V]
   void *TT;    // [C][C]  T^T
   void *P;     // [C][C]  gated k.k without beta, strictly lower
 };

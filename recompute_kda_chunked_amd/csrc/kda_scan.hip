@@ -15,7 +15,10 @@
 // MFMA accumulator tiles; a bf16 (or fp32) operand copy sits in LDS.
 //
 // Work split: wave w owns row block m = w of the chunk (Vn, O or dVn tiles,
-// all value blocks of the tile) and MKW row blocks of the state. The serial
+// all value blocks of the tile) and MKW row blocks of the state. State, Vn
+// and O tiles are held transposed (lane (i, g) has four consecutive value
+// columns of one key channel or chunk row), so that every store of them to
+// memory is one 4-element vector per tile. The serial
 // chunk loop is software-pipelined: the per-chunk operands a wave needs
 // (rows of W, qg, Aqk, kg^T, U, gamma, dO, ...) for chunk c+2 are loaded into
 // registers while chunk c is computed (three rotating register sets), so the
@@ -41,6 +44,45 @@ __device__ __forceinline__ bool scan_program(const Dims& d, int& n, int& h, int&
   return true;
 }
 
+// Four consecutive values from raw bits (bf16: two words, low half first;
+// fp32: four words), their raw load, and a four-value vector store (8 or 16
+// bytes).
+template <typename T>
+__device__ __forceinline__ f32x4 unpack4(const uint32_t (&u)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
+                 __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u)};
+  } else {
+    return f32x4{__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]),
+                 __uint_as_float(u[3])};
+  }
+}
+template <typename T>
+__device__ __forceinline__ void load4_raw(const T* p, uint32_t (&u)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    u[0] = x.x;
+    u[1] = x.y;
+  } else {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    u[0] = x.x;
+    u[1] = x.y;
+    u[2] = x.z;
+    u[3] = x.w;
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const f32x4& v) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 b;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) b[rr] = static_cast<bf16>(v[rr]);
+    *reinterpret_cast<bf16x4*>(p) = b;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+
 // Tile geometry shared by both scans.
 template <typename OpT, int D, int C, int BV>
 struct ScanGeo {
@@ -63,10 +105,11 @@ struct FwdOps {
   F w[G::NKF];                // W rows of block m (negated: -W)
   F q[G::NKF];                // qg rows of block m (output only)
   F a[G::NCF];                // Aqk rows of block m (output only)
-  uint32_t u[G::BVT][4];      // U at the Vn tile positions, raw bits (converted at
-                              // use, so the prefetch does not wait for its loads)
+  uint32_t u[G::BVT][4];      // U[r][v..v+3] at the lane's Vn^T tile entries, raw
+                              // bits (converted at use, so the prefetch does not
+                              // wait for its loads)
   F kt[G::MKW][G::NCF];       // kg^T rows of the wave's state row blocks
-  f32x4 gm[G::MKW];           // gamma at the wave's state rows
+  float gm[G::MKW];           // gamma at the lane's key channel of each row block
 };
 
 template <typename OpT, int D, int C, int BV, bool OUT_O, bool REC>
@@ -90,27 +133,9 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
 #pragma unroll
       for (int j = 0; j < G::NCF; ++j) f.a[j] = M::load(aq + j * M::KS);
     }
+    const OpT* U = static_cast<const OpT*>(ops.U) + idx * C * V + (16 * m + i) * V + v0 + 4 * g;
 #pragma unroll
-    for (int nv = 0; nv < G::BVT; ++nv) {
-      if (REC) {
-        const OpT* U = static_cast<const OpT*>(ops.U) + idx * C * V;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) f.u[nv][rr] = load_bits<OpT>(U + (16 * m + 4 * g + rr) * V + v0 + 16 * nv + i);
-      } else {
-        const OpT* src = static_cast<const OpT*>(ops.UT) + idx * V * C + (v0 + 16 * nv + i) * C + 16 * m + 4 * g;
-        if constexpr (sizeof(OpT) == 2) {  // four bf16 packed in u[nv][0..1]
-          const uint2 x = *reinterpret_cast<const uint2*>(src);
-          f.u[nv][0] = x.x;
-          f.u[nv][1] = x.y;
-        } else {
-          const uint4 x = *reinterpret_cast<const uint4*>(src);
-          f.u[nv][0] = x.x;
-          f.u[nv][1] = x.y;
-          f.u[nv][2] = x.z;
-          f.u[nv][3] = x.w;
-        }
-      }
-    }
+    for (int nv = 0; nv < G::BVT; ++nv) load4_raw<OpT>(U + 16 * nv, f.u[nv]);
   }
   const OpT* kgT = static_cast<const OpT*>(ops.kgT) + idx * K * C;
   const float* gam = ops.gam + idx * K;
@@ -119,7 +144,7 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
     const int mk = w * G::MKW + jm;
 #pragma unroll
     for (int j = 0; j < G::NCF; ++j) f.kt[jm][j] = M::load(kgT + (16 * mk + i) * C + j * M::KS + g * M::KPL);
-    f.gm[jm] = *reinterpret_cast<const f32x4*>(gam + 16 * mk + 4 * g);
+    f.gm[jm] = gam[16 * mk + i];
   }
 }
 
@@ -147,7 +172,8 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
   const int v0 = vt * BV;
   const size_t ts = static_cast<size_t>(d.H) * V;
 
-  // state tile j of this wave: row block mk = w*MKW + j/BVT, value block nv = j%BVT.
+  // state tile j of this wave: row block mk = w*MKW + j/BVT, value block
+  // nv = j%BVT, held transposed: hs[j][rr] = h[16mk + i][v0 + 16nv + 4g + rr].
   // At the sequence's first chunk the state is its initial state (or zero),
   // otherwise the carry of the previous segment.
   f32x4 hs[HPW];
@@ -155,24 +181,23 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
   const float* hin = !fresh ? carry_in
                      : (ss.init ? ss.init + static_cast<size_t>(n) * d.H * K * V : nullptr);
   const bool zero_in = hin == nullptr;
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
+  // offset of the lane's four state values in a [H][K][V] array
+  auto hoff = [&](int j) {
     const int mk = w * MKW + j / BVT, nv = j % BVT;
+    return (static_cast<size_t>(h) * K + 16 * mk + i) * V + v0 + 16 * nv + 4 * g;
+  };
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int kk = 16 * mk + 4 * g + rr, vv = v0 + 16 * nv + i;
-      hs[j][rr] = zero_in ? 0.f : hin[(static_cast<size_t>(h) * K + kk) * V + vv];
-    }
-  }
+  for (int j = 0; j < HPW; ++j)
+    hs[j] = zero_in ? zero4() : *reinterpret_cast<const f32x4*>(hin + hoff(j));
   // states at multiples of ss.ck_every chunks (the backward's segment starts)
   int next_ck = ss.ck ? (cb + ss.ck_every - 1) / ss.ck_every * ss.ck_every : 0x7fffffff;
   auto put_state = [&]() {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       const int mk = w * MKW + j / BVT, nv = j % BVT;
-      OpT* dst = hT_s + (16 * nv + i) * LDH + 16 * mk + 4 * g;
+      OpT* dst = hT_s + (16 * nv + 4 * g) * LDH + 16 * mk + i;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(hs[j][rr]);
+      for (int rr = 0; rr < 4; ++rr) dst[rr * LDH] = from_f<OpT>(hs[j][rr]);
     }
   };
   put_state();
@@ -196,60 +221,39 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
     if (c == next_ck) {
       // the state entering chunk c, needed only where c is inside the sequence
       if (c > coff0) {
-        float* dst = ss.ck + (static_cast<size_t>(c / ss.ck_every) * d.H + h) * K * V;
+        float* dst = ss.ck + static_cast<size_t>(c / ss.ck_every) * d.H * K * V;
 #pragma unroll
-        for (int j = 0; j < HPW; ++j) {
-          const int mk = w * MKW + j / BVT, nv = j % BVT;
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) dst[(16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = hs[j][rr];
-        }
+        for (int j = 0; j < HPW; ++j) *reinterpret_cast<f32x4*>(dst + hoff(j)) = hs[j];
       }
       next_ck += ss.ck_every;
     }
     if (REC) {
-      // entering state h_n as [K][V]
-      OpT* hd = static_cast<OpT*>(st.h) + idx * K * V;
+      // entering state h_n as [K][V] (hoff adds the head's h * K * V)
+      OpT* hd = static_cast<OpT*>(st.h) + (idx - h) * K * V;
 #pragma unroll
-      for (int j = 0; j < HPW; ++j) {
-        const int mk = w * MKW + j / BVT, nv = j % BVT;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          hd[(16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = from_f<OpT>(hs[j][rr]);
-      }
+      for (int j = 0; j < HPW; ++j) store4<OpT>(hd + hoff(j), hs[j]);
     }
-    // Vn = U - W h and the inter part qg h of O: row block m = w, all value blocks
+    // Vn = U - W h and the inter part qg h of O: row block m = w, all value
+    // blocks, as transposed tiles: accV[rr] = Vn[16m + i][v0 + 16nv + 4g + rr]
     f32x4 accO[BVT];
     if (w < NB) {
       const int m = w;
 #pragma unroll
       for (int nv = 0; nv < BVT; ++nv) {
-        f32x4 accV;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          if (REC || sizeof(OpT) == 4) {
-            accV[rr] = bits_to_f<OpT>(cur.u[nv][rr]);
-          } else {
-            const uint32_t wd = cur.u[nv][rr >> 1];
-            accV[rr] = __uint_as_float((rr & 1) ? (wd & 0xffff0000u) : (wd << 16));
-          }
-        }
+        f32x4 accV = unpack4<OpT>(cur.u[nv]);
         accO[nv] = zero4();
         const OpT* bh = hT_s + (16 * nv + i) * LDH + g * KPL;
 #pragma unroll
         for (int j = 0; j < G::NKF; ++j) {
           const auto b = M::load(bh + j * KS);
-          accV = M::mma(cur.w[j], b, accV);
-          if (OUT_O) accO[nv] = M::mma(cur.q[j], b, accO[nv]);
+          accV = M::mma(b, cur.w[j], accV);
+          if (OUT_O) accO[nv] = M::mma(b, cur.q[j], accO[nv]);
         }
-        OpT* dst = VnT_s + (16 * nv + i) * LDC + 16 * m + 4 * g;
+        OpT* dst = VnT_s + (16 * nv + 4 * g) * LDC + 16 * m + i;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(accV[rr]);
-        if (REC) {
-          OpT* vn = static_cast<OpT*>(st.Vn) + idx * C * V;
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            vn[(16 * m + 4 * g + rr) * V + v0 + 16 * nv + i] = from_f<OpT>(accV[rr]);
-        }
+        for (int rr = 0; rr < 4; ++rr) dst[rr * LDC] = from_f<OpT>(accV[rr]);
+        if (REC)
+          store4<OpT>(static_cast<OpT*>(st.Vn) + idx * C * V + (16 * m + i) * V + v0 + 16 * nv + 4 * g, accV);
       }
     }
     __syncthreads();
@@ -258,29 +262,27 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
       const int64_t t0 = tok0 + static_cast<int64_t>(c - coff0) * C;
       const int len = static_cast<int>(min(static_cast<int64_t>(C), tok1 - t0));
       const int nf = (16 * (m + 1) + KS - 1) / KS;  // Aqk[r][s] = 0 for s > r
+      const int r = 16 * m + i;
 #pragma unroll
       for (int nv = 0; nv < BVT; ++nv) {
         const OpT* bv = VnT_s + (16 * nv + i) * LDC + g * KPL;
 #pragma unroll
         for (int j = 0; j < G::NCF; ++j)
-          if (j < nf) accO[nv] = M::mma(cur.a[j], M::load(bv + j * KS), accO[nv]);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = 16 * m + 4 * g + rr;
-          if (r < len) o[(t0 + r) * ts + static_cast<size_t>(h) * V + v0 + 16 * nv + i] = from_f<TI>(accO[nv][rr]);
-        }
+          if (j < nf) accO[nv] = M::mma(M::load(bv + j * KS), cur.a[j], accO[nv]);
+        // accO[nv][rr] = O[r][v0 + 16nv + 4g + rr]
+        if (r < len) store4<TI>(o + (t0 + r) * ts + static_cast<size_t>(h) * V + v0 + 16 * nv + 4 * g, accO[nv]);
       }
     }
-    // h <- Diag(gamma) h + kg^T Vn
+    // h <- Diag(gamma) h + kg^T Vn, on the transposed tiles
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       const int jm = j / BVT, nv = j % BVT;
       f32x4 acc;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) acc[rr] = cur.gm[jm][rr] * hs[j][rr];
+      for (int rr = 0; rr < 4; ++rr) acc[rr] = cur.gm[jm] * hs[j][rr];
       const OpT* bv = VnT_s + (16 * nv + i) * LDC + g * KPL;
 #pragma unroll
-      for (int jj = 0; jj < G::NCF; ++jj) acc = M::mma(cur.kt[jm][jj], M::load(bv + jj * KS), acc);
+      for (int jj = 0; jj < G::NCF; ++jj) acc = M::mma(M::load(bv + jj * KS), cur.kt[jm][jj], acc);
       hs[j] = acc;
     }
     // hT_s was last read before the barrier above; the barrier below also
@@ -304,12 +306,7 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
                            : (ss.fin ? ss.fin + static_cast<size_t>(n) * d.H * K * V : nullptr);
   if (hout) {
 #pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-      const int mk = w * MKW + j / BVT, nv = j % BVT;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        hout[(static_cast<size_t>(h) * K + 16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = hs[j][rr];
-    }
+    for (int j = 0; j < HPW; ++j) *reinterpret_cast<f32x4*>(hout + hoff(j)) = hs[j];
   }
 }
 
@@ -323,7 +320,7 @@ struct BwdOps {
   F kg[G::NKF];               // kg rows of block m
   F qt[G::MKW][G::NCF];       // qg^T rows of the wave's state row blocks
   F wt[G::MKW][G::NCF];       // -W^T rows of the wave's state row blocks
-  f32x4 gm[G::MKW];
+  float gm[G::MKW];           // gamma at the lane's key channel of each row block
   uint32_t dOv[NDO];          // dO tile elements this thread stages into LDS (raw bits)
 };
 
@@ -355,7 +352,7 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
       f.qt[jm][j] = M::load(qgT + (16 * mk + i) * C + j * M::KS + g * M::KPL);
       f.wt[jm][j] = M::load(WnT + (16 * mk + i) * C + j * M::KS + g * M::KPL);
     }
-    f.gm[jm] = *reinterpret_cast<const f32x4*>(gam + 16 * mk + 4 * g);
+    f.gm[jm] = gam[16 * mk + i];
   }
   // rows past the chunk's end read its last row (unconditional loads stay
   // where they are issued; a conditional one would be moved to its use and
@@ -400,30 +397,29 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
     return static_cast<int>(min(static_cast<int64_t>(C), tok1 - t0));
   };
 
-  // dh' (gradient of the state leaving the current chunk): after the
-  // sequence's last chunk it is the final state's gradient (or zero),
-  // otherwise the carry of the following segment
+  // dh' (gradient of the state leaving the current chunk), transposed tiles
+  // as in the forward scan: hs[j][rr] = dh'[16mk + i][v0 + 16nv + 4g + rr].
+  // After the sequence's last chunk it is the final state's gradient (or
+  // zero), otherwise the carry of the following segment.
   f32x4 hs[HPW];
   const bool fresh = (ce == coff1);
   const float* hin = !fresh ? carry_in
                      : (ss.init ? ss.init + static_cast<size_t>(n) * d.H * K * V : nullptr);
   const bool zero_in = hin == nullptr;
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
+  auto hoff = [&](int j) {
     const int mk = w * MKW + j / BVT, nv = j % BVT;
+    return (static_cast<size_t>(h) * K + 16 * mk + i) * V + v0 + 16 * nv + 4 * g;
+  };
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int kk = 16 * mk + 4 * g + rr, vv = v0 + 16 * nv + i;
-      hs[j][rr] = zero_in ? 0.f : hin[(static_cast<size_t>(h) * K + kk) * V + vv];
-    }
-  }
+  for (int j = 0; j < HPW; ++j)
+    hs[j] = zero_in ? zero4() : *reinterpret_cast<const f32x4*>(hin + hoff(j));
   auto put_state = [&]() {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       const int mk = w * MKW + j / BVT, nv = j % BVT;
-      OpT* dst = dhT_s + (16 * nv + i) * LDH + 16 * mk + 4 * g;
+      OpT* dst = dhT_s + (16 * nv + 4 * g) * LDH + 16 * mk + i;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(hs[j][rr]);
+      for (int rr = 0; rr < 4; ++rr) dst[rr * LDH] = from_f<OpT>(hs[j][rr]);
     }
   };
   put_state();
@@ -449,14 +445,9 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
       dOT_s[vv * LDC + r] = from_f<OpT>(r < len ? bits_to_f<TI>(cur.dOv[j]) : 0.f);
     }
     {
-      OpT* hd = static_cast<OpT*>(st.dh) + idx * K * V;
+      OpT* hd = static_cast<OpT*>(st.dh) + (idx - h) * K * V;  // hoff adds h * K * V
 #pragma unroll
-      for (int j = 0; j < HPW; ++j) {
-        const int mk = w * MKW + j / BVT, nv = j % BVT;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          hd[(16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = from_f<OpT>(hs[j][rr]);
-      }
+      for (int j = 0; j < HPW; ++j) store4<OpT>(hd + hoff(j), hs[j]);
     }
     __syncthreads();
     if (w < NB) {
@@ -482,18 +473,19 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
       }
     }
     __syncthreads();
+    // dh = Diag(gamma) dh' + qg^T dO - W^T dVn, on the transposed tiles
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       const int jm = j / BVT, nv = j % BVT;
       f32x4 acc;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) acc[rr] = cur.gm[jm][rr] * hs[j][rr];
+      for (int rr = 0; rr < 4; ++rr) acc[rr] = cur.gm[jm] * hs[j][rr];
       const OpT* bo = dOT_s + (16 * nv + i) * LDC + g * KPL;
       const OpT* bv = dVnT_s + (16 * nv + i) * LDC + g * KPL;
 #pragma unroll
       for (int jj = 0; jj < G::NCF; ++jj) {
-        acc = M::mma(cur.qt[jm][jj], M::load(bo + jj * KS), acc);
-        acc = M::mma(cur.wt[jm][jj], M::load(bv + jj * KS), acc);
+        acc = M::mma(M::load(bo + jj * KS), cur.qt[jm][jj], acc);
+        acc = M::mma(M::load(bv + jj * KS), cur.wt[jm][jj], acc);
       }
       hs[j] = acc;
     }
@@ -515,12 +507,7 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
                            : (ss.fin ? ss.fin + static_cast<size_t>(n) * d.H * K * V : nullptr);
   if (hout) {
 #pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-      const int mk = w * MKW + j / BVT, nv = j % BVT;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        hout[(static_cast<size_t>(h) * K + 16 * mk + 4 * g + rr) * V + v0 + 16 * nv + i] = hs[j][rr];
-    }
+    for (int j = 0; j < HPW; ++j) *reinterpret_cast<f32x4*>(hout + hoff(j)) = hs[j];
   }
 }
 
