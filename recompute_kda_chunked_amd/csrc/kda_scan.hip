@@ -315,13 +315,16 @@ template <typename TI, typename OpT, int D, int C, int BV>
 struct BwdOps {
   using G = ScanGeo<OpT, D, C, BV>;
   using F = typename G::M::frag;
-  static constexpr int NDO = C * BV / 256;  // dO elements per thread
+  typedef typename Vec16<TI>::T VT;
+  static constexpr int VE = 16 / sizeof(TI);      // dO elements per 16-byte vector
+  static constexpr int NVEC = C * BV / VE;        // vectors in the dO tile
+  static constexpr int NDO = (NVEC + 255) / 256;  // vectors per thread
   F at[G::NCF];               // Aqk^T rows of block m
   F kg[G::NKF];               // kg rows of block m
   F qt[G::MKW][G::NCF];       // qg^T rows of the wave's state row blocks
   F wt[G::MKW][G::NCF];       // -W^T rows of the wave's state row blocks
   float gm[G::MKW];           // gamma at the lane's key channel of each row block
-  uint32_t dOv[NDO];          // dO tile elements this thread stages into LDS (raw bits)
+  VT dOv[NDO];                // dO tile vectors this thread stages into LDS (raw)
 };
 
 template <typename TI, typename OpT, int D, int C, int BV>
@@ -357,10 +360,13 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
   // rows past the chunk's end read its last row (unconditional loads stay
   // where they are issued; a conditional one would be moved to its use and
   // waited for there) and are zeroed where they are used
+  using O = BwdOps<TI, OpT, D, C, BV>;
 #pragma unroll
-  for (int j = 0; j < BwdOps<TI, OpT, D, C, BV>::NDO; ++j) {
-    const int e = tid + 256 * j, r = e / BV, vv = e % BV, rc = r < len ? r : len - 1;
-    f.dOv[j] = load_bits<TI>(dO + (t0 + rc) * ts + static_cast<size_t>(h) * V + v0 + vv);
+  for (int j = 0; j < O::NDO; ++j) {
+    // threads past the tile's vectors load its last one again (unused)
+    const int e0 = tid + 256 * j, e = e0 < O::NVEC ? e0 : O::NVEC - 1;
+    const int r = e / (BV / O::VE), c0 = (e % (BV / O::VE)) * O::VE, rc = r < len ? r : len - 1;
+    f.dOv[j] = *reinterpret_cast<const typename O::VT*>(dO + (t0 + rc) * ts + static_cast<size_t>(h) * V + v0 + c0);
   }
 }
 
@@ -441,8 +447,12 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
     const int len = chunk_len(chunk_t0(c));
 #pragma unroll
     for (int j = 0; j < Ops::NDO; ++j) {
-      const int e = tid + 256 * j, r = e / BV, vv = e % BV;
-      dOT_s[vv * LDC + r] = from_f<OpT>(r < len ? bits_to_f<TI>(cur.dOv[j]) : 0.f);
+      const int e = tid + 256 * j, r = e / (BV / Ops::VE), c0 = (e % (BV / Ops::VE)) * Ops::VE;
+      if (e < Ops::NVEC) {
+#pragma unroll
+        for (int q = 0; q < Ops::VE; ++q)
+          dOT_s[(c0 + q) * LDC + r] = from_f<OpT>(r < len ? static_cast<float>(cur.dOv[j][q]) : 0.f);
+      }
     }
     {
       OpT* hd = static_cast<OpT*>(st.dh) + (idx - h) * K * V;  // hoff adds h * K * V
