@@ -156,20 +156,25 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   const size_t idx = static_cast<size_t>(lc) * d.H + h;
   const size_t ts = static_cast<size_t>(d.H) * D;
   const size_t hoff = static_cast<size_t>(h) * D;
-  const TI* qr = static_cast<const TI*>(in.q) + L.t0 * ts + hoff;
-  const TI* kr = static_cast<const TI*>(in.k) + L.t0 * ts + hoff;
   const TI* vr = static_cast<const TI*>(in.v) + L.t0 * ts + hoff;
   auto row_block = [&](int jm) { return half * MR + jm; };  // valid while < NB
 
-  // Global loads of S1 (raw q, k tiles) and S2/S3 (dVn^T, T^T, dO, Vn, v)
-  // are all issued here, before any arithmetic, so their latency overlaps the
-  // prologue and the cumulative sum. Rows past the chunk's end read the last
-  // valid row (no branch) and are masked where they are used.
+  // Global loads are all issued here, before any arithmetic: first the
+  // prologue's rows (raw q, k, gate, beta; the q and k vectors also feed the
+  // transposes of S1), so the prologue can start once they arrive (loads
+  // complete in order), then those of S2/S3 (dVn^T, T^T, dO, Vn, v), whose
+  // latency overlaps the prologue and the cumulative sum. Rows past the
+  // chunk's end read the last valid row (no branch) and are masked where
+  // they are used.
   static_assert(sizeof(TI) == sizeof(OpT), "inputs and operands share a type");
   typedef typename Vec16<TI>::T VT;
   constexpr int VE = 16 / sizeof(TI), NVR = D / VE, NV = C * NVR, VPT = (NV + NT - 1) / NT;
   constexpr int T2 = (V / 16) * NB, TPW = (T2 + NW - 1) / NW, NKS = C / KS;
-  VT ldq[VPT], ldk[VPT], ldo[VPT], ldn[VPT];
+  using PR = ProRows<TI, D, C, NW>;
+  static_assert(PR::NIT == VPT && PR::LPR == NVR, "prologue rows are the transposes' vectors");
+  PR pr;
+  prologue_load<TI, D, C, NW>(d, in, h, L, pr);
+  VT ldo[VPT], ldn[VPT];
   typename M::frag fa[TPW][NKS], fb[TPW][NKS];
   uint32_t vin[TPW][4];
   {
@@ -181,8 +186,6 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     for (int j = 0; j < VPT; ++j) {
       const int e0 = tid + NT * j, e = e0 < NV ? e0 : 0, r = e / NVR, c = (e % NVR) * VE;
       const int rc = r < L.len ? r : L.len - 1;
-      ldq[j] = *reinterpret_cast<const VT*>(qr + rc * ts + c);
-      ldk[j] = *reinterpret_cast<const VT*>(kr + rc * ts + c);
       ldo[j] = *reinterpret_cast<const VT*>(dOr + rc * ts + c);
       ldn[j] = *reinterpret_cast<const VT*>(Vn + r * V + c);
     }
@@ -197,14 +200,13 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         fa[jt][ks] = M::load(dVnT + (16 * mv + i) * C + ks * KS + g * KPL);
         fb[jt][ks] = M::load(TT + (16 * nr + i) * C + ks * KS + g * KPL);
       }
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) vin[jt][rr] = load_bits<TI>(vr + (r < L.len ? r : L.len - 1) * ts + vv + rr);
+      load4_raw<TI>(vr + (r < L.len ? r : L.len - 1) * ts + vv, vin[jt]);
     }
   }
 
   // ---- S1: prologue, transposed raw q/k, cumulative gate G^T
   auto Gf = [&](int r, int kk_) -> GV& { return GT[kk_ * LDG + r]; };
-  prologue_rows<TI, D, C, NW>(d, in, h, L, rq, rqs, rk, be, Gf);
+  prologue_compute<TI, D, C, NW>(d, L, pr, rq, rqs, rk, be, Gf);
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
@@ -212,8 +214,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       const bool ok = r < L.len;
 #pragma unroll
       for (int q2 = 0; q2 < VE; ++q2) {
-        qT[(c + q2) * LDQ + r] = ok ? ldq[j][q2] : static_cast<TI>(0.f);
-        kT[(c + q2) * LDQ + r] = ok ? ldk[j][q2] : static_cast<TI>(0.f);
+        qT[(c + q2) * LDQ + r] = ok ? pr.qv[j][q2] : static_cast<TI>(0.f);
+        kT[(c + q2) * LDQ + r] = ok ? pr.kv[j][q2] : static_cast<TI>(0.f);
       }
     }
   }
@@ -241,10 +243,11 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       for (int ks = 0; ks < NKS; ++ks) acc = M::mma(fa[jt][ks], fb[jt][ks], acc);
       OpT* dst = dBv_s + r * LDA + vv;
       float part = 0.f;
+      const f32x4 vv4 = unpack4<TI>(vin[jt]);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         dst[rr] = from_f<OpT>(acc[rr]);
-        part += r < L.len ? acc[rr] * bits_to_f<TI>(vin[jt][rr]) : 0.f;
+        part += r < L.len ? acc[rr] * vv4[rr] : 0.f;
         dvv[jt][rr] = be[r] * acc[rr];
       }
       part = sum_groups(part);

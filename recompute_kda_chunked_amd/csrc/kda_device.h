@@ -134,6 +134,45 @@ struct Mma<float> {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Four consecutive values from raw bits (bf16: two words, low half first;
+// fp32: four words), their raw load, and a four-value vector store (8 or 16
+// bytes).
+template <typename T>
+__device__ __forceinline__ f32x4 unpack4(const uint32_t (&u)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
+                 __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u)};
+  } else {
+    return f32x4{__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]),
+                 __uint_as_float(u[3])};
+  }
+}
+template <typename T>
+__device__ __forceinline__ void load4_raw(const T* p, uint32_t (&u)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    u[0] = x.x;
+    u[1] = x.y;
+  } else {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    u[0] = x.x;
+    u[1] = x.y;
+    u[2] = x.z;
+    u[3] = x.w;
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const f32x4& v) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 b;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) b[rr] = static_cast<bf16>(v[rr]);
+    *reinterpret_cast<bf16x4*>(p) = b;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+
 // acc += sum_{kk in [k_lo, k_hi)} A[i][kk] * B[i'][kk] for one 16x16 tile.
 // A and B point at the first row of the tile; lda/ldb are row strides in
 // elements. k_lo and k_hi - k_lo are multiples of Mma<OpT>::KS.

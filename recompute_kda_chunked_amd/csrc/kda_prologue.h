@@ -91,14 +91,7 @@ __device__ __forceinline__ ChunkLoc locate(const Inputs& in, int N, int c) {
 // Row part of the prologue. Each row is read with 16-byte vector loads by
 // LPR = D / (16 / sizeof(TI)) consecutive lanes, so one wave instruction
 // covers 64 / LPR rows; wave w takes row groups w, w + NW, ... and issues the
-// loads of all its rows before any arithmetic. For each row it writes the
-// per-row scalars and the gate value of each channel to G(r, k) (a functor
-// returning a float reference into LDS). Rows r >= len are padding:
-// q = k = 0, beta = 0, g = 0, so they contribute nothing anywhere.
-//   rq[r]  = 1/sqrt(|q|^2 + eps)  (so qbar = q * rq)
-//   rqs[r] = scale * rq           (so qh = q * rqs)
-//   rk[r]  = 1/sqrt(|k|^2 + eps)  (kh = k * rk)
-//   be[r]  = sigmoid(raw_beta)
+// loads of all its rows before any arithmetic.
 template <typename TI>
 struct Vec16;
 template <>
@@ -110,61 +103,92 @@ struct Vec16<float> {
   typedef f32x4 T;
 };
 
-template <typename TI, int D, int C, int NW, class GRef>
-__device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, int h,
-                                              const ChunkLoc& L, float* rq, float* rqs,
-                                              float* rk, float* be, GRef G) {
+// The prologue's row loads for one chunk, in the row layout above: lane
+// (w, lane) of iteration it holds row (w + NW * it) * RPI + lane / LPR,
+// channels (lane % LPR) * VE .. + VE.
+template <typename TI, int D, int C, int NW>
+struct ProRows {
   typedef typename Vec16<TI>::T VT;
-  constexpr int VE = 16 / sizeof(TI);  // elements per vector load
-  constexpr int LPR = D / VE;          // lanes per row
-  constexpr int RPI = 64 / LPR;        // rows per wave instruction
-  constexpr int NIT = (C + NW * RPI - 1) / (NW * RPI);
+  static constexpr int VE = 16 / sizeof(TI);  // elements per vector load
+  static constexpr int LPR = D / VE;          // lanes per row
+  static constexpr int RPI = 64 / LPR;        // rows per wave instruction
+  static constexpr int NIT = (C + NW * RPI - 1) / (NW * RPI);
   static_assert(D % VE == 0 && 64 % LPR == 0, "prologue row layout");
+  VT qv[NIT], kv[NIT], xv[NIT];
+  uint32_t bv[NIT];
+  float alog, db[VE];
+};
+
+// Issue the prologue's loads. Rows past the chunk's end load the last valid
+// row instead (always in bounds, no branch) and are masked at use: a load
+// under a branch, or one converted on arrival, would make the wave wait for
+// it right away.
+template <typename TI, int D, int C, int NW>
+__device__ __forceinline__ void prologue_load(const Dims& d, const Inputs& in, int h,
+                                              const ChunkLoc& L, ProRows<TI, D, C, NW>& p) {
+  using P = ProRows<TI, D, C, NW>;
+  typedef typename P::VT VT;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int sub = lane % LPR, rsub = lane / LPR, c0 = sub * VE;
+  const int rsub = lane / P::LPR, c0 = (lane % P::LPR) * P::VE;
   const size_t ts = static_cast<size_t>(d.H) * D;
   const size_t hoff = static_cast<size_t>(h) * D + c0;
   const TI* q = static_cast<const TI*>(in.q) + L.t0 * ts + hoff;
   const TI* k = static_cast<const TI*>(in.k) + L.t0 * ts + hoff;
   const TI* x = static_cast<const TI*>(in.g) + L.t0 * ts + hoff;
   const TI* rb = static_cast<const TI*>(in.beta) + L.t0 * d.H + h;
-  // Rows past the chunk's end load the last valid row instead (always in
-  // bounds, no branch) and are masked at use: a load under a branch, or one
-  // converted on arrival, would make the wave wait for it right away.
-  VT qv[NIT], kv[NIT], xv[NIT];
-  uint32_t bv[NIT];
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int r = (w + NW * it) * RPI + rsub;
+  for (int it = 0; it < P::NIT; ++it) {
+    const int r = (w + NW * it) * P::RPI + rsub;
     const int rc = r < L.len ? r : L.len - 1;
-    qv[it] = *reinterpret_cast<const VT*>(q + rc * ts);
-    kv[it] = *reinterpret_cast<const VT*>(k + rc * ts);
-    xv[it] = *reinterpret_cast<const VT*>(x + rc * ts);
-    bv[it] = load_bits<TI>(rb + static_cast<size_t>(rc) * d.H);
+    p.qv[it] = *reinterpret_cast<const VT*>(q + rc * ts);
+    p.kv[it] = *reinterpret_cast<const VT*>(k + rc * ts);
+    p.xv[it] = *reinterpret_cast<const VT*>(x + rc * ts);
+    p.bv[it] = load_bits<TI>(rb + static_cast<size_t>(rc) * d.H);
   }
+  p.alog = in.A_log[h];
+#pragma unroll
+  for (int j = 0; j < P::VE; j += 4) {
+    const f32x4 b4 = *reinterpret_cast<const f32x4*>(in.dt_bias + static_cast<size_t>(h) * D + c0 + j);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) p.db[j + jj] = b4[jj];
+  }
+}
+
+// The prologue's arithmetic on loaded rows: for each row the per-row scalars
+// and the gate value of each channel into G(r, k) (a functor returning a
+// reference into LDS). Rows r >= len are padding: q = k = 0, beta = 0, g = 0,
+// so they contribute nothing anywhere.
+//   rq[r]  = 1/sqrt(|q|^2 + eps)  (so qbar = q * rq)
+//   rqs[r] = scale * rq           (so qh = q * rqs)
+//   rk[r]  = 1/sqrt(|k|^2 + eps)  (kh = k * rk)
+//   be[r]  = sigmoid(raw_beta)
+template <typename TI, int D, int C, int NW, class GRef>
+__device__ __forceinline__ void prologue_compute(const Dims& d, const ChunkLoc& L,
+                                                 const ProRows<TI, D, C, NW>& p, float* rq,
+                                                 float* rqs, float* rk, float* be, GRef G) {
+  using P = ProRows<TI, D, C, NW>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int sub = lane % P::LPR, rsub = lane / P::LPR, c0 = sub * P::VE;
   typedef typename GateT<TI>::T GV;
-  const GV ea = exp(static_cast<GV>(in.A_log[h]));
-  float db[VE];
+  const GV ea = exp(static_cast<GV>(p.alog));
 #pragma unroll
-  for (int j = 0; j < VE; ++j) db[j] = in.dt_bias[static_cast<size_t>(h) * D + c0 + j];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int r = (w + NW * it) * RPI + rsub;
+  for (int it = 0; it < P::NIT; ++it) {
+    const int r = (w + NW * it) * P::RPI + rsub;
     const bool valid = r < L.len;
     float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int j = 0; j < VE; ++j) {
-      const float a = to_f(qv[it][j]), b = to_f(kv[it][j]);
+    for (int j = 0; j < P::VE; ++j) {
+      const float a = to_f(p.qv[it][j]), b = to_f(p.kv[it][j]);
       sq += a * a;
       sk += b * b;
     }
-    sq = group_sum<LPR>(sq);
-    sk = group_sum<LPR>(sk);
+    sq = group_sum<P::LPR>(sq);
+    sk = group_sum<P::LPR>(sk);
     if (r < C) {
 #pragma unroll
-      for (int j = 0; j < VE; ++j) {
+      for (int j = 0; j < P::VE; ++j) {
         // the gate map in the cumulative gate's precision
-        const GV xb = static_cast<GV>(to_f(xv[it][j])) + static_cast<GV>(db[j]);
+        const GV xb = static_cast<GV>(to_f(p.xv[it][j])) + static_cast<GV>(p.db[j]);
         G(r, c0 + j) = valid ? gate_map<GV>(d.gate_mode, ea, xb, static_cast<GV>(d.lb)) : GV(0);
       }
       if (sub == 0) {
@@ -173,10 +197,20 @@ __device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, i
         rq[r] = a;
         rqs[r] = d.scale * a;
         rk[r] = b;
-        be[r] = valid ? sigmoidf(bits_to_f<TI>(bv[it])) : 0.f;
+        be[r] = valid ? sigmoidf(bits_to_f<TI>(p.bv[it])) : 0.f;
       }
     }
   }
+}
+
+// Both parts: loads, then arithmetic.
+template <typename TI, int D, int C, int NW, class GRef>
+__device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, int h,
+                                              const ChunkLoc& L, float* rq, float* rqs,
+                                              float* rk, float* be, GRef G) {
+  ProRows<TI, D, C, NW> p;
+  prologue_load<TI, D, C, NW>(d, in, h, L, p);
+  prologue_compute<TI, D, C, NW>(d, L, p, rq, rqs, rk, be, G);
 }
 
 // In-place inclusive cumulative sum over the C rows of every channel k of
