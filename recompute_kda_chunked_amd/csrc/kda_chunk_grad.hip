@@ -175,7 +175,10 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   PR pr;
   prologue_load<TI, D, C, NW>(d, in, h, L, pr);
   VT ldo[VPT], ldn[VPT];
-  typename M::frag fa[TPW][NKS], fb[TPW][NKS];
+  // wave w takes the TPW tiles w*TPW .. of dBv^T (value block mv, row block
+  // nr); they share one value block, so its dVn^T rows are loaded once
+  static_assert(NB % TPW == 0, "a wave's tiles share one value block");
+  typename M::frag fa[NKS], fb[TPW][NKS];
   uint32_t vin[TPW][4];
   {
     const OpT* dVnT = static_cast<const OpT*>(st.dVnT) + idx * V * C;
@@ -189,17 +192,19 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       ldo[j] = *reinterpret_cast<const VT*>(dOr + rc * ts + c);
       ldn[j] = *reinterpret_cast<const VT*>(Vn + r * V + c);
     }
+    {
+      const int t = w * TPW < T2 ? w * TPW : 0, mv = t / NB;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) fa[ks] = M::load(dVnT + (16 * mv + i) * C + ks * KS + g * KPL);
+    }
 #pragma unroll
     for (int jt = 0; jt < TPW; ++jt) {
-      const int t0 = w + NW * jt, t = t0 < T2 ? t0 : 0;
+      const int t0 = w * TPW + jt, t = t0 < T2 ? t0 : 0;
       const int mv = t / NB, nr = t % NB;
       const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
       // the whole reduction is taken (T^T[r][s] is stored as 0 for s < r)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        fa[jt][ks] = M::load(dVnT + (16 * mv + i) * C + ks * KS + g * KPL);
-        fb[jt][ks] = M::load(TT + (16 * nr + i) * C + ks * KS + g * KPL);
-      }
+      for (int ks = 0; ks < NKS; ++ks) fb[jt][ks] = M::load(TT + (16 * nr + i) * C + ks * KS + g * KPL);
       load4_raw<TI>(vr + (r < L.len ? r : L.len - 1) * ts + vv, vin[jt]);
     }
   }
@@ -234,13 +239,13 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     f32x4 dvv[TPW];
 #pragma unroll
     for (int jt = 0; jt < TPW; ++jt) {
-      const int t = w + NW * jt;
+      const int t = w * TPW + jt;
       if (t >= T2) break;
       const int mv = t / NB, nr = t % NB;
       const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
       f32x4 acc = zero4();
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) acc = M::mma(fa[jt][ks], fb[jt][ks], acc);
+      for (int ks = 0; ks < NKS; ++ks) acc = M::mma(fa[ks], fb[jt][ks], acc);
       OpT* dst = dBv_s + r * LDA + vv;
       float part = 0.f;
       const f32x4 vv4 = unpack4<TI>(vin[jt]);
@@ -276,14 +281,11 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     TI* dvo = dv + L.t0 * ts + hoff;
 #pragma unroll
     for (int jt = 0; jt < TPW; ++jt) {
-      const int t = w + NW * jt;
+      const int t = w * TPW + jt;
       if (t >= T2) break;
       const int mv = t / NB, nr = t % NB;
       const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
-      if (r < L.len) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dvo[r * ts + vv + rr] = from_f<TI>(dvv[jt][rr]);
-      }
+      if (r < L.len) store4<TI>(dvo + r * ts + vv, dvv[jt]);
     }
   }
   __syncthreads();
