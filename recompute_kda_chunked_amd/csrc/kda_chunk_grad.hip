@@ -150,6 +150,12 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
   const int kb = w % NKB, half = w / NKB, kk = 16 * kb + i;
+  // Row order of the transposed tiles qT, kT and GT: the rows of channel c
+  // are permuted in groups of 8 by an XOR with its channel bits from 3 up, so
+  // that the transposing writes (lanes on channels 8 apart) spread over the
+  // LDS banks; each 8-row group stays contiguous for the 16-byte reads.
+  auto swz = [](int c) { return ((c >> 3) & (C / 8 - 1)) << 3; };
+  const int swk = swz(kk);  // this lane's channel
   const int lc = blockIdx.x / d.H, h = blockIdx.x % d.H;
   const int cglob = seg_begin + lc;
   const ChunkLoc L = locate<C>(in, d.N, cglob);
@@ -210,7 +216,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   }
 
   // ---- S1: prologue, transposed raw q/k, cumulative gate G^T
-  auto Gf = [&](int r, int kk_) -> GV& { return GT[kk_ * LDG + r]; };
+  auto Gf = [&](int r, int kk_) -> GV& { return GT[kk_ * LDG + (r ^ swz(kk_))]; };
   prologue_compute<TI, D, C, NW>(d, L, pr, rq, rqs, rk, be, Gf);
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
@@ -219,8 +225,9 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       const bool ok = r < L.len;
 #pragma unroll
       for (int q2 = 0; q2 < VE; ++q2) {
-        qT[(c + q2) * LDQ + r] = ok ? pr.qv[j][q2] : static_cast<TI>(0.f);
-        kT[(c + q2) * LDQ + r] = ok ? pr.kv[j][q2] : static_cast<TI>(0.f);
+        const int rs = r ^ swz(c + q2);
+        qT[(c + q2) * LDQ + rs] = ok ? pr.qv[j][q2] : static_cast<TI>(0.f);
+        kT[(c + q2) * LDQ + rs] = ok ? pr.kv[j][q2] : static_cast<TI>(0.f);
       }
     }
   }
@@ -309,7 +316,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       for (int jj = 0; jj < KPL; ++jj) hd += frag_at<OpT>(fh[j], jj) * frag_at<OpT>(fdh[j], jj);
     }
     hdh = static_cast<TG>(sum_groups(hd));
-    const GV Gc = GT[kk * LDG + C - 1];
+    const GV Gc = GT[kk * LDG + ((C - 1) ^ swk)];
     TG colsum = 0;
 #pragma unroll
     for (int jm = 0; jm < MR; ++jm) {
@@ -326,10 +333,10 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int r = 16 * m + 4 * g + rr;
-        const GV Gv = GT[kk * LDG + r];
+        const GV Gv = GT[kk * LDG + (r ^ swk)];
         const float eG = kexp<OpT>(Gv), eGc = kexp<OpT>(Gc - Gv);
-        const float qh = to_f(qT[kk * LDQ + r]) * rqs[r];
-        const float kh = to_f(kT[kk * LDQ + r]) * rk[r];
+        const float qh = to_f(qT[kk * LDQ + (r ^ swk)]) * rqs[r];
+        const float kh = to_f(kT[kk * LDQ + (r ^ swk)]) * rk[r];
         const float dqg = rQg[rr], dkg = rKg[rr], dKb = -rKb[rr];
         const float b = be[r];
         aq[jm][rr] += dqg * eG;
@@ -422,9 +429,11 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     const GV* Gk = GT + kk * LDG;
     const TI* qk = qT + kk * LDQ;
     const TI* kq = kT + kk * LDQ;
-    auto khat = [&](int r) { return static_cast<TG>(to_f(kq[r])) * static_cast<TG>(rk[r]); };
-    auto qhat = [&](int r) { return static_cast<TG>(to_f(qk[r])) * static_cast<TG>(rqs[r]); };
-    auto dec = [&](int r, int s_) { return VJ::ex(static_cast<TG>(Gk[r]) - static_cast<TG>(Gk[s_])); };
+    auto khat = [&](int r) { return static_cast<TG>(to_f(kq[r ^ swk])) * static_cast<TG>(rk[r]); };
+    auto qhat = [&](int r) { return static_cast<TG>(to_f(qk[r ^ swk])) * static_cast<TG>(rqs[r]); };
+    auto dec = [&](int r, int s_) {
+      return VJ::ex(static_cast<TG>(Gk[r ^ swk]) - static_cast<TG>(Gk[s_ ^ swk]));
+    };
     // Eight consecutive rows r0..r0+7 (r0 a multiple of 8) of this channel's
     // raw q or k, its row scale and G, read as 16-byte LDS vectors (bf16
     // operands; the fp32 path reads one row per lane).
@@ -434,11 +443,11 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     auto rows8 = [&](const TI* col, const float* scale, int r0) {
       Rows8 o;
       if constexpr (VJ::KPL == 8) {
-        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(col + r0);
+        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(col + (r0 ^ swk));
         const f32x4 s0v = *reinterpret_cast<const f32x4*>(scale + r0);
         const f32x4 s1v = *reinterpret_cast<const f32x4*>(scale + r0 + 4);
-        const f32x4 g0v = *reinterpret_cast<const f32x4*>(Gk + r0);
-        const f32x4 g1v = *reinterpret_cast<const f32x4*>(Gk + r0 + 4);
+        const f32x4 g0v = *reinterpret_cast<const f32x4*>(Gk + (r0 ^ swk));
+        const f32x4 g1v = *reinterpret_cast<const f32x4*>(Gk + (r0 ^ swk) + 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           o.x[j] = to_f(xv[j]);
@@ -466,7 +475,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         if constexpr (VJ::KPL == 8) {
           const int sb = s0 + g * 8;
           const Rows8 v = rows8(kq, rk, sb);
-          const float gb = Gk[b0];
+          const float gb = Gk[b0 ^ swk];
           fb = VJ::make([&](int j) {
             return sb + j < s_hi ? v.x[j] * v.sc[j] * VJ::ex(gb - v.G[j]) : TG(0);
           });
@@ -511,7 +520,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
             // u is 0, 8, 16 or 24: rows c0 + (u & 15) .. + 7 of kh (u < 16) or qh
             const int rb = c0 + (u & 15);
             const Rows8 v = u < 16 ? rows8(kq, rk, rb) : rows8(qk, rqs, rb);
-            const float gc = Gk[c0];
+            const float gc = Gk[c0 ^ swk];
             fb = VJ::make([&](int j) { return v.x[j] * v.sc[j] * VJ::ex(v.G[j] - gc); });
           } else {
             fb = VJ::make([&](int j) {
@@ -563,8 +572,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int r = 16 * m + 4 * g + rr;
-      const float pq = sum16(to_f(qT[kk * LDQ + r]) * rq[r] * aq[jm][rr]);
-      const float pk = sum16(to_f(kT[kk * LDQ + r]) * rk[r] * ak[jm][rr]);
+      const float pq = sum16(to_f(qT[kk * LDQ + (r ^ swk)]) * rq[r] * aq[jm][rr]);
+      const float pk = sum16(to_f(kT[kk * LDQ + (r ^ swk)]) * rk[r] * ak[jm][rr]);
       if (i == 0) {
         rowp[0][kb][r] = pq;
         rowp[1][kb][r] = pk;
@@ -572,7 +581,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     }
     // row C-1 holds G_c: add sum_r kg*dkg over all row groups and gamma * (h . dh')
     if (m == NB - 1 && g == 3) {
-      const GV Gc = GT[kk * LDG + C - 1];
+      const GV Gc = GT[kk * LDG + ((C - 1) ^ swk)];
       TG cs = 0;
 #pragma unroll
       for (int hh = 0; hh < SPLIT; ++hh) cs += csum[hh][kb][i];
@@ -665,8 +674,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         const int r = 16 * m + 4 * g + rr;
         if (r < L.len) {
           const float qd = rsum[0][r], kd = rsum[1][r];
-          const float qbar = to_f(qT[kk * LDQ + r]) * rq[r];
-          const float khat_ = to_f(kT[kk * LDQ + r]) * rk[r];
+          const float qbar = to_f(qT[kk * LDQ + (r ^ swk)]) * rq[r];
+          const float khat_ = to_f(kT[kk * LDQ + (r ^ swk)]) * rk[r];
           dqo[r * ts + kk] = from_f<TI>(rqs[r] * (aq[jm][rr] - qbar * qd));
           dko[r * ts + kk] = from_f<TI>(rk[r] * (ak[jm][rr] - khat_ * kd));
         }
