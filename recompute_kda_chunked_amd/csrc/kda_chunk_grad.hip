@@ -469,7 +469,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       //   raw[r] = sum_s dX[r][s] * kh_s exp(G_b - G_s)
       typename VJ::acc rq_ = VJ::zero(), rk_ = VJ::zero();
       const int s_hi = 16 * (I + 1);
-#pragma unroll 1
+#pragma unroll
       for (int s0 = 0; s0 < (s_hi + VJ::KS - 1) / VJ::KS * VJ::KS; s0 += VJ::KS) {
         typename VJ::frag fb;
         if constexpr (VJ::KPL == 8) {
@@ -507,11 +507,11 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       // u < 16 and (dAqk, qh) above:  y[s] = sum_r dX[r][s] * a_r exp(G_r - G_b)
       const int J = I;
       TG cc[4] = {0, 0, 0, 0}, gs[4] = {0, 0, 0, 0};
-#pragma unroll 1
+#pragma unroll
       for (int I2 = J; I2 < NB; ++I2) {
         const int c0 = 16 * I2;
         typename VJ::acc y = VJ::zero();
-#pragma unroll 1
+#pragma unroll
         for (int u0 = 0; u0 < 32; u0 += VJ::KS) {
           const int u = u0 + g * VJ::KPL;
           const OpT* ap = (u < 16 ? dXkT : dXqT) + (16 * J + i) * LDX + c0 + (u & 15);
