@@ -136,30 +136,44 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
   }
   auto G = [&](int r, int kk) -> GV& { return Gs[r * LDG + kk]; };
   prologue_rows<TI, D, C, 4>(d, in, h, L, rq, rqs, rk, be, G);
-  __syncthreads();
-  cumsum_rows<D, C, 256>(G, ptot);
 
-  // ---- gated products P (= Akk / beta) and Aqk, 16x16 block pairs
-  for (int p = w; p < NB * (NB + 1) / 2; p += 4) {
-    int I = 0, J = p;
-    while (J > I) { J -= I + 1; ++I; }
-    const int ra = 16 * I + i, rb = 16 * J + i;
-    // Raw rows for every k-step, all in flight together. Rows past the chunk's
-    // end read the last valid row; their scales rqs / rk are zero.
-    const int rac = ra < L.len ? ra : L.len - 1, rbc = rb < L.len ? rb : L.len - 1;
-    constexpr int NKS = K / KS;
+  // ---- gated products P (= Akk / beta) and Aqk, 16x16 block pairs. Wave w
+  // takes pairs w, w + 4, ...; the raw rows of its next pair are loaded while
+  // the current one is computed (two register sets), and those of its first
+  // pair while the cumulative sum runs.
+  constexpr int NPAIR = NB * (NB + 1) / 2, PPW = (NPAIR + 3) / 4, NKS = K / KS;
+  struct PairRows {
     typename M::frag xa[NKS], xk[NKS], xb[NKS];
+  };
+  auto pair_blocks = [](int p, int& I, int& J) {
+    I = 0;
+    J = p;
+    while (J > I) { J -= I + 1; ++I; }
+  };
+  // Rows past the chunk's end read the last valid row (their scales rqs / rk
+  // are zero); a pair index past the last pair loads the last pair again
+  // (unused), so the loads are unconditional.
+  auto load_pair = [&](PairRows& f, int p) {
+    int I, J;
+    pair_blocks(p < NPAIR ? p : NPAIR - 1, I, J);
+    const int ra = 16 * I + i, rb = 16 * J + i;
+    const int rac = ra < L.len ? ra : L.len - 1, rbc = rb < L.len ? rb : L.len - 1;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int kk = ks * KS + g * KPL;
-      xa[ks] = M::load(qr + rac * ts + kk);
-      xk[ks] = M::load(kr + rac * ts + kk);
-      xb[ks] = M::load(kr + rbc * ts + kk);
+      f.xa[ks] = M::load(qr + rac * ts + kk);
+      f.xk[ks] = M::load(kr + rac * ts + kk);
+      f.xb[ks] = M::load(kr + rbc * ts + kk);
     }
-    auto el = [](const typename M::frag& f, int j) -> float {
-      if constexpr (KPL == 1) return to_f(f);
-      else return to_f(f[j]);
-    };
+  };
+  auto el = [](const typename M::frag& f, int j) -> float {
+    if constexpr (KPL == 1) return to_f(f);
+    else return to_f(f[j]);
+  };
+  auto do_pair = [&](const PairRows& f, int p) {
+    int I, J;
+    pair_blocks(p, I, J);
+    const int ra = 16 * I + i, rb = 16 * J + i;
     const float sq = rqs[ra], sk = rk[ra], sb = rk[rb];
     f32x4 accP = zero4(), accQ = zero4();
 #pragma unroll
@@ -172,9 +186,9 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
         ea[j] = kexp<OpT>(Gs[ra * LDG + kk + j] - gb);
         eb[j] = kexp<OpT>(gb - Gs[rb * LDG + kk + j]);
       }
-      const auto fq = M::make([&](int j) { return el(xa[ks], j) * sq * ea[j]; });
-      const auto fk = M::make([&](int j) { return el(xk[ks], j) * sk * ea[j]; });
-      const auto fb = M::make([&](int j) { return el(xb[ks], j) * sb * eb[j]; });
+      const auto fq = M::make([&](int j) { return el(f.xa[ks], j) * sq * ea[j]; });
+      const auto fk = M::make([&](int j) { return el(f.xk[ks], j) * sk * ea[j]; });
+      const auto fb = M::make([&](int j) { return el(f.xb[ks], j) * sb * eb[j]; });
       accP = M::mma(fk, fb, accP);
       accQ = M::mma(fq, fb, accQ);
     }
@@ -184,6 +198,18 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
       Ms[r * LDM + s] = (s < r) ? accP[rr] : 0.f;
       As[r * LDM + s] = (s <= r) ? accQ[rr] : 0.f;
     }
+  };
+  PairRows pa, pb;
+  load_pair(pa, w);
+  __syncthreads();
+  cumsum_rows<D, C, 256>(G, ptot);
+#pragma unroll
+  for (int it = 0; it < PPW; ++it) {
+    const int p = w + 4 * it;
+    PairRows& cur = (it & 1) ? pb : pa;
+    PairRows& nxt = (it & 1) ? pa : pb;
+    if (it + 1 < PPW) load_pair(nxt, p + 4);
+    if (p < NPAIR) do_pair(cur, p);
   }
   __syncthreads();
 

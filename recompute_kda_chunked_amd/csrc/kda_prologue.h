@@ -136,6 +136,14 @@ __device__ __forceinline__ void prologue_load(const Dims& d, const Inputs& in, i
   const TI* k = static_cast<const TI*>(in.k) + L.t0 * ts + hoff;
   const TI* x = static_cast<const TI*>(in.g) + L.t0 * ts + hoff;
   const TI* rb = static_cast<const TI*>(in.beta) + L.t0 * d.H + h;
+  // the per-head parameters first: the arithmetic needs them with the first row
+  p.alog = in.A_log[h];
+#pragma unroll
+  for (int j = 0; j < P::VE; j += 4) {
+    const f32x4 b4 = *reinterpret_cast<const f32x4*>(in.dt_bias + static_cast<size_t>(h) * D + c0 + j);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) p.db[j + jj] = b4[jj];
+  }
 #pragma unroll
   for (int it = 0; it < P::NIT; ++it) {
     const int r = (w + NW * it) * P::RPI + rsub;
@@ -144,13 +152,6 @@ __device__ __forceinline__ void prologue_load(const Dims& d, const Inputs& in, i
     p.kv[it] = *reinterpret_cast<const VT*>(k + rc * ts);
     p.xv[it] = *reinterpret_cast<const VT*>(x + rc * ts);
     p.bv[it] = load_bits<TI>(rb + static_cast<size_t>(rc) * d.H);
-  }
-  p.alog = in.A_log[h];
-#pragma unroll
-  for (int j = 0; j < P::VE; j += 4) {
-    const f32x4 b4 = *reinterpret_cast<const f32x4*>(in.dt_bias + static_cast<size_t>(h) * D + c0 + j);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) p.db[j + jj] = b4[jj];
   }
 }
 
