@@ -94,7 +94,7 @@ struct TileT<float, D, C> {
 };
 
 template <typename TI, typename OpT, int D, int C, bool BWD>
-__global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_begin,
+__global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int seg_begin,
                                                      ChunkOps ops) {
   using M = Mma<OpT>;
   constexpr int K = D, V = D, NB = C / 16, KPL = M::KPL, KS = M::KS;
@@ -199,35 +199,16 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
       As[r * LDM + s] = (s <= r) ? accQ[rr] : 0.f;
     }
   };
-  PairRows pa, pb;
-  load_pair(pa, w);
-  __syncthreads();
-  cumsum_rows<D, C, 256>(G, ptot);
-#pragma unroll
-  for (int it = 0; it < PPW; ++it) {
-    const int p = w + 4 * it;
-    PairRows& cur = (it & 1) ? pb : pa;
-    PairRows& nxt = (it & 1) ? pa : pb;
-    if (it + 1 < PPW) load_pair(nxt, p + 4);
-    if (p < NPAIR) do_pair(cur, p);
-  }
-  __syncthreads();
-
-  // ---- outputs that leave before the inverse: Aqk (or its transpose), P,
-  // gamma, then one pass over (row pair, VE channels) items computing every
-  // gated element-wise operand from vector loads of q, k, v:
-  //   qg = qh e^G, kg = kh e^{G_c - G}, Kb = beta kh e^G, Bv = beta v
-  // Row-major ones are stored directly; transposed ones are staged in LDS
-  // (row pairs packed) and leave as contiguous vectors, or stay as the
-  // operands of W and U.
+  // ---- the element-wise pass after the pairs works on (row pair, VE
+  // channels) items read as vectors of q, k, v; in the forward layout those
+  // loads are issued with the wave's last pair, so they arrive while the
+  // pairs finish (the backward layout keeps more registers live and issues
+  // them after the pairs: holding them longer would halve its occupancy)
   typedef typename Vec16<TI>::T VT;
   constexpr int VE = 16 / sizeof(TI), LPR = D / VE;
   constexpr int NITEM = (C / 2) * LPR, IPT = (NITEM + 255) / 256;
-  // staged values per item: [0] kg (both), [1] Kb, [2] Bv, [3] qg (backward)
-  constexpr int NSV = BWD ? 4 : 3;
-  float sv[IPT][NSV][2][VE];
-  {
-    VT xq[IPT][2], xk[IPT][2], xv[IPT][2];
+  VT xq[IPT][2], xk[IPT][2], xv[IPT][2];
+  auto load_items = [&]() {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       const int item = tid + 256 * it, rp = item / LPR, c0 = (item % LPR) * VE;
@@ -242,6 +223,35 @@ __global__ void __launch_bounds__(256) k_chunk_local(Dims d, Inputs in, int seg_
         xv[it][h2] = *reinterpret_cast<const VT*>(vr + rc * ts + cc);
       }
     }
+  };
+
+  PairRows pa, pb;
+  load_pair(pa, w);
+  __syncthreads();
+  cumsum_rows<D, C, 256>(G, ptot);
+#pragma unroll
+  for (int it = 0; it < PPW; ++it) {
+    const int p = w + 4 * it;
+    PairRows& cur = (it & 1) ? pb : pa;
+    PairRows& nxt = (it & 1) ? pa : pb;
+    if (it + 1 < PPW) load_pair(nxt, p + 4);
+    else if (!BWD) load_items();
+    if (p < NPAIR) do_pair(cur, p);
+  }
+  __syncthreads();
+  if (BWD) load_items();
+
+  // ---- outputs that leave before the inverse: Aqk (or its transpose), P,
+  // gamma, then one pass over the items computing every gated element-wise
+  // operand:
+  //   qg = qh e^G, kg = kh e^{G_c - G}, Kb = beta kh e^G, Bv = beta v
+  // Row-major ones are stored directly; transposed ones are staged in LDS
+  // (row pairs packed) and leave as contiguous vectors, or stay as the
+  // operands of W and U.
+  // staged values per item: [0] kg (both), [1] Kb, [2] Bv, [3] qg (backward)
+  constexpr int NSV = BWD ? 4 : 3;
+  float sv[IPT][NSV][2][VE];
+  {
     // stores of this phase follow all of its loads (loads and stores share one
     // completion counter)
     {
