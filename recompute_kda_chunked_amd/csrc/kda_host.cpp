@@ -101,8 +101,12 @@ Plan make_plan(const kda_problem* p, bool bwd) {
   const size_t per = (bwd ? bwd_ops_per(P) : fwd_ops_per(P)) * P.H;
   int seg = p->seg_chunks;
   if (seg <= 0) {
+    // the fewest segments that fit the budget, then equal segment lengths
+    // (no short last segment: every launch fills the same number of rounds)
     const size_t fit = budget_bytes() / per;
-    seg = static_cast<int>(fit < 1 ? 1 : (fit > static_cast<size_t>(P.NC) ? P.NC : fit));
+    const int cap = static_cast<int>(fit < 1 ? 1 : (fit > static_cast<size_t>(P.NC) ? P.NC : fit));
+    const int ns = (P.NC + cap - 1) / cap;
+    seg = (P.NC + ns - 1) / ns;
   }
   if (seg > P.NC) seg = P.NC;
   if (seg < 1) seg = 1;
