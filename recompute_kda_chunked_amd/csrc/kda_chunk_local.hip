@@ -93,7 +93,10 @@ struct TileT<float, D, C> {
   }
 };
 
-template <typename TI, typename OpT, int D, int C, bool BWD>
+// BWD: backward layouts (AqkT, kg, qgT, WnT, TT, P as well). STATE (forward
+// layout only): just the operands of the state recurrence (Wn, U, kg^T,
+// gamma), for a pass that only carries the state.
+template <typename TI, typename OpT, int D, int C, bool BWD, bool STATE>
 __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int seg_begin,
                                                      ChunkOps ops) {
   using M = Mma<OpT>;
@@ -161,7 +164,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int kk = ks * KS + g * KPL;
-      f.xa[ks] = M::load(qr + rac * ts + kk);
+      if (!STATE) f.xa[ks] = M::load(qr + rac * ts + kk);
       f.xk[ks] = M::load(kr + rac * ts + kk);
       f.xb[ks] = M::load(kr + rbc * ts + kk);
     }
@@ -186,17 +189,19 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
         ea[j] = kexp<OpT>(Gs[ra * LDG + kk + j] - gb);
         eb[j] = kexp<OpT>(gb - Gs[rb * LDG + kk + j]);
       }
-      const auto fq = M::make([&](int j) { return el(f.xa[ks], j) * sq * ea[j]; });
       const auto fk = M::make([&](int j) { return el(f.xk[ks], j) * sk * ea[j]; });
       const auto fb = M::make([&](int j) { return el(f.xb[ks], j) * sb * eb[j]; });
       accP = M::mma(fk, fb, accP);
-      accQ = M::mma(fq, fb, accQ);
+      if (!STATE) {
+        const auto fq = M::make([&](int j) { return el(f.xa[ks], j) * sq * ea[j]; });
+        accQ = M::mma(fq, fb, accQ);
+      }
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int r = 16 * I + 4 * g + rr, s = 16 * J + i;
       Ms[r * LDM + s] = (s < r) ? accP[rr] : 0.f;
-      As[r * LDM + s] = (s <= r) ? accQ[rr] : 0.f;
+      if (!STATE) As[r * LDM + s] = (s <= r) ? accQ[rr] : 0.f;
     }
   };
   // ---- the element-wise pass after the pairs works on (row pair, VE
@@ -218,7 +223,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
         // their scales rqs, rk and beta are zero
         const int r = 2 * rp + h2, rc = (item < NITEM && r < L.len) ? r : L.len - 1;
         const int cc = item < NITEM ? c0 : 0;
-        xq[it][h2] = *reinterpret_cast<const VT*>(qr + rc * ts + cc);
+        if (!STATE) xq[it][h2] = *reinterpret_cast<const VT*>(qr + rc * ts + cc);
         xk[it][h2] = *reinterpret_cast<const VT*>(kr + rc * ts + cc);
         xv[it][h2] = *reinterpret_cast<const VT*>(vr + rc * ts + cc);
       }
@@ -254,12 +259,14 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   {
     // stores of this phase follow all of its loads (loads and stores share one
     // completion counter)
-    {
+    if (!STATE) {
       OpT* aq = static_cast<OpT*>(BWD ? ops.AqkT : ops.Aqk) + idx * C * C;
       for (int e = tid; e < C * C; e += 256) {
         const int a = e / C, b = e % C;
         aq[e] = from_f<OpT>(BWD ? As[b * LDM + a] : As[a * LDM + b]);
       }
+    }
+    {
       if (BWD) {
         OpT* P = static_cast<OpT*>(ops.P) + idx * C * C;
         for (int e = tid; e < C * C; e += 256) P[e] = from_f<OpT>(Ms[(e / C) * LDM + e % C]);
@@ -282,14 +289,14 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
           const GV gr = Gs[r * LDG + c0 + j];
           const float eG = kexp<OpT>(gr), eGc = kexp<OpT>(Gs[(C - 1) * LDG + c0 + j] - gr);
           const float kh = to_f(xk[it][h2][j]) * sk;
-          const float qg = to_f(xq[it][h2][j]) * sq * eG;
+          const float qg = STATE ? 0.f : to_f(xq[it][h2][j]) * sq * eG;
           sv[it][0][h2][j] = kh * eGc;
           sv[it][1][h2][j] = b * kh * eG;
           sv[it][2][h2][j] = b * to_f(xv[it][h2][j]);
           if (BWD) sv[it][NSV - 1][h2][j] = qg;
           out[j] = from_f<OpT>(BWD ? sv[it][0][h2][j] : qg);
         }
-        *reinterpret_cast<VT*>(rowm + r * K + c0) = out;
+        if (!STATE) *reinterpret_cast<VT*>(rowm + r * K + c0) = out;
       }
     }
   }
@@ -429,23 +436,26 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
 }
 
 template <typename TI, typename OpT, int D, int C>
-static hipError_t launch_cl(bool bwd, const Dims& d, const Inputs& in, int seg_begin,
+static hipError_t launch_cl(int mode, const Dims& d, const Inputs& in, int seg_begin,
                             int seg_chunks, const ChunkOps& ops, hipStream_t s) {
   const dim3 grid(seg_chunks * d.H), block(256);
-  if (bwd)
-    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, true>), grid, block, 0, s, d, in,
+  if (mode == KL_BWD)
+    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, true, false>), grid, block, 0, s, d, in,
+                       seg_begin, ops);
+  else if (mode == KL_STATE)
+    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, false, true>), grid, block, 0, s, d, in,
                        seg_begin, ops);
   else
-    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, false>), grid, block, 0, s, d, in,
+    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, false, false>), grid, block, 0, s, d, in,
                        seg_begin, ops);
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_local(int dtype, int D, int C, bool bwd, const Dims& d,
+hipError_t launch_chunk_local(int dtype, int D, int C, int mode, const Dims& d,
                               const Inputs& in, int seg_begin, int seg_chunks,
                               const ChunkOps& ops, hipStream_t s) {
 #define KDA_CL(TI, DD, CC) \
-  if (D == DD && C == CC) return launch_cl<TI, TI, DD, CC>(bwd, d, in, seg_begin, seg_chunks, ops, s);
+  if (D == DD && C == CC) return launch_cl<TI, TI, DD, CC>(mode, d, in, seg_begin, seg_chunks, ops, s);
   if (dtype == 0) {
     KDA_CL(float, 64, 16) KDA_CL(float, 64, 32) KDA_CL(float, 64, 64)
     KDA_CL(float, 128, 16) KDA_CL(float, 128, 32)

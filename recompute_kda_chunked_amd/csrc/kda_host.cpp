@@ -310,7 +310,7 @@ int kda_fwd_ex(const kda_problem* p, const void* q, const void* k, const void* v
   KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
   for (int sg = 0; sg < P.NS; ++sg) {
     const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
-    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, false, d, in, c0, c1 - c0, ops, s));
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, KL_FWD, d, in, c0, c1 - c0, ops, s));
     KDA_TRY(KDA_KERNEL_SCAN_FWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops, o, nullptr, carry[sg & 1],
                             carry[(sg + 1) & 1], ss, s));
   }
@@ -385,13 +385,13 @@ int kda_bwd_ex(const kda_problem* p, const void* q, const void* k, const void* v
   // forward saved them)
   for (int sg = 0; !io->ckpt && sg + 1 < P.NS; ++sg) {
     const int c0 = sg * P.seg, c1 = c0 + P.seg;
-    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, false, d, in, c0, c1 - c0, ops_f, s));
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, KL_STATE, d, in, c0, c1 - c0, ops_f, s));
     KDA_TRY(KDA_KERNEL_SCAN_FWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_f, nullptr, nullptr,
                             ckpt + sg * slot, ckpt + (sg + 1) * slot, fwd_ss, s));
   }
   for (int sg = P.NS - 1; sg >= 0; --sg) {
     const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
-    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, true, d, in, c0, c1 - c0, ops_b, s));
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, KL_BWD, d, in, c0, c1 - c0, ops_b, s));
     // the recording scan writes no carry: the next segment's entering state is known
     KDA_TRY(KDA_KERNEL_SCAN_FWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_b, nullptr, &sts,
                             ckpt + sg * slot, nullptr, fwd_ss, s));

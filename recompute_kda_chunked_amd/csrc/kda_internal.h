@@ -71,7 +71,10 @@ hipError_t launch_chunk_table(const int32_t* cu, int N, int C, int32_t* coff, hi
 hipError_t launch_prologue(int dtype, int D, int C, const Dims& d, const Inputs& in,
                            int64_t n_chunks, float* qh, float* kh, float* beta, float* gcum,
                            hipStream_t s);
-hipError_t launch_chunk_local(int dtype, int D, int C, bool bwd, const Dims& d,
+// mode: KL_FWD (forward operand layout, for the output scan), KL_BWD
+// (backward layouts), KL_STATE (forward layout, state operands only).
+enum { KL_FWD = 0, KL_BWD = 1, KL_STATE = 2 };
+hipError_t launch_chunk_local(int dtype, int D, int C, int mode, const Dims& d,
                               const Inputs& in, int seg_begin, int seg_chunks,
                               const ChunkOps& ops, hipStream_t s);
 // Forward-direction scan over one segment. out_o != nullptr writes O;
