@@ -138,7 +138,10 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     As[e] = 0.f;
   }
   auto G = [&](int r, int kk) -> GV& { return Gs[r * LDG + kk]; };
-  prologue_rows<TI, D, C, 4>(d, in, h, L, rq, rqs, rk, be, G);
+  // the gate in GateUnits (base 2 for bf16): every exponential below is of a
+  // difference of these values
+  using GU = GateUnits<OpT>;
+  prologue_rows<TI, D, C, 4>(d, in, h, L, rq, rqs, rk, be, G, static_cast<GV>(GU::scale));
 
   // ---- gated products P (= Akk / beta) and Aqk, 16x16 block pairs. Wave w
   // takes pairs w, w + 4, ...; the raw rows of its next pair are loaded while
@@ -186,8 +189,8 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
         const GV gb = Gs[16 * I * LDG + kk + j];
-        ea[j] = kexp<OpT>(Gs[ra * LDG + kk + j] - gb);
-        eb[j] = kexp<OpT>(gb - Gs[rb * LDG + kk + j]);
+        ea[j] = GU::ex(Gs[ra * LDG + kk + j] - gb);
+        eb[j] = GU::ex(gb - Gs[rb * LDG + kk + j]);
       }
       const auto fk = M::make([&](int j) { return el(f.xk[ks], j) * sk * ea[j]; });
       const auto fb = M::make([&](int j) { return el(f.xb[ks], j) * sb * eb[j]; });
@@ -272,7 +275,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
         for (int e = tid; e < C * C; e += 256) P[e] = from_f<OpT>(Ms[(e / C) * LDM + e % C]);
       }
       float* gam = ops.gam + idx * K;
-      for (int kk = tid; kk < K; kk += 256) gam[kk] = kexp<OpT>(Gs[(C - 1) * LDG + kk]);
+      for (int kk = tid; kk < K; kk += 256) gam[kk] = GU::ex(Gs[(C - 1) * LDG + kk]);
     }
     OpT* rowm = static_cast<OpT*>(BWD ? ops.kg : ops.qg) + idx * C * K;
 #pragma unroll
@@ -287,7 +290,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
 #pragma unroll
         for (int j = 0; j < VE; ++j) {
           const GV gr = Gs[r * LDG + c0 + j];
-          const float eG = kexp<OpT>(gr), eGc = kexp<OpT>(Gs[(C - 1) * LDG + c0 + j] - gr);
+          const float eG = GU::ex(gr), eGc = GU::ex(Gs[(C - 1) * LDG + c0 + j] - gr);
           const float kh = to_f(xk[it][h2][j]) * sk;
           const float qg = STATE ? 0.f : to_f(xq[it][h2][j]) * sq * eG;
           sv[it][0][h2][j] = kh * eGc;

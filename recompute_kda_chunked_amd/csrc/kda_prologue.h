@@ -42,6 +42,21 @@ __device__ __forceinline__ float kexp<float>(double x) { return static_cast<floa
 template <>
 __device__ __forceinline__ float kexp<bf16>(float x) { return __expf(x); }
 
+// Units of the chunk-local kernel's cumulative gate. bf16 problems keep it in
+// base-2 units (G log2 e, summed from g log2 e), so each exponential of a
+// gate difference is a single v_exp_f32; fp32 problems keep natural units in
+// fp64 (see GateT).
+template <typename OpT>
+struct GateUnits {
+  static constexpr float scale = 1.4426950408889634f;
+  static __device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x); }
+};
+template <>
+struct GateUnits<float> {
+  static constexpr double scale = 1.0;
+  static __device__ __forceinline__ float ex(double x) { return static_cast<float>(exp(x)); }
+};
+
 template <typename T>
 __device__ __forceinline__ T sigmoid_t(T x);
 template <>
@@ -163,10 +178,12 @@ __device__ __forceinline__ void prologue_load(const Dims& d, const Inputs& in, i
 //   rqs[r] = scale * rq           (so qh = q * rqs)
 //   rk[r]  = 1/sqrt(|k|^2 + eps)  (kh = k * rk)
 //   be[r]  = sigmoid(raw_beta)
+// gscale multiplies every gate value written to G (1 for natural units).
 template <typename TI, int D, int C, int NW, class GRef>
 __device__ __forceinline__ void prologue_compute(const Dims& d, const ChunkLoc& L,
                                                  const ProRows<TI, D, C, NW>& p, float* rq,
-                                                 float* rqs, float* rk, float* be, GRef G) {
+                                                 float* rqs, float* rk, float* be, GRef G,
+                                                 typename GateT<TI>::T gscale = 1) {
   using P = ProRows<TI, D, C, NW>;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int sub = lane % P::LPR, rsub = lane / P::LPR, c0 = sub * P::VE;
@@ -190,7 +207,7 @@ __device__ __forceinline__ void prologue_compute(const Dims& d, const ChunkLoc& 
       for (int j = 0; j < P::VE; ++j) {
         // the gate map in the cumulative gate's precision
         const GV xb = static_cast<GV>(to_f(p.xv[it][j])) + static_cast<GV>(p.db[j]);
-        G(r, c0 + j) = valid ? gate_map<GV>(d.gate_mode, ea, xb, static_cast<GV>(d.lb)) : GV(0);
+        G(r, c0 + j) = valid ? gate_map<GV>(d.gate_mode, ea, xb, static_cast<GV>(d.lb)) * gscale : GV(0);
       }
       if (sub == 0) {
         const float a = valid ? 1.0f / sqrtf(sq + d.eps) : 0.f;
@@ -208,10 +225,11 @@ __device__ __forceinline__ void prologue_compute(const Dims& d, const ChunkLoc& 
 template <typename TI, int D, int C, int NW, class GRef>
 __device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, int h,
                                               const ChunkLoc& L, float* rq, float* rqs,
-                                              float* rk, float* be, GRef G) {
+                                              float* rk, float* be, GRef G,
+                                              typename GateT<TI>::T gscale = 1) {
   ProRows<TI, D, C, NW> p;
   prologue_load<TI, D, C, NW>(d, in, h, L, p);
-  prologue_compute<TI, D, C, NW>(d, L, p, rq, rqs, rk, be, G);
+  prologue_compute<TI, D, C, NW>(d, L, p, rq, rqs, rk, be, G, gscale);
 }
 
 // In-place inclusive cumulative sum over the C rows of every channel k of
