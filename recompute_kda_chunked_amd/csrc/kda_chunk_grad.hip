@@ -377,8 +377,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       uint32_t pv[4];  // raw: converted at use
 #pragma unroll
       for (int j = 0; j < NKV; ++j) {
-        fu[j] = M::load(Ug + (16 * ns + i) * V + j * KS + g * KPL);
-        fw[j] = M::load(Wng + (16 * ns + i) * K + j * KS + g * KPL);
+        fu[j] = M::load(Ug + FragMajor<OpT>::frag(ns, j, V, lane));  // both fragment-major
+        fw[j] = M::load(Wng + FragMajor<OpT>::frag(ns, j, K, lane));
       }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) pv[rr] = load_bits<OpT>(Pg + (16 * m + 4 * g + rr) * C + 16 * ns + i);

@@ -32,8 +32,8 @@ namespace kda {
 
 // A [D][C] tile (channel rows, chunk-row columns) staged in LDS: written as
 // packed row pairs by the element-wise pass, read as MFMA operand fragments
-// (KPL consecutive chunk rows of one channel) or drained to memory as
-// contiguous vectors.
+// (KPL consecutive chunk rows of one channel) or drained to memory in
+// fragment-major order (contiguous vectors).
 template <typename OpT, int D, int C>
 struct TileT;
 
@@ -64,11 +64,13 @@ struct TileT<bf16, D, C> {
   static __device__ __forceinline__ bf16x8 frag(const bf16* t, int kk, int s) {
     return *reinterpret_cast<const bf16x8*>(t + off(kk, s));
   }
+  // slot e of the fragment-major [D][C] array: channel 16 rb + (e & 15),
+  // rows sf * 32 + 8 * ((e >> 4) & 3) .. + 7
   static __device__ __forceinline__ void drain(const bf16* t, bf16* dst, int tid) {
     for (int e = tid; e < D * NU; e += 256) {
-      const int kk = e / NU, u = e % NU;
-      *reinterpret_cast<bf16x8*>(dst + kk * C + 8 * u) =
-          *reinterpret_cast<const bf16x8*>(t + kk * C + 8 * (u ^ swz(kk)));
+      const int blk = e >> 6, lane = e & 63;
+      const int kk = 16 * (blk / (C / 32)) + (lane & 15), s = 32 * (blk % (C / 32)) + 8 * (lane >> 4);
+      *reinterpret_cast<bf16x8*>(dst + 8 * e) = frag(t, kk, s);
     }
   }
 };
@@ -84,11 +86,14 @@ struct TileT<float, D, C> {
     t[kk * LD + s + 1] = b;
   }
   static __device__ __forceinline__ float frag(const float* t, int kk, int s) { return t[kk * LD + s]; }
+  // fragment-major [D][C]: element 4 e + q is channel 16 rb + (4 e + q) % 16,
+  // row 4 sf + ((4 e) >> 4) % 4, four consecutive channels per vector
   static __device__ __forceinline__ void drain(const float* t, float* dst, int tid) {
     for (int e = tid; e < D * C / 4; e += 256) {
-      const int kk = e / (C / 4), s = 4 * (e % (C / 4));
+      const int blk = e >> 4, l0 = (4 * e) & 63;
+      const int kk = 16 * (blk / (C / 4)) + (l0 & 15), s = 4 * (blk % (C / 4)) + (l0 >> 4);
       const float* src = t + kk * LD + s;
-      *reinterpret_cast<f32x4*>(dst + kk * C + s) = f32x4{src[0], src[1], src[2], src[3]};
+      *reinterpret_cast<f32x4*>(dst + 4 * e) = f32x4{src[0], src[LD], src[2 * LD], src[3 * LD]};
     }
   }
 };
@@ -263,10 +268,13 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     // stores of this phase follow all of its loads (loads and stores share one
     // completion counter)
     if (!STATE) {
-      OpT* aq = static_cast<OpT*>(BWD ? ops.AqkT : ops.Aqk) + idx * C * C;
-      for (int e = tid; e < C * C; e += 256) {
-        const int a = e / C, b = e % C;
-        aq[e] = from_f<OpT>(BWD ? As[b * LDM + a] : As[a * LDM + b]);
+      // fragment-major, one lane slot (KPL elements of row a) per thread
+      typedef typename M::frag F;
+      F* aq = reinterpret_cast<F*>(static_cast<OpT*>(BWD ? ops.AqkT : ops.Aqk) + idx * C * C);
+      for (int e = tid; e < C * C / KPL; e += 256) {
+        const int blk = e >> 6, lane = e & 63;
+        const int a = 16 * (blk / (C / KS)) + (lane & 15), b = KS * (blk % (C / KS)) + KPL * (lane >> 4);
+        aq[e] = M::make([&](int j) { return BWD ? As[(b + j) * LDM + a] : As[a * LDM + b + j]; });
       }
     }
     {
@@ -299,7 +307,17 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
           if (BWD) sv[it][NSV - 1][h2][j] = qg;
           out[j] = from_f<OpT>(BWD ? sv[it][0][h2][j] : qg);
         }
-        if (!STATE) *reinterpret_cast<VT*>(rowm + r * K + c0) = out;
+        if (!STATE) {
+          // fragment-major [C][K]: the VE channels are one lane slot (bf16)
+          // or VE slots 16 apart (fp32)
+          OpT* dst = rowm + FragMajor<OpT>::off(r, c0, K);
+          if constexpr (VE == KPL) {
+            *reinterpret_cast<VT*>(dst) = out;
+          } else {
+#pragma unroll
+            for (int j = 0; j < VE; ++j) dst[16 * j] = out[j];
+          }
+        }
       }
     }
   }
@@ -420,19 +438,14 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
       }
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        // acc[n][rr] = W[16n + i][16mk + 4g + rr]
-        OpT* dst = Wn + (16 * n + i) * K + 16 * mk + 4 * g;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(-acc[n][rr]);
+        // acc[n][rr] = W[16n + i][16mk + 4g + rr]; all three fragment-major
+        store4_fm<OpT>(Wn, 16 * n + i, 16 * mk + 4 * g, K, -acc[n]);
         if (BWD) {
           // acc2[n][rr] = W[16n + 4g + rr][16mk + i]  ->  WnT[k][r..r+3]
-          OpT* dT = static_cast<OpT*>(ops.WnT) + idx * K * C + (16 * mk + i) * C + 16 * n + 4 * g;
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) dT[rr] = from_f<OpT>(-acc2[n][rr]);
+          store4_fm<OpT>(static_cast<OpT*>(ops.WnT) + idx * K * C, 16 * mk + i, 16 * n + 4 * g, C,
+                         -acc2[n]);
         }
-        OpT* du = static_cast<OpT*>(ops.U) + idx * C * V + (16 * n + i) * V + 16 * mk + 4 * g;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) du[rr] = from_f<OpT>(accu[n][rr]);
+        store4_fm<OpT>(static_cast<OpT*>(ops.U) + idx * C * V, 16 * n + i, 16 * mk + 4 * g, V, accu[n]);
       }
     }
   }

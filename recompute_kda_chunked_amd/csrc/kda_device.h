@@ -173,6 +173,51 @@ __device__ __forceinline__ void store4(T* p, const f32x4& v) {
   }
 }
 
+// Fragment-major operand arrays. An [R][S] matrix that is read as MFMA
+// operand fragments (rows in blocks of 16, the reduction dimension S in
+// pieces of KS) is stored one fragment after another: fragment (rb, sf) is
+// 64 lane slots of KPL elements, slot (i, g) = i + 16 g holding row 16 rb + i,
+// columns sf KS + g KPL .. + KPL - 1. A wave's fragment load is then one
+// contiguous run of 64 KPL elements instead of 16 strided row pieces.
+// R is a multiple of 16 and S of KS.
+template <typename OpT>
+struct FragMajor {
+  using M = Mma<OpT>;
+  // element (r, s)
+  static __device__ __forceinline__ int off(int r, int s, int S) {
+    return (((r >> 4) * (S / M::KS) + s / M::KS) * 64 + (r & 15) + 16 * ((s % M::KS) / M::KPL)) *
+               M::KPL + s % M::KPL;
+  }
+  // the lane's slot of fragment (rb, sf)
+  static __device__ __forceinline__ int frag(int rb, int sf, int S, int lane) {
+    return ((rb * (S / M::KS) + sf) * 64 + lane) * M::KPL;
+  }
+  // elements (r, s0 .. s0 + 3), s0 a multiple of 4: contiguous for bf16
+  // (within one slot), 16 slots apart for fp32
+  static constexpr int kStep4 = M::KPL >= 4 ? 1 : 16;
+};
+
+template <typename OpT>
+__device__ __forceinline__ void store4_fm(OpT* a, int r, int s0, int S, const f32x4& v) {
+  OpT* p = a + FragMajor<OpT>::off(r, s0, S);
+  if constexpr (FragMajor<OpT>::kStep4 == 1) {
+    store4<OpT>(p, v);
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) p[16 * rr] = v[rr];
+  }
+}
+template <typename OpT>
+__device__ __forceinline__ void load4_fm_raw(const OpT* a, int r, int s0, int S, uint32_t (&u)[4]) {
+  const OpT* p = a + FragMajor<OpT>::off(r, s0, S);
+  if constexpr (FragMajor<OpT>::kStep4 == 1) {
+    load4_raw<OpT>(p, u);
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) u[rr] = __float_as_uint(p[16 * rr]);
+  }
+}
+
 // acc += sum_{kk in [k_lo, k_hi)} A[i][kk] * B[i'][kk] for one 16x16 tile.
 // A and B point at the first row of the tile; lda/ldb are row strides in
 // elements. k_lo and k_hi - k_lo are multiples of Mma<OpT>::KS.

@@ -26,7 +26,9 @@ struct Inputs {
 // Per-(chunk, head) operands produced by the chunk-local kernel for one
 // segment; element (lc, h) of each array is at index lc * H + h where lc is
 // the chunk index relative to the segment start. Operand element type is
-// bf16 for bf16 problems and fp32 for fp32 problems.
+// bf16 for bf16 problems and fp32 for fp32 problems. Wn, U, qg, kgT, Aqk,
+// AqkT, kg, qgT and WnT are stored fragment-major (FragMajor in
+// kda_device.h); TT and P are row-major.
 struct ChunkOps {
   void *Wn;    // [C][K]  -W  (W = T (beta * kh * e^G))
   void *U;     // [C][V]  U = T (beta * v)

@@ -73,30 +73,34 @@ struct FwdOps {
   float gm[G::MKW];           // gamma at the lane's key channel of each row block
 };
 
+// The chunk operands are fragment-major (FragMajor): each fragment load below
+// is one contiguous 64-slot run.
 template <typename OpT, int D, int C, int BV, bool OUT_O, bool REC>
 __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const ChunkOps& ops,
                                              size_t idx, int v0, int w, int i, int g) {
   using G = ScanGeo<OpT, D, C, BV>;
   using M = typename G::M;
+  using FM = FragMajor<OpT>;
   constexpr int K = G::K, V = G::V;
+  const int lane = i + 16 * g;
   {
     // waves past the last row block (C < 64) load that block's rows again and
     // leave them unused: the loads stay unconditional
     const int m = w < G::NB ? w : G::NB - 1;
-    const OpT* Wn = static_cast<const OpT*>(ops.Wn) + idx * C * K + (16 * m + i) * K + g * M::KPL;
+    const OpT* Wn = static_cast<const OpT*>(ops.Wn) + idx * C * K;
 #pragma unroll
-    for (int j = 0; j < G::NKF; ++j) f.w[j] = M::load(Wn + j * M::KS);
+    for (int j = 0; j < G::NKF; ++j) f.w[j] = M::load(Wn + FM::frag(m, j, K, lane));
     if (OUT_O) {
-      const OpT* qg = static_cast<const OpT*>(ops.qg) + idx * C * K + (16 * m + i) * K + g * M::KPL;
+      const OpT* qg = static_cast<const OpT*>(ops.qg) + idx * C * K;
 #pragma unroll
-      for (int j = 0; j < G::NKF; ++j) f.q[j] = M::load(qg + j * M::KS);
-      const OpT* aq = static_cast<const OpT*>(ops.Aqk) + idx * C * C + (16 * m + i) * C + g * M::KPL;
+      for (int j = 0; j < G::NKF; ++j) f.q[j] = M::load(qg + FM::frag(m, j, K, lane));
+      const OpT* aq = static_cast<const OpT*>(ops.Aqk) + idx * C * C;
 #pragma unroll
-      for (int j = 0; j < G::NCF; ++j) f.a[j] = M::load(aq + j * M::KS);
+      for (int j = 0; j < G::NCF; ++j) f.a[j] = M::load(aq + FM::frag(m, j, C, lane));
     }
-    const OpT* U = static_cast<const OpT*>(ops.U) + idx * C * V + (16 * m + i) * V + v0 + 4 * g;
+    const OpT* U = static_cast<const OpT*>(ops.U) + idx * C * V;
 #pragma unroll
-    for (int nv = 0; nv < G::BVT; ++nv) load4_raw<OpT>(U + 16 * nv, f.u[nv]);
+    for (int nv = 0; nv < G::BVT; ++nv) load4_fm_raw<OpT>(U, 16 * m + i, v0 + 16 * nv + 4 * g, V, f.u[nv]);
   }
   const OpT* kgT = static_cast<const OpT*>(ops.kgT) + idx * K * C;
   const float* gam = ops.gam + idx * K;
@@ -104,7 +108,7 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
   for (int jm = 0; jm < G::MKW; ++jm) {
     const int mk = w * G::MKW + jm;
 #pragma unroll
-    for (int j = 0; j < G::NCF; ++j) f.kt[jm][j] = M::load(kgT + (16 * mk + i) * C + j * M::KS + g * M::KPL);
+    for (int j = 0; j < G::NCF; ++j) f.kt[jm][j] = M::load(kgT + FM::frag(mk, j, C, lane));
     f.gm[jm] = gam[16 * mk + i];
   }
 }
@@ -295,15 +299,17 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
                                              int g) {
   using G = ScanGeo<OpT, D, C, BV>;
   using M = typename G::M;
+  using FM = FragMajor<OpT>;
   constexpr int K = G::K, V = G::V;
+  const int lane = i + 16 * g;
   {
     const int m = w < G::NB ? w : G::NB - 1;  // unconditional, as in the forward
-    const OpT* at = static_cast<const OpT*>(ops.AqkT) + idx * C * C + (16 * m + i) * C + g * M::KPL;
+    const OpT* at = static_cast<const OpT*>(ops.AqkT) + idx * C * C;
 #pragma unroll
-    for (int j = 0; j < G::NCF; ++j) f.at[j] = M::load(at + j * M::KS);
-    const OpT* kg = static_cast<const OpT*>(ops.kg) + idx * C * K + (16 * m + i) * K + g * M::KPL;
+    for (int j = 0; j < G::NCF; ++j) f.at[j] = M::load(at + FM::frag(m, j, C, lane));
+    const OpT* kg = static_cast<const OpT*>(ops.kg) + idx * C * K;
 #pragma unroll
-    for (int j = 0; j < G::NKF; ++j) f.kg[j] = M::load(kg + j * M::KS);
+    for (int j = 0; j < G::NKF; ++j) f.kg[j] = M::load(kg + FM::frag(m, j, K, lane));
   }
   const OpT* qgT = static_cast<const OpT*>(ops.qgT) + idx * K * C;
   const OpT* WnT = static_cast<const OpT*>(ops.WnT) + idx * K * C;
@@ -313,8 +319,8 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
     const int mk = w * G::MKW + jm;
 #pragma unroll
     for (int j = 0; j < G::NCF; ++j) {
-      f.qt[jm][j] = M::load(qgT + (16 * mk + i) * C + j * M::KS + g * M::KPL);
-      f.wt[jm][j] = M::load(WnT + (16 * mk + i) * C + j * M::KS + g * M::KPL);
+      f.qt[jm][j] = M::load(qgT + FM::frag(mk, j, C, lane));
+      f.wt[jm][j] = M::load(WnT + FM::frag(mk, j, C, lane));
     }
     f.gm[jm] = gam[16 * mk + i];
   }
