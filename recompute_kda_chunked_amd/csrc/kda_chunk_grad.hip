@@ -186,6 +186,12 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   static_assert(NB % TPW == 0, "a wave's tiles share one value block");
   typename M::frag fa[NKS], fb[TPW][NKS];
   uint32_t vin[TPW][4];
+  using FM = FragMajor<OpT>;
+  // vector e of the fragment-major Vn: VE elements in slot order, row
+  // vn_row(e), columns vn_col(e) .. + VE - 1 (bf16: one lane slot) or rows
+  // vn_row(e) .. + 3 of column vn_col(e) (fp32: four lane slots)
+  auto vn_row = [](int e) { const int sl = e * VE / KPL; return 16 * ((sl >> 6) / (V / KS)) + (sl & 15); };
+  auto vn_col = [](int e) { const int sl = e * VE / KPL; return KS * ((sl >> 6) % (V / KS)) + KPL * ((sl & 63) >> 4); };
   {
     const OpT* dVnT = static_cast<const OpT*>(st.dVnT) + idx * V * C;
     const OpT* TT = static_cast<const OpT*>(ops.TT) + idx * C * C;
@@ -196,12 +202,12 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       const int e0 = tid + NT * j, e = e0 < NV ? e0 : 0, r = e / NVR, c = (e % NVR) * VE;
       const int rc = r < L.len ? r : L.len - 1;
       ldo[j] = *reinterpret_cast<const VT*>(dOr + rc * ts + c);
-      ldn[j] = *reinterpret_cast<const VT*>(Vn + r * V + c);
+      ldn[j] = *reinterpret_cast<const VT*>(Vn + e * VE);
     }
     {
       const int t = w * TPW < T2 ? w * TPW : 0, mv = t / NB;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) fa[ks] = M::load(dVnT + (16 * mv + i) * C + ks * KS + g * KPL);
+      for (int ks = 0; ks < NKS; ++ks) fa[ks] = M::load(dVnT + FM::frag(mv, ks, C, lane));
     }
 #pragma unroll
     for (int jt = 0; jt < TPW; ++jt) {
@@ -210,7 +216,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
       // the whole reduction is taken (T^T[r][s] is stored as 0 for s < r)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) fb[jt][ks] = M::load(TT + (16 * nr + i) * C + ks * KS + g * KPL);
+      for (int ks = 0; ks < NKS; ++ks) fb[jt][ks] = M::load(TT + FM::frag(nr, ks, C, lane));
       load4_raw<TI>(vr + (r < L.len ? r : L.len - 1) * ts + vv, vin[jt]);
     }
   }
@@ -273,16 +279,23 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 #pragma unroll
         for (int q2 = 0; q2 < VE; ++q2) zo[q2] = r < L.len ? ldo[j][q2] : static_cast<TI>(0.f);
         *reinterpret_cast<VT*>(dO_s + r * LDA + c) = zo;
-        *reinterpret_cast<VT*>(Vn_s + r * LDA + c) = ldn[j];
+        const int rn = vn_row(e), cn = vn_col(e);
+        if constexpr (VE == KPL) {
+          *reinterpret_cast<VT*>(Vn_s + rn * LDA + cn) = ldn[j];
+        } else {
+#pragma unroll
+          for (int q2 = 0; q2 < VE; ++q2) Vn_s[(rn + q2) * LDA + cn] = ldn[j][q2];
+        }
       }
     }
     {
-      const OpT* bh = static_cast<const OpT*>(st.h) + idx * K * V + kk * V + g * KPL;
-      const OpT* bdh = static_cast<const OpT*>(st.dh) + idx * K * V + kk * V + g * KPL;
+      // rows kk of h and dh' (fragment-major [K][V])
+      const OpT* bh = static_cast<const OpT*>(st.h) + idx * K * V;
+      const OpT* bdh = static_cast<const OpT*>(st.dh) + idx * K * V;
 #pragma unroll
       for (int j = 0; j < NVS; ++j) {
-        fh[j] = M::load(bh + j * KS);
-        fdh[j] = M::load(bdh + j * KS);
+        fh[j] = M::load(bh + FM::frag(kb, j, V, lane));
+        fdh[j] = M::load(bdh + FM::frag(kb, j, V, lane));
       }
     }
     TI* dvo = dv + L.t0 * ts + hoff;

@@ -404,8 +404,14 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     Tb[r * LDT + s] = from_f<OpT>(Ts[r * LDM + s]);
   }
   if (BWD) {
-    OpT* TT = static_cast<OpT*>(ops.TT) + idx * C * C;
-    for (int e = tid; e < C * C; e += 256) TT[e] = from_f<OpT>(Ts[(e % C) * LDM + e / C]);
+    // T^T, fragment-major, one lane slot per thread
+    typedef typename M::frag F;
+    F* TT = reinterpret_cast<F*>(static_cast<OpT*>(ops.TT) + idx * C * C);
+    for (int e = tid; e < C * C / KPL; e += 256) {
+      const int blk = e >> 6, lane = e & 63;
+      const int a = 16 * (blk / (C / KS)) + (lane & 15), b = KS * (blk % (C / KS)) + KPL * (lane >> 4);
+      TT[e] = M::make([&](int j) { return Ts[(b + j) * LDM + a]; });
+    }
   }
   __syncthreads();
 

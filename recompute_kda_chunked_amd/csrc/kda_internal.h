@@ -27,8 +27,8 @@ struct Inputs {
 // segment; element (lc, h) of each array is at index lc * H + h where lc is
 // the chunk index relative to the segment start. Operand element type is
 // bf16 for bf16 problems and fp32 for fp32 problems. Wn, U, qg, kgT, Aqk,
-// AqkT, kg, qgT and WnT are stored fragment-major (FragMajor in
-// kda_device.h); TT and P are row-major.
+// AqkT, kg, qgT, WnT and TT are stored fragment-major (FragMajor in
+// kda_device.h); P is row-major.
 struct ChunkOps {
   void *Wn;    // [C][K]  -W  (W = T (beta * kh * e^G))
   void *U;     // [C][V]  U = T (beta * v)
@@ -47,7 +47,7 @@ struct ChunkOps {
 
 // States recorded by the backward scans for one segment, element (lc, h) at
 // lc * H + h: entering state h_n and leaving-state gradient dh'_n as [K][V],
-// Vn as [C][V], dVn^T as [V][C] (operand element type).
+// Vn as [C][V], dVn^T as [V][C] (operand element type, all fragment-major).
 struct SegStates {
   void *h, *dh, *Vn, *dVnT;
 };

@@ -193,10 +193,11 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
       next_ck += ss.ck_every;
     }
     if (REC) {
-      // entering state h_n as [K][V] (hoff adds the head's h * K * V)
-      OpT* hd = static_cast<OpT*>(st.h) + (idx - h) * K * V;
+      // entering state h_n, fragment-major [K][V]
+      OpT* hd = static_cast<OpT*>(st.h) + idx * K * V;
 #pragma unroll
-      for (int j = 0; j < HPW; ++j) store4<OpT>(hd + hoff(j), hs[j]);
+      for (int j = 0; j < HPW; ++j)
+        store4_fm<OpT>(hd, 16 * (w * MKW + j / BVT) + i, v0 + 16 * (j % BVT) + 4 * g, V, hs[j]);
     }
     // Vn = U - W h and the inter part qg h of O: row block m = w, all value
     // blocks, as transposed tiles: accV[rr] = Vn[16m + i][v0 + 16nv + 4g + rr]
@@ -218,7 +219,7 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) dst[rr * LDC] = from_f<OpT>(accV[rr]);
         if (REC)
-          store4<OpT>(static_cast<OpT*>(st.Vn) + idx * C * V + (16 * m + i) * V + v0 + 16 * nv + 4 * g, accV);
+          store4_fm<OpT>(static_cast<OpT*>(st.Vn) + idx * C * V, 16 * m + i, v0 + 16 * nv + 4 * g, V, accV);
       }
     }
     __syncthreads();
@@ -422,9 +423,11 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
       }
     }
     {
-      OpT* hd = static_cast<OpT*>(st.dh) + (idx - h) * K * V;  // hoff adds h * K * V
+      // dh', fragment-major [K][V]
+      OpT* hd = static_cast<OpT*>(st.dh) + idx * K * V;
 #pragma unroll
-      for (int j = 0; j < HPW; ++j) store4<OpT>(hd + hoff(j), hs[j]);
+      for (int j = 0; j < HPW; ++j)
+        store4_fm<OpT>(hd, 16 * (w * MKW + j / BVT) + i, v0 + 16 * (j % BVT) + 4 * g, V, hs[j]);
     }
     __syncthreads();
     if (w < NB) {
@@ -441,12 +444,10 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
 #pragma unroll
         for (int j = 0; j < G::NKF; ++j) acc = M::mma(cur.kg[j], M::load(bd + j * KS), acc);
         OpT* dst = dVnT_s + (16 * nv + i) * LDC + 16 * m + 4 * g;
-        OpT* gd = static_cast<OpT*>(st.dVnT) + idx * V * C + (v0 + 16 * nv + i) * C + 16 * m + 4 * g;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          dst[rr] = from_f<OpT>(acc[rr]);
-          gd[rr] = from_f<OpT>(acc[rr]);
-        }
+        for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(acc[rr]);
+        // dVn^T, fragment-major [V][C]
+        store4_fm<OpT>(static_cast<OpT*>(st.dVnT) + idx * V * C, v0 + 16 * nv + i, 16 * m + 4 * g, C, acc);
       }
     }
     __syncthreads();
