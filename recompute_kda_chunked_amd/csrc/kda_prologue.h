@@ -170,6 +170,34 @@ __device__ __forceinline__ void prologue_load(const Dims& d, const Inputs& in, i
   }
 }
 
+// The gate values of one row vector (VE channels) times gscale, in the
+// precision of GV; rows past the chunk's end (valid false) get 0. MODE is the
+// gate map (hoisted out of the row loop). For fp32 gates the smooth map is
+// evaluated as lb * gscale / (1 + 2^(c x + c b)) with c = -e^A log2 e, one
+// fused multiply-add, v_exp_f32 and v_rcp_f32 per channel.
+template <int MODE, typename TI, int VE, typename GV>
+__device__ __forceinline__ void gate_vec(const Dims& d, GV ea, const float* db,
+                                         const typename Vec16<TI>::T& xv, bool valid, GV gscale,
+                                         GV* out) {
+  if constexpr (MODE == 0 && sizeof(GV) == 4) {
+    const float c = -static_cast<float>(ea) * 1.4426950408889634f;
+    const float amp = d.lb * static_cast<float>(gscale);
+#pragma unroll
+    for (int j = 0; j < VE; ++j) {
+      const float t = __builtin_amdgcn_exp2f(fmaf(c, to_f(xv[j]), c * db[j]));
+      const float gv = amp * __builtin_amdgcn_rcpf(1.0f + t);
+      out[j] = valid ? gv : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < VE; ++j) {
+      const GV xb = static_cast<GV>(to_f(xv[j])) + static_cast<GV>(db[j]);
+      const GV gv = gate_map<GV>(MODE, ea, xb, static_cast<GV>(d.lb)) * gscale;
+      out[j] = valid ? gv : GV(0);
+    }
+  }
+}
+
 // The prologue's arithmetic on loaded rows: for each row the per-row scalars
 // and the gate value of each channel into G(r, k) (a functor returning a
 // reference into LDS). Rows r >= len are padding: q = k = 0, beta = 0, g = 0,
@@ -179,11 +207,11 @@ __device__ __forceinline__ void prologue_load(const Dims& d, const Inputs& in, i
 //   rk[r]  = 1/sqrt(|k|^2 + eps)  (kh = k * rk)
 //   be[r]  = sigmoid(raw_beta)
 // gscale multiplies every gate value written to G (1 for natural units).
-template <typename TI, int D, int C, int NW, class GRef>
-__device__ __forceinline__ void prologue_compute(const Dims& d, const ChunkLoc& L,
-                                                 const ProRows<TI, D, C, NW>& p, float* rq,
-                                                 float* rqs, float* rk, float* be, GRef G,
-                                                 typename GateT<TI>::T gscale = 1) {
+template <int MODE, typename TI, int D, int C, int NW, class GRef>
+__device__ __forceinline__ void prologue_compute_m(const Dims& d, const ChunkLoc& L,
+                                                   const ProRows<TI, D, C, NW>& p, float* rq,
+                                                   float* rqs, float* rk, float* be, GRef G,
+                                                   typename GateT<TI>::T gscale) {
   using P = ProRows<TI, D, C, NW>;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int sub = lane % P::LPR, rsub = lane / P::LPR, c0 = sub * P::VE;
@@ -203,12 +231,10 @@ __device__ __forceinline__ void prologue_compute(const Dims& d, const ChunkLoc& 
     sq = group_sum<P::LPR>(sq);
     sk = group_sum<P::LPR>(sk);
     if (r < C) {
+      GV gv[P::VE];
+      gate_vec<MODE, TI, P::VE, GV>(d, ea, p.db, p.xv[it], valid, gscale, gv);
 #pragma unroll
-      for (int j = 0; j < P::VE; ++j) {
-        // the gate map in the cumulative gate's precision
-        const GV xb = static_cast<GV>(to_f(p.xv[it][j])) + static_cast<GV>(p.db[j]);
-        G(r, c0 + j) = valid ? gate_map<GV>(d.gate_mode, ea, xb, static_cast<GV>(d.lb)) * gscale : GV(0);
-      }
+      for (int j = 0; j < P::VE; ++j) G(r, c0 + j) = gv[j];
       if (sub == 0) {
         const float a = valid ? 1.0f / sqrtf(sq + d.eps) : 0.f;
         const float b = valid ? 1.0f / sqrtf(sk + d.eps) : 0.f;
@@ -219,6 +245,17 @@ __device__ __forceinline__ void prologue_compute(const Dims& d, const ChunkLoc& 
       }
     }
   }
+}
+
+template <typename TI, int D, int C, int NW, class GRef>
+__device__ __forceinline__ void prologue_compute(const Dims& d, const ChunkLoc& L,
+                                                 const ProRows<TI, D, C, NW>& p, float* rq,
+                                                 float* rqs, float* rk, float* be, GRef G,
+                                                 typename GateT<TI>::T gscale = 1) {
+  if (d.gate_mode == 0)
+    prologue_compute_m<0, TI, D, C, NW>(d, L, p, rq, rqs, rk, be, G, gscale);
+  else
+    prologue_compute_m<1, TI, D, C, NW>(d, L, p, rq, rqs, rk, be, G, gscale);
 }
 
 // Both parts: loads, then arithmetic.
