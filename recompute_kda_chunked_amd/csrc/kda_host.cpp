@@ -152,13 +152,28 @@ size_t states_bytes(const Plan& P) {
 
 size_t state_slot(const Plan& P) { return up(static_cast<size_t>(P.H) * P.D * P.D * 4); }
 
+// The chunk table at the workspace start: chunk offsets [N+1] int32, then the
+// per-chunk locations [NC] int2.
+size_t table_bytes(const Plan& P) {
+  return up((P.N + 1) * 4) + up(static_cast<size_t>(P.NC > 0 ? P.NC : 1) * 8);
+}
+struct Table {
+  int32_t* coff;
+  int2* cloc;
+};
+Table carve_table(const Plan& P, unsigned char*& cur) {
+  Table t{reinterpret_cast<int32_t*>(cur), reinterpret_cast<int2*>(cur + up((P.N + 1) * 4))};
+  cur += table_bytes(P);
+  return t;
+}
+
 size_t fwd_bytes(const Plan& P) {
-  return up((P.N + 1) * 4) + 2 * state_slot(P) + ops_bytes(P, false);
+  return table_bytes(P) + 2 * state_slot(P) + ops_bytes(P, false);
 }
 
 size_t bwd_bytes(const Plan& P) {
   const size_t ops = ops_bytes(P, true) > ops_bytes(P, false) ? ops_bytes(P, true) : ops_bytes(P, false);
-  return up((P.N + 1) * 4) + up(static_cast<size_t>(P.NC) * P.H * (P.D + 1) * 8) +
+  return table_bytes(P) + up(static_cast<size_t>(P.NC) * P.H * (P.D + 1) * 8) +
          static_cast<size_t>(P.NS + 1) * state_slot(P) + 2 * state_slot(P) + ops + states_bytes(P);
 }
 
@@ -241,7 +256,7 @@ size_t kda_bwd_workspace_bytes(const kda_problem* p) {
 
 size_t kda_prologue_workspace_bytes(const kda_problem* p) {
   if (check_problem(p) != KDA_OK) return 0;
-  return up((p->n_seqs + 1) * 4);
+  return table_bytes(make_plan(p, false));
 }
 
 int kda_prologue(const kda_problem* p, const void* q, const void* k, const void* raw_g,
@@ -256,9 +271,10 @@ int kda_prologue(const kda_problem* p, const void* q, const void* k, const void*
   if (workspace_bytes < kda_prologue_workspace_bytes(p)) return KDA_ERR_WORKSPACE;
   const Plan P = make_plan(p, false);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t* coff = static_cast<int32_t*>(workspace);
-  Inputs in{q, k, nullptr, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, coff};
-  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
+  unsigned char* cur = static_cast<unsigned char*>(workspace);
+  const Table tb = carve_table(P, cur);
+  Inputs in{q, k, nullptr, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, tb.coff, tb.cloc};
+  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, P.NC, tb.coff, tb.cloc, s));
   if (P.NC > 0)
     KDA_TRY(KDA_KERNEL_PROLOGUE, static_cast<int64_t>(P.NC) * P.H, launch_prologue(P.dtype, P.D, P.C, make_dims(p), in, P.NC, qh, kh, beta, gcum, s));
   return KDA_OK;
@@ -297,8 +313,7 @@ int kda_fwd_ex(const kda_problem* p, const void* q, const void* k, const void* v
   const ScanStates ss{io->h0, io->ht, ck_every ? io->ckpt : nullptr, ck_every};
   hipStream_t s = static_cast<hipStream_t>(stream);
   unsigned char* cur = static_cast<unsigned char*>(workspace);
-  int32_t* coff = reinterpret_cast<int32_t*>(cur);
-  cur += up((P.N + 1) * 4);
+  const Table tb = carve_table(P, cur);
   float* carry[2];
   carry[0] = reinterpret_cast<float*>(cur);
   cur += state_slot(P);
@@ -306,8 +321,8 @@ int kda_fwd_ex(const kda_problem* p, const void* q, const void* k, const void* v
   cur += state_slot(P);
   const ChunkOps ops = carve_ops(P, false, cur);
   const Dims d = make_dims(p);
-  const Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, coff};
-  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
+  const Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, tb.coff, tb.cloc};
+  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, P.NC, tb.coff, tb.cloc, s));
   for (int sg = 0; sg < P.NS; ++sg) {
     const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
     KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, KL_FWD, d, in, c0, c1 - c0, ops, s));
@@ -347,8 +362,7 @@ int kda_bwd_ex(const kda_problem* p, const void* q, const void* k, const void* v
   const ScanStates bwd_ss{io->dht, io->dh0, nullptr, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
   unsigned char* cur = static_cast<unsigned char*>(workspace);
-  int32_t* coff = reinterpret_cast<int32_t*>(cur);
-  cur += up((P.N + 1) * 4);
+  const Table tb = carve_table(P, cur);
   double* partials = reinterpret_cast<double*>(cur);
   cur += up(static_cast<size_t>(P.NC) * P.H * (P.D + 1) * 8);
   // state entering each segment (slot sg); the forward's checkpoints when given
@@ -379,8 +393,8 @@ int kda_bwd_ex(const kda_problem* p, const void* q, const void* k, const void* v
     cur += up(n * C * K * e);
   }
   const Dims d = make_dims(p);
-  const Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, coff};
-  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, coff, s));
+  const Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, tb.coff, tb.cloc};
+  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, P.NC, tb.coff, tb.cloc, s));
   // checkpoint pass: the state entering each segment (skipped when the
   // forward saved them)
   for (int sg = 0; !io->ckpt && sg + 1 < P.NS; ++sg) {

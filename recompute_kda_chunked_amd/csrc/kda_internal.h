@@ -21,6 +21,7 @@ struct Inputs {
   const float *A_log, *dt_bias;
   const int32_t *cu;    // cu_seqlens [N+1]
   const int32_t *coff;  // chunk offsets [N+1]
+  const int2 *cloc;     // per chunk: {first token, valid rows} [NC]
 };
 
 // Per-(chunk, head) operands produced by the chunk-local kernel for one
@@ -69,7 +70,10 @@ struct ScanStates {
 
 // Launchers (defined next to their kernels). Each returns hipSuccess or the
 // launch error. `dtype` is 0 (fp32) or 1 (bf16); D = K = V; C = chunk.
-hipError_t launch_chunk_table(const int32_t* cu, int N, int C, int32_t* coff, hipStream_t s);
+// coff[n] = first chunk of sequence n (coff[N] = NC); cloc[c] = {first token,
+// valid rows} of chunk c, for the NC chunks.
+hipError_t launch_chunk_table(const int32_t* cu, int N, int C, int NC, int32_t* coff, int2* cloc,
+                              hipStream_t s);
 hipError_t launch_prologue(int dtype, int D, int C, const Dims& d, const Inputs& in,
                            int64_t n_chunks, float* qh, float* kh, float* beta, float* gcum,
                            hipStream_t s);

@@ -81,26 +81,17 @@ __device__ __forceinline__ T gate_map(int mode, T ea, T xb, T lb) {
   return c > lb ? c : lb;
 }
 
-// Location of chunk c (global index) of a packed batch.
+// Location of chunk c (global index) of a packed batch, from the chunk
+// table (one dependent load).
 struct ChunkLoc {
-  int n;       // sequence
   int64_t t0;  // first token
   int len;     // valid rows (1..C)
-  bool first;  // first chunk of its sequence
-  bool last;   // last chunk of its sequence
 };
 
 template <int C>
 __device__ __forceinline__ ChunkLoc locate(const Inputs& in, int N, int c) {
-  ChunkLoc L;
-  L.n = find_seq(in.coff, N, c);
-  const int j = c - in.coff[L.n];
-  L.t0 = static_cast<int64_t>(in.cu[L.n]) + static_cast<int64_t>(j) * C;
-  const int64_t rem = static_cast<int64_t>(in.cu[L.n + 1]) - L.t0;
-  L.len = rem < C ? static_cast<int>(rem) : C;
-  L.first = (j == 0);
-  L.last = (c == in.coff[L.n + 1] - 1);
-  return L;
+  const int2 e = in.cloc[c];
+  return ChunkLoc{static_cast<int64_t>(e.x), e.y};
 }
 
 // Row part of the prologue. Each row is read with 16-byte vector loads by

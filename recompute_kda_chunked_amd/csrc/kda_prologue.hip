@@ -5,8 +5,8 @@ namespace kda {
 
 // coff[n] = number of chunks (of length C) in sequences 0..n-1; coff[N] is the
 // total. One block; each thread owns a contiguous run of sequences.
-__global__ void __launch_bounds__(256) k_chunk_table(const int32_t* cu, int N, int C,
-                                                     int32_t* coff) {
+__global__ void __launch_bounds__(256) k_chunk_table(const int32_t* cu, int N, int C, int NC,
+                                                     int32_t* coff, int2* cloc) {
   __shared__ int32_t part[256];
   const int t = threadIdx.x;
   const int per = (N + 255) / 256;
@@ -30,10 +30,18 @@ __global__ void __launch_bounds__(256) k_chunk_table(const int32_t* cu, int N, i
     coff[n] = run;
     run += (cu[n + 1] - cu[n] + C - 1) / C;
   }
+  // the block's coff stores are complete and visible after the barrier
+  __syncthreads();
+  for (int c = t; c < NC; c += 256) {
+    const int n = find_seq(coff, N, c);
+    const int t0 = cu[n] + (c - coff[n]) * C, rem = cu[n + 1] - t0;
+    cloc[c] = int2{t0, rem < C ? rem : C};
+  }
 }
 
-hipError_t launch_chunk_table(const int32_t* cu, int N, int C, int32_t* coff, hipStream_t s) {
-  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, cu, N, C, coff);
+hipError_t launch_chunk_table(const int32_t* cu, int N, int C, int NC, int32_t* coff, int2* cloc,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, cu, N, C, NC, coff, cloc);
   return hipGetLastError();
 }
 
