@@ -29,6 +29,8 @@
 // Block-to-XCD mapping: blocks are dealt round-robin to the 8 XCDs, so the
 // NVT value tiles of one (sequence, head) get block ids that are equal mod 8
 // and share that XCD's L2 for the per-chunk operands they all read.
+#include <type_traits>
+
 #include "kda_prologue.h"
 
 namespace kda {
@@ -74,8 +76,12 @@ struct FwdOps {
 };
 
 // The chunk operands are fragment-major (FragMajor): each fragment load below
-// is one contiguous 64-slot run.
-template <typename OpT, int D, int C, int BV, bool OUT_O, bool REC>
+// is one contiguous 64-slot run. PART selects the operands of one phase of a
+// chunk step (0: W and U; 1: qg and Aqk; 2: kg^T and gamma; -1: all), so
+// that a step can issue the next operands in portions between its phases
+// instead of all at once (a wave that issues many loads back to back stalls
+// until the memory pipeline accepts them).
+template <typename OpT, int D, int C, int BV, bool OUT_O, bool REC, int PART = -1>
 __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const ChunkOps& ops,
                                              size_t idx, int v0, int w, int i, int g) {
   using G = ScanGeo<OpT, D, C, BV>;
@@ -83,33 +89,35 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
   using FM = FragMajor<OpT>;
   constexpr int K = G::K, V = G::V;
   const int lane = i + 16 * g;
-  {
-    // waves past the last row block (C < 64) load that block's rows again and
-    // leave them unused: the loads stay unconditional
-    const int m = w < G::NB ? w : G::NB - 1;
+  // waves past the last row block (C < 64) load that block's rows again and
+  // leave them unused: the loads stay unconditional
+  const int m = w < G::NB ? w : G::NB - 1;
+  if (PART < 0 || PART == 0) {
     const OpT* Wn = static_cast<const OpT*>(ops.Wn) + idx * C * K;
 #pragma unroll
     for (int j = 0; j < G::NKF; ++j) f.w[j] = M::load(Wn + FM::frag(m, j, K, lane));
-    if (OUT_O) {
-      const OpT* qg = static_cast<const OpT*>(ops.qg) + idx * C * K;
-#pragma unroll
-      for (int j = 0; j < G::NKF; ++j) f.q[j] = M::load(qg + FM::frag(m, j, K, lane));
-      const OpT* aq = static_cast<const OpT*>(ops.Aqk) + idx * C * C;
-#pragma unroll
-      for (int j = 0; j < G::NCF; ++j) f.a[j] = M::load(aq + FM::frag(m, j, C, lane));
-    }
     const OpT* U = static_cast<const OpT*>(ops.U) + idx * C * V;
 #pragma unroll
     for (int nv = 0; nv < G::BVT; ++nv) load4_fm_raw<OpT>(U, 16 * m + i, v0 + 16 * nv + 4 * g, V, f.u[nv]);
   }
-  const OpT* kgT = static_cast<const OpT*>(ops.kgT) + idx * K * C;
-  const float* gam = ops.gam + idx * K;
+  if (OUT_O && (PART < 0 || PART == 1)) {
+    const OpT* qg = static_cast<const OpT*>(ops.qg) + idx * C * K;
 #pragma unroll
-  for (int jm = 0; jm < G::MKW; ++jm) {
-    const int mk = w * G::MKW + jm;
+    for (int j = 0; j < G::NKF; ++j) f.q[j] = M::load(qg + FM::frag(m, j, K, lane));
+    const OpT* aq = static_cast<const OpT*>(ops.Aqk) + idx * C * C;
 #pragma unroll
-    for (int j = 0; j < G::NCF; ++j) f.kt[jm][j] = M::load(kgT + FM::frag(mk, j, C, lane));
-    f.gm[jm] = gam[16 * mk + i];
+    for (int j = 0; j < G::NCF; ++j) f.a[j] = M::load(aq + FM::frag(m, j, C, lane));
+  }
+  if (PART < 0 || PART == 2) {
+    const OpT* kgT = static_cast<const OpT*>(ops.kgT) + idx * K * C;
+    const float* gam = ops.gam + idx * K;
+#pragma unroll
+    for (int jm = 0; jm < G::MKW; ++jm) {
+      const int mk = w * G::MKW + jm;
+#pragma unroll
+      for (int j = 0; j < G::NCF; ++j) f.kt[jm][j] = M::load(kgT + FM::frag(mk, j, C, lane));
+      f.gm[jm] = gam[16 * mk + i];
+    }
   }
 }
 
@@ -178,11 +186,12 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
 
   auto step = [&](int c, const Ops& cur, Ops& fill) {
     const size_t idx = static_cast<size_t>(c - seg_begin) * d.H + h;
-    // unconditional (the last chunk again past the end): on every path the
-    // same number of loads follows each set, so the waits before a set's use
-    // can leave the two later sets in flight
-    load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(
-        fill, ops, static_cast<size_t>(min(c + 2, ce - 1) - seg_begin) * d.H + h, v0, w, i, g);
+    // operands of chunk c + 2, in three portions over the step; unconditional
+    // (the last chunk again past the end): on every path the same number of
+    // loads follows each set, so the waits before a set's use can leave the
+    // two later sets in flight
+    const size_t idx2 = static_cast<size_t>(min(c + 2, ce - 1) - seg_begin) * d.H + h;
+    load_fwd_ops<OpT, D, C, BV, OUT_O, REC, 0>(fill, ops, idx2, v0, w, i, g);
     if (c == next_ck) {
       // the state entering chunk c, needed only where c is inside the sequence
       if (c > coff0) {
@@ -222,6 +231,7 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
           store4_fm<OpT>(static_cast<OpT*>(st.Vn) + idx * C * V, 16 * m + i, v0 + 16 * nv + 4 * g, V, accV);
       }
     }
+    load_fwd_ops<OpT, D, C, BV, OUT_O, REC, 1>(fill, ops, idx2, v0, w, i, g);
     __syncthreads();
     if (OUT_O && w < NB) {
       const int m = w;
@@ -239,6 +249,7 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
         if (r < len) store4<TI>(o + (t0 + r) * ts + static_cast<size_t>(h) * V + v0 + 16 * nv + 4 * g, accO[nv]);
       }
     }
+    load_fwd_ops<OpT, D, C, BV, OUT_O, REC, 2>(fill, ops, idx2, v0, w, i, g);
     // h <- Diag(gamma) h + kg^T Vn, on the transposed tiles
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
@@ -293,7 +304,9 @@ struct BwdOps {
   VT dOv[NDO];                // dO tile vectors this thread stages into LDS (raw)
 };
 
-template <typename TI, typename OpT, int D, int C, int BV>
+// PART: 0 the dO tile, 1 Aqk^T and kg, 2 qg^T, -W^T and gamma, -1 all (issued
+// in portions over a step, as in the forward scan).
+template <typename TI, typename OpT, int D, int C, int BV, int PART = -1>
 __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const ChunkOps& ops,
                                              size_t idx, const TI* dO, int64_t t0, int len,
                                              size_t ts, int h, int v0, int tid, int w, int i,
@@ -303,7 +316,7 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
   using FM = FragMajor<OpT>;
   constexpr int K = G::K, V = G::V;
   const int lane = i + 16 * g;
-  {
+  if (PART < 0 || PART == 1) {
     const int m = w < G::NB ? w : G::NB - 1;  // unconditional, as in the forward
     const OpT* at = static_cast<const OpT*>(ops.AqkT) + idx * C * C;
 #pragma unroll
@@ -312,19 +325,22 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
 #pragma unroll
     for (int j = 0; j < G::NKF; ++j) f.kg[j] = M::load(kg + FM::frag(m, j, K, lane));
   }
-  const OpT* qgT = static_cast<const OpT*>(ops.qgT) + idx * K * C;
-  const OpT* WnT = static_cast<const OpT*>(ops.WnT) + idx * K * C;
-  const float* gam = ops.gam + idx * K;
+  if (PART < 0 || PART == 2) {
+    const OpT* qgT = static_cast<const OpT*>(ops.qgT) + idx * K * C;
+    const OpT* WnT = static_cast<const OpT*>(ops.WnT) + idx * K * C;
+    const float* gam = ops.gam + idx * K;
 #pragma unroll
-  for (int jm = 0; jm < G::MKW; ++jm) {
-    const int mk = w * G::MKW + jm;
+    for (int jm = 0; jm < G::MKW; ++jm) {
+      const int mk = w * G::MKW + jm;
 #pragma unroll
-    for (int j = 0; j < G::NCF; ++j) {
-      f.qt[jm][j] = M::load(qgT + FM::frag(mk, j, C, lane));
-      f.wt[jm][j] = M::load(WnT + FM::frag(mk, j, C, lane));
+      for (int j = 0; j < G::NCF; ++j) {
+        f.qt[jm][j] = M::load(qgT + FM::frag(mk, j, C, lane));
+        f.wt[jm][j] = M::load(WnT + FM::frag(mk, j, C, lane));
+      }
+      f.gm[jm] = gam[16 * mk + i];
     }
-    f.gm[jm] = gam[16 * mk + i];
   }
+  if (PART >= 1) return;
   // rows past the chunk's end read its last row (unconditional loads stay
   // where they are issued; a conditional one would be moved to its use and
   // waited for there) and are zeroed where they are used
@@ -400,17 +416,21 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
 
   // three rotating operand sets: chunk c - 2 loads while chunk c is computed
   Ops s0, s1, s2;
-  auto load = [&](Ops& f, int c) {
+  auto load = [&](Ops& f, int c, auto part) {
     const int64_t t0 = chunk_t0(c);
-    load_bwd_ops<TI, OpT, D, C, BV>(f, ops, static_cast<size_t>(c - seg_begin) * d.H + h, dO, t0,
-                                    chunk_len(t0), ts, h, v0, tid, w, i, g);
+    load_bwd_ops<TI, OpT, D, C, BV, decltype(part)::value>(
+        f, ops, static_cast<size_t>(c - seg_begin) * d.H + h, dO, t0, chunk_len(t0), ts, h, v0,
+        tid, w, i, g);
   };
-  load(s0, ce - 1);
-  load(s1, max(ce - 2, cb));
+  using All = std::integral_constant<int, -1>;
+  load(s0, ce - 1, All{});
+  load(s1, max(ce - 2, cb), All{});
   auto step = [&](int c, const Ops& cur, Ops& fill) {
     const size_t idx = static_cast<size_t>(c - seg_begin) * d.H + h;
-    // unconditional (the first chunk again past the start), as in the forward scan
-    load(fill, max(c - 2, cb));
+    // unconditional (the first chunk again past the start), as in the forward
+    // scan, and in three portions over the step
+    const int c2 = max(c - 2, cb);
+    load(fill, c2, std::integral_constant<int, 0>{});
     // dO tile, transposed into LDS ([BV][C]); padded rows are zero
     const int len = chunk_len(chunk_t0(c));
 #pragma unroll
@@ -429,6 +449,7 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
       for (int j = 0; j < HPW; ++j)
         store4_fm<OpT>(hd, 16 * (w * MKW + j / BVT) + i, v0 + 16 * (j % BVT) + 4 * g, V, hs[j]);
     }
+    load(fill, c2, std::integral_constant<int, 1>{});
     __syncthreads();
     if (w < NB) {
       const int m = w;
@@ -450,6 +471,7 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
         store4_fm<OpT>(static_cast<OpT*>(st.dVnT) + idx * V * C, v0 + 16 * nv + i, 16 * m + 4 * g, C, acc);
       }
     }
+    load(fill, c2, std::integral_constant<int, 2>{});
     __syncthreads();
     // dh = Diag(gamma) dh' + qg^T dO - W^T dVn, on the transposed tiles
 #pragma unroll
