@@ -165,10 +165,9 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   const TI* vr = static_cast<const TI*>(in.v) + L.t0 * ts + hoff;
   auto row_block = [&](int jm) { return half * MR + jm; };  // valid while < NB
 
-  // Global loads are all issued here, before any arithmetic: first the
-  // prologue's rows (raw q, k, gate, beta; the q and k vectors also feed the
-  // transposes of S1), so the prologue can start once they arrive (loads
-  // complete in order), then those of S2/S3 (dVn^T, T^T, dO, Vn, v), whose
+  // Global loads come before any global store: first the prologue's rows
+  // (raw q, k, gate, beta; the q and k vectors also feed the transposes of
+  // S1), then those of S2/S3 (dVn^T, T^T, dO, Vn, v) during S1, so their
   // latency overlaps the prologue and the cumulative sum. Rows past the
   // chunk's end read the last valid row (no branch) and are masked where
   // they are used.
@@ -192,18 +191,16 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // vn_row(e) .. + 3 of column vn_col(e) (fp32: four lane slots)
   auto vn_row = [](int e) { const int sl = e * VE / KPL; return 16 * ((sl >> 6) / (V / KS)) + (sl & 15); };
   auto vn_col = [](int e) { const int sl = e * VE / KPL; return KS * ((sl >> 6) % (V / KS)) + KPL * ((sl & 63) >> 4); };
+  // S2's operands (dVn^T, T^T, v) are requested once the prologue's rows are
+  // in use, S3's (dO, Vn) after the transposes: the memory pipeline takes a
+  // wave's loads at a bounded rate, and a wave issuing all of them at once
+  // would stall before its first arithmetic.
+  // ---- S1: prologue, transposed raw q/k, cumulative gate G^T
+  auto Gf = [&](int r, int kk_) -> GV& { return GT[kk_ * LDG + (r ^ swz(kk_))]; };
+  prologue_compute<TI, D, C, NW>(d, L, pr, rq, rqs, rk, be, Gf);
   {
     const OpT* dVnT = static_cast<const OpT*>(st.dVnT) + idx * V * C;
     const OpT* TT = static_cast<const OpT*>(ops.TT) + idx * C * C;
-    const TI* dOr = dO + L.t0 * ts + hoff;
-    const OpT* Vn = static_cast<const OpT*>(st.Vn) + idx * C * V;
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int e0 = tid + NT * j, e = e0 < NV ? e0 : 0, r = e / NVR, c = (e % NVR) * VE;
-      const int rc = r < L.len ? r : L.len - 1;
-      ldo[j] = *reinterpret_cast<const VT*>(dOr + rc * ts + c);
-      ldn[j] = *reinterpret_cast<const VT*>(Vn + e * VE);
-    }
     {
       const int t = w * TPW < T2 ? w * TPW : 0, mv = t / NB;
 #pragma unroll
@@ -220,10 +217,6 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       load4_raw<TI>(vr + (r < L.len ? r : L.len - 1) * ts + vv, vin[jt]);
     }
   }
-
-  // ---- S1: prologue, transposed raw q/k, cumulative gate G^T
-  auto Gf = [&](int r, int kk_) -> GV& { return GT[kk_ * LDG + (r ^ swz(kk_))]; };
-  prologue_compute<TI, D, C, NW>(d, L, pr, rq, rqs, rk, be, Gf);
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
@@ -235,6 +228,17 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         qT[(c + q2) * LDQ + rs] = ok ? pr.qv[j][q2] : static_cast<TI>(0.f);
         kT[(c + q2) * LDQ + rs] = ok ? pr.kv[j][q2] : static_cast<TI>(0.f);
       }
+    }
+  }
+  {
+    const TI* dOr = dO + L.t0 * ts + hoff;
+    const OpT* Vn = static_cast<const OpT*>(st.Vn) + idx * C * V;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int e0 = tid + NT * j, e = e0 < NV ? e0 : 0, r = e / NVR, c = (e % NVR) * VE;
+      const int rc = r < L.len ? r : L.len - 1;
+      ldo[j] = *reinterpret_cast<const VT*>(dOr + rc * ts + c);
+      ldn[j] = *reinterpret_cast<const VT*>(Vn + e * VE);
     }
   }
   for (int e = tid; e < NW * C; e += NT) dbp[e / C][e % C] = 0.f;
