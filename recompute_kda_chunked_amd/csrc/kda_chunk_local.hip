@@ -52,13 +52,10 @@ struct TileT<bf16, D, C> {
   static __device__ __forceinline__ int off(int kk, int s) {
     return kk * C + 8 * ((s >> 3) ^ swz(kk)) + (s & 7);
   }
-  // rows s and s + 1 (s even) of channel kk
-  static __device__ __forceinline__ void put2(bf16* t, int kk, int s, float a, float b) {
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    bf16x2 v;
-    v[0] = static_cast<bf16>(a);
-    v[1] = static_cast<bf16>(b);
-    *reinterpret_cast<bf16x2*>(t + off(kk, s)) = v;
+  // rows s and s + 1 (s even) of channel kk, as a packed pair
+  typedef __attribute__((ext_vector_type(2))) __bf16 Pair;
+  static __device__ __forceinline__ void put2(bf16* t, int kk, int s, Pair v) {
+    *reinterpret_cast<Pair*>(t + off(kk, s)) = v;
   }
   // rows s .. s + 7 (s a multiple of 8) of channel kk
   static __device__ __forceinline__ bf16x8 frag(const bf16* t, int kk, int s) {
@@ -81,9 +78,10 @@ struct TileT<float, D, C> {
   static constexpr int LD = C + 1;
   static constexpr int kElems = D * LD;
   static constexpr int kBytes = kElems * 4;
-  static __device__ __forceinline__ void put2(float* t, int kk, int s, float a, float b) {
-    t[kk * LD + s] = a;
-    t[kk * LD + s + 1] = b;
+  typedef __attribute__((ext_vector_type(2))) float Pair;
+  static __device__ __forceinline__ void put2(float* t, int kk, int s, Pair v) {
+    t[kk * LD + s] = v[0];
+    t[kk * LD + s + 1] = v[1];
   }
   static __device__ __forceinline__ float frag(const float* t, int kk, int s) { return t[kk * LD + s]; }
   // fragment-major [D][C]: element 4 e + q is channel 16 rb + (4 e + q) % 16,
@@ -114,19 +112,24 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   using TL = TileT<OpT, D, C>;
   typedef typename GateT<OpT>::T GV;
   constexpr int SZ_G = C * LDG * (int)sizeof(GV), SZ_S = 2 * TL::kBytes;
-  // the cumulative gate, then two staged transposed tiles at a time
-  __shared__ __attribute__((aligned(16))) unsigned char regG[SZ_G > SZ_S ? SZ_G : SZ_S];
+  constexpr int SZ_T = (C * LDM + 16 * C) * 4;
+  constexpr int SZ_GR = SZ_G > SZ_S ? SZ_G : SZ_S;
+  // The cumulative gate; then the staging area of the transposed kg^T (qg^T)
+  // tiles; then T (fp32) and the inverse's scratch; then the staged operands
+  // of W and U. Aqk leaves from registers, so at most the gate region, P and
+  // the row scalars are live at once (54 KB at D = 128, C = 64: three blocks
+  // per CU).
+  __shared__ __attribute__((aligned(16))) unsigned char regG[SZ_GR > SZ_T ? SZ_GR : SZ_T];
   __shared__ __attribute__((aligned(16))) unsigned char regM[SZ_R];  // P, then Tb
-  __shared__ float As[C * LDM];                                         // Aqk, then T
-  __shared__ float Sx[16 * C];
   __shared__ float rq[C], rqs[C], rk[C], be[C];
-  __shared__ GV ptot[4 * D];
+  __shared__ GV ptot[256];  // cumulative-sum partials: (256 / D) parts of D channels
   GV* Gs = reinterpret_cast<GV*>(regG);
   OpT* tile0 = reinterpret_cast<OpT*>(regG);
   OpT* tile1 = tile0 + TL::kElems;
   float* Ms = reinterpret_cast<float*>(regM);
   OpT* Tb = reinterpret_cast<OpT*>(regM);
-  float* Ts = As;
+  float* Ts = reinterpret_cast<float*>(regG);
+  float* Sx = Ts + C * LDM;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
@@ -138,10 +141,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   const TI* kr = static_cast<const TI*>(in.k) + L.t0 * ts + static_cast<size_t>(h) * D;
   const TI* vr = static_cast<const TI*>(in.v) + L.t0 * ts + static_cast<size_t>(h) * D;
 
-  for (int e = tid; e < C * LDM; e += 256) {
-    Ms[e] = 0.f;
-    As[e] = 0.f;
-  }
+  for (int e = tid; e < C * LDM; e += 256) Ms[e] = 0.f;
   auto G = [&](int r, int kk) -> GV& { return Gs[r * LDG + kk]; };
   // the gate in GateUnits (base 2 for bf16): every exponential below is of a
   // difference of these values
@@ -181,7 +181,12 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     if constexpr (KPL == 1) return to_f(f);
     else return to_f(f[j]);
   };
-  auto do_pair = [&](const PairRows& f, int p) {
+  // The Aqk tile of pair p is returned in aq (masked), to be stored after all
+  // of the phase's loads are issued: forward, transposed (MFMA operands
+  // swapped: aq[rr] = Aqk[16I + i][16J + 4g + rr]); backward, as Aqk^T rows
+  // (aq[rr] = Aqk[16I + 4g + rr][16J + i] = Aqk^T[16J + i][16I + 4g + rr]).
+  // Either way the lane's four values are consecutive in the stored matrix.
+  auto do_pair = [&](const PairRows& f, int p, f32x4& aq) {
     int I, J;
     pair_blocks(p, I, J);
     const int ra = 16 * I + i, rb = 16 * J + i;
@@ -202,14 +207,36 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
       accP = M::mma(fk, fb, accP);
       if (!STATE) {
         const auto fq = M::make([&](int j) { return el(f.xa[ks], j) * sq * ea[j]; });
-        accQ = M::mma(fq, fb, accQ);
+        accQ = BWD ? M::mma(fq, fb, accQ) : M::mma(fb, fq, accQ);
       }
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int r = 16 * I + 4 * g + rr, s = 16 * J + i;
       Ms[r * LDM + s] = (s < r) ? accP[rr] : 0.f;
-      if (!STATE) As[r * LDM + s] = (s <= r) ? accQ[rr] : 0.f;
+      // Aqk[r'][s'] = 0 for s' > r': forward r' = 16I + i, s' = 16J + 4g + rr
+      aq[rr] = (BWD ? s <= r : 16 * J + 4 * g + rr <= ra) ? accQ[rr] : 0.f;
+    }
+  };
+  // Aqk (forward) or Aqk^T (backward), fragment-major: the tiles of the
+  // wave's pairs, and zeros in the blocks above (Aqk) or below (Aqk^T) the
+  // diagonal, which the scans read as parts of whole fragments
+  auto store_aqk = [&](const f32x4 (&aqv)[PPW]) {
+    OpT* dst = static_cast<OpT*>(BWD ? ops.AqkT : ops.Aqk) + idx * C * C;
+#pragma unroll
+    for (int it = 0; it < PPW; ++it) {
+      const int p = w + 4 * it;
+      if (p >= NPAIR) break;
+      int I, J;
+      pair_blocks(p, I, J);
+      if (BWD) store4_fm<OpT>(dst, 16 * J + i, 16 * I + 4 * g, C, aqv[it]);
+      else store4_fm<OpT>(dst, 16 * I + i, 16 * J + 4 * g, C, aqv[it]);
+    }
+    for (int zb = w; zb < NB * (NB - 1) / 2; zb += 4) {
+      int I = 1, J = zb;  // zb-th block pair with J < I
+      while (J >= I) { J -= I; ++I; }
+      if (BWD) store4_fm<OpT>(dst, 16 * I + i, 16 * J + 4 * g, C, zero4());
+      else store4_fm<OpT>(dst, 16 * J + i, 16 * I + 4 * g, C, zero4());
     }
   };
   // ---- the element-wise pass after the pairs works on (row pair, VE
@@ -239,6 +266,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   };
 
   PairRows pa, pb;
+  f32x4 aqv[PPW];
   load_pair(pa, w);
   __syncthreads();
   cumsum_rows<D, C, 256>(G, ptot);
@@ -249,7 +277,8 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     PairRows& nxt = (it & 1) ? pa : pb;
     if (it + 1 < PPW) load_pair(nxt, p + 4);
     else if (!BWD) load_items();
-    if (p < NPAIR) do_pair(cur, p);
+    aqv[it] = zero4();
+    if (p < NPAIR) do_pair(cur, p, aqv[it]);
   }
   __syncthreads();
   if (BWD) load_items();
@@ -263,20 +292,13 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   // operands of W and U.
   // staged values per item: [0] kg (both), [1] Kb, [2] Bv, [3] qg (backward)
   constexpr int NSV = BWD ? 4 : 3;
-  float sv[IPT][NSV][2][VE];
+  // held in the operand type (bf16 pairs pack into one register): they are
+  // rounded to it when staged anyway
+  typename TL::Pair sv[IPT][NSV][VE];
   {
     // stores of this phase follow all of its loads (loads and stores share one
     // completion counter)
-    if (!STATE) {
-      // fragment-major, one lane slot (KPL elements of row a) per thread
-      typedef typename M::frag F;
-      F* aq = reinterpret_cast<F*>(static_cast<OpT*>(BWD ? ops.AqkT : ops.Aqk) + idx * C * C);
-      for (int e = tid; e < C * C / KPL; e += 256) {
-        const int blk = e >> 6, lane = e & 63;
-        const int a = 16 * (blk / (C / KS)) + (lane & 15), b = KS * (blk % (C / KS)) + KPL * (lane >> 4);
-        aq[e] = M::make([&](int j) { return BWD ? As[(b + j) * LDM + a] : As[a * LDM + b + j]; });
-      }
-    }
+    if (!STATE) store_aqk(aqv);
     {
       if (BWD) {
         OpT* P = static_cast<OpT*>(ops.P) + idx * C * C;
@@ -301,11 +323,12 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
           const float eG = GU::ex(gr), eGc = GU::ex(Gs[(C - 1) * LDG + c0 + j] - gr);
           const float kh = to_f(xk[it][h2][j]) * sk;
           const float qg = STATE ? 0.f : to_f(xq[it][h2][j]) * sq * eG;
-          sv[it][0][h2][j] = kh * eGc;
-          sv[it][1][h2][j] = b * kh * eG;
-          sv[it][2][h2][j] = b * to_f(xv[it][h2][j]);
-          if (BWD) sv[it][NSV - 1][h2][j] = qg;
-          out[j] = from_f<OpT>(BWD ? sv[it][0][h2][j] : qg);
+          const OpT kg = from_f<OpT>(kh * eGc);
+          sv[it][0][j][h2] = kg;
+          sv[it][1][j][h2] = from_f<OpT>(b * kh * eG);
+          sv[it][2][j][h2] = from_f<OpT>(b * to_f(xv[it][h2][j]));
+          if (BWD) sv[it][NSV - 1][j][h2] = from_f<OpT>(qg);
+          out[j] = BWD ? kg : from_f<OpT>(qg);
         }
         if (!STATE) {
           // fragment-major [C][K]: the VE channels are one lane slot (bf16)
@@ -321,7 +344,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
       }
     }
   }
-  __syncthreads();  // the gate region and As are free from here
+  __syncthreads();  // the gate region is free from here
   // round 1: kg^T (and qg^T) leave through the staging area
   auto stage = [&](OpT* tile, int which) {
 #pragma unroll
@@ -330,7 +353,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
       if (item >= NITEM) break;
 #pragma unroll
       for (int j = 0; j < VE; ++j)
-        TL::put2(tile, c0 + j, 2 * rp, sv[it][which][0][j], sv[it][which][1][j]);
+        TL::put2(tile, c0 + j, 2 * rp, sv[it][which][j]);
     }
   };
   stage(tile0, 0);
@@ -339,11 +362,10 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   TL::drain(tile0, static_cast<OpT*>(ops.kgT) + idx * K * C, tid);
   if (BWD) TL::drain(tile1, static_cast<OpT*>(ops.qgT) + idx * K * C, tid);
   __syncthreads();
-  // round 2: the operands of W and U stay in LDS
-  stage(tile0, 1);
-  stage(tile1, 2);
 
-  // ---- T = (I + Akk)^-1: diagonal 16x16 blocks by forward substitution
+  // ---- T = (I + Akk)^-1 (in the staging area, free again), diagonal 16x16
+  // blocks by forward substitution. The operands of W and U wait in
+  // registers (sv) meanwhile.
   for (int e = tid; e < C * LDM; e += 256) Ts[e] = 0.f;
   __syncthreads();
   if (w < NB && lane < 16) {
@@ -413,6 +435,10 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
       TT[e] = M::make([&](int j) { return Ts[(b + j) * LDM + a]; });
     }
   }
+  __syncthreads();
+  // round 2: the operands of W and U into the staging area (T is in Tb)
+  stage(tile0, 1);
+  stage(tile1, 2);
   __syncthreads();
 
   // ---- W = T Kb and U = T Bv (MFMA). Kb^T / Bv^T fragments come from the
