@@ -127,7 +127,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // after the VJP the operand region holds the scratch of the reverse
   // cumulative sum and of the partial reductions
   constexpr int OFF_S = 0;
-  static_assert(OFF_S + (int)sizeof(TG) * NT + 4 * NT <= SZU, "LDS scratch must fit");
+  constexpr int OFF_X = (OFF_S + (int)sizeof(TG) * (NT + 64) + 15) / 16 * 16;
+  static_assert(OFF_X + 3 * C * (D + 8) * (int)sizeof(TI) <= SZU, "LDS scratch must fit");
   __shared__ __attribute__((aligned(16))) GV GT[K * LDG];
   __shared__ __attribute__((aligned(16))) TI qT[K * LDQ];
   __shared__ __attribute__((aligned(16))) TI kT[K * LDQ];
@@ -569,17 +570,20 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // latency overlaps this phase and no load follows a store in S8)
   constexpr int PER = (C * D + NT - 1) / NT;
   static_assert(NT % D == 0, "one channel per thread in the gate VJP");
-  uint32_t xin[PER];  // raw bits: converted at use, so the loads stay in flight
+  // The raw gate rows come in as 16-byte vectors and wait in LDS for the gate
+  // VJP (whose thread-per-channel mapping would otherwise take a 2-byte load
+  // per element); dq, dk and draw_g go out the same way, staged in LDS.
+  VT xrow[VPT];
   const float dbias = in.dt_bias[hoff + tid % D];
   // exp(A_log) in the gate's precision, as the forward's gate map takes it
   const TG eat = exp(static_cast<TG>(in.A_log[h]));
   {
     const TI* xr = static_cast<const TI*>(in.g) + L.t0 * ts + hoff;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = tid + NT * j, r = e / D, kc = e % D;
+    for (int j = 0; j < VPT; ++j) {
+      const int e0 = tid + NT * j, e = e0 < NV ? e0 : 0, r = e / NVR, c = (e % NVR) * VE;
       const int rc = r < L.len ? r : L.len - 1;  // clamped row, masked at use
-      xin[j] = load_bits<TI>(xr + rc * ts + kc);
+      xrow[j] = *reinterpret_cast<const VT*>(xr + rc * ts + c);
     }
   }
 #pragma unroll
@@ -610,6 +614,15 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   TG* dGT = reinterpret_cast<TG*>(GT);
   TG* ptg = reinterpret_cast<TG*>(uni + OFF_S);
   TG* red = reinterpret_cast<TG*>(uni + OFF_S + sizeof(TG) * NT);
+  // raw gate rows (then draw_g), dq and dk, [C][LDA] each
+  TI* xg_s = reinterpret_cast<TI*>(uni + OFF_X);
+  TI* dq_s = xg_s + C * LDA;
+  TI* dk_s = dq_s + C * LDA;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
+    if (e < NV) *reinterpret_cast<VT*>(xg_s + r * LDA + c) = xrow[j];
+  }
 #pragma unroll
   for (int jm = 0; jm < MR; ++jm) {
     const int m = row_block(jm);
@@ -659,7 +672,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     for (int j = 0; j < PER; ++j) {
       const int e = tid + NT * j, r = e / D, kc = e % D;
       const bool ok = e < C * D && r < L.len;
-      const TG xb = static_cast<TG>(bits_to_f<TI>(xin[j])) + static_cast<TG>(dbias);
+      const TG xb = static_cast<TG>(to_f(xg_s[(r < C ? r : 0) * LDA + kc])) + static_cast<TG>(dbias);
       const TG dgv = ok ? static_cast<TG>(dGT[kc * LDG + (r < C ? r : 0)]) : TG(0);
       TG dx, dA;
       if (d.gate_mode == 0) {
@@ -693,16 +706,17 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
           const float qd = rsum[0][r], kd = rsum[1][r];
           const float qbar = to_f(qT[kk * LDQ + (r ^ swk)]) * rq[r];
           const float khat_ = to_f(kT[kk * LDQ + (r ^ swk)]) * rk[r];
-          dqo[r * ts + kk] = from_f<TI>(rqs[r] * (aq[jm][rr] - qbar * qd));
-          dko[r * ts + kk] = from_f<TI>(rk[r] * (ak[jm][rr] - khat_ * kd));
+          dq_s[r * LDA + kk] = from_f<TI>(rqs[r] * (aq[jm][rr] - qbar * qd));
+          dk_s[r * LDA + kk] = from_f<TI>(rk[r] * (ak[jm][rr] - khat_ * kd));
         }
       }
     }
-    TI* dgo = dg + L.t0 * ts + hoff;
+    // draw_g over the raw gate: each element is read and rewritten by the
+    // same thread
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int e = tid + NT * j, r = e / D, kc = e % D;
-      if (e < C * D && r < L.len) dgo[r * ts + kc] = from_f<TI>(dxv[j]);
+      if (e < C * D) xg_s[r * LDA + kc] = from_f<TI>(dxv[j]);
     }
     // tid % D is this thread's channel for every e above
     ptg[tid] = pdt;
@@ -725,6 +739,16 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       TG s2 = 0;
       for (int j = 0; j < NW; ++j) s2 += red[j];
       part[K] = static_cast<double>(s2);
+    }
+    TI* dgo = dg + L.t0 * ts + hoff;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
+      if (e < NV && r < L.len) {
+        *reinterpret_cast<VT*>(dqo + r * ts + c) = *reinterpret_cast<const VT*>(dq_s + r * LDA + c);
+        *reinterpret_cast<VT*>(dko + r * ts + c) = *reinterpret_cast<const VT*>(dk_s + r * LDA + c);
+        *reinterpret_cast<VT*>(dgo + r * ts + c) = *reinterpret_cast<const VT*>(xg_s + r * LDA + c);
+      }
     }
   }
 }
