@@ -511,16 +511,29 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
   }
 }
 
-// Value-tile width of both scans: 32 columns, N*H*V/32 blocks of 4 waves
-// (one wave per SIMD, so the rotating operand sets may use AGPRs as well).
-constexpr int kBvFwd = 32, kBvBwd = 32;
+// Value-tile width of both scans. The scans are bound by the operand traffic
+// each block pulls through its CU (every value tile of a head loads the same
+// chunk operands), so the width trades CUs in use against bytes per unit of
+// work: 32 columns while N*H*V/32 blocks (1 wave per SIMD, rotating operand
+// sets in AGPRs as well) fit in one pass over the CUs; 64 columns once they
+// would not (half the operand traffic per state column; measured at H96:
+// forward scan 0.153 -> 0.128 ms, reverse 0.191 -> 0.143 ms per launch,
+// where at H64 64 columns are 1.4x slower than 32).
+static bool wide_tiles(const Dims& d, int D) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const long groups = (static_cast<long>(d.N) * d.H + 7) / 8;
+  return groups * 8 * (D / 32) > cus;
+}
 
-template <typename TI, int D, int C>
-static hipError_t launch_sf(const Dims& d, const Inputs& in, int seg_begin, int seg_end,
-                            const ChunkOps& ops, void* o, const SegStates* st,
-                            const float* carry_in, float* carry_out, const ScanStates& ss,
-                            hipStream_t s) {
-  constexpr int BV = kBvFwd, NVT = D / BV;
+template <typename TI, int D, int C, int BV>
+static hipError_t launch_sf_bv(const Dims& d, const Inputs& in, int seg_begin, int seg_end,
+                               const ChunkOps& ops, void* o, const SegStates* st,
+                               const float* carry_in, float* carry_out, const ScanStates& ss,
+                               hipStream_t s) {
+  constexpr int NVT = D / BV;
   const int groups = (d.N * d.H + 7) / 8;
   const dim3 grid(groups * 8 * NVT), block(256);
   SegStates z{};
@@ -537,16 +550,36 @@ static hipError_t launch_sf(const Dims& d, const Inputs& in, int seg_begin, int 
 }
 
 template <typename TI, int D, int C>
-static hipError_t launch_sb(const Dims& d, const Inputs& in, const void* dO, int seg_begin,
-                            int seg_end, const ChunkOps& ops, const SegStates& st,
+static hipError_t launch_sf(const Dims& d, const Inputs& in, int seg_begin, int seg_end,
+                            const ChunkOps& ops, void* o, const SegStates* st,
                             const float* carry_in, float* carry_out, const ScanStates& ss,
                             hipStream_t s) {
-  constexpr int BV = kBvBwd, NVT = D / BV;
+  if (D >= 64 && wide_tiles(d, D))
+    return launch_sf_bv<TI, D, C, 64>(d, in, seg_begin, seg_end, ops, o, st, carry_in, carry_out, ss, s);
+  return launch_sf_bv<TI, D, C, 32>(d, in, seg_begin, seg_end, ops, o, st, carry_in, carry_out, ss, s);
+}
+
+template <typename TI, int D, int C, int BV>
+static hipError_t launch_sb_bv(const Dims& d, const Inputs& in, const void* dO, int seg_begin,
+                               int seg_end, const ChunkOps& ops, const SegStates& st,
+                               const float* carry_in, float* carry_out, const ScanStates& ss,
+                               hipStream_t s) {
+  constexpr int NVT = D / BV;
   const int groups = (d.N * d.H + 7) / 8;
   hipLaunchKernelGGL((k_scan_bwd<TI, TI, D, C, BV>), dim3(groups * 8 * NVT), dim3(256), 0, s,
                      d, in, static_cast<const TI*>(dO), seg_begin, seg_end, ops, st, carry_in,
                      carry_out, ss);
   return hipGetLastError();
+}
+
+template <typename TI, int D, int C>
+static hipError_t launch_sb(const Dims& d, const Inputs& in, const void* dO, int seg_begin,
+                            int seg_end, const ChunkOps& ops, const SegStates& st,
+                            const float* carry_in, float* carry_out, const ScanStates& ss,
+                            hipStream_t s) {
+  if (D >= 64 && wide_tiles(d, D))
+    return launch_sb_bv<TI, D, C, 64>(d, in, dO, seg_begin, seg_end, ops, st, carry_in, carry_out, ss, s);
+  return launch_sb_bv<TI, D, C, 32>(d, in, dO, seg_begin, seg_end, ops, st, carry_in, carry_out, ss, s);
 }
 
 #define KDA_DISPATCH(FN, ...)                                              \
@@ -556,7 +589,6 @@ static hipError_t launch_sb(const Dims& d, const Inputs& in, const void* dO, int
     if (D == 64 && C == 64) return FN<float, 64, 64>(__VA_ARGS__);         \
     if (D == 128 && C == 16) return FN<float, 128, 16>(__VA_ARGS__);       \
     if (D == 128 && C == 32) return FN<float, 128, 32>(__VA_ARGS__);       \
-    if (D == 128 && C == 64) return FN<float, 128, 64>(__VA_ARGS__);       \
   } else {                                                                 \
     if (D == 64 && C == 32) return FN<bf16, 64, 32>(__VA_ARGS__);          \
     if (D == 64 && C == 64) return FN<bf16, 64, 64>(__VA_ARGS__);          \

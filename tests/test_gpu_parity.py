@@ -100,6 +100,17 @@ def test_bf16_ragged_varlen(D, chunk):
     check(gpu_run(x, chunk), oracle_run(x), torch.bfloat16, label="bf16 D%d C%d" % (D, chunk))
 
 
+@pytest.mark.parametrize("D,dtype,chunk", [(64, torch.bfloat16, 64), (128, torch.bfloat16, 64),
+                                           (64, torch.float32, 32), (128, torch.float32, 32)])
+def test_wide_value_tiles(D, dtype, chunk):
+    # enough (sequence, head) pairs that N*H*V/32 scan blocks exceed the CU
+    # count (256 on MI355X): both scans switch to 64-column value tiles
+    H = 96 if D == 64 else 48
+    announce("wide value tiles D%d %s chunk %d, N=3 H=%d" % (D, dtype, chunk, H))
+    x = kda_inputs.make_inputs([40, 9, 77], H, D, D, dtype, seed=21, device="cuda")
+    check(gpu_run(x, chunk), oracle_run(x), dtype, label="wide D%d C%d" % (D, chunk))
+
+
 def test_fp32_d128_and_segment_streaming():
     announce("fp32 D128 chunk 32, one-chunk segments")
     x = kda_inputs.make_inputs([70, 1, 130], 2, 128, 128, torch.float32, seed=13, device="cuda")
