@@ -25,6 +25,8 @@
 // cumulative sum of dG within the chunk; then the prologue is differentiated
 // (L2 normalisation, sigmoid, gate map). Gate-parameter gradients leave as
 // per-chunk partials for a fixed-order reduction.
+#include <type_traits>
+
 #include "kda_prologue.h"
 
 namespace kda {
@@ -165,6 +167,18 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   const size_t hoff = static_cast<size_t>(h) * D;
   const TI* vr = static_cast<const TI*>(in.v) + L.t0 * ts + hoff;
   auto row_block = [&](int jm) { return half * MR + jm; };  // valid while < NB
+  // Rows r0 .. r0 + 3 (r0 a multiple of 4) of this lane's channel in the
+  // transposed tiles, read as one vector: the row permutation moves whole
+  // groups of 8 rows, so four aligned rows stay adjacent. Likewise four
+  // consecutive row scalars.
+  typedef std::conditional_t<sizeof(GV) == 4, f32x4, f64x4> GV4;
+  auto gt4 = [&](int r0) { return *reinterpret_cast<const GV4*>(GT + kk * LDG + (r0 ^ swk)); };
+  auto tile4 = [&](const TI* t, int r0) {
+    uint32_t u[4];
+    load4_raw<TI>(t + kk * LDQ + (r0 ^ swk), u);
+    return unpack4<TI>(u);
+  };
+  auto sc4 = [](const float* a, int r0) { return *reinterpret_cast<const f32x4*>(a + r0); };
 
   // Global loads come before any global store: first the prologue's rows
   // (raw q, k, gate, beta; the q and k vectors also feed the transposes of
@@ -348,15 +362,19 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         rQg = M::mma(M::load(dO_s + ro), fh[j], rQg);
         rKg = M::mma(M::load(Vn_s + ro), fdh[j], rKg);
       }
+      const int r0 = 16 * m + 4 * g;
+      const GV4 G4 = gt4(r0);
+      const f32x4 q4 = tile4(qT, r0), k4 = tile4(kT, r0);
+      const f32x4 rqs4 = sc4(rqs, r0), rk4 = sc4(rk, r0), be4 = sc4(be, r0);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int r = 16 * m + 4 * g + rr;
-        const GV Gv = GT[kk * LDG + (r ^ swk)];
+        const int r = r0 + rr;
+        const GV Gv = G4[rr];
         const float eG = kexp<OpT>(Gv), eGc = kexp<OpT>(Gc - Gv);
-        const float qh = to_f(qT[kk * LDQ + (r ^ swk)]) * rqs[r];
-        const float kh = to_f(kT[kk * LDQ + (r ^ swk)]) * rk[r];
+        const float qh = q4[rr] * rqs4[rr];
+        const float kh = k4[rr] * rk4[rr];
         const float dqg = rQg[rr], dkg = rKg[rr], dKb = -rKb[rr];
-        const float b = be[r];
+        const float b = be4[rr];
         aq[jm][rr] += dqg * eG;
         ak[jm][rr] += dkg * eGc + b * dKb * eG;
         // -kg*dkg here and +kg*dkg in the G_c row cancel in the reverse
@@ -509,13 +527,17 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       }
       rq_ = VJ::fix(rq_);
       rk_ = VJ::fix(rk_);
+      const int r0 = b0 + 4 * g;
+      const GV4 G4 = gt4(r0);
+      const f32x4 q4 = tile4(qT, r0), k4 = tile4(kT, r0), rqs4 = sc4(rqs, r0), rk4 = sc4(rk, r0);
+      const TG gb0 = static_cast<TG>(Gk[b0 ^ swk]);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int r = b0 + 4 * g + rr;
-        const TG f = dec(r, b0);
+        const TG f = VJ::ex(static_cast<TG>(G4[rr]) - gb0);  // exp(G_r - G_b)
         // dG takes the column side's operand values for this pair, rounded as
         // that side's MFMA operands are (see Vjp)
-        const TG Aq = VJ::rnd(qhat(r) * f), Ak = VJ::rnd(khat(r) * f);
+        const TG Aq = VJ::rnd(static_cast<TG>(q4[rr]) * static_cast<TG>(rqs4[rr]) * f),
+                 Ak = VJ::rnd(static_cast<TG>(k4[rr]) * static_cast<TG>(rk4[rr]) * f);
         aq[jm][rr] += static_cast<float>(rq_[rr] * f);
         ak[jm][rr] += static_cast<float>(rk_[rr] * f);
         aG[jm][rr] += Aq * rq_[rr] + Ak * rk_[rr];
@@ -525,6 +547,9 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       // u < 16 and (dAqk, qh) above:  y[s] = sum_r dX[r][s] * a_r exp(G_r - G_b)
       const int J = I;
       TG cc[4] = {0, 0, 0, 0}, gs[4] = {0, 0, 0, 0};
+      // rows s = 16J + 4g .. + 3: G_s, raw k and its scale, for every block I2
+      const GV4 Gs4 = gt4(16 * J + 4 * g);
+      const f32x4 ks4 = tile4(kT, 16 * J + 4 * g), rks4 = sc4(rk, 16 * J + 4 * g);
 #pragma unroll
       for (int I2 = J; I2 < NB; ++I2) {
         const int c0 = 16 * I2;
@@ -549,12 +574,13 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
           y = VJ::mma(VJ::load(ap), fb, y);
         }
         y = VJ::fix(y);
+        const TG gc0 = static_cast<TG>(Gk[c0 ^ swk]);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int s_ = 16 * J + 4 * g + rr;
-          const TG f = dec(c0, s_);
+          const TG f = VJ::ex(gc0 - static_cast<TG>(Gs4[rr]));  // exp(G_b - G_s), b = c0
           cc[rr] += y[rr] * f;
-          gs[rr] += VJ::rnd(khat(s_) * f) * y[rr];  // the row side's B operand value
+          // the row side's B operand value
+          gs[rr] += VJ::rnd(static_cast<TG>(ks4[rr]) * static_cast<TG>(rks4[rr]) * f) * y[rr];
         }
       }
 #pragma unroll
@@ -590,11 +616,13 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   for (int jm = 0; jm < MR; ++jm) {
     const int m = row_block(jm);
     if (m >= NB) break;
+    const int r0 = 16 * m + 4 * g;
+    const f32x4 q4 = tile4(qT, r0), k4 = tile4(kT, r0), rq4 = sc4(rq, r0), rk4 = sc4(rk, r0);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int r = 16 * m + 4 * g + rr;
-      const float pq = sum16(to_f(qT[kk * LDQ + (r ^ swk)]) * rq[r] * aq[jm][rr]);
-      const float pk = sum16(to_f(kT[kk * LDQ + (r ^ swk)]) * rk[r] * ak[jm][rr]);
+      const int r = r0 + rr;
+      const float pq = sum16(q4[rr] * rq4[rr] * aq[jm][rr]);
+      const float pk = sum16(k4[rr] * rk4[rr] * ak[jm][rr]);
       if (i == 0) {
         rowp[0][kb][r] = pq;
         rowp[1][kb][r] = pk;
@@ -699,13 +727,15 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     for (int jm = 0; jm < MR; ++jm) {
       const int m = row_block(jm);
       if (m >= NB) break;
+      const int r0 = 16 * m + 4 * g;
+      const f32x4 q4 = tile4(qT, r0), k4 = tile4(kT, r0), rq4 = sc4(rq, r0), rk4 = sc4(rk, r0);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int r = 16 * m + 4 * g + rr;
+        const int r = r0 + rr;
         if (r < L.len) {
           const float qd = rsum[0][r], kd = rsum[1][r];
-          const float qbar = to_f(qT[kk * LDQ + (r ^ swk)]) * rq[r];
-          const float khat_ = to_f(kT[kk * LDQ + (r ^ swk)]) * rk[r];
+          const float qbar = q4[rr] * rq4[rr];
+          const float khat_ = k4[rr] * rk4[rr];
           dq_s[r * LDA + kk] = from_f<TI>(rqs[r] * (aq[jm][rr] - qbar * qd));
           dk_s[r * LDA + kk] = from_f<TI>(rk[r] * (ak[jm][rr] - khat_ * kd));
         }
