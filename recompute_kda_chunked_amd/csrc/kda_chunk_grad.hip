@@ -281,9 +281,9 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       OpT* dst = dBv_s + r * LDA + vv;
       float part = 0.f;
       const f32x4 vv4 = unpack4<TI>(vin[jt]);
+      store4<OpT>(dst, acc);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        dst[rr] = from_f<OpT>(acc[rr]);
         part += r < L.len ? acc[rr] * vv4[rr] : 0.f;
         dvv[jt][rr] = be[r] * acc[rr];
       }
@@ -451,9 +451,9 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     for (int rr = 0; rr < 4; ++rr) {
       dXq[(r0 + rr) * LDX + s_] = from_f<OpT>(xq[jp][rr]);
       dXk[(r0 + rr) * LDX + s_] = from_f<OpT>(xk[jp][rr]);
-      dXqT[s_ * LDX + r0 + rr] = from_f<OpT>(xq[jp][rr]);
-      dXkT[s_ * LDX + r0 + rr] = from_f<OpT>(xk[jp][rr]);
     }
+    store4<OpT>(dXqT + s_ * LDX + r0, xq[jp]);  // four adjacent columns
+    store4<OpT>(dXkT + s_ * LDX + r0, xk[jp]);
   }
   __syncthreads();
 

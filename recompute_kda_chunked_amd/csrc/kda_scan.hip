@@ -464,9 +464,7 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
         const OpT* bd = dhT_s + (16 * nv + i) * LDH + g * KPL;
 #pragma unroll
         for (int j = 0; j < G::NKF; ++j) acc = M::mma(cur.kg[j], M::load(bd + j * KS), acc);
-        OpT* dst = dVnT_s + (16 * nv + i) * LDC + 16 * m + 4 * g;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f<OpT>(acc[rr]);
+        store4<OpT>(dVnT_s + (16 * nv + i) * LDC + 16 * m + 4 * g, acc);
         // dVn^T, fragment-major [V][C]
         store4_fm<OpT>(static_cast<OpT*>(st.dVnT) + idx * V * C, v0 + 16 * nv + i, 16 * m + 4 * g, C, acc);
       }
