@@ -399,7 +399,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   {
     const OpT* Ug = static_cast<const OpT*>(ops.U) + idx * C * V;
     const OpT* Wng = static_cast<const OpT*>(ops.Wn) + idx * C * K;
-    const OpT* Pg = static_cast<const OpT*>(ops.P) + idx * C * C;
+    const OpT* PTg = static_cast<const OpT*>(ops.PT) + idx * C * C;
 #pragma unroll
     for (int jp = 0; jp < PPW; ++jp) {
       const int p = w + NW * jp;
@@ -407,7 +407,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       if (p >= NPAIR) break;
       int m = 0, ns = p;
       while (ns > m) { ns -= m + 1; ++m; }
-      // global operands of this pair first (U and -W rows of block ns, P)
+      // global operands of this pair first (U and -W rows of block ns, P^T)
       constexpr int NKV = V / KS;
       typename M::frag fu[NKV], fw[NKV];
       uint32_t pv[4];  // raw: converted at use
@@ -416,8 +416,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         fu[j] = M::load(Ug + FragMajor<OpT>::frag(ns, j, V, lane));  // both fragment-major
         fw[j] = M::load(Wng + FragMajor<OpT>::frag(ns, j, K, lane));
       }
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) pv[rr] = load_bits<OpT>(Pg + (16 * m + 4 * g + rr) * C + 16 * ns + i);
+      load4_raw<OpT>(PTg + (16 * ns + i) * C + 16 * m + 4 * g, pv);  // P[16m + 4g + rr][16ns + i]
       const f32x4 aqk = tile_nt<OpT>(zero4(), dO_s + 16 * m * LDA, LDA, Vn_s + 16 * ns * LDA, LDA, 0, V, lane);
       f32x4 a1 = zero4(), a2 = zero4();
 #pragma unroll
@@ -426,13 +425,14 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         a1 = M::mma(M::load(dBv_s + ao), fu[j], a1);
         a2 = M::mma(M::load(dKb_s + ao), fw[j], a2);
       }
+      const f32x4 p4 = unpack4<OpT>(pv);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int r = 16 * m + 4 * g + rr, s_ = 16 * ns + i;
         xq[jp][rr] = (s_ <= r) ? aqk[rr] : 0.f;
         const float dakk = (s_ < r) ? (a2[rr] - a1[rr]) : 0.f;
         xk[jp][rr] = be[r] * dakk;
-        const float pb = sum16(dakk * bits_to_f<OpT>(pv[rr]));
+        const float pb = sum16(dakk * p4[rr]);
         if (i == 0) dbp[w][r] += pb;
       }
     }

@@ -301,8 +301,10 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     if (!STATE) store_aqk(aqv);
     {
       if (BWD) {
-        OpT* P = static_cast<OpT*>(ops.P) + idx * C * C;
-        for (int e = tid; e < C * C; e += 256) P[e] = from_f<OpT>(Ms[(e / C) * LDM + e % C]);
+        // P^T, so that the gradient kernel reads a lane's four rows of one
+        // column as one vector
+        OpT* PT = static_cast<OpT*>(ops.PT) + idx * C * C;
+        for (int e = tid; e < C * C; e += 256) PT[e] = from_f<OpT>(Ms[(e % C) * LDM + e / C]);
       }
       float* gam = ops.gam + idx * K;
       for (int kk = tid; kk < K; kk += 256) gam[kk] = GU::ex(Gs[(C - 1) * LDG + kk]);

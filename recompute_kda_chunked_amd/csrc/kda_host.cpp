@@ -134,7 +134,7 @@ ChunkOps carve_ops(const Plan& P, bool bwd, unsigned char*& cur) {
     o.qgT = take(n * K * C * e);
     o.WnT = take(n * K * C * e);
     o.TT = take(n * C * C * e);
-    o.P = take(n * C * C * e);
+    o.PT = take(n * C * C * e);
   }
   return o;
 }

@@ -29,7 +29,7 @@ struct Inputs {
 // the chunk index relative to the segment start. Operand element type is
 // bf16 for bf16 problems and fp32 for fp32 problems. Wn, U, qg, kgT, Aqk,
 // AqkT, kg, qgT, WnT and TT are stored fragment-major (FragMajor in
-// kda_device.h); P is row-major.
+// kda_device.h); PT is row-major.
 struct ChunkOps {
   void *Wn;    // [C][K]  -W  (W = T (beta * kh * e^G))
   void *U;     // [C][V]  U = T (beta * v)
@@ -43,7 +43,7 @@ struct ChunkOps {
   void *qgT;   // [K][C]
   void *WnT;   // [K][C]
   void *TT;    // [C][C]  T^T
-  void *P;     // [C][C]  gated k.k without beta, strictly lower
+  void *PT;    // [C][C]  P^T, P = gated k.k without beta (strictly lower)
 };
 
 // States recorded by the backward scans for one segment, element (lc, h) at
