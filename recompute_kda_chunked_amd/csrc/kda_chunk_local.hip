@@ -283,13 +283,13 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   __syncthreads();
   if (BWD) load_items();
 
-  // ---- outputs that leave before the inverse: Aqk (or its transpose), P,
+  // ---- outputs that leave before the inverse: Aqk (or its transpose), P^T,
   // gamma, then one pass over the items computing every gated element-wise
   // operand:
   //   qg = qh e^G, kg = kh e^{G_c - G}, Kb = beta kh e^G, Bv = beta v
-  // Row-major ones are stored directly; transposed ones are staged in LDS
-  // (row pairs packed) and leave as contiguous vectors, or stay as the
-  // operands of W and U.
+  // The untransposed ones (qg or kg) are stored directly, fragment-major;
+  // transposed ones are staged in LDS (row pairs packed) and leave as
+  // contiguous vectors, or wait in registers as the operands of W and U.
   // staged values per item: [0] kg (both), [1] Kb, [2] Bv, [3] qg (backward)
   constexpr int NSV = BWD ? 4 : 3;
   // held in the operand type (bf16 pairs pack into one register): they are
