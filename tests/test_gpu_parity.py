@@ -184,6 +184,19 @@ def test_prologue_step():
         assert e <= 1e-6, (name, e)
 
 
+def test_many_short_sequences():
+    # 300 sequences (more than the chunk table's 256 threads, so each thread
+    # takes two), lengths 1..130 with empty ones among them, three segments
+    announce("many short sequences, N=300")
+    rng = np.random.default_rng(23)
+    lens = [int(v) for v in rng.integers(0, 131, size=300)]
+    lens[0], lens[7], lens[299] = 0, 1, 0
+    x = kda_inputs.make_inputs(lens, 2, 64, 64, torch.float32, seed=23, device="cuda")
+    ref = oracle_run(x)
+    check(gpu_run(x, 32), ref, torch.float32, label="N300 C32")
+    check(gpu_run(x, 64, seg_chunks=97), ref, torch.float32, label="N300 C64 seg97")
+
+
 def test_bitwise_deterministic():
     announce("run-to-run determinism")
     x = kda_inputs.make_inputs([300, 77], 4, 128, 128, torch.bfloat16, seed=19, device="cuda")
