@@ -161,6 +161,14 @@ __device__ __forceinline__ void prologue_load(const Dims& d, const Inputs& in, i
   }
 }
 
+// 1/sqrt(x) on v_rsq_f32 (about 1 ulp) instead of a correctly rounded sqrt
+// and divide (some 40 instructions); a subnormal x is scaled by 2^64 first,
+// which the hardware instruction does not take.
+__device__ __forceinline__ float rsqrt_scaled(float x) {
+  const bool tiny = x < 1.17549435e-38f;
+  return __builtin_amdgcn_rsqf(tiny ? x * 0x1p64f : x) * (tiny ? 0x1p32f : 1.f);
+}
+
 // The gate values of one row vector (VE channels) times gscale, in the
 // precision of GV; rows past the chunk's end (valid false) get 0. MODE is the
 // gate map (hoisted out of the row loop). For fp32 gates the smooth map is
@@ -227,8 +235,8 @@ __device__ __forceinline__ void prologue_compute_m(const Dims& d, const ChunkLoc
 #pragma unroll
       for (int j = 0; j < P::VE; ++j) G(r, c0 + j) = gv[j];
       if (sub == 0) {
-        const float a = valid ? 1.0f / sqrtf(sq + d.eps) : 0.f;
-        const float b = valid ? 1.0f / sqrtf(sk + d.eps) : 0.f;
+        const float a = valid ? rsqrt_scaled(sq + d.eps) : 0.f;
+        const float b = valid ? rsqrt_scaled(sk + d.eps) : 0.f;
         rq[r] = a;
         rqs[r] = d.scale * a;
         rk[r] = b;
