@@ -72,12 +72,28 @@ def _ptr(a: np.ndarray | None):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def _widen_gate(raw_g, dt_bias, T, H, K):
+    """Scalar gate per head and token (raw_g [T,H], dt_bias [H]): the Gated
+    DeltaNet form that FLA's chunk_gdn computes ("KDA at the production
+    shape...", sections 1.1 and 1.2: KDA differs from it only by a decay per
+    key channel). It is the per-channel operator with all K channels of the
+    gate equal, so the inputs are repeated over K here."""
+    if raw_g.ndim != 2:
+        return raw_g, dt_bias, False
+    if raw_g.shape != (T, H) or dt_bias.shape != (H,):
+        raise ValueError("a per-head gate takes raw_g [T,H] and dt_bias [H]")
+    return (np.repeat(raw_g[:, :, None], K, axis=2), np.repeat(dt_bias[:, None], K, axis=1),
+            True)
+
+
 def kda(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, dO=None,
         scale: float = 1.0, lower_bound: float = -5.0, eps: float = 1e-6,
         gate_mode: int = GATE_SIGMOID_BOUND, n_threads: int = 0,
         lib_path: str | None = None, h0=None, dht=None, final_state: bool = False) -> dict:
     """Run the oracle. Shapes: q,k,raw_g [T,H,K]; v [T,H,V]; raw_beta [T,H];
-    A_log [H]; dt_bias [H,K]; cu_seqlens [N+1] (defaults to one sequence);
+    A_log [H]; dt_bias [H,K]; or, for a gate per head, raw_g [T,H] and
+    dt_bias [H] (draw_g and ddt_bias then take those shapes too); cu_seqlens
+    [N+1] (defaults to one sequence);
     dO [T,H,V] or None (forward only); h0 [N,H,K,V] or None (each sequence
     starts from zero); dht [N,H,K,V] or None (no loss on the final state).
 
@@ -90,6 +106,7 @@ def kda(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, dO=None,
     A_log, dt_bias = _f64(A_log), _f64(dt_bias)
     T, H, K = q.shape
     V = v.shape[2]
+    raw_g, dt_bias, per_head = _widen_gate(raw_g, dt_bias, T, H, K)
     if k.shape != (T, H, K) or raw_g.shape != (T, H, K) or v.shape[:2] != (T, H):
         raise ValueError("shape mismatch among q, k, v, raw_g")
     if raw_beta.shape != (T, H) or A_log.shape != (H,) or dt_bias.shape != (H, K):
@@ -136,6 +153,10 @@ def kda(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, dO=None,
                            _ptr(h0), _ptr(ht), _ptr(dht), _ptr(dh0), int(n_threads))
     if rc != 0:
         raise RuntimeError("kda_oracle failed with status %d" % rc)
+    if per_head and dO is not None:
+        # each per-head value feeds all K channels: its gradient is their sum
+        out["draw_g"] = out["draw_g"].sum(axis=2)
+        out["ddt_bias"] = out["ddt_bias"].sum(axis=1)
     return out
 
 
@@ -143,10 +164,12 @@ def prologue(q, k, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, chunk: int 
              scale: float = 1.0, lower_bound: float = -5.0, eps: float = 1e-6,
              gate_mode: int = GATE_SIGMOID_BOUND) -> dict:
     """The prologue alone: qh, kh [T,H,K], beta [T,H] and gcum [T,H,K] (the
-    cumulative gate restarted every ``chunk`` tokens of each sequence)."""
+    cumulative gate restarted every ``chunk`` tokens of each sequence; a
+    per-head gate, raw_g [T,H] and dt_bias [H], gives K equal channels)."""
     q, k, raw_g, raw_beta = map(_f64, (q, k, raw_g, raw_beta))
     A_log, dt_bias = _f64(A_log), _f64(dt_bias)
     T, H, K = q.shape
+    raw_g, dt_bias, _ = _widen_gate(raw_g, dt_bias, T, H, K)
     if cu_seqlens is None:
         cu = np.array([0, T], dtype=np.int64)
     else:
