@@ -21,24 +21,27 @@ if ROOT not in sys.path:
 
 METRIC = "KDA fwd+bwd tokens/s at 1×8K×H64×D128 bf16; peak allocated GiB; %HBM roof"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC_GDN = ("GDN (scalar gate per head) fwd+bwd tokens/s at 1×8K×H64×D128 bf16; "
+              "peak allocated GiB; %HBM roof")
 # Algorithmic bytes per (token, head): what the method itself must move.
-#   forward:  read q, k, v, raw_g (D each) + raw_beta, write O (D)
-#   backward: read q, k, v, raw_g, dO (D each) + raw_beta,
-#             write dq, dk, dv, draw_g (D each) + draw_beta
-def alg_bytes_per_token_head(D: int, esz: int) -> dict:
-    fwd = (4 * D + 1 + D) * esz
-    bwd = (5 * D + 1 + 4 * D + 1) * esz
+#   forward:  read q, k, v (D each), raw_g (G), raw_beta, write O (D)
+#   backward: read q, k, v, dO (D each), raw_g (G), raw_beta,
+#             write dq, dk, dv (D each), draw_g (G), draw_beta
+# with G = D gate values per token-head, or 1 for a gate per head.
+def alg_bytes_per_token_head(D: int, esz: int, G: int) -> dict:
+    fwd = (3 * D + G + 1 + D) * esz
+    bwd = (4 * D + G + 1 + 3 * D + G + 1) * esz
     return {"fwd": fwd, "bwd": bwd, "total": fwd + bwd}
 
 
 # Algorithmic bytes of each kernel per (token, head) of the launch: the
 # compulsory reads/writes of the step it implements (workspace traffic is
 # overhead and is not counted).
-def kernel_alg_bytes(name: str, D: int, esz: int) -> float:
+def kernel_alg_bytes(name: str, D: int, esz: int, G: int) -> float:
     if name == "chunk_grad":      # reads q,k,v,raw_g,raw_beta,dO; writes 5 grads
-        return (5 * D + 1 + 4 * D + 1) * esz
+        return (4 * D + G + 1 + 3 * D + G + 1) * esz
     if name == "chunk_local":     # reads q,k,v,raw_g,raw_beta
-        return (4 * D + 1) * esz
+        return (3 * D + G + 1) * esz
     if name == "scan_fwd":        # writes O (forward launches)
         return D * esz
     if name == "scan_bwd":        # reads dO
@@ -193,30 +196,33 @@ def main() -> int:
     del out
 
     esz = 2 if w.dtype == "bf16" else 4
+    G = 1 if w.gate_per_head else w.D
     th = w.T * w.H
-    alg = alg_bytes_per_token_head(w.D, esz)
+    alg = alg_bytes_per_token_head(w.D, esz, G)
     e2e_frac = alg["total"] * th / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
     d = per_launch[dominant]
     # one launch covers one segment of chunks for all heads: its unit count is
     # (chunk, head) pairs x chunk length = token-heads (the workloads' sequence
     # lengths are multiples of the chunk, so every chunk is full)
     units = d["chunk_heads_per_launch"] * w.chunk
-    achieved = kernel_alg_bytes(dominant, w.D, esz) * units / (d["avg_ms"] / 1e3) / 1e9
+    kab = kernel_alg_bytes(dominant, w.D, esz, G)
+    achieved = kab * units / (d["avg_ms"] / 1e3) / 1e9
     traffic = profile_traffic(dominant, w.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else round(traffic / (d["avg_ms"] / 1e3) / 1e9, 1),
                 "traffic_bytes_per_launch": traffic,
-                "alg_bytes_per_launch": kernel_alg_bytes(dominant, w.D, esz) * units,
-                "kernel": dominant, "alg_bytes_per_token_head": kernel_alg_bytes(dominant, w.D, esz)}
+                "alg_bytes_per_launch": kab * units,
+                "kernel": dominant, "alg_bytes_per_token_head": kab}
 
     line = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC_GDN if w.gate_per_head else METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "n_seqs": len(w.seqlens), "tokens": w.T, "heads": w.H,
-                   "head_dim": w.D, "chunk": w.chunk, "fwd_checkpoints": bool(args.checkpoints)},
+                   "head_dim": w.D, "chunk": w.chunk, "gate": "per head" if w.gate_per_head
+                   else "per channel", "fwd_checkpoints": bool(args.checkpoints)},
         "peak_alloc_gib": round(peak_alloc, 3), "peak_reserved_gib": round(peak_res, 3),
         "e2e_hbm_roof_frac": round(e2e_frac, 4), "wall_s_timed": round(wall, 3),
         "kernels": {k: {kk: round(vv, 4) if isinstance(vv, float) else vv for kk, vv in v.items()}

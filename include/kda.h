@@ -25,7 +25,8 @@
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller, row-major with
  *     the innermost dimension contiguous: q, k, raw_g [T, H, K]; v, o, dO
- *     [T, H, V]; raw_beta [T, H]; A_log [H] (fp32); dt_bias [H, K] (fp32);
+ *     [T, H, V]; raw_beta [T, H]; A_log [H] (fp32); dt_bias [H, K] (fp32)
+ *     (raw_g [T, H] and dt_bias [H] under KDA_GATE_PER_HEAD);
  *     cu_seqlens [n_seqs + 1] (int32, device copy). Pointers must be 16-byte
  *     aligned.
  *   - dtype selects the element type of q, k, v, raw_g, raw_beta, dO, o and
@@ -67,8 +68,13 @@ enum { KDA_F32 = 0, KDA_BF16 = 1 };
      KDA_GATE_SIGMOID_BOUND   g = L * sigmoid(exp(A_log[h]) * z)
      KDA_GATE_SOFTPLUS_CLAMP  g = max(L, -exp(A_log[h]) * softplus(z));
                               no gradient flows where the bound holds.
+   Either may be OR-ed with KDA_GATE_PER_HEAD: one scalar gate per head and
+   token, the Gated DeltaNet form of FLA's chunk_gdn ("KDA at the production
+   shape...", sections 1.1 and 1.2; KDA adds a decay per key channel). Then
+   raw_g and draw_g are [T, H], dt_bias and ddt_bias are [H], z = raw_g[t,h]
+   + dt_bias[h], and every channel of the state decays by the same exp(g).
    Other values: KDA_ERR_UNSUPPORTED. */
-enum { KDA_GATE_SIGMOID_BOUND = 0, KDA_GATE_SOFTPLUS_CLAMP = 1 };
+enum { KDA_GATE_SIGMOID_BOUND = 0, KDA_GATE_SOFTPLUS_CLAMP = 1, KDA_GATE_PER_HEAD = 16 };
 
 typedef struct {
   int32_t n_seqs;          /* N >= 1 packed sequences (empty sequences allowed) */
@@ -79,7 +85,8 @@ typedef struct {
                               16, 32, 64; fp32 K=128: 16, 32; bf16 K=64 or
                               128: 32, 64 (others: KDA_ERR_UNSUPPORTED) */
   int32_t dtype;           /* KDA_F32 or KDA_BF16 */
-  int32_t gate_mode;       /* KDA_GATE_SIGMOID_BOUND or KDA_GATE_SOFTPLUS_CLAMP */
+  int32_t gate_mode;       /* KDA_GATE_SIGMOID_BOUND or KDA_GATE_SOFTPLUS_CLAMP,
+                              optionally | KDA_GATE_PER_HEAD */
   float scale;             /* multiplies qh; 1.0 for the plain o_t = S_t^T qh_t */
   float gate_lower_bound;  /* L < 0, e.g. -5 */
   float l2_eps;            /* eps of the Q/K L2 normalisation, e.g. 1e-6 */
@@ -118,7 +125,8 @@ int kda_fwd(const kda_problem *p, const void *q, const void *k, const void *v,
 
 /* Backward: recomputes every intermediate from the inputs, streaming over
    segments of chunks, and writes dq, dk, draw_g [T,H,K], dv [T,H,V],
-   draw_beta [T,H] (dtype) and dA_log [H], ddt_bias [H,K] (fp32). The
+   draw_beta [T,H] (dtype) and dA_log [H], ddt_bias [H,K] (fp32); draw_g
+   [T,H] and ddt_bias [H] under KDA_GATE_PER_HEAD. The
    gate-parameter gradients are reduced in a fixed order (bitwise
    reproducible run to run). */
 int kda_bwd(const kda_problem *p, const void *q, const void *k, const void *v,

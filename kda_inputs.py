@@ -29,6 +29,7 @@ class Workload:
     seed: int
     A_log: float = 0.0
     dt_bias: float = 0.0
+    gate_per_head: bool = False  # raw_g [T,H], dt_bias [H] (scalar gate)
 
     @property
     def T(self) -> int:
@@ -54,6 +55,10 @@ WORKLOADS = {
     "t8k_h64_bf16": Workload("t8k_h64_bf16", (8192,), 64, 128, "bf16", 64, seed=3),
     "varlen8x8k_h16_bf16": Workload("varlen8x8k_h16_bf16", (8192,) * 8, 16, 128, "bf16", 64, seed=4),
     "t128k_h96_bf16": Workload("t128k_h96_bf16", (131072,), 96, 128, "bf16", 64, seed=5),
+    # the 8K x H64 shape with one scalar gate per head and token (the Gated
+    # DeltaNet form)
+    "gdn_t8k_h64_bf16": Workload("gdn_t8k_h64_bf16", (8192,), 64, 128, "bf16", 64, seed=6,
+                                 gate_per_head=True),
 }
 
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "raw_g": 3, "raw_beta": 4, "dO": 5, "h0": 6, "dht": 7}
@@ -68,11 +73,12 @@ def _randn(shape, seed: int, tensor_id: int, device, dtype) -> torch.Tensor:
 
 def make_inputs(seqlens, H: int, K: int, V: int, dtype=torch.float32, seed: int = 0,
                 device="cpu", A_log: float = 0.0, dt_bias: float = 0.0,
-                with_dO: bool = True) -> dict:
+                with_dO: bool = True, gate_per_head: bool = False) -> dict:
     """Draw one problem. Returns torch tensors on ``device``:
     q,k,raw_g [T,H,K]; v,dO [T,H,V]; raw_beta [T,H] (all ``dtype``);
     A_log [H], dt_bias [H,K] (float32, constant fill); cu_seqlens int32 [N+1]
-    on ``device`` plus ``cu_seqlens_host`` (a Python list).
+    on ``device`` plus ``cu_seqlens_host`` (a Python list). gate_per_head:
+    raw_g [T,H] and dt_bias [H] instead.
     """
     seqlens = [int(n) for n in seqlens]
     T = sum(seqlens)
@@ -83,10 +89,12 @@ def make_inputs(seqlens, H: int, K: int, V: int, dtype=torch.float32, seed: int 
         "q": _randn((T, H, K), seed, TENSOR_IDS["q"], device, dtype),
         "k": _randn((T, H, K), seed, TENSOR_IDS["k"], device, dtype),
         "v": _randn((T, H, V), seed, TENSOR_IDS["v"], device, dtype),
-        "raw_g": _randn((T, H, K), seed, TENSOR_IDS["raw_g"], device, dtype),
+        "raw_g": _randn((T, H) if gate_per_head else (T, H, K), seed, TENSOR_IDS["raw_g"],
+                        device, dtype),
         "raw_beta": _randn((T, H), seed, TENSOR_IDS["raw_beta"], device, dtype),
         "A_log": torch.full((H,), float(A_log), dtype=torch.float32, device=device),
-        "dt_bias": torch.full((H, K), float(dt_bias), dtype=torch.float32, device=device),
+        "dt_bias": torch.full((H,) if gate_per_head else (H, K), float(dt_bias),
+                              dtype=torch.float32, device=device),
         "cu_seqlens": torch.tensor(cu, dtype=torch.int32, device=device),
         "cu_seqlens_host": cu,
     }
@@ -104,4 +112,4 @@ def make_states(n_seqs: int, H: int, K: int, V: int, seed: int = 0, device="cpu"
 
 def workload_inputs(w: Workload, device="cpu", with_dO: bool = True) -> dict:
     return make_inputs(w.seqlens, w.H, w.D, w.D, w.torch_dtype, w.seed, device,
-                       w.A_log, w.dt_bias, with_dO)
+                       w.A_log, w.dt_bias, with_dO, w.gate_per_head)

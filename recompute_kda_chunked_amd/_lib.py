@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(HERE, "_build", "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
-KDA_GATE_SIGMOID_BOUND, KDA_GATE_SOFTPLUS_CLAMP = 0, 1
+KDA_GATE_SIGMOID_BOUND, KDA_GATE_SOFTPLUS_CLAMP, KDA_GATE_PER_HEAD = 0, 1, 16
 
 # Every function the header declares (checked against include/kda.h by the tests).
 EXPORTS = ("kda_fwd_workspace_bytes", "kda_bwd_workspace_bytes", "kda_check_problem",

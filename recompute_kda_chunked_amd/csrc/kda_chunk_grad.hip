@@ -599,11 +599,11 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // The raw gate rows come in as 16-byte vectors and wait in LDS for the gate
   // VJP (whose thread-per-channel mapping would otherwise take a 2-byte load
   // per element); dq, dk and draw_g go out the same way, staged in LDS.
+  // (a per-head gate, d.gate_head, is read in S8 instead)
   VT xrow[VPT];
-  const float dbias = in.dt_bias[hoff + tid % D];
-  // exp(A_log) in the gate's precision, as the forward's gate map takes it
-  const TG eat = exp(static_cast<TG>(in.A_log[h]));
-  {
+  float dbias = 0.f;
+  if (!d.gate_head) {
+    dbias = in.dt_bias[hoff + tid % D];
     const TI* xr = static_cast<const TI*>(in.g) + L.t0 * ts + hoff;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -612,6 +612,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       xrow[j] = *reinterpret_cast<const VT*>(xr + rc * ts + c);
     }
   }
+  // exp(A_log) in the gate's precision, as the forward's gate map takes it
+  const TG eat = exp(static_cast<TG>(in.A_log[h]));
 #pragma unroll
   for (int jm = 0; jm < MR; ++jm) {
     const int m = row_block(jm);
@@ -646,10 +648,12 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   TI* xg_s = reinterpret_cast<TI*>(uni + OFF_X);
   TI* dq_s = xg_s + C * LDA;
   TI* dk_s = dq_s + C * LDA;
+  if (!d.gate_head) {
 #pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
-    if (e < NV) *reinterpret_cast<VT*>(xg_s + r * LDA + c) = xrow[j];
+    for (int j = 0; j < VPT; ++j) {
+      const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
+      if (e < NV) *reinterpret_cast<VT*>(xg_s + r * LDA + c) = xrow[j];
+    }
   }
 #pragma unroll
   for (int jm = 0; jm < MR; ++jm) {
@@ -696,13 +700,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     // (fp64 for fp32 problems: the dA_log sum cancels heavily)
     TG pdt = 0, pA = 0;
     float dxv[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = tid + NT * j, r = e / D, kc = e % D;
-      const bool ok = e < C * D && r < L.len;
-      const TG xb = static_cast<TG>(to_f(xg_s[(r < C ? r : 0) * LDA + kc])) + static_cast<TG>(dbias);
-      const TG dgv = ok ? static_cast<TG>(dGT[kc * LDG + (r < C ? r : 0)]) : TG(0);
-      TG dx, dA;
+    // dx = dg/dx and dA = dg/dA times dgv, for a raw gate plus bias xb
+    auto gate_vjp = [&](TG xb, TG dgv, TG& dx, TG& dA) {
       if (d.gate_mode == 0) {
         // g = L sigmoid(z), z = e^A (x + b): dg/dx = e^A L s (1 - s), dg/dA = z L s (1 - s)
         const TG z = eat * xb, sz = VJ::sig(z);
@@ -717,9 +716,43 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         dx = act ? -dgv * eat * VJ::sig(xb) : TG(0);
         dA = act ? dgv * c : TG(0);
       }
-      dxv[j] = static_cast<float>(dx);
-      pdt += dx;
-      pA += dA;
+    };
+    if (d.gate_head) {
+      // one raw value per row: TPR threads share row hr, and the row's dG
+      // summed over all channels (fixed order: a run of D / TPR channels per
+      // thread, then a butterfly over the row's TPR lanes) drives the gate
+      // map's VJP once
+      constexpr int TPR = NT / C;
+      static_assert(NT % C == 0 && D % TPR == 0 && TPR <= 64, "per-head gate VJP layout");
+      const int hr = tid / TPR;
+      const TI* xr = static_cast<const TI*>(in.g) + L.t0 * d.H + h;
+      const uint32_t xhead = load_bits<TI>(xr + static_cast<size_t>(hr < L.len ? hr : L.len - 1) * d.H);
+      dbias = in.dt_bias[h];
+      TG sg = 0;
+#pragma unroll
+      for (int j = 0; j < D / TPR; ++j) sg += dGT[((tid % TPR) * (D / TPR) + j) * LDG + hr];
+#pragma unroll
+      for (int o = TPR / 2; o > 0; o >>= 1) sg += __shfl_xor(sg, o, kWave);
+      const bool ok = hr < L.len && tid % TPR == 0;
+      TG dx, dA;
+      gate_vjp(static_cast<TG>(bits_to_f<TI>(xhead)) + static_cast<TG>(dbias), ok ? sg : TG(0),
+               dx, dA);
+      if (ok) dg[(L.t0 + hr) * d.H + h] = from_f<TI>(static_cast<float>(dx));
+      pdt = dx;
+      pA = dA;
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int e = tid + NT * j, r = e / D, kc = e % D;
+        const bool ok = e < C * D && r < L.len;
+        const TG xb = static_cast<TG>(to_f(xg_s[(r < C ? r : 0) * LDA + kc])) + static_cast<TG>(dbias);
+        const TG dgv = ok ? static_cast<TG>(dGT[kc * LDG + (r < C ? r : 0)]) : TG(0);
+        TG dx, dA;
+        gate_vjp(xb, dgv, dx, dA);
+        dxv[j] = static_cast<float>(dx);
+        pdt += dx;
+        pA += dA;
+      }
     }
     TI* dqo = dq + L.t0 * ts + hoff;
     TI* dko = dk + L.t0 * ts + hoff;
@@ -743,12 +776,15 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     }
     // draw_g over the raw gate: each element is read and rewritten by the
     // same thread
+    if (!d.gate_head) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = tid + NT * j, r = e / D, kc = e % D;
-      if (e < C * D) xg_s[r * LDA + kc] = from_f<TI>(dxv[j]);
+      for (int j = 0; j < PER; ++j) {
+        const int e = tid + NT * j, r = e / D, kc = e % D;
+        if (e < C * D) xg_s[r * LDA + kc] = from_f<TI>(dxv[j]);
+      }
     }
-    // tid % D is this thread's channel for every e above
+    // tid % D is this thread's channel for every e above (a per-head gate
+    // leaves its row sums in these columns; the reduction adds them all)
     ptg[tid] = pdt;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) pA += __shfl_xor(pA, o, kWave);
@@ -777,7 +813,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       if (e < NV && r < L.len) {
         *reinterpret_cast<VT*>(dqo + r * ts + c) = *reinterpret_cast<const VT*>(dq_s + r * LDA + c);
         *reinterpret_cast<VT*>(dko + r * ts + c) = *reinterpret_cast<const VT*>(dk_s + r * LDA + c);
-        *reinterpret_cast<VT*>(dgo + r * ts + c) = *reinterpret_cast<const VT*>(xg_s + r * LDA + c);
+        if (!d.gate_head)
+          *reinterpret_cast<VT*>(dgo + r * ts + c) = *reinterpret_cast<const VT*>(xg_s + r * LDA + c);
       }
     }
   }
@@ -837,10 +874,39 @@ __global__ void __launch_bounds__(256) k_gate_reduce(int D, int H, int n_chunks,
   }
 }
 
-hipError_t launch_gate_reduce(int D, int H, int n_chunks, const double* partials,
-                              float* dA_log, float* ddt_bias, hipStream_t s) {
-  hipLaunchKernelGGL(k_gate_reduce, dim3(H, (D + 1 + 63) / 64), dim3(256), 0, s, D, H, n_chunks,
-                     partials, dA_log, ddt_bias);
+// The per-head gate's dA_log[h] and ddt_bias[h]: block h. Column k of the
+// partials (k <= D) is summed over the even, then the odd chunks in order by
+// one thread each; thread 0 then adds the D gate columns in order
+// (deterministic).
+__global__ void __launch_bounds__(256) k_gate_reduce_head(int D, int H, int n_chunks,
+                                                          const double* partials, float* dA_log,
+                                                          float* ddt_bias) {
+  __shared__ double red[2][129];
+  const int h = blockIdx.x, part = threadIdx.x >> 7;
+  for (int k = threadIdx.x & 127; k <= D; k += 128) {
+    double s = 0.0;
+#pragma unroll 8
+    for (int c = part; c < n_chunks; c += 2) s += partials[(static_cast<size_t>(c) * H + h) * (D + 1) + k];
+    red[part][k] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int k = 0; k < D; ++k) t += red[0][k] + red[1][k];
+    ddt_bias[h] = static_cast<float>(t);
+    dA_log[h] = static_cast<float>(red[0][D] + red[1][D]);
+  }
+}
+
+hipError_t launch_gate_reduce(int D, int H, int n_chunks, int gate_head,
+                              const double* partials, float* dA_log, float* ddt_bias,
+                              hipStream_t s) {
+  if (gate_head)
+    hipLaunchKernelGGL(k_gate_reduce_head, dim3(H), dim3(256), 0, s, D, H, n_chunks, partials,
+                       dA_log, ddt_bias);
+  else
+    hipLaunchKernelGGL(k_gate_reduce, dim3(H, (D + 1 + 63) / 64), dim3(256), 0, s, D, H,
+                       n_chunks, partials, dA_log, ddt_bias);
   return hipGetLastError();
 }
 

@@ -51,7 +51,8 @@ int check_problem(const kda_problem* p) {
     return KDA_ERR_INVALID;
   if (p->seg_chunks < 0 || p->chunk < 1) return KDA_ERR_INVALID;
   if (p->dtype != KDA_F32 && p->dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-  if (p->gate_mode != KDA_GATE_SIGMOID_BOUND && p->gate_mode != KDA_GATE_SOFTPLUS_CLAMP)
+  const int gmap = p->gate_mode & ~KDA_GATE_PER_HEAD;
+  if (gmap != KDA_GATE_SIGMOID_BOUND && gmap != KDA_GATE_SOFTPLUS_CLAMP)
     return KDA_ERR_UNSUPPORTED;
   if (p->K != p->V) return KDA_ERR_UNSUPPORTED;
   if (!supported(p->dtype, p->K, p->chunk)) return KDA_ERR_UNSUPPORTED;
@@ -234,7 +235,8 @@ Dims make_dims(const kda_problem* p) {
   d.scale = p->scale;
   d.lb = p->gate_lower_bound;
   d.eps = p->l2_eps;
-  d.gate_mode = p->gate_mode;
+  d.gate_mode = p->gate_mode & ~KDA_GATE_PER_HEAD;
+  d.gate_head = (p->gate_mode & KDA_GATE_PER_HEAD) ? 1 : 0;
   return d;
 }
 
@@ -414,7 +416,7 @@ int kda_bwd_ex(const kda_problem* p, const void* q, const void* k, const void* v
     KDA_TRY(KDA_KERNEL_CHUNK_GRAD, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_grad(P.dtype, P.D, P.C, d, in, dO, c0, c1 - c0, ops_b, sts, dq, dk, dv,
                               draw_g, draw_beta, partials, s));
   }
-  KDA_TRY(KDA_KERNEL_GATE_REDUCE, 0, launch_gate_reduce(P.D, P.H, P.NC, partials, dA_log, ddt_bias, s));
+  KDA_TRY(KDA_KERNEL_GATE_REDUCE, 0, launch_gate_reduce(P.D, P.H, P.NC, d.gate_head, partials, dA_log, ddt_bias, s));
   if (io->dh0 && has_empty_sequence(p))
     KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_state_passthrough(cu_seqlens, P.N, P.H, P.D * P.D, io->dht, io->dh0, s));
   return KDA_OK;

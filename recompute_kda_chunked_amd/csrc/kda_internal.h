@@ -13,6 +13,8 @@ struct Dims {
   int N, H;
   float scale, lb, eps;
   int gate_mode;  // 0: L * sigmoid(e^A (x + b)); 1: max(L, -e^A softplus(x + b))
+  int gate_head;  // 1: one gate per head and token (raw_g [T][H], dt_bias [H],
+                  // draw_g [T][H], ddt_bias [H]); 0: one per channel
 };
 
 // Raw operator inputs (device pointers, dtype per the problem).
@@ -106,7 +108,9 @@ hipError_t launch_chunk_grad(int dtype, int D, int C, const Dims& d, const Input
                              const ChunkOps& ops, const SegStates& st, void* dq, void* dk,
                              void* dv, void* dg, void* dbeta, double* partials,
                              hipStream_t s);
-hipError_t launch_gate_reduce(int D, int H, int n_chunks, const double* partials,
-                              float* dA_log, float* ddt_bias, hipStream_t s);
+// gate_head: ddt_bias[h] is the sum over all K partial columns of head h.
+hipError_t launch_gate_reduce(int D, int H, int n_chunks, int gate_head,
+                              const double* partials, float* dA_log, float* ddt_bias,
+                              hipStream_t s);
 
 }  // namespace kda

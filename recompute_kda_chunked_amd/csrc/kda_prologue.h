@@ -10,7 +10,9 @@
 //      (a smooth map onto (L, 0), the default)
 //   1: g = max(L, -exp(A_log[h]) * softplus(raw_g + dt_bias[h,:]))
 //      (the softplus decay clamped at the bound)
-// The
+// With gate_head set there is one gate per head and token (raw_g [T][H],
+// dt_bias [H]): the scalar-gate Gated DeltaNet form ("KDA at the production
+// shape...", sections 1.1 and 1.2), computed as K equal channels. The
 // chunk-local cumulative sum of g is taken in fp32, as the FLA forward keeps
 // its gate cumulative sum (FROST page, "Where FLA's memory goes").
 #pragma once
@@ -122,6 +124,7 @@ struct ProRows {
   static_assert(D % VE == 0 && 64 % LPR == 0, "prologue row layout");
   VT qv[NIT], kv[NIT], xv[NIT];
   uint32_t bv[NIT];
+  uint32_t xs[NIT];  // raw gate bits of a per-head gate (xv unused then)
   float alog, db[VE];
 };
 
@@ -144,19 +147,29 @@ __device__ __forceinline__ void prologue_load(const Dims& d, const Inputs& in, i
   const TI* rb = static_cast<const TI*>(in.beta) + L.t0 * d.H + h;
   // the per-head parameters first: the arithmetic needs them with the first row
   p.alog = in.A_log[h];
+  if (d.gate_head) {
+    const float b = in.dt_bias[h];
 #pragma unroll
-  for (int j = 0; j < P::VE; j += 4) {
-    const f32x4 b4 = *reinterpret_cast<const f32x4*>(in.dt_bias + static_cast<size_t>(h) * D + c0 + j);
+    for (int j = 0; j < P::VE; ++j) p.db[j] = b;
+  } else {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) p.db[j + jj] = b4[jj];
+    for (int j = 0; j < P::VE; j += 4) {
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(in.dt_bias + static_cast<size_t>(h) * D + c0 + j);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) p.db[j + jj] = b4[jj];
+    }
   }
+  const TI* xh = static_cast<const TI*>(in.g) + L.t0 * d.H + h;  // per-head gate
 #pragma unroll
   for (int it = 0; it < P::NIT; ++it) {
     const int r = (w + NW * it) * P::RPI + rsub;
     const int rc = r < L.len ? r : L.len - 1;
     p.qv[it] = *reinterpret_cast<const VT*>(q + rc * ts);
     p.kv[it] = *reinterpret_cast<const VT*>(k + rc * ts);
-    p.xv[it] = *reinterpret_cast<const VT*>(x + rc * ts);
+    if (d.gate_head)
+      p.xs[it] = load_bits<TI>(xh + static_cast<size_t>(rc) * d.H);
+    else
+      p.xv[it] = *reinterpret_cast<const VT*>(x + rc * ts);
     p.bv[it] = load_bits<TI>(rb + static_cast<size_t>(rc) * d.H);
   }
 }
@@ -197,6 +210,17 @@ __device__ __forceinline__ void gate_vec(const Dims& d, GV ea, const float* db,
   }
 }
 
+// The gate value of a per-head gate (raw bits xs of one row, bias b), times
+// gscale, repeated over the VE channels; 0 for rows past the chunk's end.
+template <int MODE, typename TI, int VE, typename GV>
+__device__ __forceinline__ void gate_head(const Dims& d, GV ea, float b, uint32_t xs, bool valid,
+                                          GV gscale, GV* out) {
+  const GV xb = static_cast<GV>(bits_to_f<TI>(xs)) + static_cast<GV>(b);
+  const GV gv = valid ? gate_map<GV>(MODE, ea, xb, static_cast<GV>(d.lb)) * gscale : GV(0);
+#pragma unroll
+  for (int j = 0; j < VE; ++j) out[j] = gv;
+}
+
 // The prologue's arithmetic on loaded rows: for each row the per-row scalars
 // and the gate value of each channel into G(r, k) (a functor returning a
 // reference into LDS). Rows r >= len are padding: q = k = 0, beta = 0, g = 0,
@@ -206,7 +230,7 @@ __device__ __forceinline__ void gate_vec(const Dims& d, GV ea, const float* db,
 //   rk[r]  = 1/sqrt(|k|^2 + eps)  (kh = k * rk)
 //   be[r]  = sigmoid(raw_beta)
 // gscale multiplies every gate value written to G (1 for natural units).
-template <int MODE, typename TI, int D, int C, int NW, class GRef>
+template <int MODE, bool PH, typename TI, int D, int C, int NW, class GRef>
 __device__ __forceinline__ void prologue_compute_m(const Dims& d, const ChunkLoc& L,
                                                    const ProRows<TI, D, C, NW>& p, float* rq,
                                                    float* rqs, float* rk, float* be, GRef G,
@@ -231,7 +255,10 @@ __device__ __forceinline__ void prologue_compute_m(const Dims& d, const ChunkLoc
     sk = group_sum<P::LPR>(sk);
     if (r < C) {
       GV gv[P::VE];
-      gate_vec<MODE, TI, P::VE, GV>(d, ea, p.db, p.xv[it], valid, gscale, gv);
+      if constexpr (PH)
+        gate_head<MODE, TI, P::VE, GV>(d, ea, p.db[0], p.xs[it], valid, gscale, gv);
+      else
+        gate_vec<MODE, TI, P::VE, GV>(d, ea, p.db, p.xv[it], valid, gscale, gv);
 #pragma unroll
       for (int j = 0; j < P::VE; ++j) G(r, c0 + j) = gv[j];
       if (sub == 0) {
@@ -251,10 +278,17 @@ __device__ __forceinline__ void prologue_compute(const Dims& d, const ChunkLoc& 
                                                  const ProRows<TI, D, C, NW>& p, float* rq,
                                                  float* rqs, float* rk, float* be, GRef G,
                                                  typename GateT<TI>::T gscale = 1) {
-  if (d.gate_mode == 0)
-    prologue_compute_m<0, TI, D, C, NW>(d, L, p, rq, rqs, rk, be, G, gscale);
-  else
-    prologue_compute_m<1, TI, D, C, NW>(d, L, p, rq, rqs, rk, be, G, gscale);
+  if (d.gate_head) {
+    if (d.gate_mode == 0)
+      prologue_compute_m<0, true, TI, D, C, NW>(d, L, p, rq, rqs, rk, be, G, gscale);
+    else
+      prologue_compute_m<1, true, TI, D, C, NW>(d, L, p, rq, rqs, rk, be, G, gscale);
+  } else {
+    if (d.gate_mode == 0)
+      prologue_compute_m<0, false, TI, D, C, NW>(d, L, p, rq, rqs, rk, be, G, gscale);
+    else
+      prologue_compute_m<1, false, TI, D, C, NW>(d, L, p, rq, rqs, rk, be, G, gscale);
+  }
 }
 
 // Both parts: loads, then arithmetic.

@@ -61,6 +61,8 @@ def _raise(lib, st: int, what: str):
 
 
 def _check_inputs(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, extra=()):
+    """Shapes, dtypes and placement; a raw_g of two dimensions selects the
+    gate per head and token (raw_g [T,H], dt_bias [H])."""
     dev = q.device
     if dev.type != "cuda":
         raise KdaError("inputs must be on a GPU device")
@@ -69,9 +71,11 @@ def _check_inputs(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, extra=()
     dt = q.dtype
     if dt not in _DT:
         raise KdaError("dtype must be float32 or bfloat16")
+    per_head = raw_g.dim() == 2
+    gk = (T, H) if per_head else (T, H, K)
     want = {"q": (q, (T, H, K), dt), "k": (k, (T, H, K), dt), "v": (v, (T, H, V), dt),
-            "raw_g": (raw_g, (T, H, K), dt), "raw_beta": (raw_beta, (T, H), dt),
-            "A_log": (A_log, (H,), torch.float32), "dt_bias": (dt_bias, (H, K), torch.float32),
+            "raw_g": (raw_g, gk, dt), "raw_beta": (raw_beta, (T, H), dt),
+            "A_log": (A_log, (H,), torch.float32), "dt_bias": (dt_bias, gk[1:], torch.float32),
             "cu_seqlens": (cu_seqlens, (cu_seqlens.shape[0],), torch.int32)}
     for name, (t, shape, dtype) in list(want.items()) + list(extra):
         if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
@@ -79,7 +83,11 @@ def _check_inputs(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, extra=()
                            % (name, shape, dtype, tuple(t.shape), t.dtype))
         if t.device != dev or not t.is_contiguous() or t.data_ptr() % 16:
             raise KdaError("%s must be contiguous, 16-byte aligned and on %s" % (name, dev))
-    return T, H, K, V, dt
+    return T, H, K, V, dt, per_head
+
+
+def _gate_flags(gate_mode, per_head):
+    return int(gate_mode) | (_lib.KDA_GATE_PER_HEAD if per_head else 0)
 
 
 def _cu_host(cu_seqlens, cu_seqlens_host):
@@ -127,7 +135,8 @@ def kda_forward(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, *,
                 cu_seqlens_host=None, scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6,
                 seg_chunks=0, gate_mode=_lib.KDA_GATE_SIGMOID_BOUND, initial_state=None,
                 output_final_state=False, save_checkpoints=False, out=None):
-    """O [T,H,V] of the KDA operator.
+    """O [T,H,V] of the KDA operator. raw_g [T,H] with dt_bias [H] gives one
+    scalar gate per head and token (the Gated DeltaNet form).
 
     initial_state: fp32 [N,H,K,V] state each sequence starts from (zero when
     None). With output_final_state or save_checkpoints the result is
@@ -136,12 +145,12 @@ def kda_forward(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, *,
     kda_backward (None unless save_checkpoints)."""
     if cu_seqlens is None:
         cu_seqlens, cu_seqlens_host = _default_cu(q.shape[0], q.device)
-    T, H, K, V, dt = _check_inputs(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens)
+    T, H, K, V, dt, ph = _check_inputs(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens)
     cu_host = _cu_host(cu_seqlens, cu_seqlens_host)
     N = len(cu_host) - 1
     _check_state("initial_state", initial_state, (N, H, K, V), q.device)
     prob = Problem(T, H, K, V, dt, cu_host, chunk, scale, lower_bound, eps, seg_chunks,
-                   gate_mode)
+                   _gate_flags(gate_mode, ph))
     lib = _lib.load()
     _raise(lib, prob.check(), "kda_fwd")
     dev = q.device
@@ -167,22 +176,23 @@ def kda_backward(q, k, v, raw_g, raw_beta, A_log, dt_bias, dO, cu_seqlens=None, 
                  cu_seqlens_host=None, scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6,
                  seg_chunks=0, gate_mode=_lib.KDA_GATE_SIGMOID_BOUND, initial_state=None,
                  d_final_state=None, checkpoints=None):
-    """Gradients (dq, dk, dv, draw_g, draw_beta, dA_log, ddt_bias) of
+    """Gradients (dq, dk, dv, draw_g, draw_beta, dA_log, ddt_bias, each shaped
+    as its input) of
     sum(O * dO) + sum(ht * d_final_state), recomputing every chunk's
     intermediates from the inputs; dh0 is appended when initial_state is
     given. checkpoints: the forward's Checkpoints for the same problem (the
     backward then skips the pass that recomputes the segment states)."""
     if cu_seqlens is None:
         cu_seqlens, cu_seqlens_host = _default_cu(q.shape[0], q.device)
-    T, H, K, V, dt = _check_inputs(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens,
-                                   extra=[("dO", (dO, tuple(v.shape), v.dtype))])
+    T, H, K, V, dt, ph = _check_inputs(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens,
+                                       extra=[("dO", (dO, tuple(v.shape), v.dtype))])
     cu_host = _cu_host(cu_seqlens, cu_seqlens_host)
     N = len(cu_host) - 1
     dev = q.device
     _check_state("initial_state", initial_state, (N, H, K, V), dev)
     _check_state("d_final_state", d_final_state, (N, H, K, V), dev)
     prob = Problem(T, H, K, V, dt, cu_host, chunk, scale, lower_bound, eps, seg_chunks,
-                   gate_mode)
+                   _gate_flags(gate_mode, ph))
     lib = _lib.load()
     _raise(lib, prob.check(), "kda_bwd")
     if checkpoints is not None and lib.kda_bwd_segment_chunks(prob.ref) != checkpoints.seg_chunks:
@@ -194,7 +204,7 @@ def kda_backward(q, k, v, raw_g, raw_beta, A_log, dt_bias, dO, cu_seqlens=None, 
     dg = torch.empty_like(raw_g)
     db = torch.empty_like(raw_beta)
     dA = torch.empty((H,), dtype=torch.float32, device=dev)
-    ddt = torch.empty((H, K), dtype=torch.float32, device=dev)
+    ddt = torch.empty_like(dt_bias)
     dh0 = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) \
         if initial_state is not None else None
     io = _state_io(h0=initial_state, dht=d_final_state, dh0=dh0,
@@ -216,9 +226,9 @@ def kda_prologue(q, k, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, *,
     """fp32 (qh, kh, beta, gcum) of the prologue step alone."""
     if cu_seqlens is None:
         cu_seqlens, cu_seqlens_host = _default_cu(q.shape[0], q.device)
-    T, H, K, V, dt = _check_inputs(q, k, q, raw_g, raw_beta, A_log, dt_bias, cu_seqlens)
+    T, H, K, V, dt, ph = _check_inputs(q, k, q, raw_g, raw_beta, A_log, dt_bias, cu_seqlens)
     prob = Problem(T, H, K, K, dt, _cu_host(cu_seqlens, cu_seqlens_host), chunk, scale,
-                   lower_bound, eps, gate_mode=gate_mode)
+                   lower_bound, eps, gate_mode=_gate_flags(gate_mode, ph))
     lib = _lib.load()
     _raise(lib, prob.check(), "kda_prologue")
     dev = q.device

@@ -68,6 +68,8 @@ def test_valid_problem_and_workspace_sizes(lib):
     (dict(chunk=48), _lib.KDA_ERR_UNSUPPORTED),
     (dict(dtype=7), _lib.KDA_ERR_UNSUPPORTED),
     (dict(gate_mode=2), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(gate_mode=2 | _lib.KDA_GATE_PER_HEAD), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(gate_mode=32), _lib.KDA_ERR_UNSUPPORTED),
 ])
 def test_bad_problems_are_rejected(lib, kw, code):
     p = good(**kw)
@@ -75,6 +77,13 @@ def test_bad_problems_are_rejected(lib, kw, code):
     assert p.fwd_ws() == 0 and p.bwd_ws() == 0
     nul = ctypes.c_void_p(0)
     assert lib.kda_fwd(p.ref, *([nul] * 9), nul, ctypes.c_size_t(0), nul) == code
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_per_head_gate_flag_is_accepted(lib, mode):
+    p = good(gate_mode=mode | _lib.KDA_GATE_PER_HEAD)
+    assert p.check() == _lib.KDA_OK
+    assert p.fwd_ws() == good(gate_mode=mode).fwd_ws() > 0
 
 
 def test_null_pointers_and_small_workspace_rejected_before_any_launch(lib):

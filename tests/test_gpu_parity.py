@@ -32,10 +32,10 @@ def rel(a, b):
     return float(np.linalg.norm(a - b) / nb)
 
 
-def gpu_run(x, chunk, seg_chunks=0, scale=1.0, with_bwd=True):
+def gpu_run(x, chunk, seg_chunks=0, scale=1.0, with_bwd=True, gate_mode=0):
     args = [x[n] for n in NAMES]
     kw = dict(cu_seqlens_host=x["cu_seqlens_host"], chunk=chunk, seg_chunks=seg_chunks,
-              scale=scale)
+              scale=scale, gate_mode=gate_mode)
     out = {"o": kda_forward(*args, x["cu_seqlens"], **kw)}
     if with_bwd:
         out.update(zip(GRADS, kda_backward(*args, x["dO"], x["cu_seqlens"], **kw)))
@@ -47,28 +47,54 @@ def to_np(t):
     return t.detach().double().cpu().numpy()
 
 
-def check(got, ref, dtype, heads=None, label=""):
+def check(got, ref, dtype, heads=None, label="", sum_scales=None):
+    """Normalised L2 error of every output against the stated tolerance.
+    sum_scales: for the gate-parameter gradients of a per-head gate in bf16,
+    {name: per-head L2 norms of the per-token terms each one sums}; those are
+    checked per head as |error| <= tolerance * norm instead."""
     tol_o, tol_g = TOL[dtype]
-    errs = {}
+    errs, sums = {}, {}
     for name, r in ref.items():
         t = got[name]
         if heads is not None:  # select on the device: full tensors can be GBs
             t = t[heads] if name in ("dA_log", "ddt_bias") else t[:, heads]
         errs[name] = rel(to_np(t), r)
+        if sum_scales is not None and name in sum_scales:
+            sums[name] = np.abs(to_np(t) - r) / sum_scales[name]
     print(label, " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
     for name, e in errs.items():
         tol = tol_o if name == "o" else tol_g
-        assert np.isfinite(e) and e <= tol, (name, e, tol)
+        if name in sums:
+            print("  %s error over the L2 norm of its terms: %s" % (name, np.array2string(
+                sums[name], precision=2)), flush=True)
+            assert np.all(sums[name] <= tol), (name, sums[name], tol)
+        else:
+            assert np.isfinite(e) and e <= tol, (name, e, tol)
     return errs
 
 
-def oracle_run(x, heads=None, scale=1.0, with_bwd=True):
+def head_gate_sum_scales(x, ref, heads=None):
+    """Per head, the L2 norms of the per-token terms of ddt_bias (draw_g) and
+    of dA_log (draw_g * (raw_g + dt_bias), the smooth gate map) from the
+    oracle's draw_g. A sum of n terms whose errors are independent at a
+    relative level e has an error near e times the L2 norm of its terms; its
+    error relative to the sum itself grows with the cancellation among the
+    terms, which these scalar sums over every token have in plenty."""
+    sel = slice(None) if heads is None else heads
+    xg = x["raw_g"][:, sel].double().cpu().numpy()
+    b = x["dt_bias"][sel].double().cpu().numpy()
+    dg = ref["draw_g"]
+    return {"ddt_bias": np.sqrt(np.sum(dg ** 2, axis=0)),
+            "dA_log": np.sqrt(np.sum((dg * (xg + b[None])) ** 2, axis=0))}
+
+
+def oracle_run(x, heads=None, scale=1.0, with_bwd=True, gate_mode=0):
     sel = (lambda t: t) if heads is None else (lambda t: t[:, heads])
     args = [sel(x[n]) for n in ("q", "k", "v", "raw_g", "raw_beta")]
     A = x["A_log"] if heads is None else x["A_log"][heads]
     B = x["dt_bias"] if heads is None else x["dt_bias"][heads]
     return oracle.kda(*args, A, B, cu_seqlens=x["cu_seqlens_host"],
-                      dO=sel(x["dO"]) if with_bwd else None, scale=scale)
+                      dO=sel(x["dO"]) if with_bwd else None, scale=scale, gate_mode=gate_mode)
 
 
 # ------------------------------------------------------------------ small, full comparison
@@ -214,12 +240,93 @@ def test_chunk_size_invariance_bf16():
     check(gpu_run(x, 64), ref, torch.bfloat16, label="C64")
 
 
+# ------------------------------------------------------------------ scalar gate per head
+
+
+def head_gate_inputs(seqlens, H, D, dtype, seed, per_head_params=True):
+    """raw_g [T,H] ~ N(0,1); a different A_log and dt_bias for every head, or
+    both zero as in the measured workloads."""
+    x = kda_inputs.make_inputs(seqlens, H, D, D, dtype, seed=seed, device="cuda",
+                               gate_per_head=True)
+    if per_head_params:
+        x["A_log"].copy_(torch.linspace(-0.6, 0.4, H))
+        x["dt_bias"].copy_(torch.linspace(0.5, -0.9, H))
+    return x
+
+
+@pytest.mark.parametrize("gate_mode", [0, 1])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_head_gate_fp32_ragged(chunk, gate_mode):
+    announce("per-head gate fp32 ragged D64 chunk %d mode %d" % (chunk, gate_mode))
+    x = head_gate_inputs(RAGGED, 3, 64, torch.float32, seed=51)
+    check(gpu_run(x, chunk, gate_mode=gate_mode), oracle_run(x, gate_mode=gate_mode),
+          torch.float32, label="head C%d m%d" % (chunk, gate_mode))
+
+
+@pytest.mark.parametrize("D,chunk", [(128, 64), (128, 32), (64, 64), (64, 32)])
+def test_head_gate_bf16_ragged_segments(D, chunk):
+    # dA_log and ddt_bias of a per-head gate are sums over all tokens of
+    # terms that cancel heavily (28-fold for head 1's dA_log at D = 64); the
+    # bf16 operands move them by up to 2.6e-2 of their value, and the
+    # per-channel path with the same gate repeated over K moves them the
+    # same way. They are held to the tolerance against the scale of their
+    # terms (head_gate_sum_scales).
+    announce("per-head gate bf16 ragged D%d chunk %d, segments of 2 chunks" % (D, chunk))
+    x = head_gate_inputs(RAGGED + [130], 2, D, torch.bfloat16, seed=52)
+    ref = oracle_run(x)
+    sc = head_gate_sum_scales(x, ref)
+    check(gpu_run(x, chunk), ref, torch.bfloat16, label="head bf16 D%d C%d" % (D, chunk),
+          sum_scales=sc)
+    check(gpu_run(x, chunk, seg_chunks=2), ref, torch.bfloat16, label="seg 2", sum_scales=sc)
+
+
+def test_head_gate_fp32_d128_slow_decay():
+    announce("per-head gate fp32 D128 chunk 32, slow decay")
+    x = head_gate_inputs([300, 1, 97], 2, 128, torch.float32, seed=53)
+    x["dt_bias"].fill_(-8.0)
+    check(gpu_run(x, 32, seg_chunks=3), oracle_run(x), torch.float32, label="head slow")
+
+
+def test_head_gate_switching_at_the_bound():
+    # gates switch per token between exactly 0 and exactly the bound, a
+    # different pattern in each head, under both gate maps
+    announce("per-head gate switching between 0 and the bound")
+    for dt, D in ((torch.float32, 64), (torch.bfloat16, 128)):
+        x = head_gate_inputs([128, 77], 2, D, dt, seed=54)
+        on = torch.rand(x["raw_g"].shape, generator=torch.Generator().manual_seed(54)) < 0.5
+        x["raw_g"].copy_(torch.where(on, 40.0, -1e4).to(dt))
+        x["A_log"].zero_()
+        x["dt_bias"].zero_()
+        for mode in (0, 1):
+            got = gpu_run(x, 64, gate_mode=mode)
+            for name in ("o",) + GRADS:
+                assert torch.isfinite(got[name]).all(), (dt, mode, name)
+            # saturated gates: the gate-parameter gradients are exactly 0
+            check(got, oracle_run(x, gate_mode=mode), dt, label="switch %s m%d" % (dt, mode))
+
+
+def test_head_gate_prologue_step():
+    announce("per-head gate prologue step")
+    x = head_gate_inputs(RAGGED, 3, 128, torch.bfloat16, seed=55)
+    qh, kh, be, gc = kda_prologue(x["q"], x["k"], x["raw_g"], x["raw_beta"], x["A_log"],
+                                  x["dt_bias"], x["cu_seqlens"],
+                                  cu_seqlens_host=x["cu_seqlens_host"], chunk=64)
+    torch.cuda.synchronize()
+    ref = oracle.prologue(x["q"], x["k"], x["raw_g"], x["raw_beta"], x["A_log"], x["dt_bias"],
+                          x["cu_seqlens_host"], chunk=64)
+    for name, t in (("qh", qh), ("kh", kh), ("beta", be), ("gcum", gc)):
+        e = rel(to_np(t), ref[name])
+        print("head prologue", name, "%.2e" % e, flush=True)
+        assert e <= 1e-6, (name, e)
+
+
 # ------------------------------------------------------------------ full-size workloads (sampled heads)
 
 
 @pytest.mark.parametrize("name,heads", [("t8k_h64_bf16", [0, 29, 63]),
                                         ("varlen8x8k_h16_bf16", [3, 15]),
-                                        ("t128k_h96_bf16", [0, 95])])
+                                        ("t128k_h96_bf16", [0, 95]),
+                                        ("gdn_t8k_h64_bf16", [1, 40])])
 def test_bf16_workloads_sampled_heads(name, heads):
     """Full-size launch (every head, the bench's configuration); the oracle
     recomputes the sampled heads, which are independent of the others."""
@@ -228,6 +335,7 @@ def test_bf16_workloads_sampled_heads(name, heads):
     x = kda_inputs.workload_inputs(w, device="cuda")
     got = gpu_run(x, w.chunk)
     ref = oracle_run(x, heads=heads)
-    check(got, ref, torch.bfloat16, heads=heads, label=name)
+    check(got, ref, torch.bfloat16, heads=heads, label=name,
+          sum_scales=head_gate_sum_scales(x, ref, heads) if w.gate_per_head else None)
     del got, x
     torch.cuda.empty_cache()
