@@ -98,8 +98,10 @@ struct TileT<float, D, C> {
 
 // BWD: backward layouts (AqkT, kg, qgT, WnT, TT, P as well). STATE (forward
 // layout only): just the operands of the state recurrence (Wn, U, kg^T,
-// gamma), for a pass that only carries the state.
-template <typename TI, typename OpT, int D, int C, bool BWD, bool STATE>
+// gamma), for a pass that only carries the state. PH: a gate per head
+// (Dims::gate_head), equal in every channel, so each gate factor is one
+// exponential per row instead of one per element.
+template <typename TI, typename OpT, int D, int C, bool BWD, bool STATE, bool PH>
 __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int seg_begin,
                                                      ChunkOps ops) {
   using M = Mma<OpT>;
@@ -192,15 +194,27 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     const int ra = 16 * I + i, rb = 16 * J + i;
     const float sq = rqs[ra], sk = rk[ra], sb = rk[rb];
     f32x4 accP = zero4(), accQ = zero4();
+    // per-head gate: the factors of rows ra and rb (every channel alike)
+    float ea0 = 0.f, eb0 = 0.f;
+    if constexpr (PH) {
+      const GV gb = Gs[16 * I * LDG];
+      ea0 = GU::ex(Gs[ra * LDG] - gb);
+      eb0 = GU::ex(gb - Gs[rb * LDG]);
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int kk = ks * KS + g * KPL;
       float ea[KPL], eb[KPL];
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
-        const GV gb = Gs[16 * I * LDG + kk + j];
-        ea[j] = GU::ex(Gs[ra * LDG + kk + j] - gb);
-        eb[j] = GU::ex(gb - Gs[rb * LDG + kk + j]);
+        if constexpr (PH) {
+          ea[j] = ea0;
+          eb[j] = eb0;
+        } else {
+          const GV gb = Gs[16 * I * LDG + kk + j];
+          ea[j] = GU::ex(Gs[ra * LDG + kk + j] - gb);
+          eb[j] = GU::ex(gb - Gs[rb * LDG + kk + j]);
+        }
       }
       const auto fk = M::make([&](int j) { return el(f.xk[ks], j) * sk * ea[j]; });
       const auto fb = M::make([&](int j) { return el(f.xb[ks], j) * sb * eb[j]; });
@@ -318,11 +332,21 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
       for (int h2 = 0; h2 < 2; ++h2) {
         const int r = 2 * rp + h2;
         const float sq = rqs[r], sk = rk[r], b = be[r];
+        float eGr = 0.f, eGcr = 0.f;  // per-head gate: one pair per row
+        if constexpr (PH) {
+          const GV gr = Gs[r * LDG];
+          eGr = GU::ex(gr);
+          eGcr = GU::ex(Gs[(C - 1) * LDG] - gr);
+        }
         VT out;
 #pragma unroll
         for (int j = 0; j < VE; ++j) {
-          const GV gr = Gs[r * LDG + c0 + j];
-          const float eG = GU::ex(gr), eGc = GU::ex(Gs[(C - 1) * LDG + c0 + j] - gr);
+          float eG = eGr, eGc = eGcr;
+          if constexpr (!PH) {
+            const GV gr = Gs[r * LDG + c0 + j];
+            eG = GU::ex(gr);
+            eGc = GU::ex(Gs[(C - 1) * LDG + c0 + j] - gr);
+          }
           const float kh = to_f(xk[it][h2][j]) * sk;
           const float qg = STATE ? 0.f : to_f(xq[it][h2][j]) * sq * eG;
           const OpT kg = from_f<OpT>(kh * eGc);
@@ -485,27 +509,30 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   }
 }
 
-template <typename TI, typename OpT, int D, int C>
+template <typename TI, typename OpT, int D, int C, bool PH>
 static hipError_t launch_cl(int mode, const Dims& d, const Inputs& in, int seg_begin,
                             int seg_chunks, const ChunkOps& ops, hipStream_t s) {
   const dim3 grid(seg_chunks * d.H), block(256);
   if (mode == KL_BWD)
-    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, true, false>), grid, block, 0, s, d, in,
-                       seg_begin, ops);
+    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, true, false, PH>), grid, block, 0, s, d,
+                       in, seg_begin, ops);
   else if (mode == KL_STATE)
-    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, false, true>), grid, block, 0, s, d, in,
-                       seg_begin, ops);
+    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, false, true, PH>), grid, block, 0, s, d,
+                       in, seg_begin, ops);
   else
-    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, false, false>), grid, block, 0, s, d, in,
-                       seg_begin, ops);
+    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, false, false, PH>), grid, block, 0, s, d,
+                       in, seg_begin, ops);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_local(int dtype, int D, int C, int mode, const Dims& d,
                               const Inputs& in, int seg_begin, int seg_chunks,
                               const ChunkOps& ops, hipStream_t s) {
-#define KDA_CL(TI, DD, CC) \
-  if (D == DD && C == CC) return launch_cl<TI, TI, DD, CC>(mode, d, in, seg_begin, seg_chunks, ops, s);
+#define KDA_CL(TI, DD, CC)                                                                  \
+  if (D == DD && C == CC)                                                                   \
+    return d.gate_head                                                                      \
+               ? launch_cl<TI, TI, DD, CC, true>(mode, d, in, seg_begin, seg_chunks, ops, s) \
+               : launch_cl<TI, TI, DD, CC, false>(mode, d, in, seg_begin, seg_chunks, ops, s);
   if (dtype == 0) {
     KDA_CL(float, 64, 16) KDA_CL(float, 64, 32) KDA_CL(float, 64, 64)
     KDA_CL(float, 128, 16) KDA_CL(float, 128, 32)
