@@ -106,7 +106,9 @@ struct Vjp<float> {
 template <int D>
 constexpr int grad_split() { return D >= 128 ? 1 : 2; }
 
-template <typename TI, typename OpT, int D, int C>
+// PH: a gate per head (Dims::gate_head): one raw gate value and one gate
+// VJP per row.
+template <typename TI, typename OpT, int D, int C, bool PH>
 __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, Inputs in, const TI* dO,
                                                     int seg_begin, ChunkOps ops, SegStates st,
                                                     TI* dq, TI* dk, TI* dv, TI* dg, TI* dbeta,
@@ -599,10 +601,10 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // The raw gate rows come in as 16-byte vectors and wait in LDS for the gate
   // VJP (whose thread-per-channel mapping would otherwise take a 2-byte load
   // per element); dq, dk and draw_g go out the same way, staged in LDS.
-  // (a per-head gate, d.gate_head, is read in S8 instead)
+  // (a per-head gate is read in S8 instead)
   VT xrow[VPT];
   float dbias = 0.f;
-  if (!d.gate_head) {
+  if constexpr (!PH) {
     dbias = in.dt_bias[hoff + tid % D];
     const TI* xr = static_cast<const TI*>(in.g) + L.t0 * ts + hoff;
 #pragma unroll
@@ -648,7 +650,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   TI* xg_s = reinterpret_cast<TI*>(uni + OFF_X);
   TI* dq_s = xg_s + C * LDA;
   TI* dk_s = dq_s + C * LDA;
-  if (!d.gate_head) {
+  if constexpr (!PH) {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
@@ -717,7 +719,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         dA = act ? dgv * c : TG(0);
       }
     };
-    if (d.gate_head) {
+    if constexpr (PH) {
       // one raw value per row: TPR threads share row hr, and the row's dG
       // summed over all channels (fixed order: a run of D / TPR channels per
       // thread, then a butterfly over the row's TPR lanes) drives the gate
@@ -776,7 +778,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     }
     // draw_g over the raw gate: each element is read and rewritten by the
     // same thread
-    if (!d.gate_head) {
+    if constexpr (!PH) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int e = tid + NT * j, r = e / D, kc = e % D;
@@ -813,19 +815,19 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       if (e < NV && r < L.len) {
         *reinterpret_cast<VT*>(dqo + r * ts + c) = *reinterpret_cast<const VT*>(dq_s + r * LDA + c);
         *reinterpret_cast<VT*>(dko + r * ts + c) = *reinterpret_cast<const VT*>(dk_s + r * LDA + c);
-        if (!d.gate_head)
+        if constexpr (!PH)
           *reinterpret_cast<VT*>(dgo + r * ts + c) = *reinterpret_cast<const VT*>(xg_s + r * LDA + c);
       }
     }
   }
 }
 
-template <typename TI, int D, int C>
+template <typename TI, int D, int C, bool PH>
 static hipError_t launch_cg(const Dims& d, const Inputs& in, const void* dO, int seg_begin,
                             int seg_chunks, const ChunkOps& ops, const SegStates& st, void* dq,
                             void* dk, void* dv, void* dg, void* dbeta, double* partials,
                             hipStream_t s) {
-  hipLaunchKernelGGL((k_chunk_grad<TI, TI, D, C>), dim3(seg_chunks * d.H), dim3(D * 4 * grad_split<D>()), 0, s, d,
+  hipLaunchKernelGGL((k_chunk_grad<TI, TI, D, C, PH>), dim3(seg_chunks * d.H), dim3(D * 4 * grad_split<D>()), 0, s, d,
                      in, static_cast<const TI*>(dO), seg_begin, ops, st, static_cast<TI*>(dq),
                      static_cast<TI*>(dk), static_cast<TI*>(dv), static_cast<TI*>(dg),
                      static_cast<TI*>(dbeta), partials);
@@ -837,10 +839,12 @@ hipError_t launch_chunk_grad(int dtype, int D, int C, const Dims& d, const Input
                              const ChunkOps& ops, const SegStates& st, void* dq, void* dk,
                              void* dv, void* dg, void* dbeta, double* partials,
                              hipStream_t s) {
-#define KDA_CG(TI, DD, CC)                                                                  \
-  if (D == DD && C == CC)                                                                   \
-    return launch_cg<TI, DD, CC>(d, in, dO, seg_begin, seg_chunks, ops, st, dq, dk, dv, dg, \
-                                 dbeta, partials, s);
+#define KDA_CG(TI, DD, CC)                                                                     \
+  if (D == DD && C == CC)                                                                      \
+    return d.gate_head ? launch_cg<TI, DD, CC, true>(d, in, dO, seg_begin, seg_chunks, ops, st, \
+                                                     dq, dk, dv, dg, dbeta, partials, s)        \
+                       : launch_cg<TI, DD, CC, false>(d, in, dO, seg_begin, seg_chunks, ops,    \
+                                                      st, dq, dk, dv, dg, dbeta, partials, s);
   if (dtype == 0) {
     KDA_CG(float, 64, 16) KDA_CG(float, 64, 32) KDA_CG(float, 64, 64)
     KDA_CG(float, 128, 16) KDA_CG(float, 128, 32)

@@ -1,6 +1,7 @@
 """GPU parity of the extensions beyond the measured setting, against the FP64
 oracle (needs an MI355X): the softplus-clamp gate map, initial and final
-states with their gradients, and forward-saved segment checkpoints.
+states with their gradients, forward-saved segment checkpoints, and the
+scalar gate per head through all of them.
 
 Tolerances as for the operator itself (normalised L2 over a whole tensor):
 fp32 problems 1e-5; bf16 problems 5e-3 for O and the final state, 2e-2 for
@@ -170,3 +171,34 @@ def test_autograd_with_states():
     got = {"o": o, "ht": ht, "dh0": h0.grad}
     got.update({g: leaves[n].grad for n, g in zip(NAMES, GRADS)})
     check(got, ref, torch.float32, label="autograd")
+
+
+# ------------------------------------------------------------------ scalar gate per head
+
+
+@pytest.mark.parametrize("chunk,seg", [(32, 2), (64, 0)])
+def test_head_gate_with_states_and_checkpoints(chunk, seg):
+    # one gate per head and token, each head with its own A_log and dt_bias,
+    # through initial/final states, forward-saved checkpoints and autograd
+    announce("per-head gate, states and checkpoints, fp32 D64 C%d seg %d" % (chunk, seg))
+    x = kda_inputs.make_inputs(RAGGED_EMPTY, 3, 64, 64, torch.float32, seed=46, device="cuda",
+                               gate_per_head=True)
+    x["A_log"].copy_(torch.tensor([0.3, -0.5, 0.1]))
+    x["dt_bias"].copy_(torch.tensor([-1.0, 0.6, 2.0]))
+    st = kda_inputs.make_states(len(RAGGED_EMPTY), 3, 64, 64, seed=46, device="cuda")
+    ref = oracle_run(x, st=st)
+    plain = gpu_run(x, chunk, seg_chunks=seg, st=st)
+    check(plain, ref, torch.float32, label="head states")
+    saved = gpu_run(x, chunk, seg_chunks=seg, st=st, checkpoints=True)
+    for name in plain:
+        assert torch.equal(plain[name], saved[name]), name
+    leaves = {n: x[n].clone().requires_grad_(True) for n in NAMES}
+    h0 = st["h0"].clone().requires_grad_(True)
+    o, ht = kda(*[leaves[n] for n in NAMES], x["cu_seqlens"],
+                cu_seqlens_host=x["cu_seqlens_host"], chunk=chunk, seg_chunks=seg,
+                initial_state=h0, output_final_state=True)
+    ((o * x["dO"]).sum() + (ht * st["dht"]).sum()).backward()
+    got = {"o": o, "ht": ht, "dh0": h0.grad}
+    got.update({g: leaves[n].grad for n, g in zip(NAMES, GRADS)})
+    assert got["draw_g"].shape == x["raw_g"].shape and got["ddt_bias"].shape == (3,)
+    check(got, ref, torch.float32, label="head autograd")
