@@ -1,0 +1,71 @@
+"""Seeded random problems against the FP64 oracle (needs an MI355X): packed
+batches of 1-5 sequences of 0-150 tokens (empty and one-token sequences
+included; bf16 batches lengthened to 256 token-heads), 1-3 heads, D 64 or 128, every built chunk size, both gate maps,
+per-channel and per-head gates, random scale and streaming segments.
+
+Tolerances as in test_gpu_parity (normalised L2): fp32 1e-5; bf16 5e-3 for
+O and 2e-2 for each gradient; the two gate-parameter gradients, which are
+sums over every token of a head (and over channels for dA_log), are held to
+the gradient tolerance times the L2 norm of their terms instead: with random
+A_log and dt_bias on short batches such sums can cancel to near zero (one
+fp32 case, a single head with a gate per head, reaches 1.001e-5 of its sum).
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+from test_gpu_parity import GRADS, NAMES, check, gate_sum_scales, oracle_run
+
+from recompute_kda_chunked_amd import kda_backward, kda_forward
+
+pytestmark = pytest.mark.gpu
+
+# bf16 rounding errors are correlated along an output row (a row's few
+# rounded scalars enter all of its elements), so the normalised L2 error of
+# a handful of rows scatters by tens of percent around its mean (about 4e-3
+# for O): bf16 problems get at least this many (token, head) rows
+MIN_BF16_ROWS = 256
+
+BUILT = {(torch.float32, 64): (16, 32, 64), (torch.float32, 128): (16, 32),
+         (torch.bfloat16, 64): (32, 64), (torch.bfloat16, 128): (32, 64)}
+
+
+def draw_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    n = int(rng.integers(1, 6))
+    lens = [int(v) for v in rng.integers(0, 151, size=n)]
+    if n > 1 and rng.random() < 0.5:
+        lens[int(rng.integers(0, n))] = 1
+    if n > 1 and rng.random() < 0.5:
+        lens[int(rng.integers(0, n))] = 0
+    if sum(lens) == 0:
+        lens[-1] = 1
+    dtype = torch.float32 if rng.random() < 0.5 else torch.bfloat16
+    D = 64 if rng.random() < 0.5 else 128
+    chunk = int(rng.choice(BUILT[(dtype, D)]))
+    H = int(rng.integers(1, 4))
+    if dtype == torch.bfloat16 and sum(lens) * H < MIN_BF16_ROWS:
+        lens[-1] += -(-MIN_BF16_ROWS // H) - sum(lens)
+    return dict(lens=lens, H=H, D=D, dtype=dtype, chunk=chunk,
+                per_head=bool(rng.random() < 0.5), gate_mode=int(rng.integers(0, 2)),
+                seg=int(rng.integers(0, 4)), scale=float(rng.choice([1.0, D ** -0.5])),
+                A_log=float(rng.uniform(-0.5, 0.5)), dt_bias=float(rng.uniform(-1.0, 1.0)))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_problem(seed):
+    c = draw_case(seed)
+    print("\n[case] seed %d %s" % (seed, c), flush=True)
+    x = kda_inputs.make_inputs(c["lens"], c["H"], c["D"], c["D"], c["dtype"], seed=60 + seed,
+                               device="cuda", A_log=c["A_log"], dt_bias=c["dt_bias"],
+                               gate_per_head=c["per_head"])
+    kw = dict(cu_seqlens_host=x["cu_seqlens_host"], chunk=c["chunk"], seg_chunks=c["seg"],
+              scale=c["scale"], gate_mode=c["gate_mode"])
+    args = [x[n] for n in NAMES]
+    got = {"o": kda_forward(*args, x["cu_seqlens"], **kw)}
+    got.update(zip(GRADS, kda_backward(*args, x["dO"], x["cu_seqlens"], **kw)))
+    torch.cuda.synchronize()
+    ref = oracle_run(x, scale=c["scale"], gate_mode=c["gate_mode"])
+    check(got, ref, c["dtype"], label="seed %d" % seed,
+          sum_scales=gate_sum_scales(x, ref, gate_mode=c["gate_mode"]))
