@@ -1,7 +1,8 @@
 """Seeded random problems against the FP64 oracle (needs an MI355X): packed
 batches of 1-5 sequences of 0-150 tokens (empty and one-token sequences
-included; bf16 batches lengthened to 256 token-heads), 1-3 heads, D 64 or 128, every built chunk size, both gate maps,
-per-channel and per-head gates, random scale and streaming segments.
+included; bf16 batches lengthened to 256 token-heads), 1-3 heads, D 64 or
+128, every built chunk size, both gate maps, per-channel and per-head gates,
+random scale and streaming segments.
 
 Tolerances as in test_gpu_parity (normalised L2): fp32 1e-5; bf16 5e-3 for
 O and 2e-2 for each gradient; the two gate-parameter gradients, which are
