@@ -143,6 +143,11 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   __shared__ float rsum[2][C];  // rowp summed over key blocks
   __shared__ GV ptot[NT];
   __shared__ TG csum[SPLIT][NKB][16];
+  // per-head gate: the gate factors of S6 depend on rows only, one table for
+  // the block: eblk[I][s] = exp(G_{16I} - G_s) for s < 16(I + 1) (0 above),
+  // ediag[r] = exp(G_r - G_{16 floor(r/16)})
+  __shared__ TG eblk[PH ? NB * C : 1];
+  __shared__ TG ediag[PH ? C : 1];
 
   OpT* dBv_s = reinterpret_cast<OpT*>(uni);
   OpT* dO_s = dBv_s + C * LDA;
@@ -262,6 +267,18 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   for (int e = tid; e < 2 * NKB * C; e += NT) (&rowp[0][0][0])[e] = 0.f;
   __syncthreads();
   cumsum_rows<D, C, NT>(Gf, ptot);
+  if constexpr (PH) {
+    // every channel holds the same cumulative gate; channel 0's column of
+    // G^T is stored in row order (its permutation is the identity). Read
+    // first in S6, after several barriers.
+    for (int e = tid; e < NB * C; e += NT) {
+      const int I = e / C, s_ = e % C;
+      eblk[e] = s_ < 16 * (I + 1) ? VJ::ex(static_cast<TG>(GT[16 * I]) - static_cast<TG>(GT[s_]))
+                                  : TG(0);
+    }
+    for (int r = tid; r < C; r += NT)
+      ediag[r] = VJ::ex(static_cast<TG>(GT[r]) - static_cast<TG>(GT[r & ~15]));
+  }
 
   // ---- S2: dBv = T^T dVn (tiles of dBv^T: value rows, chunk-row columns),
   // ---- S3: dO and Vn tiles into LDS. The h, dh' fragments S4 needs are
@@ -515,12 +532,13 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
           const Rows8 v = rows8(kq, rk, sb);
           const float gb = Gk[b0 ^ swk];
           fb = VJ::make([&](int j) {
-            return sb + j < s_hi ? v.x[j] * v.sc[j] * VJ::ex(gb - v.G[j]) : TG(0);
+            const TG e = PH ? eblk[I * C + sb + j] : VJ::ex(gb - v.G[j]);
+            return sb + j < s_hi ? v.x[j] * v.sc[j] * e : TG(0);
           });
         } else {
           fb = VJ::make([&](int j) {
             const int s_ = s0 + g * VJ::KPL + j;
-            return s_ < s_hi ? khat(s_) * dec(b0, s_) : TG(0);
+            return s_ < s_hi ? khat(s_) * (PH ? eblk[I * C + s_] : dec(b0, s_)) : TG(0);
           });
         }
         const int ao = (16 * I + i) * LDX + s0 + g * VJ::KPL;
@@ -535,7 +553,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       const TG gb0 = static_cast<TG>(Gk[b0 ^ swk]);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const TG f = VJ::ex(static_cast<TG>(G4[rr]) - gb0);  // exp(G_r - G_b)
+        const TG f = PH ? ediag[r0 + rr] : VJ::ex(static_cast<TG>(G4[rr]) - gb0);  // exp(G_r - G_b)
         // dG takes the column side's operand values for this pair, rounded as
         // that side's MFMA operands are (see Vjp)
         const TG Aq = VJ::rnd(static_cast<TG>(q4[rr]) * static_cast<TG>(rqs4[rr]) * f),
@@ -566,11 +584,13 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
             const int rb = c0 + (u & 15);
             const Rows8 v = u < 16 ? rows8(kq, rk, rb) : rows8(qk, rqs, rb);
             const float gc = Gk[c0 ^ swk];
-            fb = VJ::make([&](int j) { return v.x[j] * v.sc[j] * VJ::ex(v.G[j] - gc); });
+            fb = VJ::make([&](int j) {
+              return v.x[j] * v.sc[j] * (PH ? ediag[rb + j] : VJ::ex(v.G[j] - gc));
+            });
           } else {
             fb = VJ::make([&](int j) {
               const int uu = u + j, r = c0 + (uu & 15);
-              return (uu < 16 ? khat(r) : qhat(r)) * dec(r, c0);
+              return (uu < 16 ? khat(r) : qhat(r)) * (PH ? ediag[r] : dec(r, c0));
             });
           }
           y = VJ::mma(VJ::load(ap), fb, y);
@@ -579,7 +599,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         const TG gc0 = static_cast<TG>(Gk[c0 ^ swk]);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const TG f = VJ::ex(gc0 - static_cast<TG>(Gs4[rr]));  // exp(G_b - G_s), b = c0
+          // exp(G_b - G_s), b = c0
+          const TG f = PH ? eblk[I2 * C + 16 * J + 4 * g + rr] : VJ::ex(gc0 - static_cast<TG>(Gs4[rr]));
           cc[rr] += y[rr] * f;
           // the row side's B operand value
           gs[rr] += VJ::rnd(static_cast<TG>(ks4[rr]) * static_cast<TG>(rks4[rr]) * f) * y[rr];
