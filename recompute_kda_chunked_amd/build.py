@@ -23,12 +23,18 @@ SOURCES = ["kda_host.cpp", "kda_prologue.hip", "kda_chunk_local.hip", "kda_scan.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# Per-source additions. The gradient kernel (one 8-wave block per CU, so
+# little latency hiding across waves) is scheduled for instruction-level
+# parallelism: 1.8% faster, bit-identical results. The same strategy made the
+# chunk-local kernel 12% slower (it runs three blocks per CU and lost
+# occupancy), so it applies to this file only.
+SOURCE_FLAGS = {"kda_chunk_grad.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))
