@@ -371,7 +371,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     }
   }
   __syncthreads();  // the gate region is free from here
-  // round 1: kg^T (and qg^T) leave through the staging area
+  // first staging pass: kg^T (and qg^T) leave through the staging area
   auto stage = [&](OpT* tile, int which) {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
@@ -462,7 +462,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     }
   }
   __syncthreads();
-  // round 2: the operands of W and U into the staging area (T is in Tb)
+  // second staging pass: the operands of W and U into the staging area (T is in Tb)
   stage(tile0, 1);
   stage(tile1, 2);
   __syncthreads();
