@@ -2,8 +2,10 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-if ROOT not in sys.path:
-    sys.path.insert(0, ROOT)
+TESTS = os.path.dirname(os.path.abspath(__file__))
+for p in (ROOT, TESTS):  # the tests share helpers from test_gpu_parity
+    if p not in sys.path:
+        sys.path.insert(0, p)
 
 
 def pytest_configure(config):
