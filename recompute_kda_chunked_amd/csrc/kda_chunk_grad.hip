@@ -899,27 +899,27 @@ __global__ void __launch_bounds__(256) k_gate_reduce(int D, int H, int n_chunks,
   }
 }
 
-// The per-head gate's dA_log[h] and ddt_bias[h]: block h. Column k of the
-// partials (k <= D) is summed over the even, then the odd chunks in order by
-// one thread each; thread 0 then adds the D gate columns in order
-// (deterministic).
-__global__ void __launch_bounds__(256) k_gate_reduce_head(int D, int H, int n_chunks,
+// The per-head gate's dA_log[h] and ddt_bias[h]: block h of 512 threads.
+// Column k of the partials (k <= D) is summed by four threads over the
+// chunks c = part, part + 4, ... in order; the four parts are added in part
+// order, then thread 0 adds the D gate columns in order (deterministic).
+__global__ void __launch_bounds__(512) k_gate_reduce_head(int D, int H, int n_chunks,
                                                           const double* partials, float* dA_log,
                                                           float* ddt_bias) {
-  __shared__ double red[2][129];
+  __shared__ double red[4][129];
   const int h = blockIdx.x, part = threadIdx.x >> 7;
   for (int k = threadIdx.x & 127; k <= D; k += 128) {
     double s = 0.0;
 #pragma unroll 8
-    for (int c = part; c < n_chunks; c += 2) s += partials[(static_cast<size_t>(c) * H + h) * (D + 1) + k];
+    for (int c = part; c < n_chunks; c += 4) s += partials[(static_cast<size_t>(c) * H + h) * (D + 1) + k];
     red[part][k] = s;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     double t = 0.0;
-    for (int k = 0; k < D; ++k) t += red[0][k] + red[1][k];
+    for (int k = 0; k < D; ++k) t += ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
     ddt_bias[h] = static_cast<float>(t);
-    dA_log[h] = static_cast<float>(red[0][D] + red[1][D]);
+    dA_log[h] = static_cast<float>(((red[0][D] + red[1][D]) + red[2][D]) + red[3][D]);
   }
 }
 
@@ -927,7 +927,7 @@ hipError_t launch_gate_reduce(int D, int H, int n_chunks, int gate_head,
                               const double* partials, float* dA_log, float* ddt_bias,
                               hipStream_t s) {
   if (gate_head)
-    hipLaunchKernelGGL(k_gate_reduce_head, dim3(H), dim3(256), 0, s, D, H, n_chunks, partials,
+    hipLaunchKernelGGL(k_gate_reduce_head, dim3(H), dim3(512), 0, s, D, H, n_chunks, partials,
                        dA_log, ddt_bias);
   else
     hipLaunchKernelGGL(k_gate_reduce, dim3(H, (D + 1 + 63) / 64), dim3(256), 0, s, D, H,

@@ -4,28 +4,29 @@
 namespace kda {
 
 // coff[n] = number of chunks (of length C) in sequences 0..n-1; coff[N] is the
-// total. One block; each thread owns a contiguous run of sequences.
+// total. One block; each thread owns a contiguous run of sequences. The
+// threads' chunk counts are prefix-summed by a shuffle scan in each wave,
+// then the four wave totals are added in wave order.
 __global__ void __launch_bounds__(256) k_chunk_table(const int32_t* cu, int N, int C, int NC,
                                                      int32_t* coff, int2* cloc) {
-  __shared__ int32_t part[256];
-  const int t = threadIdx.x;
+  __shared__ int32_t wsum[4];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int per = (N + 255) / 256;
   const int b = min(N, t * per), e = min(N, b + per);
   int32_t local = 0;
   for (int n = b; n < e; ++n) local += (cu[n + 1] - cu[n] + C - 1) / C;
-  part[t] = local;
-  __syncthreads();
-  if (t == 0) {
-    int32_t run = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int32_t v = part[i];
-      part[i] = run;
-      run += v;
-    }
-    coff[N] = run;
+  int32_t incl = local;  // inclusive scan within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
   }
+  if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  int32_t run = part[t];
+  int32_t woff = 0;
+  for (int i = 0; i < w; ++i) woff += wsum[i];
+  if (t == 255) coff[N] = woff + incl;
+  int32_t run = woff + incl - local;
   for (int n = b; n < e; ++n) {
     coff[n] = run;
     run += (cu[n + 1] - cu[n] + C - 1) / C;
