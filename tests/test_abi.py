@@ -132,3 +132,22 @@ def test_state_io_validation_before_any_launch(lib):
     args[9] = nul  # dq
     assert lib.kda_bwd_ex(p.ref, *args, None, fake, ctypes.c_size_t(p.bwd_ws()),
                           nul) == _lib.KDA_ERR_INVALID
+
+
+def test_no_fallback_without_the_library(monkeypatch, tmp_path):
+    # a missing library is an error, never a silent CPU or PyTorch path
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load()
+
+
+def test_host_tensors_are_refused():
+    import torch
+    from recompute_kda_chunked_amd import KdaError, kda_forward
+    T, H, D = 8, 1, 64
+    x = {n: torch.zeros((T, H, D)) for n in ("q", "k", "v", "raw_g")}
+    with pytest.raises(KdaError, match="GPU"):
+        kda_forward(x["q"], x["k"], x["v"], x["raw_g"], torch.zeros((T, H)), torch.zeros(H),
+                    torch.zeros((H, D)), torch.tensor([0, T], dtype=torch.int32),
+                    cu_seqlens_host=[0, T])
