@@ -512,18 +512,22 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
 // Value-tile width of both scans. The scans are bound by the operand traffic
 // each block pulls through its CU (every value tile of a head loads the same
 // chunk operands), so the width trades CUs in use against bytes per unit of
-// work: 32 columns while N*H*V/32 blocks (1 wave per SIMD, rotating operand
-// sets in AGPRs as well) fit in one pass over the CUs; 64 columns once they
-// would not (half the operand traffic per state column; measured at H96:
-// forward scan 0.153 -> 0.128 ms, reverse 0.191 -> 0.143 ms per launch,
-// where at H64 64 columns are 1.4x slower than 32).
+// work: 32 columns while the N*H*V/32 blocks (1 wave per SIMD, rotating
+// operand sets in AGPRs as well) fit in one pass over the CUs or fill whole
+// multiples of it; 64 columns when they would leave the CUs unevenly loaded
+// (half the operand traffic per state column). Measured: at H96 (384 blocks
+// of 32 columns) 64 columns take the forward scan 0.150 -> 0.128 ms and the
+// reverse 0.181 -> 0.144 ms per launch; at 8 sequences x H16 (512 blocks, two
+// per CU) 32 columns take them 0.225 -> 0.154 and 0.331 -> 0.218 ms; at H64
+// (256 blocks) 64 columns are 1.4x slower than 32.
 static bool wide_tiles(const Dims& d, int D) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   const long groups = (static_cast<long>(d.N) * d.H + 7) / 8;
-  return groups * 8 * (D / 32) > cus;
+  const long narrow = groups * 8 * (D / 32);
+  return narrow > cus && narrow % cus != 0;
 }
 
 template <typename TI, int D, int C, int BV>
