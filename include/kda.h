@@ -88,7 +88,13 @@ typedef struct {
   int32_t gate_mode;       /* KDA_GATE_SIGMOID_BOUND or KDA_GATE_SOFTPLUS_CLAMP,
                               optionally | KDA_GATE_PER_HEAD */
   float scale;             /* multiplies qh; 1.0 for the plain o_t = S_t^T qh_t */
-  float gate_lower_bound;  /* L < 0, e.g. -5 */
+  float gate_lower_bound;  /* L, -5.9 <= L < 0 (e.g. -5). The kernels split
+                              every decay exp(G_r - G_s) of a chunk around
+                              the first row of a 16-row block, so a factor
+                              reaches exp(15 |L|), which must stay finite in
+                              fp32 for either dtype: L < -5.9 returns
+                              KDA_ERR_UNSUPPORTED, L >= 0 or not finite
+                              KDA_ERR_INVALID */
   float l2_eps;            /* eps of the Q/K L2 normalisation, e.g. 1e-6 */
   int32_t seg_chunks;      /* backward streaming segment in chunks; 0 = automatic */
   const int32_t *cu_seqlens_host; /* host copy of cu_seqlens [N+1]: non-decreasing

@@ -29,6 +29,10 @@ namespace {
 
 thread_local char g_msg[256];
 
+// Largest |L| (gate_lower_bound) for which every gate factor the kernels form
+// stays finite in fp32: 15 * 5.9 = 88.5 < ln(FLT_MAX) = 88.72.
+constexpr float kMaxGateBound = 5.9f;
+
 bool supported(int dtype, int D, int C) {
   if (dtype == KDA_F32)
     return (D == 64 && (C == 16 || C == 32 || C == 64)) || (D == 128 && (C == 16 || C == 32));
@@ -47,6 +51,10 @@ int check_problem(const kda_problem* p) {
     if (cu[n + 1] < cu[n]) return KDA_ERR_INVALID;
   if (cu[p->n_seqs] != p->total_tokens) return KDA_ERR_INVALID;
   if (!(p->gate_lower_bound < 0.f) || !std::isfinite(p->gate_lower_bound)) return KDA_ERR_INVALID;
+  // The gated products split exp(G_r - G_s) around the first row of a 16-row
+  // block, so a factor reaches exp(15 |L|); it must stay finite in fp32
+  // (ln FLT_MAX = 88.72), which holds for |L| <= kMaxGateBound.
+  if (p->gate_lower_bound < -kMaxGateBound) return KDA_ERR_UNSUPPORTED;
   if (!(p->l2_eps >= 0.f) || !std::isfinite(p->l2_eps) || !std::isfinite(p->scale))
     return KDA_ERR_INVALID;
   if (p->seg_chunks < 0 || p->chunk < 1) return KDA_ERR_INVALID;

@@ -60,6 +60,10 @@ def test_valid_problem_and_workspace_sizes(lib):
     (dict(H=0), _lib.KDA_ERR_INVALID),
     (dict(T=0, cu_host=[0, 0]), _lib.KDA_ERR_INVALID),
     (dict(lower_bound=1.0), _lib.KDA_ERR_INVALID),
+    (dict(lower_bound=float("nan")), _lib.KDA_ERR_INVALID),
+    (dict(lower_bound=-10.0), _lib.KDA_ERR_UNSUPPORTED),             # exp(15*10) overflows fp32
+    (dict(lower_bound=-6.0), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(lower_bound=-10.0, dtype=_lib.KDA_F32, K=64, V=64), _lib.KDA_ERR_UNSUPPORTED),
     (dict(eps=-1.0), _lib.KDA_ERR_INVALID),
     (dict(seg_chunks=-2), _lib.KDA_ERR_INVALID),
     (dict(K=96, V=96), _lib.KDA_ERR_UNSUPPORTED),
@@ -77,6 +81,12 @@ def test_bad_problems_are_rejected(lib, kw, code):
     assert p.fwd_ws() == 0 and p.bwd_ws() == 0
     nul = ctypes.c_void_p(0)
     assert lib.kda_fwd(p.ref, *([nul] * 9), nul, ctypes.c_size_t(0), nul) == code
+
+
+@pytest.mark.parametrize("lb", [-5.0, -5.9, -0.5])
+def test_gate_bounds_within_the_finite_range_are_accepted(lib, lb):
+    assert good(lower_bound=lb).check() == _lib.KDA_OK
+    assert good(lower_bound=lb, dtype=_lib.KDA_F32, K=64, V=64).check() == _lib.KDA_OK
 
 
 @pytest.mark.parametrize("mode", [0, 1])

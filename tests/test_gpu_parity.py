@@ -17,6 +17,13 @@ pytestmark = pytest.mark.gpu
 NAMES = ("q", "k", "v", "raw_g", "raw_beta", "A_log", "dt_bias")
 GRADS = ("dq", "dk", "dv", "draw_g", "draw_beta", "dA_log", "ddt_bias")
 TOL = {torch.float32: (1e-5, 1e-5), torch.bfloat16: (5e-3, 2e-2)}
+# Worst single (token, head) row: ||x_row - ref_row|| over the RMS row norm of
+# the reference tensor. A row that is wrong (a dropped term, a row from the
+# wrong chunk, sequence or head) is off by about its own norm, i.e. of order
+# 1 here. Rounding alone keeps the worst row of every tested tensor below
+# 9.4e-2 (bf16; the [T,H] tensors, one value per row, have the longest tails
+# over millions of rows) and 4e-6 (fp32); the bounds sit between the two.
+ROW_TOL = {torch.float32: 1e-4, torch.bfloat16: 0.25}
 
 
 def announce(msg):
@@ -30,6 +37,27 @@ def rel(a, b):
     if nb == 0:
         return float(np.max(np.abs(a))) if a.size else 0.0
     return float(np.linalg.norm(a - b) / nb)
+
+
+def row_stats(a, b):
+    """(sum of squared errors, sum of squared reference values, largest row
+    error, number of rows) of a [T, H, D] or [T, H] tensor pair, rows being
+    (token, head) pairs."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    d2 = (a - b) ** 2
+    if a.ndim == 3:
+        rows = np.sqrt(d2.sum(axis=2))
+    else:
+        rows = np.sqrt(d2)
+    return float(d2.sum()), float((b * b).sum()), float(rows.max()) if rows.size else 0.0, rows.size
+
+
+def worst_row(a, b):
+    """Largest row error over the RMS row norm (0 for an all-zero reference)."""
+    e2, r2, mx, n = row_stats(a, b)
+    rms = np.sqrt(r2 / n) if n else 0.0
+    return mx / rms if rms > 0 else mx
 
 
 def gpu_run(x, chunk, seg_chunks=0, scale=1.0, with_bwd=True, gate_mode=0):
@@ -53,18 +81,24 @@ def check(got, ref, dtype, heads=None, label="", sum_scales=None):
     {name: per-head L2 norms of the per-token terms each one sums}; those are
     checked per head as |error| <= tolerance * norm instead."""
     tol_o, tol_g = TOL[dtype]
-    errs, sums = {}, {}
+    errs, sums, rows = {}, {}, {}
     for name, r in ref.items():
         t = got[name]
         if heads is not None:  # select on the device: full tensors can be GBs
             t = t[heads] if name in ("dA_log", "ddt_bias") else t[:, heads]
-        errs[name] = rel(to_np(t), r)
+        a = to_np(t)
+        errs[name] = rel(a, r)
+        if name not in ("dA_log", "ddt_bias"):
+            rows[name] = worst_row(a, r)
         if sum_scales is not None and name in sum_scales:
             # where every term is exactly zero the error itself is compared,
             # as the normalised error takes max|x| when the reference is 0
             scale = sum_scales[name]
             sums[name] = np.abs(to_np(t) - r) / np.where(scale > 0, scale, 1.0)
     print(label, " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
+    print("  worst row / rms row:", " ".join("%s=%.2e" % kv for kv in rows.items()), flush=True)
+    for name, e in rows.items():
+        assert np.isfinite(e) and e <= ROW_TOL[dtype], (name, "worst row", e, ROW_TOL[dtype])
     for name, e in errs.items():
         tol = tol_o if name == "o" else tol_g
         if name in sums:
@@ -332,24 +366,3 @@ def test_head_gate_prologue_step():
         e = rel(to_np(t), ref[name])
         print("head prologue", name, "%.2e" % e, flush=True)
         assert e <= 1e-6, (name, e)
-
-
-# ------------------------------------------------------------------ full-size workloads (sampled heads)
-
-
-@pytest.mark.parametrize("name,heads", [("t8k_h64_bf16", [0, 29, 63]),
-                                        ("varlen8x8k_h16_bf16", [3, 15]),
-                                        ("t128k_h96_bf16", [0, 95]),
-                                        ("gdn_t8k_h64_bf16", [1, 40])])
-def test_bf16_workloads_sampled_heads(name, heads):
-    """Full-size launch (every head, the bench's configuration); the oracle
-    recomputes the sampled heads, which are independent of the others."""
-    w = kda_inputs.WORKLOADS[name]
-    announce("%s sampled heads %s" % (name, heads))
-    x = kda_inputs.workload_inputs(w, device="cuda")
-    got = gpu_run(x, w.chunk)
-    ref = oracle_run(x, heads=heads)
-    check(got, ref, torch.bfloat16, heads=heads, label=name,
-          sum_scales=gate_sum_scales(x, ref, heads) if w.gate_per_head else None)
-    del got, x
-    torch.cuda.empty_cache()

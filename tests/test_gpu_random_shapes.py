@@ -5,11 +5,13 @@ included; bf16 batches lengthened to 256 token-heads), 1-3 heads, D 64 or
 random scale and streaming segments.
 
 Tolerances as in test_gpu_parity (normalised L2): fp32 1e-5; bf16 5e-3 for
-O and 2e-2 for each gradient; the two gate-parameter gradients, which are
-sums over every token of a head (and over channels for dA_log), are held to
-the gradient tolerance times the L2 norm of their terms instead: with random
-A_log and dt_bias on short batches such sums can cancel to near zero (one
-fp32 case, a single head with a gate per head, reaches 1.001e-5 of its sum).
+O and 2e-2 for each gradient, for every output of every problem, except the
+two gate-parameter gradients of a gate per head: dA_log[h] and ddt_bias[h]
+are then single sums over every token and channel of the head, which cancel
+heavily with random A_log and dt_bias on short batches (41-fold in one fp32
+draw, whose dA_log then reaches 1.001e-5 of its sum at a per-term accuracy of
+2.4e-7), so they are held to the tolerance times the L2 norm of their terms.
+Each case prints the cancellation ratio of both sums.
 """
 import numpy as np
 import pytest
@@ -68,5 +70,15 @@ def test_random_problem(seed):
     got.update(zip(GRADS, kda_backward(*args, x["dO"], x["cu_seqlens"], **kw)))
     torch.cuda.synchronize()
     ref = oracle_run(x, scale=c["scale"], gate_mode=c["gate_mode"])
-    check(got, ref, c["dtype"], label="seed %d" % seed,
-          sum_scales=gate_sum_scales(x, ref, gate_mode=c["gate_mode"]))
+    sc = gate_sum_scales(x, ref, gate_mode=c["gate_mode"])
+    for name in ("dA_log", "ddt_bias"):
+        # cancellation ratio of each sum: L2 norm of its terms over |sum|
+        ratio = sc[name] / np.maximum(np.abs(ref[name]), 1e-300)
+        print("  %s cancellation (terms' norm / |sum|): max %.1f" % (name, float(np.max(ratio))),
+              flush=True)
+    # only the sums of a per-head gate (one value per head over every token and
+    # channel, cancelling up to 41-fold in these draws) are held against the
+    # norm of their terms (see test_gpu_parity.check); the per-channel gate's
+    # sums and every other output meet the stated metric as they are
+    relaxed = c["per_head"]
+    check(got, ref, c["dtype"], label="seed %d" % seed, sum_scales=sc if relaxed else None)
