@@ -179,6 +179,8 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
       f.xb[ks] = M::load(kr + rbc * ts + kk);
     }
   };
+  // forward layout of a bf16 problem: Aqk as a bf16 pair (see do_pair, store_aqk)
+  constexpr bool HL = !BWD && !STATE && sizeof(OpT) == 2;
   auto el = [](const typename M::frag& f, int j) -> float {
     if constexpr (KPL == 1) return to_f(f);
     else return to_f(f[j]);
@@ -217,11 +219,32 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
         }
       }
       const auto fk = M::make([&](int j) { return el(f.xk[ks], j) * sk * ea[j]; });
-      const auto fb = M::make([&](int j) { return el(f.xb[ks], j) * sb * eb[j]; });
-      accP = M::mma(fk, fb, accP);
-      if (!STATE) {
-        const auto fq = M::make([&](int j) { return el(f.xa[ks], j) * sq * ea[j]; });
-        accQ = BWD ? M::mma(fq, fb, accQ) : M::mma(fb, fq, accQ);
+      if constexpr (HL) {
+        // Aqk of the forward layout from bf16 pairs of both operands (hi hi,
+        // lo hi, hi lo): the output takes Aqk directly, and rounding its
+        // operands to bf16 alone would add about one bf16 rounding's worth of
+        // error to O. P (for the inverse) keeps single bf16 operands.
+        float bq[KPL], qv[KPL];
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          bq[j] = el(f.xb[ks], j) * sb * eb[j];
+          qv[j] = el(f.xa[ks], j) * sq * ea[j];
+        }
+        const auto fb = M::make([&](int j) { return bq[j]; });
+        const auto fq = M::make([&](int j) { return qv[j]; });
+        const auto fbl = M::make([&](int j) { return bq[j] - el(fb, j); });
+        const auto fql = M::make([&](int j) { return qv[j] - el(fq, j); });
+        accP = M::mma(fk, fb, accP);
+        accQ = M::mma(fb, fq, accQ);
+        accQ = M::mma(fbl, fq, accQ);
+        accQ = M::mma(fb, fql, accQ);
+      } else {
+        const auto fb = M::make([&](int j) { return el(f.xb[ks], j) * sb * eb[j]; });
+        accP = M::mma(fk, fb, accP);
+        if (!STATE) {
+          const auto fq = M::make([&](int j) { return el(f.xa[ks], j) * sq * ea[j]; });
+          accQ = BWD ? M::mma(fq, fb, accQ) : M::mma(fb, fq, accQ);
+        }
       }
     }
 #pragma unroll
@@ -234,23 +257,41 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   };
   // Aqk (forward) or Aqk^T (backward), fragment-major: the tiles of the
   // wave's pairs, and zeros in the blocks above (Aqk) or below (Aqk^T) the
-  // diagonal, which the scans read as parts of whole fragments
+  // diagonal, which the scans read as parts of whole fragments. The forward
+  // layout of a bf16 problem also stores what rounding Aqk to bf16 dropped
+  // (Aqk_lo), so that the output's intra-chunk product sees Aqk to about
+  // 2^-17 of its value.
+  auto lo4 = [](const f32x4& v) {
+    f32x4 r;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) r[rr] = v[rr] - to_f(from_f<OpT>(v[rr]));
+    return r;
+  };
   auto store_aqk = [&](const f32x4 (&aqv)[PPW]) {
     OpT* dst = static_cast<OpT*>(BWD ? ops.AqkT : ops.Aqk) + idx * C * C;
+    OpT* dlo = HL ? static_cast<OpT*>(ops.Aqk_lo) + idx * C * C : nullptr;
 #pragma unroll
     for (int it = 0; it < PPW; ++it) {
       const int p = w + 4 * it;
       if (p >= NPAIR) break;
       int I, J;
       pair_blocks(p, I, J);
-      if (BWD) store4_fm<OpT>(dst, 16 * J + i, 16 * I + 4 * g, C, aqv[it]);
-      else store4_fm<OpT>(dst, 16 * I + i, 16 * J + 4 * g, C, aqv[it]);
+      if (BWD) {
+        store4_fm<OpT>(dst, 16 * J + i, 16 * I + 4 * g, C, aqv[it]);
+      } else {
+        store4_fm<OpT>(dst, 16 * I + i, 16 * J + 4 * g, C, aqv[it]);
+        if constexpr (HL) store4_fm<OpT>(dlo, 16 * I + i, 16 * J + 4 * g, C, lo4(aqv[it]));
+      }
     }
     for (int zb = w; zb < NB * (NB - 1) / 2; zb += 4) {
       int I = 1, J = zb;  // zb-th block pair with J < I
       while (J >= I) { J -= I; ++I; }
-      if (BWD) store4_fm<OpT>(dst, 16 * I + i, 16 * J + 4 * g, C, zero4());
-      else store4_fm<OpT>(dst, 16 * J + i, 16 * I + 4 * g, C, zero4());
+      if (BWD) {
+        store4_fm<OpT>(dst, 16 * I + i, 16 * J + 4 * g, C, zero4());
+      } else {
+        store4_fm<OpT>(dst, 16 * J + i, 16 * I + 4 * g, C, zero4());
+        if constexpr (HL) store4_fm<OpT>(dlo, 16 * J + i, 16 * I + 4 * g, C, zero4());
+      }
     }
   };
   // ---- the element-wise pass after the pairs works on (row pair, VE
@@ -465,12 +506,31 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   // second staging pass: the operands of W and U into the staging area (T is in Tb)
   stage(tile0, 1);
   stage(tile1, 2);
+  // The forward layout keeps U in fp32 (the state-only pass as well, so that
+  // the states it recomputes equal those the output scan carries, bit for
+  // bit). T has a unit diagonal (exactly 1 in
+  // bf16), so the diagonal term of U = T Bv is Bv itself: what rounding Bv =
+  // beta * v to the operand type dropped is added back at each U element,
+  // from v rows read again here (four values of row 16n + i per tile).
+  constexpr int NMW = (K / 16 + 3) / 4;
+  constexpr bool UFIX = !BWD && sizeof(OpT) == 2;
+  uint32_t vfix[UFIX ? NMW : 1][UFIX ? NB : 1][4];
+  if constexpr (UFIX) {
+#pragma unroll
+    for (int jm = 0; jm < NMW; ++jm) {
+      const int mk = (w + 4 * jm) % (K / 16);  // waves past the last key block: loaded, unused
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const int r = 16 * n + i, rc = r < L.len ? r : L.len - 1;
+        load4_raw<TI>(vr + rc * ts + 16 * mk + 4 * g, vfix[jm][n]);
+      }
+    }
+  }
   __syncthreads();
 
   // ---- W = T Kb and U = T Bv (MFMA). Kb^T / Bv^T fragments come from the
   // staged tiles: lane (i, g) holds channel i and k-slots s0 + g*KPL + j.
   constexpr int NSF = C / KS;  // fragments along the chunk
-  constexpr int NMW = (K / 16 + 3) / 4;
   OpT* Wn = static_cast<OpT*>(ops.Wn) + idx * C * K;
   {
 #pragma unroll
@@ -503,7 +563,22 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
           store4_fm<OpT>(static_cast<OpT*>(ops.WnT) + idx * K * C, 16 * mk + i, 16 * n + 4 * g, C,
                          -acc2[n]);
         }
-        store4_fm<OpT>(static_cast<OpT*>(ops.U) + idx * C * V, 16 * n + i, 16 * mk + 4 * g, V, accu[n]);
+        if constexpr (BWD) {
+          store4_fm<OpT>(static_cast<OpT*>(ops.U) + idx * C * V, 16 * n + i, 16 * mk + 4 * g, V, accu[n]);
+        } else {
+          // fp32, row-major: accu[n][rr] = U[16n + i][16mk + 4g + rr]
+          f32x4 u = accu[n];
+          if constexpr (UFIX) {
+            const int r = 16 * n + i;
+            const f32x4 v4 = unpack4<TI>(vfix[jm][n]);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const float bv = be[r] * v4[rr];  // as staged (element pass)
+              u[rr] += bv - to_f(from_f<OpT>(bv));
+            }
+          }
+          *reinterpret_cast<f32x4*>(ops.Uf + idx * C * V + (16 * n + i) * V + 16 * mk + 4 * g) = u;
+        }
       }
     }
   }

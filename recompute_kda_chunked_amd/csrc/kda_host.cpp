@@ -80,7 +80,7 @@ struct Plan {
 
 size_t fwd_ops_per(const Plan& P) {  // bytes per (chunk, head), forward operands
   const size_t C = P.C, K = P.D;
-  return (4 * C * K + C * C) * P.esz + K * 4;
+  return (3 * C * K + C * C * (P.esz == 2 ? 2 : 1)) * P.esz + C * K * 4 + K * 4;
 }
 size_t bwd_ops_per(const Plan& P) {  // backward operands + recorded states
   const size_t C = P.C, K = P.D;
@@ -133,11 +133,13 @@ ChunkOps carve_ops(const Plan& P, bool bwd, unsigned char*& cur) {
   o.Wn = take(n * C * K * e);
   o.kgT = take(n * K * C * e);
   o.gam = static_cast<float*>(take(n * K * 4));
-  o.U = take(n * C * K * e);
   if (!bwd) {
+    o.Uf = static_cast<float*>(take(n * C * K * 4));
     o.qg = take(n * C * K * e);
     o.Aqk = take(n * C * C * e);
+    if (e == 2) o.Aqk_lo = take(n * C * C * e);
   } else {
+    o.U = take(n * C * K * e);
     o.AqkT = take(n * C * C * e);
     o.kg = take(n * C * K * e);
     o.qgT = take(n * K * C * e);

@@ -30,14 +30,19 @@ struct Inputs {
 // segment; element (lc, h) of each array is at index lc * H + h where lc is
 // the chunk index relative to the segment start. Operand element type is
 // bf16 for bf16 problems and fp32 for fp32 problems. Wn, U, qg, kgT, Aqk,
-// AqkT, kg, qgT, WnT and TT are stored fragment-major (FragMajor in
-// kda_device.h); PT is row-major.
+// Aqk_lo, AqkT, kg, qgT, WnT and TT are stored fragment-major (FragMajor in
+// kda_device.h); PT and Uf are row-major. The forward layout keeps U in fp32
+// and Aqk as a bf16 pair (Aqk + Aqk_lo) because the output takes them
+// directly: rounding either to bf16 would add a bf16 rounding's worth of
+// error to O.
 struct ChunkOps {
   void *Wn;    // [C][K]  -W  (W = T (beta * kh * e^G))
-  void *U;     // [C][V]  U = T (beta * v)
+  void *U;     // [C][V]  U = T (beta * v)                (backward only)
+  float *Uf;   // [C][V]  U in fp32, row-major            (forward only)
   void *qg;    // [C][K]  qh * e^G                       (forward only)
   void *kgT;   // [K][C]  (kh * e^{G_c - G})^T
   void *Aqk;   // [C][C]  gated q.k, lower incl. diagonal (forward only)
+  void *Aqk_lo;  // [C][C] Aqk - Aqk rounded to bf16 (forward, bf16 only)
   float *gam;  // [K]     e^{G_c}
   // backward extras
   void *AqkT;  // [C][C]

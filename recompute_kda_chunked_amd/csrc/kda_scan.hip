@@ -68,9 +68,11 @@ struct FwdOps {
   F w[G::NKF];                // W rows of block m (negated: -W)
   F q[G::NKF];                // qg rows of block m (output only)
   F a[G::NCF];                // Aqk rows of block m (output only)
+  F al[G::NCF];               // Aqk_lo rows of block m (output, bf16 only)
   uint32_t u[G::BVT][4];      // U[r][v..v+3] at the lane's Vn^T tile entries, raw
                               // bits (converted at use, so the prefetch does not
-                              // wait for its loads)
+                              // wait for its loads): fp32 (forward layout) or
+                              // the operand type (backward layout, REC)
   F kt[G::MKW][G::NCF];       // kg^T rows of the wave's state row blocks
   float gm[G::MKW];           // gamma at the lane's key channel of each row block
 };
@@ -96,9 +98,15 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
     const OpT* Wn = static_cast<const OpT*>(ops.Wn) + idx * C * K;
 #pragma unroll
     for (int j = 0; j < G::NKF; ++j) f.w[j] = M::load(Wn + FM::frag(m, j, K, lane));
-    const OpT* U = static_cast<const OpT*>(ops.U) + idx * C * V;
+    if constexpr (REC) {
+      const OpT* U = static_cast<const OpT*>(ops.U) + idx * C * V;
 #pragma unroll
-    for (int nv = 0; nv < G::BVT; ++nv) load4_fm_raw<OpT>(U, 16 * m + i, v0 + 16 * nv + 4 * g, V, f.u[nv]);
+      for (int nv = 0; nv < G::BVT; ++nv) load4_fm_raw<OpT>(U, 16 * m + i, v0 + 16 * nv + 4 * g, V, f.u[nv]);
+    } else {
+      const float* U = ops.Uf + idx * C * V + (16 * m + i) * V + v0 + 4 * g;
+#pragma unroll
+      for (int nv = 0; nv < G::BVT; ++nv) load4_raw<float>(U + 16 * nv, f.u[nv]);
+    }
   }
   if (OUT_O && (PART < 0 || PART == 1)) {
     const OpT* qg = static_cast<const OpT*>(ops.qg) + idx * C * K;
@@ -107,6 +115,11 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
     const OpT* aq = static_cast<const OpT*>(ops.Aqk) + idx * C * C;
 #pragma unroll
     for (int j = 0; j < G::NCF; ++j) f.a[j] = M::load(aq + FM::frag(m, j, C, lane));
+    if constexpr (sizeof(OpT) == 2) {
+      const OpT* al = static_cast<const OpT*>(ops.Aqk_lo) + idx * C * C;
+#pragma unroll
+      for (int j = 0; j < G::NCF; ++j) f.al[j] = M::load(al + FM::frag(m, j, C, lane));
+    }
   }
   if (PART < 0 || PART == 2) {
     const OpT* kgT = static_cast<const OpT*>(ops.kgT) + idx * K * C;
@@ -130,8 +143,14 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
   using M = typename G::M;
   constexpr int K = G::K, V = G::V, NB = G::NB, NVT = G::NVT, BVT = G::BVT;
   constexpr int HPW = G::HPW, MKW = G::MKW, LDH = G::LDH, LDC = G::LDC, KS = M::KS, KPL = M::KPL;
+  // The output's intra-chunk product Aqk Vn of a bf16 problem takes both
+  // factors as bf16 pairs (hi + lo, three MFMAs: hi hi, hi lo, lo hi): a
+  // plain bf16 rounding of either would add one bf16 rounding's worth of
+  // error to O. The state update keeps the single bf16 Vn.
+  constexpr bool HL = OUT_O && sizeof(OpT) == 2;
   __shared__ __attribute__((aligned(16))) OpT hT_s[BV * LDH];
   __shared__ __attribute__((aligned(16))) OpT VnT_s[BV * LDC];
+  __shared__ __attribute__((aligned(16))) OpT VnTlo_s[HL ? BV * LDC : 1];
 
   int n, h, vt;
   if (!scan_program<NVT>(d, n, h, vt)) return;
@@ -144,6 +163,8 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
   const int v0 = vt * BV;
   const size_t ts = static_cast<size_t>(d.H) * V;
+  // U: fp32 in the forward layout, the operand type in the backward one (REC)
+  using UT = std::conditional_t<REC, OpT, float>;
 
   // state tile j of this wave: row block mk = w*MKW + j/BVT, value block
   // nv = j%BVT, held transposed: hs[j][rr] = h[16mk + i][v0 + 16nv + 4g + rr].
@@ -215,7 +236,7 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
       const int m = w;
 #pragma unroll
       for (int nv = 0; nv < BVT; ++nv) {
-        f32x4 accV = unpack4<OpT>(cur.u[nv]);
+        f32x4 accV = unpack4<UT>(cur.u[nv]);
         accO[nv] = zero4();
         const OpT* bh = hT_s + (16 * nv + i) * LDH + g * KPL;
 #pragma unroll
@@ -226,7 +247,11 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
         }
         OpT* dst = VnT_s + (16 * nv + 4 * g) * LDC + 16 * m + i;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dst[rr * LDC] = from_f<OpT>(accV[rr]);
+        for (int rr = 0; rr < 4; ++rr) {
+          const OpT hi = from_f<OpT>(accV[rr]);
+          dst[rr * LDC] = hi;
+          if constexpr (HL) VnTlo_s[(16 * nv + 4 * g + rr) * LDC + 16 * m + i] = from_f<OpT>(accV[rr] - to_f(hi));
+        }
         if (REC)
           store4_fm<OpT>(static_cast<OpT*>(st.Vn) + idx * C * V, 16 * m + i, v0 + 16 * nv + 4 * g, V, accV);
       }
@@ -242,9 +267,17 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
 #pragma unroll
       for (int nv = 0; nv < BVT; ++nv) {
         const OpT* bv = VnT_s + (16 * nv + i) * LDC + g * KPL;
+        const OpT* bvl = VnTlo_s + (HL ? (16 * nv + i) * LDC + g * KPL : 0);
 #pragma unroll
         for (int j = 0; j < G::NCF; ++j)
-          if (j < nf) accO[nv] = M::mma(M::load(bv + j * KS), cur.a[j], accO[nv]);
+          if (j < nf) {
+            const auto vh = M::load(bv + j * KS);
+            accO[nv] = M::mma(vh, cur.a[j], accO[nv]);
+            if constexpr (HL) {
+              accO[nv] = M::mma(M::load(bvl + j * KS), cur.a[j], accO[nv]);
+              accO[nv] = M::mma(vh, cur.al[j], accO[nv]);
+            }
+          }
         // accO[nv][rr] = O[r][v0 + 16nv + 4g + rr]
         if (r < len) store4<TI>(o + (t0 + r) * ts + static_cast<size_t>(h) * V + v0 + 16 * nv + 4 * g, accO[nv]);
       }

@@ -1,6 +1,6 @@
 """Seeded random problems against the FP64 oracle (needs an MI355X): packed
 batches of 1-5 sequences of 0-150 tokens (empty and one-token sequences
-included; bf16 batches lengthened to 256 token-heads), 1-3 heads, D 64 or
+included), 1-3 heads, D 64 or
 128, every built chunk size, both gate maps, per-channel and per-head gates,
 random scale and streaming segments.
 
@@ -24,12 +24,6 @@ from recompute_kda_chunked_amd import kda_backward, kda_forward
 
 pytestmark = pytest.mark.gpu
 
-# bf16 rounding errors are correlated along an output row (a row's few
-# rounded scalars enter all of its elements), so the normalised L2 error of
-# a handful of rows scatters by tens of percent around its mean (about 4e-3
-# for O): bf16 problems get at least this many (token, head) rows
-MIN_BF16_ROWS = 256
-
 BUILT = {(torch.float32, 64): (16, 32, 64), (torch.float32, 128): (16, 32),
          (torch.bfloat16, 64): (32, 64), (torch.bfloat16, 128): (32, 64)}
 
@@ -48,8 +42,6 @@ def draw_case(seed):
     D = 64 if rng.random() < 0.5 else 128
     chunk = int(rng.choice(BUILT[(dtype, D)]))
     H = int(rng.integers(1, 4))
-    if dtype == torch.bfloat16 and sum(lens) * H < MIN_BF16_ROWS:
-        lens[-1] += -(-MIN_BF16_ROWS // H) - sum(lens)
     return dict(lens=lens, H=H, D=D, dtype=dtype, chunk=chunk,
                 per_head=bool(rng.random() < 0.5), gate_mode=int(rng.integers(0, 2)),
                 seg=int(rng.integers(0, 4)), scale=float(rng.choice([1.0, D ** -0.5])),
