@@ -194,6 +194,23 @@ int kda_bwd_ex(const kda_problem *p, const void *q, const void *k, const void *v
                float *dA_log, float *ddt_bias, const kda_state_io *io,
                void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+   capture, tight serving loops, harnesses that forbid hipMalloc): kda_fwd
+   with its workspace in a device array of KDA_NOALLOC_SCRATCH_BYTES that the
+   library holds on each GPU it runs on until the process ends (the caller
+   passes inputs and outputs only; layouts and result as kda_fwd, O
+   bit-identical to it). The call runs the forward over the longest segment
+   of chunks whose workspace fits the array; a problem whose one-chunk
+   segment needs more (its state carry slots are 2 * H * K * V * 4 bytes)
+   returns KDA_ERR_WORKSPACE. It allocates nothing. Calls on one GPU share
+   the array: calls that overlap in time race and must be ordered by the
+   caller. Returns KDA_ERR_HIP if the array's device address cannot be
+   obtained. */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kda_fwd_noalloc(const kda_problem *p, const void *q, const void *k, const void *v,
+                    const void *raw_g, const void *raw_beta, const float *A_log,
+                    const float *dt_bias, const int32_t *cu_seqlens, void *o, void *stream);
+
 /* Optional per-kernel timing, for measurement tools. Between
    kda_profile_begin() and kda_profile_end(), every kernel the calling thread
    launches through this library is bracketed by two HIP events recorded on

@@ -19,7 +19,9 @@ KDA_GATE_SIGMOID_BOUND, KDA_GATE_SOFTPLUS_CLAMP, KDA_GATE_PER_HEAD = 0, 1, 16
 EXPORTS = ("kda_fwd_workspace_bytes", "kda_bwd_workspace_bytes", "kda_check_problem",
            "kda_prologue_workspace_bytes", "kda_prologue", "kda_fwd", "kda_bwd",
            "kda_checkpoint_bytes", "kda_bwd_segment_chunks", "kda_fwd_ex", "kda_bwd_ex",
-           "kda_profile_begin", "kda_profile_end", "kda_kernel_name", "kda_status_string")
+           "kda_profile_begin", "kda_profile_end", "kda_kernel_name", "kda_status_string",
+           "kda_fwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 KERNEL_COUNT = 7
 
 
@@ -90,6 +92,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kda_fwd_ex.restype = ctypes.c_int
     lib.kda_bwd_ex.argtypes = [pp] + [vp] * 16 + [iop, vp, sz, vp]
     lib.kda_bwd_ex.restype = ctypes.c_int
+    lib.kda_fwd_noalloc.argtypes = [pp] + [vp] * 9 + [vp]
+    lib.kda_fwd_noalloc.restype = ctypes.c_int
     lib.kda_profile_begin.argtypes = []
     lib.kda_profile_begin.restype = ctypes.c_int
     lib.kda_profile_end.argtypes = [ctypes.POINTER(ctypes.c_int32),

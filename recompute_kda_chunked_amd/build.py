@@ -19,7 +19,7 @@ LIB = os.path.join(OUT_DIR, "libkda.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["kda_host.cpp", "kda_prologue.hip", "kda_chunk_local.hip", "kda_scan.hip",
-           "kda_chunk_grad.hip"]
+           "kda_chunk_grad.hip", "kda_noalloc.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -172,6 +172,24 @@ def kda_forward(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, *,
     return o
 
 
+def kda_forward_noalloc(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, o, *,
+                        cu_seqlens_host, scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6,
+                        gate_mode=_lib.KDA_GATE_SIGMOID_BOUND):
+    """kda_fwd_noalloc: O written into the caller's `o` [T,H,V] with the
+    library's own device scratch (no allocation by the library, none here
+    either: the host copy of cu_seqlens must be given)."""
+    T, H, K, V, dt, ph = _check_inputs(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens,
+                                       extra=[("o", (o, tuple(v.shape), v.dtype))])
+    prob = Problem(T, H, K, V, dt, [int(c) for c in cu_seqlens_host], chunk, scale, lower_bound,
+                   eps, 0, _gate_flags(gate_mode, ph))
+    lib = _lib.load()
+    st = lib.kda_fwd_noalloc(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(raw_g), _ptr(raw_beta),
+                             _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(o),
+                             _stream(q.device))
+    _raise(lib, st, "kda_fwd_noalloc")
+    return o
+
+
 def kda_backward(q, k, v, raw_g, raw_beta, A_log, dt_bias, dO, cu_seqlens=None, *,
                  cu_seqlens_host=None, scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6,
                  seg_chunks=0, gate_mode=_lib.KDA_GATE_SIGMOID_BOUND, initial_state=None,

@@ -161,3 +161,17 @@ def test_host_tensors_are_refused():
         kda_forward(x["q"], x["k"], x["v"], x["raw_g"], torch.zeros((T, H)), torch.zeros(H),
                     torch.zeros((H, D)), torch.tensor([0, T], dtype=torch.int32),
                     cu_seqlens_host=[0, T])
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    # one chunk of every head plus the two state carry slots must fit the
+    # 64 MiB scratch: at H=512, D=128 the carry slots alone take 64 MiB. The
+    # check is on the host, before any HIP call (the pointers are never
+    # dereferenced).
+    fake = ctypes.c_void_p(0x1000)
+    nul = ctypes.c_void_p(0)
+    big = good(H=512, T=64, cu_host=[0, 64])
+    assert big.check() == _lib.KDA_OK
+    assert lib.kda_fwd_noalloc(big.ref, *([fake] * 9), nul) == _lib.KDA_ERR_WORKSPACE
+    assert lib.kda_fwd_noalloc(good().ref, *([nul] * 9), nul) == _lib.KDA_ERR_INVALID
+    assert lib.kda_fwd_noalloc(good(H=0).ref, *([fake] * 9), nul) == _lib.KDA_ERR_INVALID
