@@ -224,12 +224,16 @@ int kda_fwd_noalloc(const kda_problem *p, const void *q, const void *k, const vo
 enum {
   KDA_KERNEL_CHUNK_TABLE = 0,
   KDA_KERNEL_PROLOGUE = 1,
-  KDA_KERNEL_CHUNK_LOCAL = 2,
-  KDA_KERNEL_SCAN_FWD = 3,
-  KDA_KERNEL_SCAN_BWD = 4,
+  KDA_KERNEL_CHUNK_LOCAL = 2,       /* forward operand layout (kda_fwd) */
+  KDA_KERNEL_SCAN_FWD = 3,          /* the output scan (kda_fwd) */
+  KDA_KERNEL_SCAN_BWD = 4,          /* reverse state-gradient scan */
   KDA_KERNEL_CHUNK_GRAD = 5,
   KDA_KERNEL_GATE_REDUCE = 6,
-  KDA_KERNEL_COUNT = 7
+  KDA_KERNEL_CHUNK_LOCAL_BWD = 7,   /* backward operand layout */
+  KDA_KERNEL_CHUNK_LOCAL_STATE = 8, /* state operands only (checkpoint pass) */
+  KDA_KERNEL_SCAN_REC = 9,          /* forward-direction scan recording h, Vn */
+  KDA_KERNEL_SCAN_STATE = 10,       /* forward-direction scan, states only */
+  KDA_KERNEL_COUNT = 11
 };
 int kda_profile_begin(void);
 int kda_profile_end(int32_t *launches, double *total_ms, int64_t *units, int n);

@@ -22,7 +22,7 @@ EXPORTS = ("kda_fwd_workspace_bytes", "kda_bwd_workspace_bytes", "kda_check_prob
            "kda_profile_begin", "kda_profile_end", "kda_kernel_name", "kda_status_string",
            "kda_fwd_noalloc")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KDA_NOALLOC_SCRATCH_BYTES
-KERNEL_COUNT = 7
+KERNEL_COUNT = 11
 
 
 class KdaProblem(ctypes.Structure):

@@ -411,15 +411,15 @@ int kda_bwd_ex(const kda_problem* p, const void* q, const void* k, const void* v
   // forward saved them)
   for (int sg = 0; !io->ckpt && sg + 1 < P.NS; ++sg) {
     const int c0 = sg * P.seg, c1 = c0 + P.seg;
-    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, KL_STATE, d, in, c0, c1 - c0, ops_f, s));
-    KDA_TRY(KDA_KERNEL_SCAN_FWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_f, nullptr, nullptr,
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL_STATE, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, KL_STATE, d, in, c0, c1 - c0, ops_f, s));
+    KDA_TRY(KDA_KERNEL_SCAN_STATE, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_f, nullptr, nullptr,
                             ckpt + sg * slot, ckpt + (sg + 1) * slot, fwd_ss, s));
   }
   for (int sg = P.NS - 1; sg >= 0; --sg) {
     const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
-    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, KL_BWD, d, in, c0, c1 - c0, ops_b, s));
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL_BWD, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, KL_BWD, d, in, c0, c1 - c0, ops_b, s));
     // the recording scan writes no carry: the next segment's entering state is known
-    KDA_TRY(KDA_KERNEL_SCAN_FWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_b, nullptr, &sts,
+    KDA_TRY(KDA_KERNEL_SCAN_REC, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_b, nullptr, &sts,
                             ckpt + sg * slot, nullptr, fwd_ss, s));
     KDA_TRY(KDA_KERNEL_SCAN_BWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_bwd(P.dtype, P.D, P.C, d, in, dO, c0, c1, ops_b, sts,
                             dcarry[(sg + 1) & 1], dcarry[sg & 1], bwd_ss, s));
@@ -477,9 +477,10 @@ int kda_profile_end(int32_t* launches, double* total_ms, int64_t* units, int n) 
 }
 
 const char* kda_kernel_name(int kind) {
-  static const char* names[KDA_KERNEL_COUNT] = {"chunk_table", "prologue", "chunk_local",
-                                                "scan_fwd", "scan_bwd", "chunk_grad",
-                                                "gate_reduce"};
+  static const char* names[KDA_KERNEL_COUNT] = {
+      "chunk_table", "prologue",        "chunk_local",       "scan_fwd",
+      "scan_bwd",    "chunk_grad",      "gate_reduce",       "chunk_local_bwd",
+      "chunk_local_state", "scan_rec",  "scan_state"};
   return (kind >= 0 && kind < KDA_KERNEL_COUNT) ? names[kind] : "unknown";
 }
 

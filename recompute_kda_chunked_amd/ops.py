@@ -300,12 +300,14 @@ class KDAFunction(torch.autograd.Function):
 def kda(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, *, cu_seqlens_host=None,
         scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6, seg_chunks=0,
         gate_mode=_lib.KDA_GATE_SIGMOID_BOUND, initial_state=None, output_final_state=False,
-        save_checkpoints=False):
+        save_checkpoints=True):
     """Differentiable KDA operator; returns O [T,H,V], or (O, ht) with
     output_final_state. initial_state (fp32 [N,H,K,V]) is differentiable.
-    save_checkpoints keeps the states at the backward's segment starts from
-    the forward to the backward (a memory/time trade: the backward skips one
-    forward-direction pass; every chunk's w, u and h are still recomputed)."""
+    save_checkpoints (default) keeps the states at the backward's segment
+    starts (one fp32 [H,K,V] state per segment, when there is more than one)
+    from the forward to the backward, which then skips one forward-direction
+    pass; every chunk's w, u and h are still recomputed. False recomputes
+    those states in the backward too."""
     if cu_seqlens is None:
         cu_seqlens, cu_seqlens_host = _default_cu(q.shape[0], q.device)
     cu_host = _cu_host(cu_seqlens, cu_seqlens_host)

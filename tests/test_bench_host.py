@@ -36,6 +36,36 @@ def test_kernel_bytes_add_up_to_the_step():
         assert bench.kernel_alg_bytes("gate_reduce", D, esz, G) == 0.0
 
 
+def test_metric_labels_name_each_workload():
+    import json
+    import kda_inputs
+    W = kda_inputs.WORKLOADS
+    base = json.load(open(os.path.join(ROOT, "BASELINE.json")))["metric"]
+    assert bench.metric_label(W["t8k_h64_bf16"]) == base
+    labels = {n: bench.metric_label(w) for n, w in W.items()}
+    assert len(set(labels.values())) == len(labels)  # every workload its own label
+    assert "8×8K packed×H16×D128 bf16" in labels["varlen8x8k_h16_bf16"]
+    assert "1×128K×H96×D128 bf16" in labels["t128k_h96_bf16"]
+    assert "10×512 packed×H12×D64 fp32 C16" in labels["small_f32"]
+    assert labels["gdn_t8k_h64_bf16"].startswith("GDN (scalar gate per head)")
+
+
+def test_every_timed_kernel_kind_has_a_byte_count():
+    D, esz = 128, 2
+    # the recording and state-only scans move workspace only
+    assert bench.kernel_alg_bytes("scan_rec", D, esz, D) == 0.0
+    assert bench.kernel_alg_bytes("scan_state", D, esz, D) == 0.0
+    assert bench.kernel_alg_bytes("chunk_local_bwd", D, esz, D) == \
+        bench.kernel_alg_bytes("chunk_local", D, esz, D) == 1026
+    assert bench.kernel_alg_bytes("chunk_local_state", D, esz, D) == 770  # no q rows
+
+
+def test_quantiles():
+    v = [5.0, 1.0, 3.0, 2.0, 4.0]
+    assert bench.quantile(v, 0.0) == 1.0 and bench.quantile(v, 1.0) == 5.0
+    assert bench.quantile(v, 0.5) == 3.0
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
