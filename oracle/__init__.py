@@ -6,7 +6,10 @@ Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 
 ``kda_oracle.c`` holds the token-by-token recurrence and its hand-derived
 reverse sweep (see its header for the equations and the passages of the pages
-they follow). This module only marshals numpy arrays into it.
+they follow); ``gdn2_oracle.c`` the same for the gated delta rule with a
+per-channel erase gate and a per-channel write gate (GDN-2), written
+separately so that the tests can compare the two. This module only marshals
+numpy arrays into them.
 """
 from __future__ import annotations
 
@@ -20,22 +23,29 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
 _BUILD = os.path.join(_HERE, "_build")
 _LIB_PATH = os.path.join(_BUILD, "libkda_oracle.so")
+_GDN2_SRC = os.path.join(_HERE, "gdn2_oracle.c")
+_GDN2_LIB_PATH = os.path.join(_BUILD, "libgdn2_oracle.so")
 
 GATE_SIGMOID_BOUND = 0  # g = L * sigmoid(exp(A_log) * (raw_g + dt_bias))
 GATE_SOFTPLUS_CLAMP = 1  # g = max(L, -exp(A_log) * softplus(raw_g + dt_bias))
 
 
-def build(extra_flags: tuple[str, ...] = (), out_path: str | None = None) -> str:
-    """Compile the oracle with gcc (OpenMP, -O3, no host-specific ISA so the
-    library runs on any x86-64 host). Returns the library path."""
-    out = out_path or _LIB_PATH
+def _gcc(src: str, out: str, extra_flags=()) -> str:
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-           *extra_flags, "-o", tmp, _SRC, "-lm"]
+           *extra_flags, "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
+
+
+def build(extra_flags: tuple[str, ...] = (), out_path: str | None = None) -> str:
+    """Compile the oracles with gcc (OpenMP, -O3, no host-specific ISA so the
+    libraries run on any x86-64 host). Returns the KDA library path."""
+    if out_path is None:
+        _gcc(_GDN2_SRC, _GDN2_LIB_PATH, extra_flags)
+    return _gcc(_SRC, out_path or _LIB_PATH, extra_flags)
 
 
 _lib_cache: dict[str, ctypes.CDLL] = {}
@@ -157,6 +167,69 @@ def kda(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, dO=None,
         # each per-head value feeds all K channels: its gradient is their sum
         out["draw_g"] = out["draw_g"].sum(axis=2)
         out["ddt_bias"] = out["ddt_bias"].sum(axis=1)
+    return out
+
+
+def _cu(cu_seqlens, T):
+    if cu_seqlens is None:
+        return np.array([0, T], dtype=np.int64)
+    cu = np.ascontiguousarray(np.asarray(
+        cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64))
+    if cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must be non-decreasing from 0 to T")
+    return cu
+
+
+def gdn2(q, k, v, raw_g, raw_b, raw_w, A_log, dt_bias, cu_seqlens=None, dO=None,
+         scale: float = 1.0, lower_bound: float = -5.0, eps: float = 1e-6,
+         gate_mode: int = GATE_SIGMOID_BOUND, n_threads: int = 0,
+         lib_path: str | None = None) -> dict:
+    """GDN-2 oracle (gdn2_oracle.c): the gated delta rule with a per-channel
+    erase gate b = sigmoid(raw_b) [T,H,K] and write gate w = sigmoid(raw_w)
+    [T,H,V] in place of KDA's scalar beta. Shapes as for kda(); returns a
+    dict of float64 arrays: ``o`` and, when dO is given, ``dq, dk, dv,
+    draw_g, draw_b, draw_w, dA_log, ddt_bias``."""
+    q, k, v, raw_g, raw_b, raw_w = map(_f64, (q, k, v, raw_g, raw_b, raw_w))
+    A_log, dt_bias = _f64(A_log), _f64(dt_bias)
+    T, H, K = q.shape
+    V = v.shape[2]
+    if (k.shape != (T, H, K) or raw_g.shape != (T, H, K) or raw_b.shape != (T, H, K)
+            or v.shape != (T, H, V) or raw_w.shape != (T, H, V)):
+        raise ValueError("shape mismatch among q, k, v, raw_g, raw_b, raw_w")
+    if A_log.shape != (H,) or dt_bias.shape != (H, K):
+        raise ValueError("shape mismatch among A_log, dt_bias")
+    cu = _cu(cu_seqlens, T)
+    out = {"o": np.zeros((T, H, V))}
+    names = ("dq", "dk", "dv", "draw_g", "draw_b", "draw_w", "dA_log", "ddt_bias")
+    grads = [None] * 8
+    if dO is not None:
+        dO = _f64(dO)
+        if dO.shape != (T, H, V):
+            raise ValueError("dO shape mismatch")
+        shapes = ((T, H, K), (T, H, K), (T, H, V), (T, H, K), (T, H, K), (T, H, V), (H,), (H, K))
+        out.update({n_: np.zeros(s_) for n_, s_ in zip(names, shapes)})
+        grads = [out[n_] for n_ in names]
+    path = lib_path or _GDN2_LIB_PATH
+    if path not in _lib_cache:
+        if not os.path.exists(path):
+            if path != _GDN2_LIB_PATH:
+                raise FileNotFoundError(path)
+            build()
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.gdn2_oracle.argtypes = ([ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                     ctypes.c_double, ctypes.c_int] + [dp] * 9 + [dp] * 9
+                                    + [ctypes.c_int])
+        lib.gdn2_oracle.restype = ctypes.c_int
+        _lib_cache[path] = lib
+    rc = _lib_cache[path].gdn2_oracle(
+        len(cu) - 1, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, K, V, float(scale),
+        float(lower_bound), float(eps), int(gate_mode), _ptr(q), _ptr(k), _ptr(v), _ptr(raw_g),
+        _ptr(raw_b), _ptr(raw_w), _ptr(A_log), _ptr(dt_bias), _ptr(dO), _ptr(out["o"]),
+        *[_ptr(g) for g in grads], int(n_threads))
+    if rc != 0:
+        raise RuntimeError("gdn2_oracle failed with status %d" % rc)
     return out
 
 
