@@ -44,7 +44,8 @@ def metric_label(w) -> str:
     if len(w.seqlens) > 1:
         shape += " packed"
     dt = "bf16" if w.dtype == "bf16" else "fp32"
-    op = "GDN (scalar gate per head)" if w.gate_per_head else "KDA"
+    op = ("GDN (scalar gate per head)" if w.gate_per_head else
+          "GDN-2 (per-channel erase and write gates)" if w.gdn2 else "KDA")
     chunk = "" if w.chunk == 64 else " C%d" % w.chunk
     return "%s fwd+bwd tokens/s at %s×H%d×D%d %s%s; peak allocated GiB; %%HBM roof" % (
         op, shape, w.H, w.D, dt, chunk)
@@ -54,10 +55,12 @@ def metric_label(w) -> str:
 #   forward:  read q, k, v (D each), raw_g (G), raw_beta, write O (D)
 #   backward: read q, k, v, dO (D each), raw_g (G), raw_beta,
 #             write dq, dk, dv (D each), draw_g (G), draw_beta
-# with G = D gate values per token-head, or 1 for a gate per head.
-def alg_bytes_per_token_head(D: int, esz: int, G: int) -> dict:
-    fwd = (3 * D + G + 1 + D) * esz
-    bwd = (4 * D + G + 1 + 3 * D + G + 1) * esz
+# with G = D gate values per token-head, or 1 for a gate per head. GDN-2
+# (B = 2 D) reads raw_b and raw_w (D each) instead of raw_beta and writes
+# their gradients instead of draw_beta.
+def alg_bytes_per_token_head(D: int, esz: int, G: int, B: int = 1) -> dict:
+    fwd = (3 * D + G + B + D) * esz
+    bwd = (4 * D + G + B + 3 * D + G + B) * esz
     return {"fwd": fwd, "bwd": bwd, "total": fwd + bwd}
 
 
@@ -66,13 +69,13 @@ def alg_bytes_per_token_head(D: int, esz: int, G: int) -> dict:
 # it must write); workspace traffic is overhead and is not counted, so the
 # recording and state-only scans, whose inputs and outputs are all
 # workspace, have none.
-def kernel_alg_bytes(name: str, D: int, esz: int, G: int) -> float:
+def kernel_alg_bytes(name: str, D: int, esz: int, G: int, B: int = 1) -> float:
     if name == "chunk_grad":      # reads q,k,v,raw_g,raw_beta,dO; writes 5 grads
-        return (4 * D + G + 1 + 3 * D + G + 1) * esz
+        return (4 * D + G + B + 3 * D + G + B) * esz
     if name in ("chunk_local", "chunk_local_bwd"):   # reads q,k,v,raw_g,raw_beta
-        return (3 * D + G + 1) * esz
+        return (3 * D + G + B) * esz
     if name == "chunk_local_state":                  # reads k,v,raw_g,raw_beta
-        return (2 * D + G + 1) * esz
+        return (2 * D + G + B) * esz
     if name == "scan_fwd":        # writes O
         return D * esz
     if name == "scan_bwd":        # reads dO
@@ -187,9 +190,17 @@ def cpu_baseline(x, w) -> dict:
 
 
 def make_step(x, w, args, checkpoints: bool):
-    from recompute_kda_chunked_amd import kda_backward, kda_forward
+    from recompute_kda_chunked_amd import gdn2_backward, gdn2_forward, kda_backward, kda_forward
     names = ("q", "k", "v", "raw_g", "raw_beta", "A_log", "dt_bias")
     kw = dict(cu_seqlens_host=x["cu_seqlens_host"], chunk=w.chunk, seg_chunks=args.seg_chunks)
+    if w.gdn2:  # no forward-saved states on this path: the backward makes them
+        g2 = ("q", "k", "v", "raw_g", "raw_b", "raw_w", "A_log", "dt_bias")
+
+        def step_g2():
+            o = gdn2_forward(*(x[n] for n in g2), x["cu_seqlens"], **kw)
+            g = gdn2_backward(*(x[n] for n in g2), x["dO"], x["cu_seqlens"], **kw)
+            return o, g
+        return step_g2
 
     def step():
         if checkpoints:
@@ -296,7 +307,7 @@ def main() -> int:
     w = kda_inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     x = kda_inputs.workload_inputs(w, device=dev)
-    ckpt = not args.no_checkpoints
+    ckpt = not args.no_checkpoints and not w.gdn2
     step = make_step(x, w, args, checkpoints=ckpt)
 
     # ---- the first step of the process (library and code objects load here)
@@ -316,10 +327,14 @@ def main() -> int:
     tokens_per_s = w.T / (ms / 1e3)
 
     # the other backward variant, for reference (same inputs, same step count)
-    alt_step = make_step(x, w, args, checkpoints=not ckpt)
-    for _ in range(2):
-        alt_step()
-    alt_ms, alt_per, _ = timed(alt_step, args.steps)
+    alt = None
+    if not w.gdn2:
+        alt_step = make_step(x, w, args, checkpoints=not ckpt)
+        for _ in range(2):
+            alt_step()
+        alt_ms, alt_per, _ = timed(alt_step, args.steps)
+        alt = {"ms_per_step": round(alt_ms, 4), "median": round(statistics.median(alt_per), 4),
+               "tokens_per_s": round(w.T / (alt_ms / 1e3), 1)}
 
     # ---- per-kernel durations: HIP events the library records on its launch stream
     _lib.profile_begin()
@@ -330,8 +345,9 @@ def main() -> int:
 
     esz = 2 if w.dtype == "bf16" else 4
     G = 1 if w.gate_per_head else w.D
+    B = 2 * w.D if w.gdn2 else 1
     th = w.T * w.H
-    alg = alg_bytes_per_token_head(w.D, esz, G)
+    alg = alg_bytes_per_token_head(w.D, esz, G, B)
     e2e_frac = alg["total"] * th / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
     kernels = {}
     for k, (n, t, u) in prof.items():
@@ -341,7 +357,7 @@ def main() -> int:
         # pairs x chunk length = token-heads (the workloads' sequence lengths
         # are multiples of the chunk, so every chunk is full)
         units = u / n * w.chunk
-        kab = kernel_alg_bytes(k, w.D, esz, G) * units
+        kab = kernel_alg_bytes(k, w.D, esz, G, B) * units
         avg = t / n
         kernels[k] = {"launches_per_step": round(n / args.steps, 3), "avg_ms": round(avg, 4),
                       "total_ms_per_step": round(t / args.steps, 4),
@@ -358,7 +374,7 @@ def main() -> int:
                 "traffic_bytes_per_launch": traffic,
                 "alg_bytes_per_launch": d["alg_bytes_per_launch"],
                 "kernel": dominant,
-                "alg_bytes_per_token_head": kernel_alg_bytes(dominant, w.D, esz, G)}
+                "alg_bytes_per_token_head": kernel_alg_bytes(dominant, w.D, esz, G, B)}
 
     line = {
         "metric": metric_label(w), "value": round(tokens_per_s, 1), "unit": "tokens/s",
@@ -367,17 +383,17 @@ def main() -> int:
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "n_seqs": len(w.seqlens), "tokens": w.T, "heads": w.H,
                    "head_dim": w.D, "chunk": w.chunk, "gate": "per head" if w.gate_per_head
-                   else "per channel", "fwd_checkpoints": ckpt,
+                   else "per channel", "beta": "per-channel erase and write gates (GDN-2)"
+                   if w.gdn2 else "scalar", "fwd_checkpoints": ckpt,
                    "seg_chunks": args.seg_chunks or "auto"},
         "step_ms": {"median": round(statistics.median(per), 4), "p10": round(quantile(per, 0.1), 4),
                     "p90": round(quantile(per, 0.9), 4), "step0": round(step0_ms, 2)},
-        ("no_checkpoints" if ckpt else "with_checkpoints"): {
-            "ms_per_step": round(alt_ms, 4), "median": round(statistics.median(alt_per), 4),
-            "tokens_per_s": round(w.T / (alt_ms / 1e3), 1)},
         "e2e_hbm_roof_frac": round(e2e_frac, 4), "wall_s_timed": round(wall, 3),
         "kernels": kernels,
         "roofline": roofline,
     }
+    if alt:
+        line["no_checkpoints" if ckpt else "with_checkpoints"] = alt
     if peak:
         line.update(peak)
     if not args.no_cpu_baseline:

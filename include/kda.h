@@ -194,6 +194,31 @@ int kda_bwd_ex(const kda_problem *p, const void *q, const void *k, const void *v
                float *dA_log, float *ddt_bias, const kda_state_io *io,
                void *workspace, size_t workspace_bytes, void *stream);
 
+/* GDN-2 ("KDA at the production shape...", section 1.6, and the per-chunk
+   operation table of its section 2.1: akk = (b k Gamma)(k / Gamma)^T,
+   w = M^-1 (b k Gamma), u = M^-1 (w v)): the gated delta rule with a
+   channel-wise erase gate and a channel-wise write gate in place of beta,
+     b = sigmoid(raw_b) [K],  w = sigmoid(raw_w) [V]
+     S_t = (I - kh_t (b_t * kh_t)^T) Diag(exp(g_t)) S_{t-1} + kh_t (w_t * v_t)^T
+     o_t = S_t^T qh_t
+   with the prologue, gate maps, packing and layouts of kda_fwd / kda_bwd.
+   KDA is the case b = w = beta in every channel. raw_b [T, H, K] and raw_w
+   [T, H, V] are in the problem's dtype (device, caller-owned); the backward
+   writes draw_b [T, H, K] and draw_w [T, H, V] in that dtype, with dq, dk,
+   dv, draw_g, dA_log, ddt_bias as kda_bwd. Workspace sizes are those of
+   kda_fwd_workspace_bytes / kda_bwd_workspace_bytes. Not built for GDN-2
+   (KDA_ERR_UNSUPPORTED): a gate per head (KDA_GATE_PER_HEAD), and fp32 at
+   K = 64 with 64-token chunks. Errors otherwise as kda_fwd / kda_bwd. */
+int kda_gdn2_fwd(const kda_problem *p, const void *q, const void *k, const void *v,
+                 const void *raw_g, const void *raw_b, const void *raw_w, const float *A_log,
+                 const float *dt_bias, const int32_t *cu_seqlens, void *o, void *workspace,
+                 size_t workspace_bytes, void *stream);
+int kda_gdn2_bwd(const kda_problem *p, const void *q, const void *k, const void *v,
+                 const void *raw_g, const void *raw_b, const void *raw_w, const float *A_log,
+                 const float *dt_bias, const int32_t *cu_seqlens, const void *dO, void *dq,
+                 void *dk, void *dv, void *draw_g, void *draw_b, void *draw_w, float *dA_log,
+                 float *ddt_bias, void *workspace, size_t workspace_bytes, void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
    capture, tight serving loops, harnesses that forbid hipMalloc): kda_fwd
    with its workspace in a device array of KDA_NOALLOC_SCRATCH_BYTES that the

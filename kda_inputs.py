@@ -30,6 +30,7 @@ class Workload:
     A_log: float = 0.0
     dt_bias: float = 0.0
     gate_per_head: bool = False  # raw_g [T,H], dt_bias [H] (scalar gate)
+    gdn2: bool = False  # GDN-2: raw_b [T,H,K] and raw_w [T,H,V] instead of raw_beta
 
     @property
     def T(self) -> int:
@@ -59,9 +60,13 @@ WORKLOADS = {
     # DeltaNet form)
     "gdn_t8k_h64_bf16": Workload("gdn_t8k_h64_bf16", (8192,), 64, 128, "bf16", 64, seed=6,
                                  gate_per_head=True),
+    # the same shape under GDN-2: per-channel erase and write gates
+    "gdn2_t8k_h64_bf16": Workload("gdn2_t8k_h64_bf16", (8192,), 64, 128, "bf16", 64, seed=7,
+                                  gdn2=True),
 }
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "raw_g": 3, "raw_beta": 4, "dO": 5, "h0": 6, "dht": 7}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "raw_g": 3, "raw_beta": 4, "dO": 5, "h0": 6, "dht": 7,
+              "raw_b": 8, "raw_w": 9}
 
 
 def _randn(shape, seed: int, tensor_id: int, device, dtype) -> torch.Tensor:
@@ -73,12 +78,13 @@ def _randn(shape, seed: int, tensor_id: int, device, dtype) -> torch.Tensor:
 
 def make_inputs(seqlens, H: int, K: int, V: int, dtype=torch.float32, seed: int = 0,
                 device="cpu", A_log: float = 0.0, dt_bias: float = 0.0,
-                with_dO: bool = True, gate_per_head: bool = False) -> dict:
+                with_dO: bool = True, gate_per_head: bool = False, gdn2: bool = False) -> dict:
     """Draw one problem. Returns torch tensors on ``device``:
     q,k,raw_g [T,H,K]; v,dO [T,H,V]; raw_beta [T,H] (all ``dtype``);
     A_log [H], dt_bias [H,K] (float32, constant fill); cu_seqlens int32 [N+1]
     on ``device`` plus ``cu_seqlens_host`` (a Python list). gate_per_head:
-    raw_g [T,H] and dt_bias [H] instead.
+    raw_g [T,H] and dt_bias [H] instead. gdn2: also raw_b [T,H,K] and raw_w
+    [T,H,V] ~ N(0,1) in ``dtype``.
     """
     seqlens = [int(n) for n in seqlens]
     T = sum(seqlens)
@@ -100,6 +106,9 @@ def make_inputs(seqlens, H: int, K: int, V: int, dtype=torch.float32, seed: int 
     }
     if with_dO:
         out["dO"] = _randn((T, H, V), seed, TENSOR_IDS["dO"], device, dtype)
+    if gdn2:
+        out["raw_b"] = _randn((T, H, K), seed, TENSOR_IDS["raw_b"], device, dtype)
+        out["raw_w"] = _randn((T, H, V), seed, TENSOR_IDS["raw_w"], device, dtype)
     return out
 
 
@@ -112,4 +121,4 @@ def make_states(n_seqs: int, H: int, K: int, V: int, seed: int = 0, device="cpu"
 
 def workload_inputs(w: Workload, device="cpu", with_dO: bool = True) -> dict:
     return make_inputs(w.seqlens, w.H, w.D, w.D, w.torch_dtype, w.seed, device,
-                       w.A_log, w.dt_bias, with_dO, w.gate_per_head)
+                       w.A_log, w.dt_bias, with_dO, w.gate_per_head, w.gdn2)

@@ -20,7 +20,7 @@ EXPORTS = ("kda_fwd_workspace_bytes", "kda_bwd_workspace_bytes", "kda_check_prob
            "kda_prologue_workspace_bytes", "kda_prologue", "kda_fwd", "kda_bwd",
            "kda_checkpoint_bytes", "kda_bwd_segment_chunks", "kda_fwd_ex", "kda_bwd_ex",
            "kda_profile_begin", "kda_profile_end", "kda_kernel_name", "kda_status_string",
-           "kda_fwd_noalloc")
+           "kda_fwd_noalloc", "kda_gdn2_fwd", "kda_gdn2_bwd")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 KERNEL_COUNT = 11
 
@@ -92,6 +92,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kda_fwd_ex.restype = ctypes.c_int
     lib.kda_bwd_ex.argtypes = [pp] + [vp] * 16 + [iop, vp, sz, vp]
     lib.kda_bwd_ex.restype = ctypes.c_int
+    lib.kda_gdn2_fwd.argtypes = [pp] + [vp] * 10 + [vp, sz, vp]
+    lib.kda_gdn2_fwd.restype = ctypes.c_int
+    lib.kda_gdn2_bwd.argtypes = [pp] + [vp] * 18 + [vp, sz, vp]
+    lib.kda_gdn2_bwd.restype = ctypes.c_int
     lib.kda_fwd_noalloc.argtypes = [pp] + [vp] * 9 + [vp]
     lib.kda_fwd_noalloc.restype = ctypes.c_int
     lib.kda_profile_begin.argtypes = []

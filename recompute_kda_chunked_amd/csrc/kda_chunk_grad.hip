@@ -108,11 +108,19 @@ constexpr int grad_split() { return D >= 128 ? 1 : 2; }
 
 // PH: a gate per head (Dims::gate_head): one raw gate value and one gate
 // VJP per row.
-template <typename TI, typename OpT, int D, int C, bool PH>
+// G2: GDN-2 (per-channel erase gate b and write gate w instead of beta; the
+// chunk-local kernel's P is then Akk, the product of the erase-gated rows
+// b kh with kh). The gradient of beta, a row sum that beta could be hoisted
+// out of, becomes a per-channel accumulation ("KDA at the production
+// shape...", section 1.6): dv = w dBv and dw = v dBv per value channel;
+// the erase gate collects kh (dKb e^G) from the W path and kh (row-side sum)
+// from the gated-pair VJP of Akk, whose row operand is b kh. dbeta then
+// receives draw_b [T][H][K] and dw draw_w [T][H][V].
+template <typename TI, typename OpT, int D, int C, bool PH, bool G2>
 __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, Inputs in, const TI* dO,
                                                     int seg_begin, ChunkOps ops, SegStates st,
                                                     TI* dq, TI* dk, TI* dv, TI* dg, TI* dbeta,
-                                                    double* partials) {
+                                                    TI* dw, double* partials) {
   using M = Mma<OpT>;
   using VJ = Vjp<OpT>;
   using TG = typename VJ::T;
@@ -126,7 +134,9 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   constexpr int LDQ = C + 8;         // qT, kT [K][LDQ]
   constexpr int LDA = D + 8;         // [C][LDA] operand buffers
   constexpr int LDX = C + 8;         // [C][LDX] dX buffers
-  constexpr int SZ1 = 4 * C * LDA * (int)sizeof(OpT), SZ2 = 4 * C * LDX * (int)sizeof(OpT);
+  // GDN-2: the erase gate, transposed like q and k, follows the dX buffers in S6
+  constexpr int SZBT = G2 ? K * LDQ * (int)sizeof(TI) : 0;
+  constexpr int SZ1 = 4 * C * LDA * (int)sizeof(OpT), SZ2 = 4 * C * LDX * (int)sizeof(OpT) + SZBT;
   constexpr int SZU = SZ1 > SZ2 ? SZ1 : SZ2;
   // after the VJP the operand region holds the scratch of the reverse
   // cumulative sum and of the partial reductions
@@ -157,6 +167,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   OpT* dXk = dXq + C * LDX;
   OpT* dXqT = dXk + C * LDX;
   OpT* dXkT = dXqT + C * LDX;
+  TI* bT = reinterpret_cast<TI*>(dXkT + C * LDX);  // GDN-2 erase gate, [K][LDQ] (S6)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
   const int kb = w % NKB, half = w / NKB, kk = 16 * kb + i;
@@ -173,6 +184,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   const size_t ts = static_cast<size_t>(d.H) * D;
   const size_t hoff = static_cast<size_t>(h) * D;
   const TI* vr = static_cast<const TI*>(in.v) + L.t0 * ts + hoff;
+  const TI* bkr = G2 ? static_cast<const TI*>(in.bk) + L.t0 * ts + hoff : nullptr;
+  const TI* wvr = G2 ? static_cast<const TI*>(in.wv) + L.t0 * ts + hoff : nullptr;
   auto row_block = [&](int jm) { return half * MR + jm; };  // valid while < NB
   // Rows r0 .. r0 + 3 (r0 a multiple of 4) of this lane's channel in the
   // transposed tiles, read as one vector: the row permutation moves whole
@@ -207,6 +220,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   static_assert(NB % TPW == 0, "a wave's tiles share one value block");
   typename M::frag fa[NKS], fb[TPW][NKS];
   uint32_t vin[TPW][4];
+  uint32_t win[G2 ? TPW : 1][4];  // GDN-2 write gate at the dv positions
   using FM = FragMajor<OpT>;
   // vector e of the fragment-major Vn: VE elements in slot order, row
   // vn_row(e), columns vn_col(e) .. + VE - 1 (bf16: one lane slot) or rows
@@ -237,6 +251,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) fb[jt][ks] = M::load(TT + FM::frag(nr, ks, C, lane));
       load4_raw<TI>(vr + (r < L.len ? r : L.len - 1) * ts + vv, vin[jt]);
+      if constexpr (G2) load4_raw<TI>(wvr + (r < L.len ? r : L.len - 1) * ts + vv, win[jt]);
     }
   }
 #pragma unroll
@@ -286,8 +301,10 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // completion counter, so a load issued after a store would wait for it).
   constexpr int NVS = V / KS;
   typename M::frag fh[NVS], fdh[NVS];
+  uint32_t bsc[G2 ? MR : 1][4];  // GDN-2 erase gate (raw) at the S4 positions
   {
     f32x4 dvv[TPW];
+    f32x4 dwv[G2 ? TPW : 1];
 #pragma unroll
     for (int jt = 0; jt < TPW; ++jt) {
       const int t = w * TPW + jt;
@@ -301,13 +318,24 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       float part = 0.f;
       const f32x4 vv4 = unpack4<TI>(vin[jt]);
       store4<OpT>(dst, acc);
+      if constexpr (G2) {
+        // dv = w dBv, draw_w = v dBv w (1 - w), per value channel
+        const f32x4 x4 = unpack4<TI>(win[jt]);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        part += r < L.len ? acc[rr] * vv4[rr] : 0.f;
-        dvv[jt][rr] = be[r] * acc[rr];
+        for (int rr = 0; rr < 4; ++rr) {
+          const float wg = sigmoidf(x4[rr]);
+          dvv[jt][rr] = be[r] * wg * acc[rr];
+          dwv[jt][rr] = acc[rr] * vv4[rr] * wg * (1.f - wg);
+        }
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          part += r < L.len ? acc[rr] * vv4[rr] : 0.f;
+          dvv[jt][rr] = be[r] * acc[rr];
+        }
+        part = sum_groups(part);
+        if (g == 0) dbp[w][r] += part;
       }
-      part = sum_groups(part);
-      if (g == 0) dbp[w][r] += part;
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -336,24 +364,42 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         fdh[j] = M::load(bdh + FM::frag(kb, j, V, lane));
       }
     }
+    if constexpr (G2) {
+      // the erase gate of this lane's channel at the rows S4 visits
+#pragma unroll
+      for (int jm = 0; jm < MR; ++jm) {
+        const int m = row_block(jm) < NB ? row_block(jm) : NB - 1;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 16 * m + 4 * g + rr;
+          bsc[jm][rr] = load_bits<TI>(bkr + (r < L.len ? r : L.len - 1) * ts + kk);
+        }
+      }
+    }
     TI* dvo = dv + L.t0 * ts + hoff;
+    TI* dwo = G2 ? dw + L.t0 * ts + hoff : nullptr;
 #pragma unroll
     for (int jt = 0; jt < TPW; ++jt) {
       const int t = w * TPW + jt;
       if (t >= T2) break;
       const int mv = t / NB, nr = t % NB;
       const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
-      if (r < L.len) store4<TI>(dvo + r * ts + vv, dvv[jt]);
+      if (r < L.len) {
+        store4<TI>(dvo + r * ts + vv, dvv[jt]);
+        if constexpr (G2) store4<TI>(dwo + r * ts + vv, dwv[jt]);
+      }
     }
   }
   __syncthreads();
 
   // ---- S4: products with the states for the wave's (key block, row blocks)
   f32x4 aq[MR], ak[MR];
+  f32x4 ab[G2 ? MR : 1];  // GDN-2: gradient of the erase gate b (then draw_b)
   TG aG[MR][4];
 #pragma unroll
   for (int jm = 0; jm < MR; ++jm) {
     aq[jm] = ak[jm] = zero4();
+    if constexpr (G2) ab[jm] = zero4();
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) aG[jm][rr] = 0;
   }
@@ -393,7 +439,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         const float qh = q4[rr] * rqs4[rr];
         const float kh = k4[rr] * rk4[rr];
         const float dqg = rQg[rr], dkg = rKg[rr], dKb = -rKb[rr];
-        const float b = be4[rr];
+        // beta; under GDN-2 the channel's erase gate (be is 1 on valid rows)
+        const float b = G2 ? be4[rr] * sigmoidf(bits_to_f<TI>(bsc[jm][rr])) : be4[rr];
         aq[jm][rr] += dqg * eG;
         ak[jm][rr] += dkg * eGc + b * dKb * eG;
         // -kg*dkg here and +kg*dkg in the G_c row cancel in the reverse
@@ -402,8 +449,12 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         aG[jm][rr] += static_cast<TG>(dqg) * qh * eG - kgdkg + static_cast<TG>(dKb) * b * kh * eG;
         colsum += kgdkg;
         dKb_s[r * LDA + kk] = from_f<OpT>(dKb);
-        const float pb = sum16(dKb * kh * eG);
-        if (i == 0) dbp[w][r] += pb;
+        if constexpr (G2) {
+          ab[jm][rr] += dKb * kh * eG;
+        } else {
+          const float pb = sum16(dKb * kh * eG);
+          if (i == 0) dbp[w][r] += pb;
+        }
       }
     }
     colsum += __shfl_xor(colsum, 16, kWave);
@@ -415,6 +466,15 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // ---- S5: dAqk and dAkk, lower 16x16 blocks (m rows, ns columns)
   constexpr int NPAIR = NB * (NB + 1) / 2, PPW = (NPAIR + NW - 1) / NW;
   f32x4 xq[PPW], xk[PPW];
+  // GDN-2: the erase gate rows, requested now and transposed into LDS for S6
+  VT braw[G2 ? VPT : 1];
+  if constexpr (G2) {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int e0 = tid + NT * j, e = e0 < NV ? e0 : 0, r = e / NVR, c = (e % NVR) * VE;
+      braw[j] = *reinterpret_cast<const VT*>(bkr + (r < L.len ? r : L.len - 1) * ts + c);
+    }
+  }
   {
     const OpT* Ug = static_cast<const OpT*>(ops.U) + idx * C * V;
     const OpT* Wng = static_cast<const OpT*>(ops.Wn) + idx * C * K;
@@ -451,8 +511,10 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         xq[jp][rr] = (s_ <= r) ? aqk[rr] : 0.f;
         const float dakk = (s_ < r) ? (a2[rr] - a1[rr]) : 0.f;
         xk[jp][rr] = be[r] * dakk;
-        const float pb = sum16(dakk * p4[rr]);
-        if (i == 0) dbp[w][r] += pb;
+        if constexpr (!G2) {  // GDN-2: the erase gate takes it in S6, per channel
+          const float pb = sum16(dakk * p4[rr]);
+          if (i == 0) dbp[w][r] += pb;
+        }
       }
     }
   }
@@ -473,6 +535,19 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     }
     store4<OpT>(dXqT + s_ * LDX + r0, xq[jp]);  // four adjacent columns
     store4<OpT>(dXkT + s_ * LDX + r0, xk[jp]);
+  }
+  if constexpr (G2) {
+    // b = sigmoid(raw_b), transposed and row-permuted like kT (0 past the end)
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
+      if (e < NV) {
+#pragma unroll
+        for (int q2 = 0; q2 < VE; ++q2)
+          bT[(c + q2) * LDQ + (r ^ swz(c + q2))] =
+              from_f<TI>(r < L.len ? sigmoidf(to_f(braw[j][q2])) : 0.f);
+      }
+    }
   }
   __syncthreads();
 
@@ -551,16 +626,26 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       const GV4 G4 = gt4(r0);
       const f32x4 q4 = tile4(qT, r0), k4 = tile4(kT, r0), rqs4 = sc4(rqs, r0), rk4 = sc4(rk, r0);
       const TG gb0 = static_cast<TG>(Gk[b0 ^ swk]);
+      // GDN-2: the erase gate at rows r0 .. r0 + 3 (the row operand of Akk is b kh)
+      f32x4 b4 = f32x4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (G2) b4 = tile4(bT, r0);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const TG f = PH ? ediag[r0 + rr] : VJ::ex(static_cast<TG>(G4[rr]) - gb0);  // exp(G_r - G_b)
         // dG takes the column side's operand values for this pair, rounded as
         // that side's MFMA operands are (see Vjp)
+        const TG khr = static_cast<TG>(k4[rr]) * static_cast<TG>(rk4[rr]);
         const TG Aq = VJ::rnd(static_cast<TG>(q4[rr]) * static_cast<TG>(rqs4[rr]) * f),
-                 Ak = VJ::rnd(static_cast<TG>(k4[rr]) * static_cast<TG>(rk4[rr]) * f);
+                 Ak = VJ::rnd(khr * static_cast<TG>(b4[rr]) * f);
         aq[jm][rr] += static_cast<float>(rq_[rr] * f);
-        ak[jm][rr] += static_cast<float>(rk_[rr] * f);
+        ak[jm][rr] += static_cast<float>(rk_[rr] * f * static_cast<TG>(b4[rr]));
+        if constexpr (G2) ab[jm][rr] += static_cast<float>(rk_[rr] * f * khr);
         aG[jm][rr] += Aq * rq_[rr] + Ak * rk_[rr];
+      }
+      if constexpr (G2) {
+        // the erase gate's own gradient through its sigmoid: draw_b
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) ab[jm][rr] *= b4[rr] * (1.f - b4[rr]);
       }
       // column side: rows s of block J = I here, reduction over r in blocks
       // I2 >= J; the 32-long reduction index u covers (beta*dAkk, kh) for
@@ -584,13 +669,25 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
             const int rb = c0 + (u & 15);
             const Rows8 v = u < 16 ? rows8(kq, rk, rb) : rows8(qk, rqs, rb);
             const float gc = Gk[c0 ^ swk];
+            float eg[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) eg[j] = 1.f;
+            if constexpr (G2) {
+              // the row operand of the Akk part is b kh
+              if (u < 16) {
+                const bf16x8 bv8 = *reinterpret_cast<const bf16x8*>(bT + kk * LDQ + (rb ^ swk));
+#pragma unroll
+                for (int j = 0; j < 8; ++j) eg[j] = to_f(bv8[j]);
+              }
+            }
             fb = VJ::make([&](int j) {
-              return v.x[j] * v.sc[j] * (PH ? ediag[rb + j] : VJ::ex(v.G[j] - gc));
+              return v.x[j] * v.sc[j] * eg[j] * (PH ? ediag[rb + j] : VJ::ex(v.G[j] - gc));
             });
           } else {
             fb = VJ::make([&](int j) {
               const int uu = u + j, r = c0 + (uu & 15);
-              return (uu < 16 ? khat(r) : qhat(r)) * (PH ? ediag[r] : dec(r, c0));
+              const TG e = (G2 && uu < 16) ? static_cast<TG>(to_f(bT[kk * LDQ + (r ^ swk)])) : TG(1);
+              return (uu < 16 ? khat(r) : qhat(r)) * e * (PH ? ediag[r] : dec(r, c0));
             });
           }
           y = VJ::mma(VJ::load(ap), fb, y);
@@ -812,10 +909,12 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) pA += __shfl_xor(pA, o, kWave);
     if (lane == 0) red[w] = pA;
-    for (int r = tid; r < L.len; r += NT) {
-      float db_ = 0.f;
-      for (int w2 = 0; w2 < NW; ++w2) db_ += dbp[w2][r];
-      dbeta[(L.t0 + r) * d.H + h] = from_f<TI>(db_ * be[r] * (1.f - be[r]));
+    if constexpr (!G2) {
+      for (int r = tid; r < L.len; r += NT) {
+        float db_ = 0.f;
+        for (int w2 = 0; w2 < NW; ++w2) db_ += dbp[w2][r];
+        dbeta[(L.t0 + r) * d.H + h] = from_f<TI>(db_ * be[r] * (1.f - be[r]));
+      }
     }
     __syncthreads();
     double* part = partials + (static_cast<size_t>(cglob) * d.H + h) * (K + 1);
@@ -840,32 +939,52 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
           *reinterpret_cast<VT*>(dgo + r * ts + c) = *reinterpret_cast<const VT*>(xg_s + r * LDA + c);
       }
     }
+    if constexpr (G2) {
+      // draw_b [T][H][K] from the per-channel accumulators (16 lanes write
+      // 16 consecutive channels of a row)
+      TI* dbo = dbeta + L.t0 * ts + hoff;
+#pragma unroll
+      for (int jm = 0; jm < MR; ++jm) {
+        const int m = row_block(jm);
+        if (m >= NB) break;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 16 * m + 4 * g + rr;
+          if (r < L.len) dbo[r * ts + kk] = from_f<TI>(ab[jm][rr]);
+        }
+      }
+    }
   }
 }
 
-template <typename TI, int D, int C, bool PH>
+template <typename TI, int D, int C, bool PH, bool G2>
 static hipError_t launch_cg(const Dims& d, const Inputs& in, const void* dO, int seg_begin,
                             int seg_chunks, const ChunkOps& ops, const SegStates& st, void* dq,
-                            void* dk, void* dv, void* dg, void* dbeta, double* partials,
-                            hipStream_t s) {
-  hipLaunchKernelGGL((k_chunk_grad<TI, TI, D, C, PH>), dim3(seg_chunks * d.H), dim3(D * 4 * grad_split<D>()), 0, s, d,
+                            void* dk, void* dv, void* dg, void* dbeta, void* dw,
+                            double* partials, hipStream_t s) {
+  // GDN-2's fp32 erase-gate tile does not fit beside the others at fp32,
+  // D = 64, C = 64 (the host rejects that combination)
+  if constexpr (G2 && sizeof(TI) == 4 && D == 64 && C == 64) return hipErrorNotSupported;
+  else hipLaunchKernelGGL((k_chunk_grad<TI, TI, D, C, PH, G2>), dim3(seg_chunks * d.H), dim3(D * 4 * grad_split<D>()), 0, s, d,
                      in, static_cast<const TI*>(dO), seg_begin, ops, st, static_cast<TI*>(dq),
                      static_cast<TI*>(dk), static_cast<TI*>(dv), static_cast<TI*>(dg),
-                     static_cast<TI*>(dbeta), partials);
+                     static_cast<TI*>(dbeta), static_cast<TI*>(dw), partials);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_grad(int dtype, int D, int C, const Dims& d, const Inputs& in,
                              const void* dO, int seg_begin, int seg_chunks,
                              const ChunkOps& ops, const SegStates& st, void* dq, void* dk,
-                             void* dv, void* dg, void* dbeta, double* partials,
+                             void* dv, void* dg, void* dbeta, void* dw, double* partials,
                              hipStream_t s) {
 #define KDA_CG(TI, DD, CC)                                                                     \
   if (D == DD && C == CC)                                                                      \
-    return d.gate_head ? launch_cg<TI, DD, CC, true>(d, in, dO, seg_begin, seg_chunks, ops, st, \
-                                                     dq, dk, dv, dg, dbeta, partials, s)        \
-                       : launch_cg<TI, DD, CC, false>(d, in, dO, seg_begin, seg_chunks, ops,    \
-                                                      st, dq, dk, dv, dg, dbeta, partials, s);
+    return d.gdn2 ? launch_cg<TI, DD, CC, false, true>(d, in, dO, seg_begin, seg_chunks, ops, st, \
+                                                       dq, dk, dv, dg, dbeta, dw, partials, s)  \
+           : d.gate_head ? launch_cg<TI, DD, CC, true, false>(d, in, dO, seg_begin, seg_chunks, ops, st, \
+                                                     dq, dk, dv, dg, dbeta, dw, partials, s)    \
+                       : launch_cg<TI, DD, CC, false, false>(d, in, dO, seg_begin, seg_chunks, ops, \
+                                                      st, dq, dk, dv, dg, dbeta, dw, partials, s);
   if (dtype == 0) {
     KDA_CG(float, 64, 16) KDA_CG(float, 64, 32) KDA_CG(float, 64, 64)
     KDA_CG(float, 128, 16) KDA_CG(float, 128, 32)

@@ -101,7 +101,12 @@ struct TileT<float, D, C> {
 // gamma), for a pass that only carries the state. PH: a gate per head
 // (Dims::gate_head), equal in every channel, so each gate factor is one
 // exponential per row instead of one per element.
-template <typename TI, typename OpT, int D, int C, bool BWD, bool STATE, bool PH>
+// G2: GDN-2 ("KDA at the production shape...", section 1.6 and the table of
+// section 2.1: akk = (b k Gamma)(k / Gamma)^T, w = M^-1 (b k Gamma),
+// u = M^-1 (w v)): a per-channel erase gate b = sigmoid(raw_b) and write gate
+// w = sigmoid(raw_w) replace beta. The row side of the k.k products carries
+// b, so P is Akk itself (beta = 1 below), Kb = b kh e^G and Bv = w v.
+template <typename TI, typename OpT, int D, int C, bool BWD, bool STATE, bool PH, bool G2>
 __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int seg_begin,
                                                      ChunkOps ops) {
   using M = Mma<OpT>;
@@ -142,6 +147,9 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   const TI* qr = static_cast<const TI*>(in.q) + L.t0 * ts + static_cast<size_t>(h) * D;
   const TI* kr = static_cast<const TI*>(in.k) + L.t0 * ts + static_cast<size_t>(h) * D;
   const TI* vr = static_cast<const TI*>(in.v) + L.t0 * ts + static_cast<size_t>(h) * D;
+  // GDN-2 gate rows (raw), [T][H][K] and [T][H][V]
+  const TI* bkr = G2 ? static_cast<const TI*>(in.bk) + L.t0 * ts + static_cast<size_t>(h) * D : nullptr;
+  const TI* wvr = G2 ? static_cast<const TI*>(in.wv) + L.t0 * ts + static_cast<size_t>(h) * D : nullptr;
 
   for (int e = tid; e < C * LDM; e += 256) Ms[e] = 0.f;
   auto G = [&](int r, int kk) -> GV& { return Gs[r * LDG + kk]; };
@@ -157,6 +165,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   constexpr int NPAIR = NB * (NB + 1) / 2, PPW = (NPAIR + 3) / 4, NKS = K / KS;
   struct PairRows {
     typename M::frag xa[NKS], xk[NKS], xb[NKS];
+    typename M::frag xe[G2 ? NKS : 1];  // GDN-2: raw erase gate of the row-side rows
   };
   auto pair_blocks = [](int p, int& I, int& J) {
     I = 0;
@@ -177,6 +186,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
       if (!STATE) f.xa[ks] = M::load(qr + rac * ts + kk);
       f.xk[ks] = M::load(kr + rac * ts + kk);
       f.xb[ks] = M::load(kr + rbc * ts + kk);
+      if constexpr (G2) f.xe[ks] = M::load(bkr + rac * ts + kk);
     }
   };
   // forward layout of a bf16 problem: Aqk as a bf16 pair (see do_pair, store_aqk)
@@ -218,7 +228,11 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
           eb[j] = GU::ex(gb - Gs[rb * LDG + kk + j]);
         }
       }
-      const auto fk = M::make([&](int j) { return el(f.xk[ks], j) * sk * ea[j]; });
+      // the row side of P carries the erase gate under GDN-2 (P = Akk)
+      const auto fk = M::make([&](int j) {
+        const float e = G2 ? sigmoidf(el(f.xe[ks], j)) : 1.f;
+        return el(f.xk[ks], j) * sk * ea[j] * e;
+      });
       if constexpr (HL) {
         // Aqk of the forward layout from bf16 pairs of both operands (hi hi,
         // lo hi, hi lo): the output takes Aqk directly, and rounding its
@@ -303,6 +317,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   constexpr int VE = 16 / sizeof(TI), LPR = D / VE;
   constexpr int NITEM = (C / 2) * LPR, IPT = (NITEM + 255) / 256;
   VT xq[IPT][2], xk[IPT][2], xv[IPT][2];
+  VT xe[G2 ? IPT : 1][2], xw[G2 ? IPT : 1][2];  // GDN-2 raw gate rows
   auto load_items = [&]() {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
@@ -316,6 +331,10 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
         if (!STATE) xq[it][h2] = *reinterpret_cast<const VT*>(qr + rc * ts + cc);
         xk[it][h2] = *reinterpret_cast<const VT*>(kr + rc * ts + cc);
         xv[it][h2] = *reinterpret_cast<const VT*>(vr + rc * ts + cc);
+        if constexpr (G2) {
+          xe[it][h2] = *reinterpret_cast<const VT*>(bkr + rc * ts + cc);
+          xw[it][h2] = *reinterpret_cast<const VT*>(wvr + rc * ts + cc);
+        }
       }
     }
   };
@@ -391,9 +410,16 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
           const float kh = to_f(xk[it][h2][j]) * sk;
           const float qg = STATE ? 0.f : to_f(xq[it][h2][j]) * sq * eG;
           const OpT kg = from_f<OpT>(kh * eGc);
+          // beta, or under GDN-2 the channel's erase (Kb) and write (Bv) gates
+          // (b is then 1 on valid rows, 0 past the chunk's end)
+          float bk = b, bw = b;
+          if constexpr (G2) {
+            bk = b * sigmoidf(to_f(xe[it][h2][j]));
+            bw = b * sigmoidf(to_f(xw[it][h2][j]));
+          }
           sv[it][0][j][h2] = kg;
-          sv[it][1][j][h2] = from_f<OpT>(b * kh * eG);
-          sv[it][2][j][h2] = from_f<OpT>(b * to_f(xv[it][h2][j]));
+          sv[it][1][j][h2] = from_f<OpT>(bk * kh * eG);
+          sv[it][2][j][h2] = from_f<OpT>(bw * to_f(xv[it][h2][j]));
           if (BWD) sv[it][NSV - 1][j][h2] = from_f<OpT>(qg);
           out[j] = BWD ? kg : from_f<OpT>(qg);
         }
@@ -515,6 +541,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   constexpr int NMW = (K / 16 + 3) / 4;
   constexpr bool UFIX = !BWD && sizeof(OpT) == 2;
   uint32_t vfix[UFIX ? NMW : 1][UFIX ? NB : 1][4];
+  uint32_t wfix[UFIX && G2 ? NMW : 1][UFIX && G2 ? NB : 1][4];  // GDN-2 write gate
   if constexpr (UFIX) {
 #pragma unroll
     for (int jm = 0; jm < NMW; ++jm) {
@@ -523,6 +550,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
       for (int n = 0; n < NB; ++n) {
         const int r = 16 * n + i, rc = r < L.len ? r : L.len - 1;
         load4_raw<TI>(vr + rc * ts + 16 * mk + 4 * g, vfix[jm][n]);
+        if constexpr (G2) load4_raw<TI>(wvr + rc * ts + 16 * mk + 4 * g, wfix[jm][n]);
       }
     }
   }
@@ -571,9 +599,17 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
           if constexpr (UFIX) {
             const int r = 16 * n + i;
             const f32x4 v4 = unpack4<TI>(vfix[jm][n]);
+            f32x4 w4 = f32x4{1.f, 1.f, 1.f, 1.f};
+            if constexpr (G2) {
+              const f32x4 x4 = unpack4<TI>(wfix[jm][n]);
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) w4[rr] = sigmoidf(x4[rr]);
+            }
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-              const float bv = be[r] * v4[rr];  // as staged (element pass)
+              // as staged (element pass)
+              const float bw = G2 ? be[r] * w4[rr] : be[r];
+              const float bv = bw * v4[rr];
               u[rr] += bv - to_f(from_f<OpT>(bv));
             }
           }
@@ -584,30 +620,31 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   }
 }
 
-template <typename TI, typename OpT, int D, int C, bool PH>
+template <typename TI, typename OpT, int D, int C, bool PH, bool G2>
 static hipError_t launch_cl(int mode, const Dims& d, const Inputs& in, int seg_begin,
                             int seg_chunks, const ChunkOps& ops, hipStream_t s) {
   const dim3 grid(seg_chunks * d.H), block(256);
   if (mode == KL_BWD)
-    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, true, false, PH>), grid, block, 0, s, d,
+    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, true, false, PH, G2>), grid, block, 0, s, d,
                        in, seg_begin, ops);
   else if (mode == KL_STATE)
-    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, false, true, PH>), grid, block, 0, s, d,
+    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, false, true, PH, G2>), grid, block, 0, s, d,
                        in, seg_begin, ops);
   else
-    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, false, false, PH>), grid, block, 0, s, d,
-                       in, seg_begin, ops);
+    hipLaunchKernelGGL((k_chunk_local<TI, OpT, D, C, false, false, PH, G2>), grid, block, 0, s,
+                       d, in, seg_begin, ops);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_local(int dtype, int D, int C, int mode, const Dims& d,
                               const Inputs& in, int seg_begin, int seg_chunks,
                               const ChunkOps& ops, hipStream_t s) {
-#define KDA_CL(TI, DD, CC)                                                                  \
-  if (D == DD && C == CC)                                                                   \
-    return d.gate_head                                                                      \
-               ? launch_cl<TI, TI, DD, CC, true>(mode, d, in, seg_begin, seg_chunks, ops, s) \
-               : launch_cl<TI, TI, DD, CC, false>(mode, d, in, seg_begin, seg_chunks, ops, s);
+#define KDA_CL(TI, DD, CC)                                                                   \
+  if (D == DD && C == CC)                                                                    \
+    return d.gdn2 ? launch_cl<TI, TI, DD, CC, false, true>(mode, d, in, seg_begin, seg_chunks, ops, s) \
+           : d.gate_head                                                                     \
+               ? launch_cl<TI, TI, DD, CC, true, false>(mode, d, in, seg_begin, seg_chunks, ops, s) \
+               : launch_cl<TI, TI, DD, CC, false, false>(mode, d, in, seg_begin, seg_chunks, ops, s);
   if (dtype == 0) {
     KDA_CL(float, 64, 16) KDA_CL(float, 64, 32) KDA_CL(float, 64, 64)
     KDA_CL(float, 128, 16) KDA_CL(float, 128, 32)

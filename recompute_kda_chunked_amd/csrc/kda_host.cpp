@@ -67,6 +67,14 @@ int check_problem(const kda_problem* p) {
   return KDA_OK;
 }
 
+// GDN-2 is built for the per-channel gate, at every size KDA is built for
+// except fp32 with K = 64 and 64-token chunks (its gradient kernel's tiles
+// exceed the LDS there).
+bool gdn2_supported(const kda_problem* p) {
+  if (p->gate_mode & KDA_GATE_PER_HEAD) return false;
+  return !(p->dtype == KDA_F32 && p->K == 64 && p->chunk == 64);
+}
+
 constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -239,7 +247,7 @@ struct ProfScope {
   } while (0)
 
 Dims make_dims(const kda_problem* p) {
-  Dims d;
+  Dims d{};
   d.N = p->n_seqs;
   d.H = p->H;
   d.scale = p->scale;
@@ -303,15 +311,21 @@ size_t kda_checkpoint_bytes(const kda_problem* p) {
   return static_cast<size_t>(P.NS) * state_slot(P);
 }
 
-int kda_fwd_ex(const kda_problem* p, const void* q, const void* k, const void* v,
-               const void* raw_g, const void* raw_beta, const float* A_log,
-               const float* dt_bias, const int32_t* cu_seqlens, void* o,
+}  // extern "C"
+
+namespace {
+
+// The forward of KDA (raw_beta) or of GDN-2 (g2: raw_b, raw_w).
+int fwd_common(bool g2, const kda_problem* p, const void* q, const void* k, const void* v,
+               const void* raw_g, const void* raw_beta, const void* raw_b, const void* raw_w,
+               const float* A_log, const float* dt_bias, const int32_t* cu_seqlens, void* o,
                const kda_state_io* io, void* workspace, size_t workspace_bytes, void* stream) {
   const int st = check_problem(p);
   if (st != KDA_OK) return st;
-  if (!q || !k || !v || !raw_g || !raw_beta || !A_log || !dt_bias || !cu_seqlens || !o ||
-      !workspace)
+  if (!q || !k || !v || !raw_g || !A_log || !dt_bias || !cu_seqlens || !o || !workspace)
     return KDA_ERR_INVALID;
+  if (g2 ? (!raw_b || !raw_w) : !raw_beta) return KDA_ERR_INVALID;
+  if (g2 && !gdn2_supported(p)) return KDA_ERR_UNSUPPORTED;
   const Plan P = make_plan(p, false);
   if (workspace_bytes < fwd_bytes(P)) return KDA_ERR_WORKSPACE;
   const kda_state_io none{};
@@ -332,8 +346,11 @@ int kda_fwd_ex(const kda_problem* p, const void* q, const void* k, const void* v
   carry[1] = reinterpret_cast<float*>(cur);
   cur += state_slot(P);
   const ChunkOps ops = carve_ops(P, false, cur);
-  const Dims d = make_dims(p);
-  const Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, tb.coff, tb.cloc};
+  Dims d = make_dims(p);
+  d.gdn2 = g2 ? 1 : 0;
+  Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, tb.coff, tb.cloc};
+  in.bk = raw_b;
+  in.wv = raw_w;
   KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, P.NC, tb.coff, tb.cloc, s));
   for (int sg = 0; sg < P.NS; ++sg) {
     const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
@@ -346,6 +363,26 @@ int kda_fwd_ex(const kda_problem* p, const void* q, const void* k, const void* v
   return KDA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int kda_fwd_ex(const kda_problem* p, const void* q, const void* k, const void* v,
+               const void* raw_g, const void* raw_beta, const float* A_log,
+               const float* dt_bias, const int32_t* cu_seqlens, void* o,
+               const kda_state_io* io, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_common(false, p, q, k, v, raw_g, raw_beta, nullptr, nullptr, A_log, dt_bias, cu_seqlens,
+                    o, io, workspace, workspace_bytes, stream);
+}
+
+int kda_gdn2_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
+                 const void* raw_g, const void* raw_b, const void* raw_w, const float* A_log,
+                 const float* dt_bias, const int32_t* cu_seqlens, void* o, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  return fwd_common(true, p, q, k, v, raw_g, nullptr, raw_b, raw_w, A_log, dt_bias, cu_seqlens, o,
+                    nullptr, workspace, workspace_bytes, stream);
+}
+
 int kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
             const void* raw_g, const void* raw_beta, const float* A_log, const float* dt_bias,
             const int32_t* cu_seqlens, void* o, void* workspace, size_t workspace_bytes,
@@ -354,17 +391,25 @@ int kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
                     workspace, workspace_bytes, stream);
 }
 
-int kda_bwd_ex(const kda_problem* p, const void* q, const void* k, const void* v,
-               const void* raw_g, const void* raw_beta, const float* A_log,
-               const float* dt_bias, const int32_t* cu_seqlens, const void* dO, void* dq,
-               void* dk, void* dv, void* draw_g, void* draw_beta, float* dA_log,
-               float* ddt_bias, const kda_state_io* io, void* workspace,
-               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward of KDA (raw_beta, draw_beta) or of GDN-2 (g2: raw_b, raw_w,
+// draw_b in draw_beta's place, draw_w).
+int bwd_common(bool g2, const kda_problem* p, const void* q, const void* k, const void* v,
+               const void* raw_g, const void* raw_beta, const void* raw_b, const void* raw_w,
+               const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
+               const void* dO, void* dq, void* dk, void* dv, void* draw_g, void* draw_beta,
+               void* draw_w, float* dA_log, float* ddt_bias, const kda_state_io* io,
+               void* workspace, size_t workspace_bytes, void* stream) {
   const int st = check_problem(p);
   if (st != KDA_OK) return st;
-  if (!q || !k || !v || !raw_g || !raw_beta || !A_log || !dt_bias || !cu_seqlens || !dO ||
-      !dq || !dk || !dv || !draw_g || !draw_beta || !dA_log || !ddt_bias || !workspace)
+  if (!q || !k || !v || !raw_g || !A_log || !dt_bias || !cu_seqlens || !dO || !dq || !dk ||
+      !dv || !draw_g || !draw_beta || !dA_log || !ddt_bias || !workspace)
     return KDA_ERR_INVALID;
+  if (g2 ? (!raw_b || !raw_w || !draw_w) : !raw_beta) return KDA_ERR_INVALID;
+  if (g2 && !gdn2_supported(p)) return KDA_ERR_UNSUPPORTED;
   const Plan P = make_plan(p, true);
   if (workspace_bytes < bwd_bytes(P)) return KDA_ERR_WORKSPACE;
   const kda_state_io none{};
@@ -404,8 +449,11 @@ int kda_bwd_ex(const kda_problem* p, const void* q, const void* k, const void* v
     sts.dVnT = cur;
     cur += up(n * C * K * e);
   }
-  const Dims d = make_dims(p);
-  const Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, tb.coff, tb.cloc};
+  Dims d = make_dims(p);
+  d.gdn2 = g2 ? 1 : 0;
+  Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, tb.coff, tb.cloc};
+  in.bk = raw_b;
+  in.wv = raw_w;
   KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, P.NC, tb.coff, tb.cloc, s));
   // checkpoint pass: the state entering each segment (skipped when the
   // forward saved them)
@@ -424,12 +472,37 @@ int kda_bwd_ex(const kda_problem* p, const void* q, const void* k, const void* v
     KDA_TRY(KDA_KERNEL_SCAN_BWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_bwd(P.dtype, P.D, P.C, d, in, dO, c0, c1, ops_b, sts,
                             dcarry[(sg + 1) & 1], dcarry[sg & 1], bwd_ss, s));
     KDA_TRY(KDA_KERNEL_CHUNK_GRAD, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_grad(P.dtype, P.D, P.C, d, in, dO, c0, c1 - c0, ops_b, sts, dq, dk, dv,
-                              draw_g, draw_beta, partials, s));
+                              draw_g, draw_beta, draw_w, partials, s));
   }
   KDA_TRY(KDA_KERNEL_GATE_REDUCE, 0, launch_gate_reduce(P.D, P.H, P.NC, d.gate_head, partials, dA_log, ddt_bias, s));
   if (io->dh0 && has_empty_sequence(p))
     KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_state_passthrough(cu_seqlens, P.N, P.H, P.D * P.D, io->dht, io->dh0, s));
   return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_bwd_ex(const kda_problem* p, const void* q, const void* k, const void* v,
+               const void* raw_g, const void* raw_beta, const float* A_log,
+               const float* dt_bias, const int32_t* cu_seqlens, const void* dO, void* dq,
+               void* dk, void* dv, void* draw_g, void* draw_beta, float* dA_log,
+               float* ddt_bias, const kda_state_io* io, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return bwd_common(false, p, q, k, v, raw_g, raw_beta, nullptr, nullptr, A_log, dt_bias, cu_seqlens,
+                    dO, dq, dk, dv, draw_g, draw_beta, nullptr, dA_log, ddt_bias, io, workspace,
+                    workspace_bytes, stream);
+}
+
+int kda_gdn2_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
+                 const void* raw_g, const void* raw_b, const void* raw_w, const float* A_log,
+                 const float* dt_bias, const int32_t* cu_seqlens, const void* dO, void* dq,
+                 void* dk, void* dv, void* draw_g, void* draw_b, void* draw_w, float* dA_log,
+                 float* ddt_bias, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(true, p, q, k, v, raw_g, nullptr, raw_b, raw_w, A_log, dt_bias, cu_seqlens, dO,
+                    dq, dk, dv, draw_g, draw_b, draw_w, dA_log, ddt_bias, nullptr, workspace,
+                    workspace_bytes, stream);
 }
 
 int kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,

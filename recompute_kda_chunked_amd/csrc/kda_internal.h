@@ -15,6 +15,9 @@ struct Dims {
   int gate_mode;  // 0: L * sigmoid(e^A (x + b)); 1: max(L, -e^A softplus(x + b))
   int gate_head;  // 1: one gate per head and token (raw_g [T][H], dt_bias [H],
                   // draw_g [T][H], ddt_bias [H]); 0: one per channel
+  int gdn2;       // 1: GDN-2, a per-channel erase gate b = sigmoid(raw_b) [T][H][K]
+                  // and write gate w = sigmoid(raw_w) [T][H][V] replace beta
+                  // (Inputs::bk, Inputs::wv; Inputs::beta unused)
 };
 
 // Raw operator inputs (device pointers, dtype per the problem).
@@ -24,6 +27,7 @@ struct Inputs {
   const int32_t *cu;    // cu_seqlens [N+1]
   const int32_t *coff;  // chunk offsets [N+1]
   const int2 *cloc;     // per chunk: {first token, valid rows} [NC]
+  const void *bk = nullptr, *wv = nullptr;  // GDN-2: raw_b [T][H][K], raw_w [T][H][V]
 };
 
 // Per-(chunk, head) operands produced by the chunk-local kernel for one
@@ -107,11 +111,12 @@ hipError_t launch_scan_bwd(int dtype, int D, int C, const Dims& d, const Inputs&
 hipError_t launch_state_passthrough(const int32_t* cu, int N, int H, int KV, const float* src,
                                     float* dst, hipStream_t s);
 // Token-parallel gradients for one segment; writes dq, dk, dv, draw_g,
-// draw_beta for its tokens and gate-parameter partials [chunk][H][K+1].
+// draw_beta (GDN-2: draw_b [T][H][K] into dbeta, draw_w [T][H][V] into dw)
+// for its tokens and gate-parameter partials [chunk][H][K+1].
 hipError_t launch_chunk_grad(int dtype, int D, int C, const Dims& d, const Inputs& in,
                              const void* dO, int seg_begin, int seg_chunks,
                              const ChunkOps& ops, const SegStates& st, void* dq, void* dk,
-                             void* dv, void* dg, void* dbeta, double* partials,
+                             void* dv, void* dg, void* dbeta, void* dw, double* partials,
                              hipStream_t s);
 // gate_head: ddt_bias[h] is the sum over all K partial columns of head h.
 hipError_t launch_gate_reduce(int D, int H, int n_chunks, int gate_head,

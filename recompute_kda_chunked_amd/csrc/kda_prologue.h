@@ -170,7 +170,7 @@ __device__ __forceinline__ void prologue_load(const Dims& d, const Inputs& in, i
       p.xs[it] = load_bits<TI>(xh + static_cast<size_t>(rc) * d.H);
     else
       p.xv[it] = *reinterpret_cast<const VT*>(x + rc * ts);
-    p.bv[it] = load_bits<TI>(rb + static_cast<size_t>(rc) * d.H);
+    p.bv[it] = d.gdn2 ? 0u : load_bits<TI>(rb + static_cast<size_t>(rc) * d.H);
   }
 }
 
@@ -267,7 +267,9 @@ __device__ __forceinline__ void prologue_compute_m(const Dims& d, const ChunkLoc
         rq[r] = a;
         rqs[r] = d.scale * a;
         rk[r] = b;
-        be[r] = valid ? sigmoidf(bits_to_f<TI>(p.bv[it])) : 0.f;
+        // GDN-2 has no scalar beta: its gates act per channel (1 keeps the
+        // beta-scaled terms of the kernels as they are)
+        be[r] = valid ? (d.gdn2 ? 1.f : sigmoidf(bits_to_f<TI>(p.bv[it]))) : 0.f;
       }
     }
   }

@@ -77,6 +77,8 @@ def _check_inputs(q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, extra=()
             "raw_g": (raw_g, gk, dt), "raw_beta": (raw_beta, (T, H), dt),
             "A_log": (A_log, (H,), torch.float32), "dt_bias": (dt_bias, gk[1:], torch.float32),
             "cu_seqlens": (cu_seqlens, (cu_seqlens.shape[0],), torch.int32)}
+    if raw_beta is None:  # GDN-2: the gates come in `extra`
+        del want["raw_beta"]
     for name, (t, shape, dtype) in list(want.items()) + list(extra):
         if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
             raise KdaError("%s: expected shape %s dtype %s, got %s %s"
@@ -236,6 +238,58 @@ def kda_backward(q, k, v, raw_g, raw_beta, A_log, dt_bias, dO, cu_seqlens=None, 
     if dh0 is not None:
         return dq, dk, dv, dg, db, dA, ddt, dh0
     return dq, dk, dv, dg, db, dA, ddt
+
+
+def gdn2_forward(q, k, v, raw_g, raw_b, raw_w, A_log, dt_bias, cu_seqlens=None, *,
+                 cu_seqlens_host=None, scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6,
+                 seg_chunks=0, gate_mode=_lib.KDA_GATE_SIGMOID_BOUND):
+    """O [T,H,V] of GDN-2: per-channel erase gate sigmoid(raw_b) [T,H,K] and
+    write gate sigmoid(raw_w) [T,H,V] in place of KDA's beta (kda_gdn2_fwd)."""
+    if cu_seqlens is None:
+        cu_seqlens, cu_seqlens_host = _default_cu(q.shape[0], q.device)
+    T, H, K, V, dt, ph = _check_inputs(
+        q, k, v, raw_g, None, A_log, dt_bias, cu_seqlens,
+        extra=[("raw_b", (raw_b, tuple(k.shape), q.dtype)), ("raw_w", (raw_w, tuple(v.shape), q.dtype))])
+    prob = Problem(T, H, K, V, dt, _cu_host(cu_seqlens, cu_seqlens_host), chunk, scale,
+                   lower_bound, eps, seg_chunks, _gate_flags(gate_mode, ph))
+    lib = _lib.load()
+    _raise(lib, prob.check(), "kda_gdn2_fwd")
+    o = torch.empty((T, H, V), dtype=dt, device=q.device)
+    ws = torch.empty(prob.fwd_ws(), dtype=torch.uint8, device=q.device)
+    st = lib.kda_gdn2_fwd(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(raw_g), _ptr(raw_b),
+                          _ptr(raw_w), _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(o),
+                          _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(q.device))
+    _raise(lib, st, "kda_gdn2_fwd")
+    return o
+
+
+def gdn2_backward(q, k, v, raw_g, raw_b, raw_w, A_log, dt_bias, dO, cu_seqlens=None, *,
+                  cu_seqlens_host=None, scale=1.0, chunk=64, lower_bound=-5.0, eps=1e-6,
+                  seg_chunks=0, gate_mode=_lib.KDA_GATE_SIGMOID_BOUND):
+    """(dq, dk, dv, draw_g, draw_b, draw_w, dA_log, ddt_bias) of
+    sum(O * dO) for GDN-2 (kda_gdn2_bwd), each shaped as its input."""
+    if cu_seqlens is None:
+        cu_seqlens, cu_seqlens_host = _default_cu(q.shape[0], q.device)
+    T, H, K, V, dt, ph = _check_inputs(
+        q, k, v, raw_g, None, A_log, dt_bias, cu_seqlens,
+        extra=[("raw_b", (raw_b, tuple(k.shape), q.dtype)), ("raw_w", (raw_w, tuple(v.shape), q.dtype)),
+               ("dO", (dO, tuple(v.shape), v.dtype))])
+    prob = Problem(T, H, K, V, dt, _cu_host(cu_seqlens, cu_seqlens_host), chunk, scale,
+                   lower_bound, eps, seg_chunks, _gate_flags(gate_mode, ph))
+    lib = _lib.load()
+    _raise(lib, prob.check(), "kda_gdn2_bwd")
+    dev = q.device
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg, db, dw = torch.empty_like(raw_g), torch.empty_like(raw_b), torch.empty_like(raw_w)
+    dA = torch.empty((H,), dtype=torch.float32, device=dev)
+    ddt = torch.empty_like(dt_bias)
+    ws = torch.empty(prob.bwd_ws(), dtype=torch.uint8, device=dev)
+    st = lib.kda_gdn2_bwd(prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(raw_g), _ptr(raw_b),
+                          _ptr(raw_w), _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(dO),
+                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dw), _ptr(dA),
+                          _ptr(ddt), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    _raise(lib, st, "kda_gdn2_bwd")
+    return dq, dk, dv, dg, db, dw, dA, ddt
 
 
 def kda_prologue(q, k, raw_g, raw_beta, A_log, dt_bias, cu_seqlens=None, *,

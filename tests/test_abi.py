@@ -25,7 +25,7 @@ def lib():
 def header_functions():
     src = open(os.path.join(ROOT, "include", "kda.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_and_binding_agree():
@@ -175,3 +175,25 @@ def test_noalloc_rejects_problems_beyond_its_scratch(lib):
     assert lib.kda_fwd_noalloc(big.ref, *([fake] * 9), nul) == _lib.KDA_ERR_WORKSPACE
     assert lib.kda_fwd_noalloc(good().ref, *([nul] * 9), nul) == _lib.KDA_ERR_INVALID
     assert lib.kda_fwd_noalloc(good(H=0).ref, *([fake] * 9), nul) == _lib.KDA_ERR_INVALID
+
+
+def test_gdn2_entry_points_validate_before_any_launch(lib):
+    fake = ctypes.c_void_p(0x1000)
+    nul = ctypes.c_void_p(0)
+    p = good()
+    # null gate pointers, then the unbuilt combinations
+    args = [fake] * 10
+    args[5] = nul  # raw_w
+    assert lib.kda_gdn2_fwd(p.ref, *args, fake, ctypes.c_size_t(p.fwd_ws()), nul) == _lib.KDA_ERR_INVALID
+    ph = good(gate_mode=_lib.KDA_GATE_PER_HEAD)
+    assert lib.kda_gdn2_fwd(ph.ref, *([fake] * 10), fake, ctypes.c_size_t(ph.fwd_ws()),
+                            nul) == _lib.KDA_ERR_UNSUPPORTED
+    f64 = good(dtype=_lib.KDA_F32, K=64, V=64, chunk=64)
+    assert f64.check() == _lib.KDA_OK  # KDA is built there
+    assert lib.kda_gdn2_bwd(f64.ref, *([fake] * 18), fake, ctypes.c_size_t(f64.bwd_ws()),
+                            nul) == _lib.KDA_ERR_UNSUPPORTED
+    args = [fake] * 18
+    args[15] = nul  # draw_w
+    assert lib.kda_gdn2_bwd(p.ref, *args, fake, ctypes.c_size_t(p.bwd_ws()), nul) == _lib.KDA_ERR_INVALID
+    assert lib.kda_gdn2_fwd(p.ref, *([fake] * 10), fake, ctypes.c_size_t(p.fwd_ws() - 1),
+                            nul) == _lib.KDA_ERR_WORKSPACE
