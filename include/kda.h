@@ -96,7 +96,14 @@ typedef struct {
                               KDA_ERR_UNSUPPORTED, L >= 0 or not finite
                               KDA_ERR_INVALID */
   float l2_eps;            /* eps of the Q/K L2 normalisation, e.g. 1e-6 */
-  int32_t seg_chunks;      /* backward streaming segment in chunks; 0 = automatic */
+  int32_t seg_chunks;      /* most chunks one streaming segment holds (forward
+                              and backward); 0 = automatic (the segments fit
+                              the workspace budget). A segment is either a
+                              run of the chunk order (sequences one after
+                              another) or, for a packed batch with several
+                              long sequences, a window of the same chunk
+                              positions in every sequence; the library takes
+                              the plan whose scans have the shorter chain */
   const int32_t *cu_seqlens_host; /* host copy of cu_seqlens [N+1]: non-decreasing
                                      from 0 to T; used for planning only */
 } kda_problem;
@@ -153,14 +160,15 @@ int kda_bwd(const kda_problem *p, const void *q, const void *k, const void *v,
                          sum(o * dO) + sum(ht * dht).
      dh0   [N, H, K, V]  kda_bwd_ex: gradient with respect to h0 (NULL: not
                          written).
-     ckpt, ckpt_bytes    kda_fwd_ex writes, kda_bwd_ex reads, the state that
-                         enters every backward segment (kda_checkpoint_bytes
-                         bytes, at multiples of kda_bwd_segment_chunks
-                         chunks), so the backward skips the pass that
-                         recomputes them. Pass the same problem to both calls
-                         (set seg_chunks explicitly, or keep the workspace
-                         budget unchanged between them). ckpt_bytes smaller
-                         than kda_checkpoint_bytes: KDA_ERR_WORKSPACE.
+     ckpt, ckpt_bytes    kda_fwd_ex writes, kda_bwd_ex reads, the states
+                         that enter the backward's segments inside each
+                         sequence (kda_checkpoint_bytes bytes, a layout
+                         private to the library), so the backward skips the
+                         pass that recomputes them. Pass the same problem to
+                         both calls (set seg_chunks explicitly, or keep the
+                         workspace budget unchanged between them).
+                         ckpt_bytes smaller than kda_checkpoint_bytes:
+                         KDA_ERR_WORKSPACE.
    The backward still recomputes w, u and h of every chunk. kda_fwd_ex reads
    h0 and writes ht and ckpt; kda_bwd_ex reads h0, dht and ckpt (which it
    leaves unchanged) and writes dh0. The same problem and h0 must be passed
@@ -175,7 +183,8 @@ typedef struct {
 } kda_state_io;
 
 /* Bytes of the checkpoint buffer of kda_state_io for this problem, and the
-   backward's segment length in chunks (0 when the problem is invalid). */
+   backward's segment length: chunks per segment, or chunks of each sequence
+   per segment for a plan by windows (0 when the problem is invalid). */
 size_t kda_checkpoint_bytes(const kda_problem *p);
 int32_t kda_bwd_segment_chunks(const kda_problem *p);
 

@@ -733,7 +733,9 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     }
   }
   // exp(A_log) in the gate's precision, as the forward's gate map takes it
-  const TG eat = exp(static_cast<TG>(in.A_log[h]));
+  // (A_log[h] from the prologue's loads: a load issued here would wait
+  // behind this phase's others)
+  const TG eat = exp(static_cast<TG>(pr.alog));
 #pragma unroll
   for (int jm = 0; jm < MR; ++jm) {
     const int m = row_block(jm);

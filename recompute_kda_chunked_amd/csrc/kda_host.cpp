@@ -78,12 +78,26 @@ bool gdn2_supported(const kda_problem* p) {
 constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// One segment of a plan (Seg in kda_internal.h, host side).
+struct SegInfo {
+  int c0, c1;  // chunk-order indices
+  int n0, n1;  // sequences that may have chunks in it
+  int active;  // sequences that have
+  int pos0;    // plan by windows: position of every sequence's first chunk in it
+};
+
 struct Plan {
   int N, H, D, C, dtype;
   int64_t T;
-  int NC;        // chunks over all sequences
-  int seg, NS;   // chunks per segment, number of segments
-  size_t esz;    // operand element size
+  int NC;      // chunks over all sequences
+  int seg;     // segment length: chunks (sequence order), or chunks of each sequence (windows)
+  int NS;      // number of segments
+  bool win;    // plan by windows
+  int segmax;  // most chunks in one segment (the operand buffers hold that many)
+  int xslots;  // state slots of each carry buffer
+  int nck;     // checkpoint slots
+  size_t esz;  // operand element size
+  std::vector<SegInfo> segs;
 };
 
 size_t fwd_ops_per(const Plan& P) {  // bytes per (chunk, head), forward operands
@@ -102,6 +116,21 @@ size_t budget_bytes() {
   return static_cast<size_t>(mb) << 20;
 }
 
+// Largest table of sequence starts per segment a plan by windows may use
+// (segments x (sequences + 1) entries).
+constexpr int64_t kMaxWindowTable = 1 << 20;
+
+// Segments of at most `cap` chunks. Two plans:
+//   sequence order: the chunk order lists the sequences one after another
+//     and a segment is a run of `seg` chunks of it, so at most one sequence
+//     crosses each boundary;
+//   windows: segment sg holds chunks [sg w, (sg + 1) w) of every sequence,
+//     so each segment's scans run every sequence at once over w chunks.
+// The scans walk each segment's chunks one after another per (sequence,
+// head), so a plan's critical path is the sum over its segments of the most
+// chunks one sequence has in it: windows are taken when that is at most
+// three quarters of the sequence-order plan's (several long sequences in a
+// packed batch; a single sequence gives both plans the same segments).
 Plan make_plan(const kda_problem* p, bool bwd) {
   Plan P{};
   P.N = p->n_seqs;
@@ -111,30 +140,116 @@ Plan make_plan(const kda_problem* p, bool bwd) {
   P.dtype = p->dtype;
   P.T = p->total_tokens;
   P.esz = p->dtype == KDA_BF16 ? 2 : 4;
-  int64_t nc = 0;
-  for (int n = 0; n < P.N; ++n)
-    nc += (p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n] + P.C - 1) / P.C;
-  P.NC = static_cast<int>(nc);
+  const int N = P.N;
+  std::vector<int> nc(N), coff(N + 1, 0);
+  int act = 0, maxnc = 0;
+  for (int n = 0; n < N; ++n) {
+    nc[n] = (p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n] + P.C - 1) / P.C;
+    coff[n + 1] = coff[n] + nc[n];
+    act += nc[n] > 0;
+    maxnc = nc[n] > maxnc ? nc[n] : maxnc;
+  }
+  P.NC = coff[N];
   const size_t per = (bwd ? bwd_ops_per(P) : fwd_ops_per(P)) * P.H;
-  int seg = p->seg_chunks;
-  if (seg <= 0) {
+  int cap, seg;
+  if (p->seg_chunks > 0) {
+    cap = seg = p->seg_chunks;
+  } else {
     // the fewest segments that fit the budget, then equal segment lengths
     // (no short last segment: every launch fills the same number of rounds)
     const size_t fit = budget_bytes() / per;
-    const int cap = static_cast<int>(fit < 1 ? 1 : (fit > static_cast<size_t>(P.NC) ? P.NC : fit));
+    cap = static_cast<int>(fit < 1 ? 1 : (fit > static_cast<size_t>(P.NC) ? P.NC : fit));
     const int ns = (P.NC + cap - 1) / cap;
     seg = (P.NC + ns - 1) / ns;
   }
   if (seg > P.NC) seg = P.NC;
   if (seg < 1) seg = 1;
-  P.seg = seg;
-  P.NS = (P.NC + seg - 1) / seg;
+  // sequence order
+  const int ns_seq = (P.NC + seg - 1) / seg;
+  std::vector<SegInfo> sq(ns_seq);
+  int64_t cost_seq = 0;
+  for (int sg = 0, n = 0; sg < ns_seq; ++sg) {
+    SegInfo& e = sq[sg];
+    e.c0 = sg * seg;
+    e.c1 = e.c0 + seg < P.NC ? e.c0 + seg : P.NC;
+    e.pos0 = 0;
+    while (coff[n + 1] <= e.c0) ++n;  // first sequence with a chunk at or after c0
+    e.n0 = n;
+    e.active = 0;
+    int m = n, run = 0;
+    for (; m < N && coff[m] < e.c1; ++m) {
+      const int lo = coff[m] > e.c0 ? coff[m] : e.c0, hi = coff[m + 1] < e.c1 ? coff[m + 1] : e.c1;
+      if (hi > lo) {
+        ++e.active;
+        run = hi - lo > run ? hi - lo : run;
+      }
+    }
+    e.n1 = m;
+    cost_seq += run;
+  }
+  P.win = false;
+  if (ns_seq > 1 && act >= 2 && act <= cap) {
+    auto held = [&](int w) {  // chunks of a window-w segment 0
+      int64_t t = 0;
+      for (int n = 0; n < N; ++n) t += nc[n] < w ? nc[n] : w;
+      return t;
+    };
+    int lo = 1, hi = maxnc;  // held(lo) <= cap
+    while (lo < hi) {
+      const int mid = lo + (hi - lo + 1) / 2;
+      if (held(mid) <= cap) lo = mid; else hi = mid - 1;
+    }
+    const int nsw = (maxnc + lo - 1) / lo, w = (maxnc + nsw - 1) / nsw;
+    if (static_cast<int64_t>(nsw) * (N + 1) <= kMaxWindowTable && 4LL * maxnc <= 3 * cost_seq) {
+      P.win = true;
+      P.seg = w;
+      P.NS = nsw;
+      P.segs.resize(nsw);
+      int64_t below = 0;  // chunks at positions below sg * w
+      for (int sg = 0; sg < nsw; ++sg) {
+        SegInfo& e = P.segs[sg];
+        e.pos0 = sg * w;
+        e.n0 = N;
+        e.n1 = 0;
+        e.active = 0;
+        int64_t in = 0;
+        for (int n = 0; n < N; ++n) {
+          const int k = nc[n] - e.pos0;
+          if (k <= 0) continue;
+          in += k < w ? k : w;
+          ++e.active;
+          e.n0 = n < e.n0 ? n : e.n0;
+          e.n1 = n + 1;
+        }
+        e.c0 = static_cast<int>(below);
+        e.c1 = static_cast<int>(below + in);
+        below += in;
+      }
+      P.segmax = P.segs[0].c1 - P.segs[0].c0;
+      P.xslots = 0;
+      P.nck = 0;
+      for (int n = 0; n < N; ++n) {
+        P.xslots += nc[n] > w;
+        P.nck += nc[n] > w ? (nc[n] + w - 1) / w - 1 : 0;
+      }
+      if (P.xslots < 1) P.xslots = 1;
+      if (P.nck < 1) P.nck = 1;
+    }
+  }
+  if (!P.win) {
+    P.seg = seg;
+    P.NS = ns_seq;
+    P.segs = std::move(sq);
+    P.segmax = seg;
+    P.xslots = 1;
+    P.nck = ns_seq;
+  }
   return P;
 }
 
 // Carve a ChunkOps (forward or backward layout) for `seg` chunks from *cur.
 ChunkOps carve_ops(const Plan& P, bool bwd, unsigned char*& cur) {
-  const size_t n = static_cast<size_t>(P.seg) * P.H;
+  const size_t n = static_cast<size_t>(P.segmax) * P.H;
   const size_t C = P.C, K = P.D, e = P.esz;
   ChunkOps o{};
   auto take = [&](size_t bytes) { void* r = cur; cur += up(bytes); return r; };
@@ -165,35 +280,76 @@ size_t ops_bytes(const Plan& P, bool bwd) {
 }
 
 size_t states_bytes(const Plan& P) {
-  const size_t n = static_cast<size_t>(P.seg) * P.H, C = P.C, K = P.D, e = P.esz;
+  const size_t n = static_cast<size_t>(P.segmax) * P.H, C = P.C, K = P.D, e = P.esz;
   return up(n * K * K * e) * 2 + up(n * C * K * e) * 2;
 }
 
 size_t state_slot(const Plan& P) { return up(static_cast<size_t>(P.H) * P.D * P.D * 4); }
 
-// The chunk table at the workspace start: chunk offsets [N+1] int32, then the
-// per-chunk locations [NC] int2.
+// The chunk table at the workspace start (TableArgs in kda_internal.h):
+// coff [N+1], cloc [NC], ckt [N]; for a plan by windows also xr [N] and
+// pst [NS][N+1].
 size_t table_bytes(const Plan& P) {
-  return up((P.N + 1) * 4) + up(static_cast<size_t>(P.NC > 0 ? P.NC : 1) * 8);
+  size_t b = up((P.N + 1) * 4) + up(static_cast<size_t>(P.NC > 0 ? P.NC : 1) * 8) +
+             up(static_cast<size_t>(P.N) * 8);
+  if (P.win) b += up(static_cast<size_t>(P.N) * 4) + up(static_cast<size_t>(P.NS) * (P.N + 1) * 4);
+  return b;
 }
 struct Table {
   int32_t* coff;
   int2* cloc;
+  int2* ckt;
+  int32_t* xr;
+  int32_t* pst;
 };
 Table carve_table(const Plan& P, unsigned char*& cur) {
-  Table t{reinterpret_cast<int32_t*>(cur), reinterpret_cast<int2*>(cur + up((P.N + 1) * 4))};
+  unsigned char* c = cur;
+  auto take = [&](size_t bytes) { unsigned char* r = c; c += up(bytes); return r; };
+  Table t{};
+  t.coff = reinterpret_cast<int32_t*>(take((P.N + 1) * 4));
+  t.cloc = reinterpret_cast<int2*>(take(static_cast<size_t>(P.NC > 0 ? P.NC : 1) * 8));
+  t.ckt = reinterpret_cast<int2*>(take(static_cast<size_t>(P.N) * 8));
+  if (P.win) {
+    t.xr = reinterpret_cast<int32_t*>(take(static_cast<size_t>(P.N) * 4));
+    t.pst = reinterpret_cast<int32_t*>(take(static_cast<size_t>(P.NS) * (P.N + 1) * 4));
+  }
   cur += table_bytes(P);
   return t;
 }
+// Chunk-table launch arguments: plan P's table, with the checkpoint layout
+// of plan CK (the backward's plan).
+TableArgs table_args(const Plan& P, const Plan& CK, const Table& t, const int32_t* cu) {
+  TableArgs a{};
+  a.cu = cu;
+  a.N = P.N;
+  a.C = P.C;
+  a.NC = P.NC;
+  a.win = P.win ? P.seg : 0;
+  a.NS = P.NS;
+  a.ck_every = CK.seg;
+  a.ck_win = CK.win ? 1 : 0;
+  a.coff = t.coff;
+  a.cloc = t.cloc;
+  a.ckt = t.ckt;
+  a.xr = t.xr;
+  a.pst = t.pst;
+  return a;
+}
+Seg seg_of(const Plan& P, const Table& t, int sg) {
+  const SegInfo& e = P.segs[sg];
+  return Seg{e.c0, e.c1, e.n0, e.n1,
+             P.win ? t.pst + static_cast<size_t>(sg) * (P.N + 1) : nullptr, e.pos0};
+}
 
 size_t fwd_bytes(const Plan& P) {
-  return table_bytes(P) + 2 * state_slot(P) + ops_bytes(P, false);
+  return table_bytes(P) + 2 * P.xslots * state_slot(P) + ops_bytes(P, false);
 }
 
 size_t bwd_bytes(const Plan& P) {
   const size_t ops = ops_bytes(P, true) > ops_bytes(P, false) ? ops_bytes(P, true) : ops_bytes(P, false);
   return table_bytes(P) + up(static_cast<size_t>(P.NC) * P.H * (P.D + 1) * 8) +
-         static_cast<size_t>(P.NS + 1) * state_slot(P) + 2 * state_slot(P) + ops + states_bytes(P);
+         static_cast<size_t>(P.nck) * state_slot(P) + 2 * P.xslots * state_slot(P) + ops +
+         states_bytes(P);
 }
 
 bool has_empty_sequence(const kda_problem* p) {
@@ -294,7 +450,7 @@ int kda_prologue(const kda_problem* p, const void* q, const void* k, const void*
   unsigned char* cur = static_cast<unsigned char*>(workspace);
   const Table tb = carve_table(P, cur);
   Inputs in{q, k, nullptr, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, tb.coff, tb.cloc};
-  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, P.NC, tb.coff, tb.cloc, s));
+  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(table_args(P, P, tb, cu_seqlens), s));
   if (P.NC > 0)
     KDA_TRY(KDA_KERNEL_PROLOGUE, static_cast<int64_t>(P.NC) * P.H, launch_prologue(P.dtype, P.D, P.C, make_dims(p), in, P.NC, qh, kh, beta, gcum, s));
   return KDA_OK;
@@ -308,7 +464,7 @@ int32_t kda_bwd_segment_chunks(const kda_problem* p) {
 size_t kda_checkpoint_bytes(const kda_problem* p) {
   if (check_problem(p) != KDA_OK) return 0;
   const Plan P = make_plan(p, true);
-  return static_cast<size_t>(P.NS) * state_slot(P);
+  return static_cast<size_t>(P.nck) * state_slot(P);
 }
 
 }  // extern "C"
@@ -330,33 +486,34 @@ int fwd_common(bool g2, const kda_problem* p, const void* q, const void* k, cons
   if (workspace_bytes < fwd_bytes(P)) return KDA_ERR_WORKSPACE;
   const kda_state_io none{};
   if (!io) io = &none;
-  int ck_every = 0;
-  if (io->ckpt) {
-    if (io->ckpt_bytes < kda_checkpoint_bytes(p)) return KDA_ERR_WORKSPACE;
-    const Plan PB = make_plan(p, true);
-    if (PB.NS > 1) ck_every = PB.seg;  // a single segment needs no checkpoint
-  }
-  const ScanStates ss{io->h0, io->ht, ck_every ? io->ckpt : nullptr, ck_every};
+  const Plan PB = make_plan(p, true);  // the backward's segments (checkpoints)
+  if (io->ckpt && io->ckpt_bytes < kda_checkpoint_bytes(p)) return KDA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   unsigned char* cur = static_cast<unsigned char*>(workspace);
   const Table tb = carve_table(P, cur);
+  // a single backward segment needs no checkpoint
+  const ScanStates ss{io->h0, io->ht, PB.NS > 1 ? io->ckpt : nullptr,
+                      CarryMap{tb.ckt, PB.seg, nullptr, PB.nck}};
   float* carry[2];
   carry[0] = reinterpret_cast<float*>(cur);
-  cur += state_slot(P);
+  cur += P.xslots * state_slot(P);
   carry[1] = reinterpret_cast<float*>(cur);
-  cur += state_slot(P);
+  cur += P.xslots * state_slot(P);
+  const CarryMap cm{nullptr, 0, tb.xr, P.xslots};
   const ChunkOps ops = carve_ops(P, false, cur);
   Dims d = make_dims(p);
   d.gdn2 = g2 ? 1 : 0;
   Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, tb.coff, tb.cloc};
   in.bk = raw_b;
   in.wv = raw_w;
-  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, P.NC, tb.coff, tb.cloc, s));
+  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(table_args(P, PB, tb, cu_seqlens), s));
   for (int sg = 0; sg < P.NS; ++sg) {
-    const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
-    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, KL_FWD, d, in, c0, c1 - c0, ops, s));
-    KDA_TRY(KDA_KERNEL_SCAN_FWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops, o, nullptr, carry[sg & 1],
-                            carry[(sg + 1) & 1], ss, s));
+    const Seg sd = seg_of(P, tb, sg);
+    const int64_t units = static_cast<int64_t>(sd.c1 - sd.c0) * P.H;
+    const int act = P.segs[sg].active;
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL, units, launch_chunk_local(P.dtype, P.D, P.C, KL_FWD, d, in, sd.c0, sd.c1 - sd.c0, ops, s));
+    KDA_TRY(KDA_KERNEL_SCAN_FWD, units, launch_scan_fwd(P.dtype, P.D, P.C, d, in, sd, act, ops, o, nullptr, carry[sg & 1],
+                            carry[(sg + 1) & 1], cm, ss, s));
   }
   if (io->ht && has_empty_sequence(p))
     KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_state_passthrough(cu_seqlens, P.N, P.H, P.D * P.D, io->h0, io->ht, s));
@@ -415,22 +572,24 @@ int bwd_common(bool g2, const kda_problem* p, const void* q, const void* k, cons
   const kda_state_io none{};
   if (!io) io = &none;
   if (io->ckpt && io->ckpt_bytes < kda_checkpoint_bytes(p)) return KDA_ERR_WORKSPACE;
-  const ScanStates fwd_ss{io->h0, nullptr, nullptr, 0};
-  const ScanStates bwd_ss{io->dht, io->dh0, nullptr, 0};
+  const ScanStates fwd_ss{io->h0, nullptr, nullptr, CarryMap{}};
+  const ScanStates bwd_ss{io->dht, io->dh0, nullptr, CarryMap{}};
   hipStream_t s = static_cast<hipStream_t>(stream);
   unsigned char* cur = static_cast<unsigned char*>(workspace);
   const Table tb = carve_table(P, cur);
   double* partials = reinterpret_cast<double*>(cur);
   cur += up(static_cast<size_t>(P.NC) * P.H * (P.D + 1) * 8);
-  // state entering each segment (slot sg); the forward's checkpoints when given
+  // states entering the segments (checkpoint layout of ckt); the forward's
+  // checkpoints when given
   float* ckpt = io->ckpt ? io->ckpt : reinterpret_cast<float*>(cur);
-  const size_t slot = state_slot(P) / 4;
-  cur += static_cast<size_t>(P.NS + 1) * state_slot(P);
+  cur += static_cast<size_t>(P.nck) * state_slot(P);
+  const CarryMap ck_map{tb.ckt, P.seg, nullptr, P.nck};
   float* dcarry[2];
   dcarry[0] = reinterpret_cast<float*>(cur);
-  cur += state_slot(P);
+  cur += P.xslots * state_slot(P);
   dcarry[1] = reinterpret_cast<float*>(cur);
-  cur += state_slot(P);
+  cur += P.xslots * state_slot(P);
+  const CarryMap cm{nullptr, 0, tb.xr, P.xslots};
   unsigned char* ops_base = cur;
   unsigned char* c2 = ops_base;
   const ChunkOps ops_b = carve_ops(P, true, c2);
@@ -439,7 +598,7 @@ int bwd_common(bool g2, const kda_problem* p, const void* q, const void* k, cons
   cur = ops_base + (ops_bytes(P, true) > ops_bytes(P, false) ? ops_bytes(P, true) : ops_bytes(P, false));
   SegStates sts{};
   {
-    const size_t n = static_cast<size_t>(P.seg) * P.H, C = P.C, K = P.D, e = P.esz;
+    const size_t n = static_cast<size_t>(P.segmax) * P.H, C = P.C, K = P.D, e = P.esz;
     sts.h = cur;
     cur += up(n * K * K * e);
     sts.dh = cur;
@@ -454,24 +613,27 @@ int bwd_common(bool g2, const kda_problem* p, const void* q, const void* k, cons
   Inputs in{q, k, v, raw_g, raw_beta, A_log, dt_bias, cu_seqlens, tb.coff, tb.cloc};
   in.bk = raw_b;
   in.wv = raw_w;
-  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(cu_seqlens, P.N, P.C, P.NC, tb.coff, tb.cloc, s));
+  KDA_TRY(KDA_KERNEL_CHUNK_TABLE, 0, launch_chunk_table(table_args(P, P, tb, cu_seqlens), s));
   // checkpoint pass: the state entering each segment (skipped when the
   // forward saved them)
   for (int sg = 0; !io->ckpt && sg + 1 < P.NS; ++sg) {
-    const int c0 = sg * P.seg, c1 = c0 + P.seg;
-    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL_STATE, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, KL_STATE, d, in, c0, c1 - c0, ops_f, s));
-    KDA_TRY(KDA_KERNEL_SCAN_STATE, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_f, nullptr, nullptr,
-                            ckpt + sg * slot, ckpt + (sg + 1) * slot, fwd_ss, s));
+    const Seg sd = seg_of(P, tb, sg);
+    const int64_t units = static_cast<int64_t>(sd.c1 - sd.c0) * P.H;
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL_STATE, units, launch_chunk_local(P.dtype, P.D, P.C, KL_STATE, d, in, sd.c0, sd.c1 - sd.c0, ops_f, s));
+    KDA_TRY(KDA_KERNEL_SCAN_STATE, units, launch_scan_fwd(P.dtype, P.D, P.C, d, in, sd, P.segs[sg].active, ops_f, nullptr, nullptr,
+                            ckpt, ckpt, ck_map, fwd_ss, s));
   }
   for (int sg = P.NS - 1; sg >= 0; --sg) {
-    const int c0 = sg * P.seg, c1 = c0 + P.seg < P.NC ? c0 + P.seg : P.NC;
-    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL_BWD, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_local(P.dtype, P.D, P.C, KL_BWD, d, in, c0, c1 - c0, ops_b, s));
+    const Seg sd = seg_of(P, tb, sg);
+    const int64_t units = static_cast<int64_t>(sd.c1 - sd.c0) * P.H;
+    const int act = P.segs[sg].active;
+    KDA_TRY(KDA_KERNEL_CHUNK_LOCAL_BWD, units, launch_chunk_local(P.dtype, P.D, P.C, KL_BWD, d, in, sd.c0, sd.c1 - sd.c0, ops_b, s));
     // the recording scan writes no carry: the next segment's entering state is known
-    KDA_TRY(KDA_KERNEL_SCAN_REC, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_fwd(P.dtype, P.D, P.C, d, in, c0, c1, ops_b, nullptr, &sts,
-                            ckpt + sg * slot, nullptr, fwd_ss, s));
-    KDA_TRY(KDA_KERNEL_SCAN_BWD, static_cast<int64_t>(c1 - c0) * P.H, launch_scan_bwd(P.dtype, P.D, P.C, d, in, dO, c0, c1, ops_b, sts,
-                            dcarry[(sg + 1) & 1], dcarry[sg & 1], bwd_ss, s));
-    KDA_TRY(KDA_KERNEL_CHUNK_GRAD, static_cast<int64_t>(c1 - c0) * P.H, launch_chunk_grad(P.dtype, P.D, P.C, d, in, dO, c0, c1 - c0, ops_b, sts, dq, dk, dv,
+    KDA_TRY(KDA_KERNEL_SCAN_REC, units, launch_scan_fwd(P.dtype, P.D, P.C, d, in, sd, act, ops_b, nullptr, &sts,
+                            ckpt, nullptr, ck_map, fwd_ss, s));
+    KDA_TRY(KDA_KERNEL_SCAN_BWD, units, launch_scan_bwd(P.dtype, P.D, P.C, d, in, dO, sd, act, ops_b, sts,
+                            dcarry[(sg + 1) & 1], dcarry[sg & 1], cm, bwd_ss, s));
+    KDA_TRY(KDA_KERNEL_CHUNK_GRAD, units, launch_chunk_grad(P.dtype, P.D, P.C, d, in, dO, sd.c0, sd.c1 - sd.c0, ops_b, sts, dq, dk, dv,
                               draw_g, draw_beta, draw_w, partials, s));
   }
   KDA_TRY(KDA_KERNEL_GATE_REDUCE, 0, launch_gate_reduce(P.D, P.H, P.NC, d.gate_head, partials, dA_log, ddt_bias, s));

@@ -25,9 +25,39 @@ struct Inputs {
   const void *q, *k, *v, *g, *beta;
   const float *A_log, *dt_bias;
   const int32_t *cu;    // cu_seqlens [N+1]
-  const int32_t *coff;  // chunk offsets [N+1]
-  const int2 *cloc;     // per chunk: {first token, valid rows} [NC]
+  const int32_t *coff;  // chunk offsets [N+1]: sequence n has coff[n+1] - coff[n] chunks
+  const int2 *cloc;     // per chunk in the plan's chunk order: {first token, valid rows} [NC]
   const void *bk = nullptr, *wv = nullptr;  // GDN-2: raw_b [T][H][K], raw_w [T][H][V]
+};
+
+// One segment of a plan: the chunks at indices [c0, c1) of the plan's chunk
+// order (the order of cloc, of the chunk operands and of the gate-parameter
+// partials). A sequence's chunks in a segment are consecutive chunks of the
+// sequence and contiguous in that order; sequences [n0, n1) may have some.
+//   pst == nullptr (plan in sequence order: the chunk order lists the
+//     sequences one after another): sequence n has chunks
+//     [max(coff[n], c0), min(coff[n+1], c1)).
+//   pst != nullptr (plan by windows: the segment holds chunks pos0 ..
+//     pos0 + window - 1 of every sequence): sequence n has chunks
+//     [pst[n], pst[n+1]), its first at position pos0 of the sequence.
+struct Seg {
+  int c0, c1, n0, n1;
+  const int32_t* pst;
+  int pos0;
+};
+
+// Slots of the states that cross segment boundaries, each [H][K][V] fp32:
+//   ckt != nullptr (checkpoint layout): the state entering chunk p of
+//     sequence n (p counted from the sequence start) is slot
+//     ckt[n].y + (ckt[n].x + p) / every;
+//   otherwise sequence n uses slot xr[n] of each carry buffer (slot 0 when
+//     xr is null).
+// Slots are clamped to [0, nslots), the slots the buffers hold.
+struct CarryMap {
+  const int2* ckt;
+  int every;
+  const int32_t* xr;
+  int nslots;
 };
 
 // Per-(chunk, head) operands produced by the chunk-local kernel for one
@@ -67,24 +97,37 @@ struct SegStates {
 // Per-sequence state ends of a scan, all fp32 [N][H][K][V] (sequence n's
 // slice at n * H * K * V) or null:
 //   forward scan: init = initial states (null: zero), fin = final states
-//     out (null: not written), ck = states entering every chunk that is a
-//     multiple of ck_every and lies inside its sequence, slot c / ck_every of
-//     [slots][H][K][V] (null: none);
+//     out (null: not written), ck = states entering the chunks ck_map puts
+//     in a checkpoint slot (position p > 0 of sequence n with
+//     (ckt[n].x + p) % every == 0), each into its slot (null: none);
 //   reverse scan: init = final-state gradients (null: zero), fin = initial-
 //     state gradients out (null: not written); ck unused.
 struct ScanStates {
   const float* init;
   float* fin;
   float* ck;
-  int ck_every;
+  CarryMap ck_map;
 };
 
 // Launchers (defined next to their kernels). Each returns hipSuccess or the
 // launch error. `dtype` is 0 (fp32) or 1 (bf16); D = K = V; C = chunk.
-// coff[n] = first chunk of sequence n (coff[N] = NC); cloc[c] = {first token,
-// valid rows} of chunk c, for the NC chunks.
-hipError_t launch_chunk_table(const int32_t* cu, int N, int C, int NC, int32_t* coff, int2* cloc,
-                              hipStream_t s);
+// The chunk table: coff, cloc in the plan's chunk order, and per sequence
+// ckt (checkpoint layout of the plan `ck_every`, `ck_win`: by windows when
+// nonzero, else in sequence order) and, for a plan by windows of `win`
+// chunks over NS segments, xr (carry slot: rank among the sequences longer
+// than one window) and pst (segment sg's sequence starts, [NS][N+1]).
+struct TableArgs {
+  const int32_t* cu;
+  int N, C, NC;
+  int win, NS;
+  int ck_every, ck_win;
+  int32_t* coff;
+  int2* cloc;
+  int2* ckt;
+  int32_t* xr;
+  int32_t* pst;
+};
+hipError_t launch_chunk_table(const TableArgs& a, hipStream_t s);
 hipError_t launch_prologue(int dtype, int D, int C, const Dims& d, const Inputs& in,
                            int64_t n_chunks, float* qh, float* kh, float* beta, float* gcum,
                            hipStream_t s);
@@ -94,18 +137,21 @@ enum { KL_FWD = 0, KL_BWD = 1, KL_STATE = 2 };
 hipError_t launch_chunk_local(int dtype, int D, int C, int mode, const Dims& d,
                               const Inputs& in, int seg_begin, int seg_chunks,
                               const ChunkOps& ops, hipStream_t s);
-// Forward-direction scan over one segment. out_o != nullptr writes O;
-// st != nullptr records h and Vn for the backward. carry_in/out: fp32
-// [H][K][V] state of the sequence crossing the segment boundaries.
+// Forward-direction scan over one segment (`active` of its sequences have
+// chunks in it). out_o != nullptr writes O; st != nullptr records h and Vn
+// for the backward. carry_in/out: the states of the sequences that cross
+// the segment's first / last boundary, in slots per `cm`.
 hipError_t launch_scan_fwd(int dtype, int D, int C, const Dims& d, const Inputs& in,
-                           int seg_begin, int seg_end, const ChunkOps& ops, void* out_o,
+                           const Seg& sg, int active, const ChunkOps& ops, void* out_o,
                            const SegStates* st, const float* carry_in, float* carry_out,
-                           const ScanStates& ss, hipStream_t s);
+                           const CarryMap& cm, const ScanStates& ss, hipStream_t s);
 // Reverse (state-gradient) scan over one segment; records dh' and dVn^T.
+// carry_in: gradients entering from the following segment; carry_out:
+// those leaving to the preceding one.
 hipError_t launch_scan_bwd(int dtype, int D, int C, const Dims& d, const Inputs& in,
-                           const void* dO, int seg_begin, int seg_end, const ChunkOps& ops,
+                           const void* dO, const Seg& sg, int active, const ChunkOps& ops,
                            const SegStates& st, const float* carry_in, float* carry_out,
-                           const ScanStates& ss, hipStream_t s);
+                           const CarryMap& cm, const ScanStates& ss, hipStream_t s);
 // dst[n] = src[n] (or zero when src is null) for every empty sequence n;
 // KV = K * V floats per (sequence, head).
 hipError_t launch_state_passthrough(const int32_t* cu, int N, int H, int KV, const float* src,

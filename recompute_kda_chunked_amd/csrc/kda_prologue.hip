@@ -3,18 +3,18 @@
 
 namespace kda {
 
-// coff[n] = number of chunks (of length C) in sequences 0..n-1; coff[N] is the
-// total. One block; each thread owns a contiguous run of sequences. The
-// threads' chunk counts are prefix-summed by a shuffle scan in each wave,
-// then the four wave totals are added in wave order.
-__global__ void __launch_bounds__(256) k_chunk_table(const int32_t* cu, int N, int C, int NC,
-                                                     int32_t* coff, int2* cloc) {
-  __shared__ int32_t wsum[4];
+// Exclusive prefix sum over n in [0, N) of f(n), by one block of 256
+// threads: out(n, sum of f over [0, n)) for every n; returns the total. Each
+// thread owns a contiguous run of n; the runs' sums are prefix-summed by a
+// shuffle scan in each wave, then the four wave totals are added in wave
+// order. Every thread of the block must call it.
+template <typename F, typename O>
+__device__ int32_t block_scan(int N, F f, O out, int32_t* wsum) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int per = (N + 255) / 256;
   const int b = min(N, t * per), e = min(N, b + per);
   int32_t local = 0;
-  for (int n = b; n < e; ++n) local += (cu[n + 1] - cu[n] + C - 1) / C;
+  for (int n = b; n < e; ++n) local += f(n);
   int32_t incl = local;  // inclusive scan within the wave
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -25,24 +25,73 @@ __global__ void __launch_bounds__(256) k_chunk_table(const int32_t* cu, int N, i
   __syncthreads();
   int32_t woff = 0;
   for (int i = 0; i < w; ++i) woff += wsum[i];
-  if (t == 255) coff[N] = woff + incl;
+  const int32_t total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
   int32_t run = woff + incl - local;
   for (int n = b; n < e; ++n) {
-    coff[n] = run;
-    run += (cu[n + 1] - cu[n] + C - 1) / C;
+    const int32_t x = f(n);
+    out(n, run);
+    run += x;
   }
-  // the block's coff stores are complete and visible after the barrier
+  // wsum is free again, and this block's stores are visible to it
   __syncthreads();
-  for (int c = t; c < NC; c += 256) {
-    const int n = find_seq(coff, N, c);
-    const int t0 = cu[n] + (c - coff[n]) * C, rem = cu[n + 1] - t0;
-    cloc[c] = int2{t0, rem < C ? rem : C};
+  return total;
+}
+
+// The chunk table (TableArgs in kda_internal.h). The last block handles the
+// per-sequence tables (and, for a plan in sequence order, cloc); for a plan
+// by windows, block sg < NS lays out segment sg: sequence n's chunks at
+// positions [sg * win, (sg + 1) * win) follow those of sequences 0..n-1, and
+// the segment follows every chunk at a position below sg * win.
+__global__ void __launch_bounds__(256) k_chunk_table(TableArgs a) {
+  __shared__ int32_t wsum[4];
+  const int32_t* cu = a.cu;
+  const int N = a.N, C = a.C;
+  auto nchunks = [&](int n) { return (cu[n + 1] - cu[n] + C - 1) / C; };
+  auto put_loc = [&](int P, int n, int pos) {
+    const int t0 = cu[n] + pos * C, rem = cu[n + 1] - t0;
+    a.cloc[P] = int2{t0, rem < C ? rem : C};
+  };
+  if (static_cast<int>(blockIdx.x) == static_cast<int>(gridDim.x) - 1) {
+    const int32_t nc = block_scan(N, nchunks, [&](int n, int32_t pre) {
+      a.coff[n] = pre;
+      if (!a.ck_win) a.ckt[n] = int2{pre, 0};
+    }, wsum);
+    if (threadIdx.x == 0) a.coff[N] = nc;
+    if (a.ck_win) {
+      // checkpoint slots sequence by sequence: one per window start after
+      // the first
+      const int E = a.ck_every;
+      block_scan(N, [&](int n) { return max(0, (nchunks(n) + E - 1) / E - 1); },
+                 [&](int n, int32_t pre) { a.ckt[n] = int2{0, pre - 1}; }, wsum);
+    }
+    if (a.win) {
+      block_scan(N, [&](int n) { return nchunks(n) > a.win ? 1 : 0; },
+                 [&](int n, int32_t pre) { a.xr[n] = pre; }, wsum);
+    } else {
+      // coff is complete and visible after block_scan's closing barrier
+      for (int c = threadIdx.x; c < a.NC; c += 256) {
+        const int n = find_seq(a.coff, N, c);
+        put_loc(c, n, c - a.coff[n]);
+      }
+    }
+    return;
+  }
+  const int sg = blockIdx.x, W = a.win, p0 = sg * W;
+  const int32_t base = block_scan(N, [&](int n) { return min(nchunks(n), p0); },
+                                  [](int, int32_t) {}, wsum);
+  int32_t* row = a.pst + static_cast<size_t>(sg) * (N + 1);
+  const int32_t cnt = block_scan(N, [&](int n) { return min(max(nchunks(n) - p0, 0), W); },
+                                 [&](int n, int32_t pre) { row[n] = base + pre; }, wsum);
+  if (threadIdx.x == 0) row[N] = base + cnt;
+  __syncthreads();
+  for (int j = threadIdx.x; j < cnt && base + j < a.NC; j += 256) {
+    const int n = find_seq(row, N, base + j);
+    put_loc(base + j, n, p0 + (base + j - row[n]));
   }
 }
 
-hipError_t launch_chunk_table(const int32_t* cu, int N, int C, int NC, int32_t* coff, int2* cloc,
-                              hipStream_t s) {
-  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, cu, N, C, NC, coff, cloc);
+hipError_t launch_chunk_table(const TableArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_chunk_table, dim3(a.win ? a.NS + 1 : 1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

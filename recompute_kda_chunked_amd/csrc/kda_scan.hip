@@ -35,15 +35,52 @@
 
 namespace kda {
 
+// Block -> (sequence n of the segment's range [n0, n1), head h, value tile vt).
 template <int NVT>
-__device__ __forceinline__ bool scan_program(const Dims& d, int& n, int& h, int& vt) {
+__device__ __forceinline__ bool scan_program(const Seg& sg, int H, int& n, int& h, int& vt) {
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
   vt = slot % NVT;
   const int nh = (slot / NVT) * 8 + xcd;
-  if (nh >= d.N * d.H) return false;
-  n = nh / d.H;
-  h = nh % d.H;
+  if (nh >= (sg.n1 - sg.n0) * H) return false;
+  n = sg.n0 + nh / H;
+  h = nh % H;
   return true;
+}
+
+// Sequence n's chunks in a segment: chunk-order indices [cb, ce), chunk cb
+// at position pos of the sequence; first / last: the segment holds the
+// sequence's first / last chunk.
+struct SeqRange {
+  int cb, ce, pos;
+  bool first, last;
+};
+__device__ __forceinline__ SeqRange seq_range(const Seg& sg, int coff0, int coff1, int n) {
+  SeqRange r;
+  if (sg.pst) {
+    // inside the segment's range whatever the table holds
+    r.cb = min(max(sg.pst[n], sg.c0), sg.c1);
+    r.ce = min(max(sg.pst[n + 1], r.cb), sg.c1);
+    r.pos = sg.pos0;
+  } else {
+    r.cb = max(coff0, sg.c0);
+    r.ce = min(coff1, sg.c1);
+    r.pos = r.cb - coff0;
+  }
+  r.first = r.pos == 0;
+  r.last = r.pos + (r.ce - r.cb) == coff1 - coff0;
+  return r;
+}
+
+// Slot of sequence n's state at the boundary before its chunk `pos`.
+__device__ __forceinline__ size_t carry_slot(const CarryMap& m, int n, int pos) {
+  int k = 0;
+  if (m.ckt) {
+    const int2 e = m.ckt[n];
+    k = e.y + (e.x + pos) / m.every;
+  } else if (m.xr) {
+    k = m.xr[n];
+  }
+  return static_cast<size_t>(min(max(k, 0), m.nslots - 1));
 }
 
 // Tile geometry shared by both scans.
@@ -135,10 +172,10 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
 }
 
 template <typename TI, typename OpT, int D, int C, int BV, bool OUT_O, bool REC>
-__global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_begin,
-                                                  int seg_end, ChunkOps ops, TI* o,
-                                                  SegStates st, const float* carry_in,
-                                                  float* carry_out, ScanStates ss) {
+__global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, Seg sgm, ChunkOps ops,
+                                                  TI* o, SegStates st, const float* carry_in,
+                                                  float* carry_out, CarryMap cm,
+                                                  ScanStates ss) {
   using G = ScanGeo<OpT, D, C, BV>;
   using M = typename G::M;
   constexpr int K = G::K, V = G::V, NB = G::NB, NVT = G::NVT, BVT = G::BVT;
@@ -153,16 +190,17 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
   __shared__ __attribute__((aligned(16))) OpT VnTlo_s[HL ? BV * LDC : 1];
 
   int n, h, vt;
-  if (!scan_program<NVT>(d, n, h, vt)) return;
+  if (!scan_program<NVT>(sgm, d.H, n, h, vt)) return;
   // sequence bounds read once: the loop's stores could alias them as far as
   // the compiler knows, and a reload would wait for every prefetch in flight
-  const int coff0 = in.coff[n], coff1 = in.coff[n + 1];
+  const SeqRange R = seq_range(sgm, in.coff[n], in.coff[n + 1], n);
   const int64_t tok0 = in.cu[n], tok1 = in.cu[n + 1];
-  const int cb = max(coff0, seg_begin), ce = min(coff1, seg_end);
+  const int cb = R.cb, ce = R.ce, pofs = R.pos - R.cb;  // chunk c is at position c + pofs
   if (cb >= ce) return;
+  const int seg_begin = sgm.c0;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
   const int v0 = vt * BV;
-  const size_t ts = static_cast<size_t>(d.H) * V;
+  const size_t ts = static_cast<size_t>(d.H) * V, hkv = static_cast<size_t>(d.H) * K * V;
   // U: fp32 in the forward layout, the operand type in the backward one (REC)
   using UT = std::conditional_t<REC, OpT, float>;
 
@@ -171,9 +209,8 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
   // At the sequence's first chunk the state is its initial state (or zero),
   // otherwise the carry of the previous segment.
   f32x4 hs[HPW];
-  const bool fresh = (cb == coff0);
-  const float* hin = !fresh ? carry_in
-                     : (ss.init ? ss.init + static_cast<size_t>(n) * d.H * K * V : nullptr);
+  const float* hin = !R.first ? carry_in + carry_slot(cm, n, R.pos) * hkv
+                     : (ss.init ? ss.init + static_cast<size_t>(n) * hkv : nullptr);
   const bool zero_in = hin == nullptr;
   // offset of the lane's four state values in a [H][K][V] array
   auto hoff = [&](int j) {
@@ -183,8 +220,12 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
 #pragma unroll
   for (int j = 0; j < HPW; ++j)
     hs[j] = zero_in ? zero4() : *reinterpret_cast<const f32x4*>(hin + hoff(j));
-  // states at multiples of ss.ck_every chunks (the backward's segment starts)
-  int next_ck = ss.ck ? (cb + ss.ck_every - 1) / ss.ck_every * ss.ck_every : 0x7fffffff;
+  // states entering the backward's segments: chunk c has checkpoint key
+  // kofs + c, a checkpoint where the key is a multiple of ck_map.every
+  const int ck_every = ss.ck_map.every;
+  const int2 ckn = ss.ck ? ss.ck_map.ckt[n] : int2{0, 0};
+  const int kofs = ckn.x + pofs;
+  int next_ck = ss.ck ? (kofs + cb + ck_every - 1) / ck_every * ck_every - kofs : 0x7fffffff;
   auto put_state = [&]() {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
@@ -215,12 +256,13 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
     load_fwd_ops<OpT, D, C, BV, OUT_O, REC, 0>(fill, ops, idx2, v0, w, i, g);
     if (c == next_ck) {
       // the state entering chunk c, needed only where c is inside the sequence
-      if (c > coff0) {
-        float* dst = ss.ck + static_cast<size_t>(c / ss.ck_every) * d.H * K * V;
+      if (c + pofs > 0) {
+        const int k = min(max(ckn.y + (kofs + c) / ck_every, 0), ss.ck_map.nslots - 1);
+        float* dst = ss.ck + static_cast<size_t>(k) * hkv;
 #pragma unroll
         for (int j = 0; j < HPW; ++j) *reinterpret_cast<f32x4*>(dst + hoff(j)) = hs[j];
       }
-      next_ck += ss.ck_every;
+      next_ck += ck_every;
     }
     if (REC) {
       // entering state h_n, fragment-major [K][V]
@@ -260,7 +302,7 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
     __syncthreads();
     if (OUT_O && w < NB) {
       const int m = w;
-      const int64_t t0 = tok0 + static_cast<int64_t>(c - coff0) * C;
+      const int64_t t0 = tok0 + static_cast<int64_t>(c + pofs) * C;
       const int len = static_cast<int>(min(static_cast<int64_t>(C), tok1 - t0));
       const int nf = (16 * (m + 1) + KS - 1) / KS;  // Aqk[r][s] = 0 for s > r
       const int r = 16 * m + i;
@@ -312,8 +354,8 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, int seg_beg
   if (c < ce) step(c, s0, s2);
   if (c + 1 < ce) step(c + 1, s1, s0);
   // the state leaves as the next segment's carry, or as the sequence's final state
-  float* hout = ce < coff1 ? carry_out
-                           : (ss.fin ? ss.fin + static_cast<size_t>(n) * d.H * K * V : nullptr);
+  float* hout = !R.last ? (carry_out ? carry_out + carry_slot(cm, n, ce + pofs) * hkv : nullptr)
+                        : (ss.fin ? ss.fin + static_cast<size_t>(n) * hkv : nullptr);
   if (hout) {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) *reinterpret_cast<f32x4*>(hout + hoff(j)) = hs[j];
@@ -388,10 +430,10 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
 }
 
 template <typename TI, typename OpT, int D, int C, int BV>
-__global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* dO,
-                                                  int seg_begin, int seg_end, ChunkOps ops,
-                                                  SegStates st, const float* carry_in,
-                                                  float* carry_out, ScanStates ss) {
+__global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* dO, Seg sgm,
+                                                  ChunkOps ops, SegStates st,
+                                                  const float* carry_in, float* carry_out,
+                                                  CarryMap cm, ScanStates ss) {
   using G = ScanGeo<OpT, D, C, BV>;
   using M = typename G::M;
   using Ops = BwdOps<TI, OpT, D, C, BV>;
@@ -403,18 +445,19 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
   __shared__ __attribute__((aligned(16))) OpT dOT_s[BV * LDC];
 
   int n, h, vt;
-  if (!scan_program<NVT>(d, n, h, vt)) return;
+  if (!scan_program<NVT>(sgm, d.H, n, h, vt)) return;
   // sequence bounds read once: the loop's stores could alias them as far as
   // the compiler knows, and a reload would wait for every prefetch in flight
-  const int coff0 = in.coff[n], coff1 = in.coff[n + 1];
+  const SeqRange R = seq_range(sgm, in.coff[n], in.coff[n + 1], n);
   const int64_t tok0 = in.cu[n], tok1 = in.cu[n + 1];
-  const int cb = max(coff0, seg_begin), ce = min(coff1, seg_end);
+  const int cb = R.cb, ce = R.ce, pofs = R.pos - R.cb;  // chunk c is at position c + pofs
   if (cb >= ce) return;
+  const int seg_begin = sgm.c0;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
   const int v0 = vt * BV;
-  const size_t ts = static_cast<size_t>(d.H) * V;
+  const size_t ts = static_cast<size_t>(d.H) * V, hkv = static_cast<size_t>(d.H) * K * V;
   auto chunk_t0 = [&](int c) {
-    return tok0 + static_cast<int64_t>(c - coff0) * C;
+    return tok0 + static_cast<int64_t>(c + pofs) * C;
   };
   auto chunk_len = [&](int64_t t0) {
     return static_cast<int>(min(static_cast<int64_t>(C), tok1 - t0));
@@ -425,9 +468,8 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
   // After the sequence's last chunk it is the final state's gradient (or
   // zero), otherwise the carry of the following segment.
   f32x4 hs[HPW];
-  const bool fresh = (ce == coff1);
-  const float* hin = !fresh ? carry_in
-                     : (ss.init ? ss.init + static_cast<size_t>(n) * d.H * K * V : nullptr);
+  const float* hin = !R.last ? carry_in + carry_slot(cm, n, ce + pofs) * hkv
+                     : (ss.init ? ss.init + static_cast<size_t>(n) * hkv : nullptr);
   const bool zero_in = hin == nullptr;
   auto hoff = [&](int j) {
     const int mk = w * MKW + j / BVT, nv = j % BVT;
@@ -534,8 +576,8 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
   if (c - 1 >= cb) step(c - 1, s1, s0);
   // the gradient leaves as the previous segment's carry, or, past the
   // sequence's first chunk, as the initial state's gradient
-  float* hout = cb > coff0 ? carry_out
-                           : (ss.fin ? ss.fin + static_cast<size_t>(n) * d.H * K * V : nullptr);
+  float* hout = !R.first ? carry_out + carry_slot(cm, n, R.pos) * hkv
+                         : (ss.fin ? ss.fin + static_cast<size_t>(n) * hkv : nullptr);
   if (hout) {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) *reinterpret_cast<f32x4*>(hout + hoff(j)) = hs[j];
@@ -553,68 +595,72 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
 // reverse 0.181 -> 0.144 ms per launch; at 8 sequences x H16 (512 blocks, two
 // per CU) 32 columns take them 0.225 -> 0.154 and 0.331 -> 0.218 ms; at H64
 // (256 blocks) 64 columns are 1.4x slower than 32.
-static bool wide_tiles(const Dims& d, int D) {
+static bool wide_tiles(int pairs, int D) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  const long groups = (static_cast<long>(d.N) * d.H + 7) / 8;
+  const long groups = (static_cast<long>(pairs) + 7) / 8;
   const long narrow = groups * 8 * (D / 32);
   return narrow > cus && narrow % cus != 0;
 }
 
+// Blocks of a scan over segment sg: every (sequence, head) pair of its
+// sequence range, in groups of 8 (one per XCD), times the value tiles.
+static dim3 scan_grid(const Seg& sg, int H, int NVT) {
+  const int groups = ((sg.n1 - sg.n0) * H + 7) / 8;
+  return dim3(groups * 8 * NVT);
+}
+
 template <typename TI, int D, int C, int BV>
-static hipError_t launch_sf_bv(const Dims& d, const Inputs& in, int seg_begin, int seg_end,
+static hipError_t launch_sf_bv(const Dims& d, const Inputs& in, const Seg& sg,
                                const ChunkOps& ops, void* o, const SegStates* st,
-                               const float* carry_in, float* carry_out, const ScanStates& ss,
-                               hipStream_t s) {
-  constexpr int NVT = D / BV;
-  const int groups = (d.N * d.H + 7) / 8;
-  const dim3 grid(groups * 8 * NVT), block(256);
+                               const float* carry_in, float* carry_out, const CarryMap& cm,
+                               const ScanStates& ss, hipStream_t s) {
+  const dim3 grid = scan_grid(sg, d.H, D / BV), block(256);
   SegStates z{};
   if (o)
-    hipLaunchKernelGGL((k_scan_fwd<TI, TI, D, C, BV, true, false>), grid, block, 0, s, d, in,
-                       seg_begin, seg_end, ops, static_cast<TI*>(o), z, carry_in, carry_out, ss);
+    hipLaunchKernelGGL((k_scan_fwd<TI, TI, D, C, BV, true, false>), grid, block, 0, s, d, in, sg,
+                       ops, static_cast<TI*>(o), z, carry_in, carry_out, cm, ss);
   else if (st)
-    hipLaunchKernelGGL((k_scan_fwd<TI, TI, D, C, BV, false, true>), grid, block, 0, s, d, in,
-                       seg_begin, seg_end, ops, nullptr, *st, carry_in, carry_out, ss);
+    hipLaunchKernelGGL((k_scan_fwd<TI, TI, D, C, BV, false, true>), grid, block, 0, s, d, in, sg,
+                       ops, nullptr, *st, carry_in, carry_out, cm, ss);
   else
-    hipLaunchKernelGGL((k_scan_fwd<TI, TI, D, C, BV, false, false>), grid, block, 0, s, d, in,
-                       seg_begin, seg_end, ops, nullptr, z, carry_in, carry_out, ss);
+    hipLaunchKernelGGL((k_scan_fwd<TI, TI, D, C, BV, false, false>), grid, block, 0, s, d, in, sg,
+                       ops, nullptr, z, carry_in, carry_out, cm, ss);
   return hipGetLastError();
 }
 
 template <typename TI, int D, int C>
-static hipError_t launch_sf(const Dims& d, const Inputs& in, int seg_begin, int seg_end,
+static hipError_t launch_sf(const Dims& d, const Inputs& in, const Seg& sg, int active,
                             const ChunkOps& ops, void* o, const SegStates* st,
-                            const float* carry_in, float* carry_out, const ScanStates& ss,
-                            hipStream_t s) {
-  if (D >= 64 && wide_tiles(d, D))
-    return launch_sf_bv<TI, D, C, 64>(d, in, seg_begin, seg_end, ops, o, st, carry_in, carry_out, ss, s);
-  return launch_sf_bv<TI, D, C, 32>(d, in, seg_begin, seg_end, ops, o, st, carry_in, carry_out, ss, s);
+                            const float* carry_in, float* carry_out, const CarryMap& cm,
+                            const ScanStates& ss, hipStream_t s) {
+  if (sg.n1 <= sg.n0) return hipSuccess;
+  if (D >= 64 && wide_tiles(active * d.H, D))
+    return launch_sf_bv<TI, D, C, 64>(d, in, sg, ops, o, st, carry_in, carry_out, cm, ss, s);
+  return launch_sf_bv<TI, D, C, 32>(d, in, sg, ops, o, st, carry_in, carry_out, cm, ss, s);
 }
 
 template <typename TI, int D, int C, int BV>
-static hipError_t launch_sb_bv(const Dims& d, const Inputs& in, const void* dO, int seg_begin,
-                               int seg_end, const ChunkOps& ops, const SegStates& st,
-                               const float* carry_in, float* carry_out, const ScanStates& ss,
-                               hipStream_t s) {
-  constexpr int NVT = D / BV;
-  const int groups = (d.N * d.H + 7) / 8;
-  hipLaunchKernelGGL((k_scan_bwd<TI, TI, D, C, BV>), dim3(groups * 8 * NVT), dim3(256), 0, s,
-                     d, in, static_cast<const TI*>(dO), seg_begin, seg_end, ops, st, carry_in,
-                     carry_out, ss);
+static hipError_t launch_sb_bv(const Dims& d, const Inputs& in, const void* dO, const Seg& sg,
+                               const ChunkOps& ops, const SegStates& st,
+                               const float* carry_in, float* carry_out, const CarryMap& cm,
+                               const ScanStates& ss, hipStream_t s) {
+  hipLaunchKernelGGL((k_scan_bwd<TI, TI, D, C, BV>), scan_grid(sg, d.H, D / BV), dim3(256), 0, s,
+                     d, in, static_cast<const TI*>(dO), sg, ops, st, carry_in, carry_out, cm, ss);
   return hipGetLastError();
 }
 
 template <typename TI, int D, int C>
-static hipError_t launch_sb(const Dims& d, const Inputs& in, const void* dO, int seg_begin,
-                            int seg_end, const ChunkOps& ops, const SegStates& st,
-                            const float* carry_in, float* carry_out, const ScanStates& ss,
-                            hipStream_t s) {
-  if (D >= 64 && wide_tiles(d, D))
-    return launch_sb_bv<TI, D, C, 64>(d, in, dO, seg_begin, seg_end, ops, st, carry_in, carry_out, ss, s);
-  return launch_sb_bv<TI, D, C, 32>(d, in, dO, seg_begin, seg_end, ops, st, carry_in, carry_out, ss, s);
+static hipError_t launch_sb(const Dims& d, const Inputs& in, const void* dO, const Seg& sg,
+                            int active, const ChunkOps& ops, const SegStates& st,
+                            const float* carry_in, float* carry_out, const CarryMap& cm,
+                            const ScanStates& ss, hipStream_t s) {
+  if (sg.n1 <= sg.n0) return hipSuccess;
+  if (D >= 64 && wide_tiles(active * d.H, D))
+    return launch_sb_bv<TI, D, C, 64>(d, in, dO, sg, ops, st, carry_in, carry_out, cm, ss, s);
+  return launch_sb_bv<TI, D, C, 32>(d, in, dO, sg, ops, st, carry_in, carry_out, cm, ss, s);
 }
 
 #define KDA_DISPATCH(FN, ...)                                              \
@@ -633,17 +679,17 @@ static hipError_t launch_sb(const Dims& d, const Inputs& in, const void* dO, int
   return hipErrorInvalidValue;
 
 hipError_t launch_scan_fwd(int dtype, int D, int C, const Dims& d, const Inputs& in,
-                           int seg_begin, int seg_end, const ChunkOps& ops, void* out_o,
+                           const Seg& sg, int active, const ChunkOps& ops, void* out_o,
                            const SegStates* st, const float* carry_in, float* carry_out,
-                           const ScanStates& ss, hipStream_t s) {
-  KDA_DISPATCH(launch_sf, d, in, seg_begin, seg_end, ops, out_o, st, carry_in, carry_out, ss, s)
+                           const CarryMap& cm, const ScanStates& ss, hipStream_t s) {
+  KDA_DISPATCH(launch_sf, d, in, sg, active, ops, out_o, st, carry_in, carry_out, cm, ss, s)
 }
 
 hipError_t launch_scan_bwd(int dtype, int D, int C, const Dims& d, const Inputs& in,
-                           const void* dO, int seg_begin, int seg_end, const ChunkOps& ops,
+                           const void* dO, const Seg& sg, int active, const ChunkOps& ops,
                            const SegStates& st, const float* carry_in, float* carry_out,
-                           const ScanStates& ss, hipStream_t s) {
-  KDA_DISPATCH(launch_sb, d, in, dO, seg_begin, seg_end, ops, st, carry_in, carry_out, ss, s)
+                           const CarryMap& cm, const ScanStates& ss, hipStream_t s) {
+  KDA_DISPATCH(launch_sb, d, in, dO, sg, active, ops, st, carry_in, carry_out, cm, ss, s)
 }
 
 // Sequences with no tokens: their outgoing state (final state, or the

@@ -127,6 +127,28 @@ def test_checkpoint_queries_follow_the_backward_segments(lib):
     assert lib.kda_bwd_segment_chunks(bad.ref) == 0 and lib.kda_checkpoint_bytes(bad.ref) == 0
 
 
+def test_checkpoints_of_a_plan_by_windows(lib):
+    # four sequences of five 64-token chunks, at most 8 chunks per segment:
+    # runs of the chunk order would give the scans a chain of 5 + 5 + 4
+    # chunks over three segments, windows of 2 chunks of every sequence one
+    # of 2 + 2 + 1, so the backward takes windows; every sequence then
+    # crosses two window starts, each with a checkpoint
+    p = good(T=1280, cu_host=[0, 320, 640, 960, 1280], seg_chunks=8)
+    slot = 4 * 128 * 128 * 4
+    assert lib.kda_bwd_segment_chunks(p.ref) == 2
+    assert lib.kda_checkpoint_bytes(p.ref) == 4 * 2 * slot
+    # one long and one short sequence (20 + 1 chunks): windows of 3 chunks
+    # would leave the chain at 20, so the runs of 4 chunks of the chunk
+    # order stay, one checkpoint slot per segment
+    q = good(T=1280 + 64, cu_host=[0, 1280, 1344], seg_chunks=4)
+    assert lib.kda_bwd_segment_chunks(q.ref) == 4
+    assert lib.kda_checkpoint_bytes(q.ref) == 6 * slot
+    # a single sequence: runs of the given length
+    r = good(T=1280, cu_host=[0, 1280], seg_chunks=6)  # 20 chunks
+    assert lib.kda_bwd_segment_chunks(r.ref) == 6
+    assert lib.kda_checkpoint_bytes(r.ref) == 4 * slot
+
+
 def test_state_io_validation_before_any_launch(lib):
     p = good(seg_chunks=1)
     nul = ctypes.c_void_p(0)

@@ -154,6 +154,43 @@ def test_forward_checkpoints_give_the_same_gradients(dtype, D, chunk, seg):
     check(saved, oracle_run(x, st=st), dtype, label="checkpoints")
 
 
+@pytest.mark.parametrize("dtype,D,chunk,lens,budget_mb", [
+    (torch.float32, 64, 32, [640, 640, 500, 0, 700], 2),
+    (torch.bfloat16, 128, 64, [900, 0, 1000, 777, 1000], 6)])
+def test_windowed_segments_match_one_segment(dtype, D, chunk, lens, budget_mb, monkeypatch):
+    # A workspace budget small enough that both directions stream a packed
+    # batch of several long sequences in windows of the same chunk positions
+    # in every sequence: the backward in windows of 2 (fp32) or 3 (bf16)
+    # chunks, the forward in windows of 6, which writes the checkpoints of
+    # the backward's windows from inside its own. In fp32 the per-token
+    # results are bit-identical to one segment holding every chunk (the
+    # states cross the boundaries in fp32); only the gate-parameter sums add
+    # their per-chunk partials in another order. In bf16 the backward's
+    # recording scan advances the state with U rounded to bf16 inside a
+    # segment while each segment starts from the state of the forward's
+    # recurrence (fp32 U), so the gradients depend on where the segments
+    # start by rounding; they are held to the oracle.
+    announce("windows %s D%d C%d budget %d MB" % (dtype, D, chunk, budget_mb))
+    x = kda_inputs.make_inputs(lens, 2, D, D, dtype, seed=47, device="cuda")
+    st = kda_inputs.make_states(len(lens), 2, D, D, seed=47, device="cuda")
+    whole = gpu_run(x, chunk, seg_chunks=100000, st=st)
+    monkeypatch.setenv("KDA_WS_BUDGET_MB", str(budget_mb))
+    plain = gpu_run(x, chunk, st=st)
+    saved = gpu_run(x, chunk, st=st, checkpoints=True)
+    for name in plain:
+        assert torch.equal(plain[name], saved[name]), name
+        if dtype != torch.float32 and name not in ("o", "ht"):
+            continue
+        if name in ("dA_log", "ddt_bias"):
+            e = rel(to_np(plain[name]), to_np(whole[name]))
+            assert e <= 1e-6, (name, e)
+        else:
+            assert torch.equal(plain[name], whole[name]), name
+    ref = oracle_run(x, st=st)
+    check(whole, ref, dtype, label="one segment")
+    check(saved, ref, dtype, label="windows")
+
+
 # ------------------------------------------------------------------ autograd
 
 
