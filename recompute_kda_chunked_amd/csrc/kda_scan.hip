@@ -584,25 +584,24 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
   }
 }
 
-// Value-tile width of both scans. The scans are bound by the operand traffic
-// each block pulls through its CU (every value tile of a head loads the same
-// chunk operands), so the width trades CUs in use against bytes per unit of
-// work: 32 columns while the N*H*V/32 blocks (1 wave per SIMD, rotating
-// operand sets in AGPRs as well) fit in one pass over the CUs or fill whole
-// multiples of it; 64 columns when they would leave the CUs unevenly loaded
-// (half the operand traffic per state column). Measured: at H96 (384 blocks
-// of 32 columns) 64 columns take the forward scan 0.150 -> 0.128 ms and the
-// reverse 0.181 -> 0.144 ms per launch; at 8 sequences x H16 (512 blocks, two
-// per CU) 32 columns take them 0.225 -> 0.154 and 0.331 -> 0.218 ms; at H64
-// (256 blocks) 64 columns are 1.4x slower than 32.
+// Value-tile width of both scans. The scans are bound by the chunk operands
+// each block pulls through its CU (every value tile of a head loads all of
+// them), so the width trades CUs in use against operand bytes per state
+// column: 32 columns while the (sequence, head) pairs with chunks in the
+// segment give at most one such block per CU, 64 columns (half the operand
+// bytes per column) once they would give more. Measured per launch on
+// MI355X: 1 x 8192 x H64 (256 blocks of 32): 64 columns are 1.4x slower, 16
+// columns (512 blocks) 1.55x slower; 8 packed sequences x H16 in windows (512
+// blocks of 32, two per CU): 64 columns take the forward scan 0.258 -> 0.218
+// ms, the reverse 0.139 -> 0.114 and the recording scan 0.098 -> 0.088; H96
+// (384 blocks of 32): forward 0.150 -> 0.128 ms, reverse 0.181 -> 0.144.
 static bool wide_tiles(int pairs, int D) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   const long groups = (static_cast<long>(pairs) + 7) / 8;
-  const long narrow = groups * 8 * (D / 32);
-  return narrow > cus && narrow % cus != 0;
+  return groups * 8 * (D / 32) > cus;
 }
 
 // Blocks of a scan over segment sg: every (sequence, head) pair of its
