@@ -103,9 +103,10 @@ def parse(argv=None):
 
 
 def copy_calibration() -> int:
-    """Two kernels of known traffic: a 1 GiB device-to-device copy (reads and
-    writes 1 GiB) and a 1 GiB reduction (reads 1 GiB, writes 4 bytes), five
-    launches each."""
+    """Kernels of known traffic, five launches each: a 1 GiB device-to-device
+    copy (reads and writes 1 GiB), then a sum of the same bytes as int32 in
+    int64, which torch runs as a cast (reads 1 GiB, writes 2 GiB) and a
+    reduction of the cast (reads 2 GiB, writes 8 bytes)."""
     import torch
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -115,7 +116,7 @@ def copy_calibration() -> int:
     v = src.view(torch.int32)
     out = torch.empty((), dtype=torch.int64, device="cuda:0")
     for _ in range(5):
-        torch.sum(v, dtype=torch.int64, out=out)
+        torch.sum(v, dim=0, dtype=torch.int64, out=out)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_per_launch": n, "read_bytes_per_launch": n, "launches": 5}),
           flush=True)
