@@ -130,18 +130,31 @@ int kda_prologue(const kda_problem *p, const void *q, const void *k,
                  float *kh, float *beta, float *gcum, void *workspace,
                  size_t workspace_bytes, void *stream);
 
-/* Forward: writes o [T,H,V] (dtype). Saves nothing for the backward. */
+/* Forward ("KDA Memory with Recompute: FLA vs cuDNN Frontend FROST", section
+   "Sources and measurement configuration": the inputs, the in-kernel
+   normalisation, sigmoid and safe gate, packed sequences; "KDA at the
+   production shape...", section 2.1, the per-chunk operations, and section
+   1.1, the state loop): writes o [T,H,V] (dtype). Saves nothing for the
+   backward. Errors: KDA_ERR_INVALID / KDA_ERR_UNSUPPORTED from the problem
+   (as kda_check_problem) or a null pointer, KDA_ERR_WORKSPACE when
+   workspace_bytes < kda_fwd_workspace_bytes, KDA_ERR_HIP on a failed
+   launch; all but the last are found before any launch. */
 int kda_fwd(const kda_problem *p, const void *q, const void *k, const void *v,
             const void *raw_g, const void *raw_beta, const float *A_log,
             const float *dt_bias, const int32_t *cu_seqlens, void *o,
             void *workspace, size_t workspace_bytes, void *stream);
 
-/* Backward: recomputes every intermediate from the inputs, streaming over
+/* Backward (the FROST page, sections "Both sides really use recomputation"
+   and "Why the larger FROST state series still wins": recompute instead of
+   saving, gradients written once in the input dtype; all seven inputs
+   differentiated as in "Sources and measurement configuration"):
+   recomputes every intermediate from the inputs, streaming over
    segments of chunks, and writes dq, dk, draw_g [T,H,K], dv [T,H,V],
    draw_beta [T,H] (dtype) and dA_log [H], ddt_bias [H,K] (fp32); draw_g
    [T,H] and ddt_bias [H] under KDA_GATE_PER_HEAD. The
    gate-parameter gradients are reduced in a fixed order (bitwise
-   reproducible run to run). */
+   reproducible run to run). Errors as kda_fwd, with
+   kda_bwd_workspace_bytes. */
 int kda_bwd(const kda_problem *p, const void *q, const void *k, const void *v,
             const void *raw_g, const void *raw_beta, const float *A_log,
             const float *dt_bias, const int32_t *cu_seqlens, const void *dO,
