@@ -20,9 +20,9 @@
 // columns of one key channel or chunk row), so that every store of them to
 // memory is one 4-element vector per tile. The serial
 // chunk loop is software-pipelined: the per-chunk operands a wave needs
-// (rows of W, qg, Aqk, kg^T, U, gamma, dO, ...) for chunk c+2 are loaded into
-// registers while chunk c is computed (three rotating register sets), so the
-// global-load latency, longer than one chunk step, stays off the recurrence.
+// (rows of W, qg, Aqk, kg^T, U, gamma, dO, ...) for chunk c+1 are loaded into
+// registers while chunk c is computed (two alternating register sets), so the
+// global-load latency stays off the recurrence.
 // The prefetched values stay raw until use: converting them at load time
 // would make the wave wait for the loads right away.
 //
@@ -237,22 +237,23 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, Seg sgm, Ch
   };
   put_state();
 
-  // Three operand sets rotate so that chunk c + 2 is being loaded while
-  // chunk c is computed (the loop is unrolled by three, no register copies).
+  // Two operand sets alternate so that chunk c + 1 is being loaded while
+  // chunk c is computed (the loop is unrolled by two, no register copies).
+  // A third set in flight (chunk c + 2) ran no faster and pushed the
+  // operand sets into AGPRs (296 registers per wave instead of 200).
   using Ops = FwdOps<OpT, D, C, BV>;
-  Ops s0, s1, s2;
+  Ops s0, s1;
   const size_t idx0 = static_cast<size_t>(cb - seg_begin) * d.H + h;
   load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(s0, ops, idx0, v0, w, i, g);
-  load_fwd_ops<OpT, D, C, BV, OUT_O, REC>(s1, ops, cb + 1 < ce ? idx0 + d.H : idx0, v0, w, i, g);
   __syncthreads();
 
   auto step = [&](int c, const Ops& cur, Ops& fill) {
     const size_t idx = static_cast<size_t>(c - seg_begin) * d.H + h;
-    // operands of chunk c + 2, in three portions over the step; unconditional
+    // operands of chunk c + 1, in three portions over the step; unconditional
     // (the last chunk again past the end): on every path the same number of
     // loads follows each set, so the waits before a set's use can leave the
-    // two later sets in flight
-    const size_t idx2 = static_cast<size_t>(min(c + 2, ce - 1) - seg_begin) * d.H + h;
+    // next set in flight
+    const size_t idx2 = static_cast<size_t>(min(c + 1, ce - 1) - seg_begin) * d.H + h;
     load_fwd_ops<OpT, D, C, BV, OUT_O, REC, 0>(fill, ops, idx2, v0, w, i, g);
     if (c == next_ck) {
       // the state entering chunk c, needed only where c is inside the sequence
@@ -342,17 +343,14 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, Seg sgm, Ch
     put_state();
     __syncthreads();
   };
-  // whole groups of three chunks in the loop (every step issues the same
-  // loads, so each wait leaves the two newer operand sets in flight), then
-  // the last one or two chunks
+  // whole pairs of chunks in the loop (every step issues the same loads, so
+  // each wait leaves the newer operand set in flight), then the last chunk
   int c = cb;
-  for (; c + 2 < ce; c += 3) {
-    step(c, s0, s2);
+  for (; c + 1 < ce; c += 2) {
+    step(c, s0, s1);
     step(c + 1, s1, s0);
-    step(c + 2, s2, s1);
   }
-  if (c < ce) step(c, s0, s2);
-  if (c + 1 < ce) step(c + 1, s1, s0);
+  if (c < ce) step(c, s0, s1);
   // the state leaves as the next segment's carry, or as the sequence's final state
   float* hout = !R.last ? (carry_out ? carry_out + carry_slot(cm, n, ce + pofs) * hkv : nullptr)
                         : (ss.fin ? ss.fin + static_cast<size_t>(n) * hkv : nullptr);
@@ -489,8 +487,8 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
   };
   put_state();
 
-  // three rotating operand sets: chunk c - 2 loads while chunk c is computed
-  Ops s0, s1, s2;
+  // two alternating operand sets: chunk c - 1 loads while chunk c is computed
+  Ops s0, s1;
   auto load = [&](Ops& f, int c, auto part) {
     const int64_t t0 = chunk_t0(c);
     load_bwd_ops<TI, OpT, D, C, BV, decltype(part)::value>(
@@ -499,12 +497,11 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
   };
   using All = std::integral_constant<int, -1>;
   load(s0, ce - 1, All{});
-  load(s1, max(ce - 2, cb), All{});
   auto step = [&](int c, const Ops& cur, Ops& fill) {
     const size_t idx = static_cast<size_t>(c - seg_begin) * d.H + h;
     // unconditional (the first chunk again past the start), as in the forward
     // scan, and in three portions over the step
-    const int c2 = max(c - 2, cb);
+    const int c2 = max(c - 1, cb);
     load(fill, c2, std::integral_constant<int, 0>{});
     // dO tile, transposed into LDS ([BV][C]); padded rows are zero
     const int len = chunk_len(chunk_t0(c));
@@ -565,15 +562,13 @@ __global__ void __launch_bounds__(256) k_scan_bwd(Dims d, Inputs in, const TI* d
     __syncthreads();  // every wave is done reading dhT_s / dOT_s / dVnT_s of this chunk
     put_state();
   };
-  // whole groups of three chunks in the loop, then the first one or two
+  // whole pairs of chunks in the loop, then the first chunk
   int c = ce - 1;
-  for (; c - 2 >= cb; c -= 3) {
-    step(c, s0, s2);
+  for (; c - 1 >= cb; c -= 2) {
+    step(c, s0, s1);
     step(c - 1, s1, s0);
-    step(c - 2, s2, s1);
   }
-  if (c >= cb) step(c, s0, s2);
-  if (c - 1 >= cb) step(c - 1, s1, s0);
+  if (c >= cb) step(c, s0, s1);
   // the gradient leaves as the previous segment's carry, or, past the
   // sequence's first chunk, as the initial state's gradient
   float* hout = !R.first ? carry_out + carry_slot(cm, n, R.pos) * hkv
