@@ -154,10 +154,12 @@ def test_forward_checkpoints_give_the_same_gradients(dtype, D, chunk, seg):
     check(saved, oracle_run(x, st=st), dtype, label="checkpoints")
 
 
-@pytest.mark.parametrize("dtype,D,chunk,lens,budget_mb", [
-    (torch.float32, 64, 32, [640, 640, 500, 0, 700], 2),
-    (torch.bfloat16, 128, 64, [900, 0, 1000, 777, 1000], 6)])
-def test_windowed_segments_match_one_segment(dtype, D, chunk, lens, budget_mb, monkeypatch):
+@pytest.mark.parametrize("dtype,D,chunk,lens,budget_mb,per_head", [
+    (torch.float32, 64, 32, [640, 640, 500, 0, 700], 2, False),
+    (torch.bfloat16, 128, 64, [900, 0, 1000, 777, 1000], 6, False),
+    (torch.float32, 64, 32, [640, 640, 500, 0, 700], 2, True)])
+def test_windowed_segments_match_one_segment(dtype, D, chunk, lens, budget_mb, per_head,
+                                             monkeypatch):
     # A workspace budget small enough that both directions stream a packed
     # batch of several long sequences in windows of the same chunk positions
     # in every sequence: the backward in windows of 2 (fp32) or 3 (bf16)
@@ -170,8 +172,13 @@ def test_windowed_segments_match_one_segment(dtype, D, chunk, lens, budget_mb, m
     # segment while each segment starts from the state of the forward's
     # recurrence (fp32 U), so the gradients depend on where the segments
     # start by rounding; they are held to the oracle.
-    announce("windows %s D%d C%d budget %d MB" % (dtype, D, chunk, budget_mb))
-    x = kda_inputs.make_inputs(lens, 2, D, D, dtype, seed=47, device="cuda")
+    announce("windows %s D%d C%d budget %d MB%s" % (dtype, D, chunk, budget_mb,
+                                                    ", gate per head" if per_head else ""))
+    x = kda_inputs.make_inputs(lens, 2, D, D, dtype, seed=47, device="cuda",
+                               gate_per_head=per_head)
+    if per_head:
+        x["A_log"].copy_(torch.tensor([0.3, -0.5]))
+        x["dt_bias"].copy_(torch.tensor([-1.0, 0.6]))
     st = kda_inputs.make_states(len(lens), 2, D, D, seed=47, device="cuda")
     whole = gpu_run(x, chunk, seg_chunks=100000, st=st)
     monkeypatch.setenv("KDA_WS_BUDGET_MB", str(budget_mb))
