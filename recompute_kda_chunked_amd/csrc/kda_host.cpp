@@ -130,7 +130,11 @@ constexpr int64_t kMaxWindowTable = 1 << 20;
 // head), so a plan's critical path is the sum over its segments of the most
 // chunks one sequence has in it: windows are taken when that is at most
 // three quarters of the sequence-order plan's (several long sequences in a
-// packed batch; a single sequence gives both plans the same segments).
+// packed batch; a single sequence gives both plans the same segments), and
+// when the states they hold fit: every sequence crossing a window boundary
+// needs a carry slot and, in the backward, a checkpoint per window start, each
+// a [H][K][V] fp32 state. The windows' operands, carries and checkpoints must
+// stay within the budget or within what the sequence-order plan holds.
 Plan make_plan(const kda_problem* p, bool bwd) {
   Plan P{};
   P.N = p->n_seqs;
@@ -200,7 +204,18 @@ Plan make_plan(const kda_problem* p, bool bwd) {
       if (held(mid) <= cap) lo = mid; else hi = mid - 1;
     }
     const int nsw = (maxnc + lo - 1) / lo, w = (maxnc + nsw - 1) / nsw;
-    if (static_cast<int64_t>(nsw) * (N + 1) <= kMaxWindowTable && 4LL * maxnc <= 3 * cost_seq) {
+    const size_t slot = up(static_cast<size_t>(P.H) * P.D * P.D * 4);
+    int64_t cross = 0, cks = 0;  // sequences longer than a window; their window starts
+    for (int n = 0; n < N; ++n) {
+      cross += nc[n] > w;
+      cks += nc[n] > w ? (nc[n] + w - 1) / w - 1 : 0;
+    }
+    const size_t mem_w = static_cast<size_t>(held(w)) * per +
+                         static_cast<size_t>(2 * cross + (bwd ? cks : 0)) * slot;
+    const size_t mem_seq = static_cast<size_t>(seg) * per + (2 + (bwd ? ns_seq : 0)) * slot;
+    const size_t mem_cap = budget_bytes() > mem_seq ? budget_bytes() : mem_seq;
+    if (static_cast<int64_t>(nsw) * (N + 1) <= kMaxWindowTable && 4LL * maxnc <= 3 * cost_seq &&
+        mem_w <= mem_cap) {
       P.win = true;
       P.seg = w;
       P.NS = nsw;

@@ -149,6 +149,28 @@ def test_checkpoints_of_a_plan_by_windows(lib):
     assert lib.kda_checkpoint_bytes(r.ref) == 4 * slot
 
 
+def test_windows_only_where_their_states_fit(lib):
+    # 300 sequences of 7 chunks at H16, D128, at most 600 chunks per segment:
+    # windows of 2 chunks would shorten the scans' chain (7 chunks in all,
+    # against 7 in each of the 4 chunk-order segments), but every sequence
+    # would cross three window starts,
+    # so the backward would hold 900 checkpoint and 600 carry states of 1 MiB
+    # on top of its operands: the plan stays in chunk order, one checkpoint
+    # slot per segment
+    lens = [448] * 300
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    p = good(T=cu[-1], H=16, cu_host=cu, seg_chunks=600)
+    slot = 16 * 128 * 128 * 4
+    assert lib.kda_bwd_segment_chunks(p.ref) == 600
+    assert lib.kda_checkpoint_bytes(p.ref) == 4 * slot
+    # the same batch at H2, D64: the states are small and windows are taken
+    q = good(T=cu[-1], H=2, K=64, V=64, cu_host=cu, seg_chunks=600)
+    assert lib.kda_bwd_segment_chunks(q.ref) == 2
+    assert lib.kda_checkpoint_bytes(q.ref) == 300 * 3 * 2 * 64 * 64 * 4
+
+
 def test_state_io_validation_before_any_launch(lib):
     p = good(seg_chunks=1)
     nul = ctypes.c_void_p(0)

@@ -271,6 +271,28 @@ def test_many_short_sequences():
     check(gpu_run(x, 64, seg_chunks=97), ref, torch.float32, label="N300 C64 seg97")
 
 
+def test_many_sequences_in_windows():
+    # 300 sequences of 0..400 tokens, at most 600 chunks per segment: the
+    # plan takes windows of 2 chunks of every sequence (7 segments, 246
+    # sequences carrying their state across window starts, 800 checkpoints),
+    # so the chunk table's per-segment scans run over more sequences than
+    # its threads. fp32 results are bit-identical to one segment except the
+    # gate-parameter sums, which add their per-chunk partials in another order.
+    announce("300 sequences in windows of 2 chunks")
+    rng = np.random.default_rng(29)
+    lens = [int(v) for v in rng.integers(0, 401, size=300)]
+    lens[0], lens[5], lens[299] = 0, 0, 0
+    x = kda_inputs.make_inputs(lens, 2, 64, 64, torch.float32, seed=29, device="cuda")
+    win = gpu_run(x, 32, seg_chunks=600)
+    whole = gpu_run(x, 32, seg_chunks=100000)
+    for name in win:
+        if name in ("dA_log", "ddt_bias"):
+            assert rel(to_np(win[name]), to_np(whole[name])) <= 1e-6, name
+        else:
+            assert torch.equal(win[name], whole[name]), name
+    check(win, oracle_run(x), torch.float32, label="N300 windows")
+
+
 def test_bitwise_deterministic():
     announce("run-to-run determinism")
     x = kda_inputs.make_inputs([300, 77], 4, 128, 128, torch.bfloat16, seed=19, device="cuda")
