@@ -519,7 +519,13 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     }
   }
   __syncthreads();  // operand buffers are dead; the dX buffers reuse their space
-  for (int e = tid; e < 4 * C * LDX; e += NT) dXq[e] = from_f<OpT>(0.f);
+  {
+    // the four dX buffers are cleared 16 bytes per store
+    constexpr int NZ = 4 * C * LDX * (int)sizeof(OpT) / 16;
+    static_assert(4 * C * LDX * (int)sizeof(OpT) % 16 == 0, "dX buffers clear in 16-byte pieces");
+    uint4* z = reinterpret_cast<uint4*>(dXq);
+    for (int e = tid; e < NZ; e += NT) z[e] = make_uint4(0u, 0u, 0u, 0u);
+  }
   __syncthreads();
 #pragma unroll
   for (int jp = 0; jp < PPW; ++jp) {
@@ -781,8 +787,14 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   for (int jm = 0; jm < MR; ++jm) {
     const int m = row_block(jm);
     if (m >= NB) break;
+    {
+      // rows 16m + 4g .. + 3 of this lane's channel, one vector store
+      typedef std::conditional_t<sizeof(TG) == 4, f32x4, f64x4> TG4;
+      TG4 v;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) dGT[kk * LDG + 16 * m + 4 * g + rr] = aG[jm][rr];
+      for (int rr = 0; rr < 4; ++rr) v[rr] = aG[jm][rr];
+      *reinterpret_cast<TG4*>(dGT + kk * LDG + 16 * m + 4 * g) = v;
+    }
   }
   __syncthreads();
   {

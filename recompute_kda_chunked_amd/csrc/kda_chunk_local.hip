@@ -151,7 +151,8 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   const TI* bkr = G2 ? static_cast<const TI*>(in.bk) + L.t0 * ts + static_cast<size_t>(h) * D : nullptr;
   const TI* wvr = G2 ? static_cast<const TI*>(in.wv) + L.t0 * ts + static_cast<size_t>(h) * D : nullptr;
 
-  for (int e = tid; e < C * LDM; e += 256) Ms[e] = 0.f;
+  static_assert(C * LDM % 4 == 0, "the fp32 C x C buffers clear in 16-byte pieces");
+  for (int e = tid; e < C * LDM / 4; e += 256) reinterpret_cast<f32x4*>(Ms)[e] = zero4();
   auto G = [&](int r, int kk) -> GV& { return Gs[r * LDG + kk]; };
   // the gate in GateUnits (base 2 for bf16): every exponential below is of a
   // difference of these values
@@ -459,7 +460,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   // ---- T = (I + Akk)^-1 (in the staging area, free again), diagonal 16x16
   // blocks by forward substitution. The operands of W and U wait in
   // registers (sv) meanwhile.
-  for (int e = tid; e < C * LDM; e += 256) Ts[e] = 0.f;
+  for (int e = tid; e < C * LDM / 4; e += 256) reinterpret_cast<f32x4*>(Ts)[e] = zero4();
   __syncthreads();
   if (w < NB && lane < 16) {
     const int I = w, j = lane;
