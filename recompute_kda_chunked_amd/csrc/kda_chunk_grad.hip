@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // cumulative sum and of the partial reductions
   constexpr int OFF_S = 0;
   constexpr int OFF_X = (OFF_S + (int)sizeof(TG) * (NT + 64) + 15) / 16 * 16;
-  static_assert(OFF_X + 3 * C * (D + 8) * (int)sizeof(TI) <= SZU, "LDS scratch must fit");
+  static_assert(OFF_X + C * (D + 8) * (int)sizeof(TI) <= SZU, "LDS scratch must fit");
   __shared__ __attribute__((aligned(16))) GV GT[K * LDG];
   __shared__ __attribute__((aligned(16))) TI qT[K * LDQ];
   __shared__ __attribute__((aligned(16))) TI kT[K * LDQ];
@@ -724,7 +724,10 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   static_assert(NT % D == 0, "one channel per thread in the gate VJP");
   // The raw gate rows come in as 16-byte vectors and wait in LDS for the gate
   // VJP (whose thread-per-channel mapping would otherwise take a 2-byte load
-  // per element); dq, dk and draw_g go out the same way, staged in LDS.
+  // per element); draw_g goes out the same way, staged in LDS. dq and dk
+  // leave straight from the lanes that form them (16 lanes write 32
+  // contiguous bytes of a row, merged in L2): staging them through LDS
+  // cost 32 two-byte LDS stores per lane on the phase's chain.
   // (a per-head gate is read in S8 instead)
   VT xrow[VPT];
   float dbias = 0.f;
@@ -772,10 +775,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   TG* dGT = reinterpret_cast<TG*>(GT);
   TG* ptg = reinterpret_cast<TG*>(uni + OFF_S);
   TG* red = reinterpret_cast<TG*>(uni + OFF_S + sizeof(TG) * NT);
-  // raw gate rows (then draw_g), dq and dk, [C][LDA] each
+  // raw gate rows (then draw_g), [C][LDA]
   TI* xg_s = reinterpret_cast<TI*>(uni + OFF_X);
-  TI* dq_s = xg_s + C * LDA;
-  TI* dk_s = dq_s + C * LDA;
   if constexpr (!PH) {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -903,8 +904,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
           const float qd = rsum[0][r], kd = rsum[1][r];
           const float qbar = q4[rr] * rq4[rr];
           const float khat_ = k4[rr] * rk4[rr];
-          dq_s[r * LDA + kk] = from_f<TI>(rqs[r] * (aq[jm][rr] - qbar * qd));
-          dk_s[r * LDA + kk] = from_f<TI>(rk[r] * (ak[jm][rr] - khat_ * kd));
+          dqo[r * ts + kk] = from_f<TI>(rqs[r] * (aq[jm][rr] - qbar * qd));
+          dko[r * ts + kk] = from_f<TI>(rk[r] * (ak[jm][rr] - khat_ * kd));
         }
       }
     }
@@ -947,8 +948,6 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     for (int j = 0; j < VPT; ++j) {
       const int e = tid + NT * j, r = e / NVR, c = (e % NVR) * VE;
       if (e < NV && r < L.len) {
-        *reinterpret_cast<VT*>(dqo + r * ts + c) = *reinterpret_cast<const VT*>(dq_s + r * LDA + c);
-        *reinterpret_cast<VT*>(dko + r * ts + c) = *reinterpret_cast<const VT*>(dk_s + r * LDA + c);
         if constexpr (!PH)
           *reinterpret_cast<VT*>(dgo + r * ts + c) = *reinterpret_cast<const VT*>(xg_s + r * LDA + c);
       }
