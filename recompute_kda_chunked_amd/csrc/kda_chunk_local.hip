@@ -67,7 +67,7 @@ struct TileT<bf16, D, C> {
     for (int e = tid; e < D * NU; e += 256) {
       const int blk = e >> 6, lane = e & 63;
       const int kk = 16 * (blk / (C / 32)) + (lane & 15), s = 32 * (blk % (C / 32)) + 8 * (lane >> 4);
-      *reinterpret_cast<bf16x8*>(dst + 8 * e) = frag(t, kk, s);
+      vstore<true>(reinterpret_cast<bf16x8*>(dst + 8 * e), frag(t, kk, s));
     }
   }
 };
@@ -91,7 +91,7 @@ struct TileT<float, D, C> {
       const int blk = e >> 4, l0 = (4 * e) & 63;
       const int kk = 16 * (blk / (C / 4)) + (l0 & 15), s = 4 * (blk % (C / 4)) + (l0 >> 4);
       const float* src = t + kk * LD + s;
-      *reinterpret_cast<f32x4*>(dst + 4 * e) = f32x4{src[0], src[LD], src[2 * LD], src[3 * LD]};
+      vstore<true>(reinterpret_cast<f32x4*>(dst + 4 * e), f32x4{src[0], src[LD], src[2 * LD], src[3 * LD]});
     }
   }
 };
@@ -106,6 +106,10 @@ struct TileT<float, D, C> {
 // u = M^-1 (w v)): a per-channel erase gate b = sigmoid(raw_b) and write gate
 // w = sigmoid(raw_w) replace beta. The row side of the k.k products carries
 // b, so P is Akk itself (beta = 1 below), Kb = b kh e^G and Bv = w v.
+// The per-chunk operands leave with the non-temporal hint: the scans and the
+// gradient kernel read them later from HBM, and with the hint the output scan
+// runs about 5% and the recording scan about 7% faster, with this kernel's
+// own time unchanged.
 template <typename TI, typename OpT, int D, int C, bool BWD, bool STATE, bool PH, bool G2>
 __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int seg_begin,
                                                      ChunkOps ops) {
@@ -292,20 +296,20 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
       int I, J;
       pair_blocks(p, I, J);
       if (BWD) {
-        store4_fm<OpT>(dst, 16 * J + i, 16 * I + 4 * g, C, aqv[it]);
+        store4_fm<OpT, true>(dst, 16 * J + i, 16 * I + 4 * g, C, aqv[it]);
       } else {
-        store4_fm<OpT>(dst, 16 * I + i, 16 * J + 4 * g, C, aqv[it]);
-        if constexpr (HL) store4_fm<OpT>(dlo, 16 * I + i, 16 * J + 4 * g, C, lo4(aqv[it]));
+        store4_fm<OpT, true>(dst, 16 * I + i, 16 * J + 4 * g, C, aqv[it]);
+        if constexpr (HL) store4_fm<OpT, true>(dlo, 16 * I + i, 16 * J + 4 * g, C, lo4(aqv[it]));
       }
     }
     for (int zb = w; zb < NB * (NB - 1) / 2; zb += 4) {
       int I = 1, J = zb;  // zb-th block pair with J < I
       while (J >= I) { J -= I; ++I; }
       if (BWD) {
-        store4_fm<OpT>(dst, 16 * I + i, 16 * J + 4 * g, C, zero4());
+        store4_fm<OpT, true>(dst, 16 * I + i, 16 * J + 4 * g, C, zero4());
       } else {
-        store4_fm<OpT>(dst, 16 * J + i, 16 * I + 4 * g, C, zero4());
-        if constexpr (HL) store4_fm<OpT>(dlo, 16 * J + i, 16 * I + 4 * g, C, zero4());
+        store4_fm<OpT, true>(dst, 16 * J + i, 16 * I + 4 * g, C, zero4());
+        if constexpr (HL) store4_fm<OpT, true>(dlo, 16 * J + i, 16 * I + 4 * g, C, zero4());
       }
     }
   };
@@ -429,10 +433,10 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
           // or VE slots 16 apart (fp32)
           OpT* dst = rowm + FragMajor<OpT>::off(r, c0, K);
           if constexpr (VE == KPL) {
-            *reinterpret_cast<VT*>(dst) = out;
+            vstore<true>(reinterpret_cast<VT*>(dst), out);
           } else {
 #pragma unroll
-            for (int j = 0; j < VE; ++j) dst[16 * j] = out[j];
+            for (int j = 0; j < VE; ++j) vstore<true>(dst + 16 * j, out[j]);
           }
         }
       }
@@ -586,14 +590,14 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         // acc[n][rr] = W[16n + i][16mk + 4g + rr]; all three fragment-major
-        store4_fm<OpT>(Wn, 16 * n + i, 16 * mk + 4 * g, K, -acc[n]);
+        store4_fm<OpT, true>(Wn, 16 * n + i, 16 * mk + 4 * g, K, -acc[n]);
         if (BWD) {
           // acc2[n][rr] = W[16n + 4g + rr][16mk + i]  ->  WnT[k][r..r+3]
-          store4_fm<OpT>(static_cast<OpT*>(ops.WnT) + idx * K * C, 16 * mk + i, 16 * n + 4 * g, C,
+          store4_fm<OpT, true>(static_cast<OpT*>(ops.WnT) + idx * K * C, 16 * mk + i, 16 * n + 4 * g, C,
                          -acc2[n]);
         }
         if constexpr (BWD) {
-          store4_fm<OpT>(static_cast<OpT*>(ops.U) + idx * C * V, 16 * n + i, 16 * mk + 4 * g, V, accu[n]);
+          store4_fm<OpT, true>(static_cast<OpT*>(ops.U) + idx * C * V, 16 * n + i, 16 * mk + 4 * g, V, accu[n]);
         } else {
           // fp32, row-major: accu[n][rr] = U[16n + i][16mk + 4g + rr]
           f32x4 u = accu[n];
@@ -614,7 +618,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
               u[rr] += bv - to_f(from_f<OpT>(bv));
             }
           }
-          *reinterpret_cast<f32x4*>(ops.Uf + idx * C * V + (16 * n + i) * V + 16 * mk + 4 * g) = u;
+          vstore<true>(reinterpret_cast<f32x4*>(ops.Uf + idx * C * V + (16 * n + i) * V + 16 * mk + 4 * g), u);
         }
       }
     }
