@@ -415,6 +415,9 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     hdh = static_cast<TG>(sum_groups(hd));
     const GV Gc = GT[kk * LDG + ((C - 1) ^ swk)];
     TG colsum = 0;
+    float vb[4 * MR];  // beta's per-row terms, summed over the row group after the loop
+#pragma unroll
+    for (int e = 0; e < 4 * MR; ++e) vb[e] = 0.f;
 #pragma unroll
     for (int jm = 0; jm < MR; ++jm) {
       const int m = row_block(jm);
@@ -452,10 +455,14 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         if constexpr (G2) {
           ab[jm][rr] += dKb * kh * eG;
         } else {
-          const float pb = sum16(dKb * kh * eG);
-          if (i == 0) dbp[w][r] += pb;
+          vb[4 * jm + rr] = dKb * kh * eG;
         }
       }
+    }
+    if constexpr (!G2) {
+      const float pb = transpose_sum16<4 * MR>(vb);
+      const int j = i % (4 * MR), m = row_block(j / 4);
+      if (i < 4 * MR && m < NB) dbp[w][16 * m + 4 * g + j % 4] += pb;
     }
     colsum += __shfl_xor(colsum, 16, kWave);
     colsum += __shfl_xor(colsum, 32, kWave);
@@ -479,13 +486,22 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     const OpT* Ug = static_cast<const OpT*>(ops.U) + idx * C * V;
     const OpT* Wng = static_cast<const OpT*>(ops.Wn) + idx * C * K;
     const OpT* PTg = static_cast<const OpT*>(ops.PT) + idx * C * C;
+    // beta's per-row terms of the wave's pairs (row block pm, -1 past the
+    // last pair), summed over the row group after the loop
+    static_assert(PPW == 1 || PPW == 2 || PPW == 4, "pairs per wave");
+    float vb[4 * PPW];
+    int pm[PPW];
 #pragma unroll
     for (int jp = 0; jp < PPW; ++jp) {
       const int p = w + NW * jp;
       xq[jp] = xk[jp] = zero4();
-      if (p >= NPAIR) break;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) vb[4 * jp + rr] = 0.f;
+      pm[jp] = -1;
+      if (p >= NPAIR) continue;
       int m = 0, ns = p;
       while (ns > m) { ns -= m + 1; ++m; }
+      pm[jp] = m;
       // global operands of this pair first (U and -W rows of block ns, P^T)
       constexpr int NKV = V / KS;
       typename M::frag fu[NKV], fw[NKV];
@@ -511,11 +527,17 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
         xq[jp][rr] = (s_ <= r) ? aqk[rr] : 0.f;
         const float dakk = (s_ < r) ? (a2[rr] - a1[rr]) : 0.f;
         xk[jp][rr] = be[r] * dakk;
-        if constexpr (!G2) {  // GDN-2: the erase gate takes it in S6, per channel
-          const float pb = sum16(dakk * p4[rr]);
-          if (i == 0) dbp[w][r] += pb;
-        }
+        if constexpr (!G2) vb[4 * jp + rr] = dakk * p4[rr];  // GDN-2: the erase gate takes it in S6
       }
+    }
+    if constexpr (!G2) {
+      const float pb = transpose_sum16<4 * PPW>(vb);
+      const int j = i % (4 * PPW);
+      int m = -1;
+#pragma unroll
+      for (int jp = 0; jp < PPW; ++jp) m = (j / 4 == jp) ? pm[jp] : m;
+      // two pairs of a wave may share a row block: the add is atomic
+      if (i < 4 * PPW && m >= 0) atomicAdd(&dbp[w][16 * m + 4 * g + j % 4], pb);
     }
   }
   __syncthreads();  // operand buffers are dead; the dX buffers reuse their space
@@ -745,21 +767,22 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // (A_log[h] from the prologue's loads: a load issued here would wait
   // behind this phase's others)
   const TG eat = exp(static_cast<TG>(pr.alog));
+  // the wave's per-row sums over its 16 channels: value 4 jm + rr of every
+  // lane, summed across the lanes of its row group in one transposed sum
+  // that leaves row value j in lane j
+  float vq[4 * MR], vk[4 * MR];
 #pragma unroll
   for (int jm = 0; jm < MR; ++jm) {
     const int m = row_block(jm);
-    if (m >= NB) break;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) vq[4 * jm + rr] = vk[4 * jm + rr] = 0.f;
+    if (m >= NB) continue;
     const int r0 = 16 * m + 4 * g;
     const f32x4 q4 = tile4(qT, r0), k4 = tile4(kT, r0), rq4 = sc4(rq, r0), rk4 = sc4(rk, r0);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int r = r0 + rr;
-      const float pq = sum16(q4[rr] * rq4[rr] * aq[jm][rr]);
-      const float pk = sum16(k4[rr] * rk4[rr] * ak[jm][rr]);
-      if (i == 0) {
-        rowp[0][kb][r] = pq;
-        rowp[1][kb][r] = pk;
-      }
+      vq[4 * jm + rr] = q4[rr] * rq4[rr] * aq[jm][rr];
+      vk[4 * jm + rr] = k4[rr] * rk4[rr] * ak[jm][rr];
     }
     // row C-1 holds G_c: add sum_r kg*dkg over all row groups and gamma * (h . dh')
     if (m == NB - 1 && g == 3) {
@@ -768,6 +791,14 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 #pragma unroll
       for (int hh = 0; hh < SPLIT; ++hh) cs += csum[hh][kb][i];
       aG[jm][3] += cs + static_cast<TG>(kexp<OpT>(Gc)) * hdh;
+    }
+  }
+  {
+    const float pq = transpose_sum16<4 * MR>(vq), pk = transpose_sum16<4 * MR>(vk);
+    const int j = i % (4 * MR), m = row_block(j / 4);
+    if (i < 4 * MR && m < NB) {
+      rowp[0][kb][16 * m + 4 * g + j % 4] = pq;
+      rowp[1][kb][16 * m + 4 * g + j % 4] = pk;
     }
   }
   __syncthreads();  // all reads of GT as the cumulative gate are done

@@ -81,6 +81,48 @@ __device__ __forceinline__ float group_sum(float x) {
 // Sum over the 16 lanes that share g (the lanes of one tile row group).
 __device__ __forceinline__ float sum16(float x) { return group_sum<16>(x); }
 
+// N sums at once over each aligned group of 16 lanes (N = 1, 2, 4, 8 or 16
+// values per lane): on return lane l holds its group's sum of v[l % N].
+// Partners are taken in turn across the row mirror, the half-row mirror and
+// the quad swaps by 2 and by 1 (each an involution that pairs lanes differing
+// in lane bit 3, 2, 1, 0). While a lane holds fewer values than that level
+// can split, it adds its partner's copy of every value; otherwise it keeps
+// the half its lane bit selects and adds its partner's copy of that half, so
+// the values halve level by level (recursive halving). Sixteen values take
+// 45 lane moves and selects instead of the 64 moves of sixteen group_sum<16>
+// calls, and every lane ends with a different sum.
+template <int N, int CTRL, int BIT>
+__device__ __forceinline__ void halving_level(float (&a)[16], int l) {
+  if constexpr (2 * BIT > N) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) a[j] += dpp_mov<CTRL>(a[j]);
+  } else {
+    constexpr int H = N / 2;
+    const bool up = (l & BIT) != 0;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      const float keep = up ? a[j + H] : a[j], send = up ? a[j] : a[j + H];
+      a[j] = keep + dpp_mov<CTRL>(send);
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ float transpose_sum16(const float (&v)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "values per lane");
+  float a[16];
+#pragma unroll
+  for (int j = 0; j < N; ++j) a[j] = v[j];
+  const int l = static_cast<int>(threadIdx.x) & 15;
+  constexpr int N1 = 16 > N ? N : N / 2;
+  constexpr int N2 = 8 > N1 ? N1 : N1 / 2;
+  constexpr int N3 = 4 > N2 ? N2 : N2 / 2;
+  halving_level<N, 0x140, 8>(a, l);
+  halving_level<N1, 0x141, 4>(a, l);
+  halving_level<N2, 0x4E, 2>(a, l);
+  halving_level<N3, 0xB1, 1>(a, l);
+  return a[0];
+}
+
 // Sum over the four lane groups g (lanes i, i+16, i+32, i+48).
 __device__ __forceinline__ float sum_groups(float x) {
   x += __shfl_xor(x, 16, kWave);
