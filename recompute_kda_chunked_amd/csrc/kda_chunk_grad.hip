@@ -218,7 +218,14 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // wave w takes the TPW tiles w*TPW .. of dBv^T (value block mv, row block
   // nr); they share one value block, so its dVn^T rows are loaded once
   static_assert(NB % TPW == 0, "a wave's tiles share one value block");
-  typename M::frag fa[NKS], fb[TPW][NKS];
+  typename M::frag fa[NKS];
+  // T^T is staged once per block in LDS (the dKb_s region, unused until S4):
+  // every wave's tiles take all of its row blocks, and eight waves loading
+  // the same fragments from global memory would pass 8x its bytes through
+  // the CU's address unit. One 16-byte piece per thread.
+  constexpr int NTT = C * C * (int)sizeof(OpT) / 16, TTPT = (NTT + NT - 1) / NT;
+  uint4 ttv[TTPT];
+  static_assert(C <= LDA && C * LDA * (int)sizeof(OpT) % 16 == 0, "T^T fits the dKb_s region");
   uint32_t vin[TPW][4];
   uint32_t win[G2 ? TPW : 1][4];  // GDN-2 write gate at the dv positions
   using FM = FragMajor<OpT>;
@@ -237,6 +244,11 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   {
     const OpT* dVnT = static_cast<const OpT*>(st.dVnT) + idx * V * C;
     const OpT* TT = static_cast<const OpT*>(ops.TT) + idx * C * C;
+#pragma unroll
+    for (int j = 0; j < TTPT; ++j) {
+      const int e = tid + NT * j;
+      ttv[j] = reinterpret_cast<const uint4*>(TT)[e < NTT ? e : 0];
+    }
     {
       const int t = w * TPW < T2 ? w * TPW : 0, mv = t / NB;
 #pragma unroll
@@ -247,9 +259,6 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       const int t0 = w * TPW + jt, t = t0 < T2 ? t0 : 0;
       const int mv = t / NB, nr = t % NB;
       const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
-      // the whole reduction is taken (T^T[r][s] is stored as 0 for s < r)
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) fb[jt][ks] = M::load(TT + FM::frag(nr, ks, C, lane));
       load4_raw<TI>(vr + (r < L.len ? r : L.len - 1) * ts + vv, vin[jt]);
       if constexpr (G2) load4_raw<TI>(wvr + (r < L.len ? r : L.len - 1) * ts + vv, win[jt]);
     }
@@ -280,6 +289,11 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   }
   for (int e = tid; e < NW * C; e += NT) dbp[e / C][e % C] = 0.f;
   for (int e = tid; e < 2 * NKB * C; e += NT) (&rowp[0][0][0])[e] = 0.f;
+#pragma unroll
+  for (int j = 0; j < TTPT; ++j) {
+    const int e = tid + NT * j;
+    if (e < NTT) reinterpret_cast<uint4*>(dKb_s)[e] = ttv[j];
+  }
   __syncthreads();
   cumsum_rows<D, C, NT>(Gf, ptot);
   if constexpr (PH) {
@@ -312,8 +326,9 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       const int mv = t / NB, nr = t % NB;
       const int r = 16 * nr + i, vv = 16 * mv + 4 * g;
       f32x4 acc = zero4();
+      // the whole reduction is taken (T^T[r][s] is stored as 0 for s < r)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) acc = M::mma(fa[ks], fb[jt][ks], acc);
+      for (int ks = 0; ks < NKS; ++ks) acc = M::mma(fa[ks], M::load(dKb_s + FM::frag(nr, ks, C, lane)), acc);
       OpT* dst = dBv_s + r * LDA + vv;
       float part = 0.f;
       const f32x4 vv4 = unpack4<TI>(vin[jt]);
