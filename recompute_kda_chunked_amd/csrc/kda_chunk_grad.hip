@@ -762,9 +762,10 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // The raw gate rows come in as 16-byte vectors and wait in LDS for the gate
   // VJP (whose thread-per-channel mapping would otherwise take a 2-byte load
   // per element); draw_g goes out the same way, staged in LDS. dq and dk
-  // leave straight from the lanes that form them (16 lanes write 32
-  // contiguous bytes of a row, merged in L2): staging them through LDS
-  // cost 32 two-byte LDS stores per lane on the phase's chain.
+  // leave from the lanes that form them after a 4x4 transpose within each
+  // quad of lanes (four channels of one row per lane): staging them through
+  // LDS cost 32 two-byte LDS stores per lane on the phase's chain, and
+  // storing each lane's four rows of one channel took 32 two-byte stores.
   // (a per-head gate is read in S8 instead)
   VT xrow[VPT];
   float dbias = 0.f;
@@ -943,16 +944,24 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       if (m >= NB) break;
       const int r0 = 16 * m + 4 * g;
       const f32x4 q4 = tile4(qT, r0), k4 = tile4(kT, r0), rq4 = sc4(rq, r0), rk4 = sc4(rk, r0);
+      f32x4 vq, vk;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int r = r0 + rr;
-        if (r < L.len) {
-          const float qd = rsum[0][r], kd = rsum[1][r];
-          const float qbar = q4[rr] * rq4[rr];
-          const float khat_ = k4[rr] * rk4[rr];
-          dqo[r * ts + kk] = from_f<TI>(rqs[r] * (aq[jm][rr] - qbar * qd));
-          dko[r * ts + kk] = from_f<TI>(rk[r] * (ak[jm][rr] - khat_ * kd));
-        }
+        const float qd = rsum[0][r], kd = rsum[1][r];
+        const float qbar = q4[rr] * rq4[rr];
+        const float khat_ = k4[rr] * rk4[rr];
+        vq[rr] = rqs[r] * (aq[jm][rr] - qbar * qd);
+        vk[rr] = rk[r] * (ak[jm][rr] - khat_ * kd);
+      }
+      // lane i = 4a + c then holds row r0 + c of channels 16 kb + 4a .. + 3:
+      // one 4-element store per output instead of four scattered elements
+      vq = quad_transpose(vq);
+      vk = quad_transpose(vk);
+      const int r = r0 + (i & 3), c0 = 16 * kb + (i & ~3);
+      if (r < L.len) {
+        store4<TI>(dqo + r * ts + c0, vq);
+        store4<TI>(dko + r * ts + c0, vk);
       }
     }
     // draw_g over the raw gate: each element is read and rewritten by the
@@ -999,18 +1008,18 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       }
     }
     if constexpr (G2) {
-      // draw_b [T][H][K] from the per-channel accumulators (16 lanes write
-      // 16 consecutive channels of a row)
+      // draw_b [T][H][K] from the per-channel accumulators
       TI* dbo = dbeta + L.t0 * ts + hoff;
 #pragma unroll
       for (int jm = 0; jm < MR; ++jm) {
         const int m = row_block(jm);
         if (m >= NB) break;
+        f32x4 vb;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = 16 * m + 4 * g + rr;
-          if (r < L.len) dbo[r * ts + kk] = from_f<TI>(ab[jm][rr]);
-        }
+        for (int rr = 0; rr < 4; ++rr) vb[rr] = ab[jm][rr];
+        vb = quad_transpose(vb);  // as dq above
+        const int r = 16 * m + 4 * g + (i & 3);
+        if (r < L.len) store4<TI>(dbo + r * ts + 16 * kb + (i & ~3), vb);
       }
     }
   }

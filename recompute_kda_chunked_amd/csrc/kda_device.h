@@ -106,6 +106,25 @@ __device__ __forceinline__ void halving_level(float (&a)[16], int l) {
     }
   }
 }
+// 4x4 transpose within each quad of lanes (lanes 4a .. 4a + 3): lane c of a
+// quad holds x[0..3] on entry and, on return, at index k what lane k held
+// at index c. Two block-swap steps, with the partner lane c ^ 1 and then
+// c ^ 2 (quad_perm [1,0,3,2] and [2,3,0,1]): at index r a lane takes the
+// partner's value at index r ^ b where bit b of r and of c differ.
+template <int CTRL, int B>
+__device__ __forceinline__ f32x4 quad_swap_step(const f32x4& x, int c) {
+  f32x4 t, y;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) t[r] = dpp_mov<CTRL>(x[r]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) y[r] = ((r & B) != (c & B)) ? t[r ^ B] : x[r];
+  return y;
+}
+__device__ __forceinline__ f32x4 quad_transpose(const f32x4& x) {
+  const int c = static_cast<int>(threadIdx.x) & 3;
+  return quad_swap_step<0x4E, 2>(quad_swap_step<0xB1, 1>(x, c), c);
+}
+
 template <int N>
 __device__ __forceinline__ float transpose_sum16(const float (&v)[N]) {
   static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "values per lane");
