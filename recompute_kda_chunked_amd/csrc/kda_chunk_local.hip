@@ -166,32 +166,66 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   // ---- gated products P (= Akk / beta) and Aqk, 16x16 block pairs. Wave w
   // takes pairs w, w + 4, ...; the raw rows of its next pair are loaded while
   // the current one is computed (two register sets), and those of its first
-  // pair while the cumulative sum runs.
+  // pair while the cumulative sum runs. With four row blocks the pairs are
+  // numbered so that a wave's pairs share rows: wave 0 takes (3,0), (3,1),
+  // (3,2), wave 1 the diagonal (1,1), (2,2), (3,3), wave 2 (2,0), (2,1) and
+  // wave 3 (0,0), (1,0); rows the wave already holds are copied, not loaded
+  // again (76 KB of row loads per chunk-head instead of 120 KB).
   constexpr int NPAIR = NB * (NB + 1) / 2, PPW = (NPAIR + 3) / 4, NKS = K / KS;
   struct PairRows {
     typename M::frag xa[NKS], xk[NKS], xb[NKS];
     typename M::frag xe[G2 ? NKS : 1];  // GDN-2: raw erase gate of the row-side rows
   };
   auto pair_blocks = [](int p, int& I, int& J) {
-    I = 0;
-    J = p;
-    while (J > I) { J -= I + 1; ++I; }
+    if constexpr (NB == 4) {
+      // 4 bits per pair: I = {3,1,2,0,3,2,2,1,3,3}, J = {0,1,0,0,1,2,1,0,2,3}
+      I = static_cast<int>((0x3312230213ull >> (4 * p)) & 15);
+      J = static_cast<int>((0x3201210010ull >> (4 * p)) & 15);
+    } else {
+      I = 0;
+      J = p;
+      while (J > I) { J -= I + 1; ++I; }
+    }
   };
   // Rows past the chunk's end read the last valid row (their scales rqs / rk
-  // are zero); a pair index past the last pair loads the last pair again
-  // (unused), so the loads are unconditional.
-  auto load_pair = [&](PairRows& f, int p) {
-    int I, J;
-    pair_blocks(p < NPAIR ? p : NPAIR - 1, I, J);
+  // are zero). prev holds pair pp (the wave's previous pair, or pp < 0):
+  // its row side is reused when the row block is the same, and the column
+  // side's k rows come from the row side (a diagonal pair) or from prev.
+  auto load_pair = [&](PairRows& f, int p, const PairRows& prev, int pp) {
+    if (p >= NPAIR) return;
+    int I, J, Ip = -1, Jp = -1;
+    pair_blocks(p, I, J);
+    if (pp >= 0 && pp < NPAIR) pair_blocks(pp, Ip, Jp);
     const int ra = 16 * I + i, rb = 16 * J + i;
     const int rac = ra < L.len ? ra : L.len - 1, rbc = rb < L.len ? rb : L.len - 1;
+    if (Ip == I) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int kk = ks * KS + g * KPL;
-      if (!STATE) f.xa[ks] = M::load(qr + rac * ts + kk);
-      f.xk[ks] = M::load(kr + rac * ts + kk);
-      f.xb[ks] = M::load(kr + rbc * ts + kk);
-      if constexpr (G2) f.xe[ks] = M::load(bkr + rac * ts + kk);
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (!STATE) f.xa[ks] = prev.xa[ks];
+        f.xk[ks] = prev.xk[ks];
+        if constexpr (G2) f.xe[ks] = prev.xe[ks];
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int kk = ks * KS + g * KPL;
+        if (!STATE) f.xa[ks] = M::load(qr + rac * ts + kk);
+        f.xk[ks] = M::load(kr + rac * ts + kk);
+        if constexpr (G2) f.xe[ks] = M::load(bkr + rac * ts + kk);
+      }
+    }
+    if (J == I) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) f.xb[ks] = f.xk[ks];
+    } else if (J == Jp) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) f.xb[ks] = prev.xb[ks];
+    } else if (J == Ip) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) f.xb[ks] = prev.xk[ks];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) f.xb[ks] = M::load(kr + rbc * ts + ks * KS + g * KPL);
     }
   };
   // forward layout of a bf16 problem: Aqk as a bf16 pair (see do_pair, store_aqk)
@@ -346,7 +380,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
 
   PairRows pa, pb;
   f32x4 aqv[PPW];
-  load_pair(pa, w);
+  load_pair(pa, w, pb, -1);
   __syncthreads();
   cumsum_rows<D, C, 256>(G, ptot);
 #pragma unroll
@@ -354,7 +388,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     const int p = w + 4 * it;
     PairRows& cur = (it & 1) ? pb : pa;
     PairRows& nxt = (it & 1) ? pa : pb;
-    if (it + 1 < PPW) load_pair(nxt, p + 4);
+    if (it + 1 < PPW) load_pair(nxt, p + 4, cur, p);
     else if (!BWD) load_items();
     aqv[it] = zero4();
     if (p < NPAIR) do_pair(cur, p, aqv[it]);
