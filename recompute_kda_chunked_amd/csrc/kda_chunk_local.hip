@@ -633,7 +633,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
         if constexpr (BWD) {
           store4_fm<OpT, true>(static_cast<OpT*>(ops.U) + idx * C * V, 16 * n + i, 16 * mk + 4 * g, V, accu[n]);
         } else {
-          // fp32, row-major: accu[n][rr] = U[16n + i][16mk + 4g + rr]
+          // fp32 in 16x16 blocks (ChunkOps::Uf): accu[n][rr] = U[16n + i][16mk + 4g + rr]
           f32x4 u = accu[n];
           if constexpr (UFIX) {
             const int r = 16 * n + i;
@@ -652,7 +652,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
               u[rr] += bv - to_f(from_f<OpT>(bv));
             }
           }
-          vstore<true>(reinterpret_cast<f32x4*>(ops.Uf + idx * C * V + (16 * n + i) * V + 16 * mk + 4 * g), u);
+          vstore<true>(reinterpret_cast<f32x4*>(ops.Uf + idx * C * V + (n * (V / 16) + mk) * 256 + i * 16 + 4 * g), u);
         }
       }
     }

@@ -72,7 +72,9 @@ struct CarryMap {
 struct ChunkOps {
   void *Wn;    // [C][K]  -W  (W = T (beta * kh * e^G))
   void *U;     // [C][V]  U = T (beta * v)                (backward only)
-  float *Uf;   // [C][V]  U in fp32, row-major            (forward only)
+  float *Uf;   // [C][V]  U in fp32, 16x16 blocks (forward only): element (r, c) at
+               //   ((r/16) (V/16) + c/16) 256 + (r%16) 16 + c%16, so a wave's
+               //   16 rows x 4 columns per lane are one contiguous 1 KB run
   void *qg;    // [C][K]  qh * e^G                       (forward only)
   void *kgT;   // [K][C]  (kh * e^{G_c - G})^T
   void *Aqk;   // [C][C]  gated q.k, lower incl. diagonal (forward only)

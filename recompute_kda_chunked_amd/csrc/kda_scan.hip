@@ -140,9 +140,10 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
 #pragma unroll
       for (int nv = 0; nv < G::BVT; ++nv) load4_fm_raw<OpT>(U, 16 * m + i, v0 + 16 * nv + 4 * g, V, f.u[nv]);
     } else {
-      const float* U = ops.Uf + idx * C * V + (16 * m + i) * V + v0 + 4 * g;
+      // fp32 U in 16x16 blocks (ChunkOps::Uf): block (m, v0/16 + nv), row i, columns 4g ..
+      const float* U = ops.Uf + idx * C * V + (m * (V / 16) + v0 / 16) * 256 + i * 16 + 4 * g;
 #pragma unroll
-      for (int nv = 0; nv < G::BVT; ++nv) load4_raw<float>(U + 16 * nv, f.u[nv]);
+      for (int nv = 0; nv < G::BVT; ++nv) load4_raw<float>(U + 256 * nv, f.u[nv]);
     }
   }
   if (OUT_O && (PART < 0 || PART == 1)) {
