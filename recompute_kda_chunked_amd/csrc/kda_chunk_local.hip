@@ -463,9 +463,9 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
           out[j] = BWD ? kg : from_f<OpT>(qg);
         }
         if (!STATE) {
-          // fragment-major [C][K]: the VE channels are one lane slot (bf16)
-          // or VE slots 16 apart (fp32)
-          OpT* dst = rowm + FragMajor<OpT>::off(r, c0, K);
+          // fragment-major [C][K] in row-parity order (FragMajor::pslot): the
+          // VE channels are one lane slot (bf16) or VE slots 16 apart (fp32)
+          OpT* dst = rowm + FragMajor<OpT>::off_p(r, c0, K);
           if constexpr (VE == KPL) {
             vstore<true>(reinterpret_cast<VT*>(dst), out);
           } else {

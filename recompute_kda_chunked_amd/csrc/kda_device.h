@@ -267,6 +267,25 @@ struct FragMajor {
   // elements (r, s0 .. s0 + 3), s0 a multiple of 4: contiguous for bf16
   // (within one slot), 16 slots apart for fp32
   static constexpr int kStep4 = M::KPL >= 4 ? 1 : 16;
+  // Row-parity order (bf16): within each fragment the slot of (row i, piece
+  // g) is placed at ((i >> 3) * 2 + (i & 1)) * 16 + ((i >> 1) & 3) * 4 + g,
+  // so that four rows of one parity with all their pieces fill 256
+  // contiguous bytes. A reader still covers one whole fragment per wave; a
+  // writer holding rows 2p + h (h fixed per store) writes whole lines. fp32
+  // fragments keep the plain order.
+  static __device__ __forceinline__ int pslot(int i, int g) {
+    if constexpr (M::KPL >= 4) return (((i >> 3) << 1) + (i & 1)) * 16 + ((i >> 1) & 3) * 4 + g;
+    else return i + 16 * g;
+  }
+  static __device__ __forceinline__ int off_p(int r, int s, int S) {
+    if constexpr (M::KPL >= 4)
+      return (((r >> 4) * (S / M::KS) + s / M::KS) * 64 + pslot(r & 15, (s % M::KS) / M::KPL)) * M::KPL +
+             s % M::KPL;
+    else return off(r, s, S);
+  }
+  static __device__ __forceinline__ int frag_p(int rb, int sf, int S, int lane) {
+    return ((rb * (S / M::KS) + sf) * 64 + pslot(lane & 15, lane >> 4)) * M::KPL;
+  }
 };
 
 template <typename OpT, bool NT = false>

@@ -149,7 +149,7 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
   if (OUT_O && (PART < 0 || PART == 1)) {
     const OpT* qg = static_cast<const OpT*>(ops.qg) + idx * C * K;
 #pragma unroll
-    for (int j = 0; j < G::NKF; ++j) f.q[j] = M::load(qg + FM::frag(m, j, K, lane));
+    for (int j = 0; j < G::NKF; ++j) f.q[j] = M::load(qg + FM::frag_p(m, j, K, lane));  // row-parity order
     const OpT* aq = static_cast<const OpT*>(ops.Aqk) + idx * C * C;
 #pragma unroll
     for (int j = 0; j < G::NCF; ++j) f.a[j] = M::load(aq + FM::frag(m, j, C, lane));
@@ -397,7 +397,7 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
     for (int j = 0; j < G::NCF; ++j) f.at[j] = M::load(at + FM::frag(m, j, C, lane));
     const OpT* kg = static_cast<const OpT*>(ops.kg) + idx * C * K;
 #pragma unroll
-    for (int j = 0; j < G::NKF; ++j) f.kg[j] = M::load(kg + FM::frag(m, j, K, lane));
+    for (int j = 0; j < G::NKF; ++j) f.kg[j] = M::load(kg + FM::frag_p(m, j, K, lane));  // row-parity order
   }
   if (PART < 0 || PART == 2) {
     const OpT* qgT = static_cast<const OpT*>(ops.qgT) + idx * K * C;
