@@ -415,9 +415,18 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     {
       if (BWD) {
         // P^T, so that the gradient kernel reads a lane's four rows of one
-        // column as one vector
+        // column as one vector; each thread writes 16-byte pieces of its rows
         OpT* PT = static_cast<OpT*>(ops.PT) + idx * C * C;
-        for (int e = tid; e < C * C; e += 256) PT[e] = from_f<OpT>(Ms[(e % C) * LDM + e / C]);
+        constexpr int PV = 16 / (int)sizeof(OpT);  // elements per piece
+        static_assert(C % PV == 0, "P^T rows split into 16-byte pieces");
+        for (int e = tid; e < C * C / PV; e += 256) {
+          const int a = e / (C / PV), b0 = (e % (C / PV)) * PV;  // P^T[a][b0 ..] = P[b0 ..][a]
+          typedef std::conditional_t<sizeof(OpT) == 2, bf16x8, f32x4> PVec;
+          PVec v;
+#pragma unroll
+          for (int j = 0; j < PV; ++j) v[j] = from_f<OpT>(Ms[(b0 + j) * LDM + a]);
+          *reinterpret_cast<PVec*>(PT + a * C + b0) = v;
+        }
       }
       float* gam = ops.gam + idx * K;
       for (int kk = tid; kk < K; kk += 256) gam[kk] = GU::ex(Gs[(C - 1) * LDG + kk]);
