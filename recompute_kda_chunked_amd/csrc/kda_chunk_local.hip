@@ -561,10 +561,12 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     }
     __syncthreads();
   }
-  // operand copy of T (overwrites P), and T^T for the backward
-  for (int e = tid; e < C * C; e += 256) {
-    const int r = e / C, s = e % C;
-    Tb[r * LDT + s] = from_f<OpT>(Ts[r * LDM + s]);
+  // operand copy of T (overwrites P), four elements per thread and step,
+  // and T^T for the backward
+  static_assert(LDM % 4 == 0 && LDT % 4 == 0, "T rows copy in 4-element pieces");
+  for (int e = tid; e < C * C / 4; e += 256) {
+    const int r = e / (C / 4), s = (e % (C / 4)) * 4;
+    store4<OpT>(Tb + r * LDT + s, *reinterpret_cast<const f32x4*>(Ts + r * LDM + s));
   }
   if (BWD) {
     // T^T, fragment-major, one lane slot per thread
