@@ -245,6 +245,24 @@ __device__ __forceinline__ void store4(T* p, const f32x4& v) {
   }
 }
 
+// Four values as 32-bit words of the storage type, rounded as store4 rounds
+// them (bf16: two words, the lower-addressed value in the low half; fp32:
+// four words).
+template <typename T>
+__device__ __forceinline__ void pack4(const f32x4& v, uint32_t (&w)[sizeof(T) == 2 ? 2 : 4]) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 b;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) b[rr] = static_cast<bf16>(v[rr]);
+    const uint2 u = __builtin_bit_cast(uint2, b);
+    w[0] = u.x;
+    w[1] = u.y;
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) w[rr] = __float_as_uint(v[rr]);
+  }
+}
+
 // Fragment-major operand arrays. An [R][S] matrix that is read as MFMA
 // operand fragments (rows in blocks of 16, the reduction dimension S in
 // pieces of KS) is stored one fragment after another: fragment (rb, sf) is

@@ -323,7 +323,38 @@ __global__ void __launch_bounds__(256) k_scan_fwd(Dims d, Inputs in, Seg sgm, Ch
             }
           }
         // accO[nv][rr] = O[r][v0 + 16nv + 4g + rr]
-        if (r < len) store4<TI>(o + (t0 + r) * ts + static_cast<size_t>(h) * V + v0 + 16 * nv + 4 * g, accO[nv]);
+        if constexpr (BVT % 2 != 0)
+          if (r < len) store4<TI>(o + (t0 + r) * ts + static_cast<size_t>(h) * V + v0 + 16 * nv + 4 * g, accO[nv]);
+      }
+      if constexpr (BVT % 2 == 0) {
+        // Pairs of value blocks leave as 8 contiguous columns per lane: two
+        // lane swaps (upper 32 lanes of the first block with the lower 32 of
+        // the second, then odd 16-lane rows of the first with even rows of
+        // the second) give the lanes of row group g columns 8g .. 8g + 7 of
+        // the pair, so a row's 32 columns are one 64-byte run.
+        constexpr int NWD = sizeof(TI) == 2 ? 2 : 4;  // 32-bit words per four values
+#pragma unroll
+        for (int nv = 0; nv < BVT; nv += 2) {
+          uint32_t x[NWD], y[NWD];
+          pack4<TI>(accO[nv], x);
+          pack4<TI>(accO[nv + 1], y);
+#pragma unroll
+          for (int k = 0; k < NWD; ++k) {
+            const auto a = __builtin_amdgcn_permlane32_swap(x[k], y[k], false, false);
+            const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[1], false, false);
+            x[k] = b[0];
+            y[k] = b[1];
+          }
+          if (r < len) {
+            TI* dst = o + (t0 + r) * ts + static_cast<size_t>(h) * V + v0 + 16 * nv + 8 * g;
+            if constexpr (NWD == 2) {
+              *reinterpret_cast<uint4*>(dst) = make_uint4(x[0], x[1], y[0], y[1]);
+            } else {
+              *reinterpret_cast<uint4*>(dst) = make_uint4(x[0], x[1], x[2], x[3]);
+              *reinterpret_cast<uint4*>(dst + 4) = make_uint4(y[0], y[1], y[2], y[3]);
+            }
+          }
+        }
       }
     }
     load_fwd_ops<OpT, D, C, BV, OUT_O, REC, 2>(fill, ops, idx2, v0, w, i, g);
