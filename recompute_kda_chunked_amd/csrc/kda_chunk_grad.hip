@@ -62,7 +62,8 @@ struct Vjp<bf16> {
   template <class F>
   static __device__ __forceinline__ frag make(F f) { return Mma<bf16>::make(f); }
   static __device__ __forceinline__ T rnd(T x) { return to_f(static_cast<bf16>(x)); }
-  static __device__ __forceinline__ T ex(T x) { return __expf(x); }
+  // of a difference of cumulative gates, kept in base-2 units (GateUnits)
+  static __device__ __forceinline__ T ex(T x) { return __builtin_amdgcn_exp2f(x); }
   static __device__ __forceinline__ T sig(T x) { return sigmoidf(x); }
   static __device__ __forceinline__ acc fix(acc x) { return x; }
 };
@@ -240,7 +241,9 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // would stall before its first arithmetic.
   // ---- S1: prologue, transposed raw q/k, cumulative gate G^T
   auto Gf = [&](int r, int kk_) -> GV& { return GT[kk_ * LDG + (r ^ swz(kk_))]; };
-  prologue_compute<TI, D, C, NW>(d, L, pr, rq, rqs, rk, be, Gf);
+  // G^T in GateUnits (base 2 for bf16: every exponential below is of G or of a
+  // difference of G values, and takes a single v_exp_f32)
+  prologue_compute<TI, D, C, NW>(d, L, pr, rq, rqs, rk, be, Gf, static_cast<GV>(GateUnits<OpT>::scale));
   {
     const OpT* dVnT = static_cast<const OpT*>(st.dVnT) + idx * V * C;
     const OpT* TT = static_cast<const OpT*>(ops.TT) + idx * C * C;
@@ -453,7 +456,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       for (int rr = 0; rr < 4; ++rr) {
         const int r = r0 + rr;
         const GV Gv = G4[rr];
-        const float eG = kexp<OpT>(Gv), eGc = kexp<OpT>(Gc - Gv);
+        const float eG = GateUnits<OpT>::ex(Gv), eGc = GateUnits<OpT>::ex(Gc - Gv);
         const float qh = q4[rr] * rqs4[rr];
         const float kh = k4[rr] * rk4[rr];
         const float dqg = rQg[rr], dkg = rKg[rr], dKb = -rKb[rr];
@@ -806,7 +809,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       TG cs = 0;
 #pragma unroll
       for (int hh = 0; hh < SPLIT; ++hh) cs += csum[hh][kb][i];
-      aG[jm][3] += cs + static_cast<TG>(kexp<OpT>(Gc)) * hdh;
+      aG[jm][3] += cs + static_cast<TG>(GateUnits<OpT>::ex(Gc)) * hdh;
     }
   }
   {

@@ -35,19 +35,10 @@ struct GateT<float> {
   typedef double T;
 };
 
-template <typename OpT>
-__device__ __forceinline__ float kexp(typename GateT<OpT>::T x);
-// fp32 problems: the fp64 exponential, rounded once; bf16 problems: the
-// hardware base-2 exponential (v_exp_f32) with a change of base.
-template <>
-__device__ __forceinline__ float kexp<float>(double x) { return static_cast<float>(exp(x)); }
-template <>
-__device__ __forceinline__ float kexp<bf16>(float x) { return __expf(x); }
-
-// Units of the chunk-local kernel's cumulative gate. bf16 problems keep it in
-// base-2 units (G log2 e, summed from g log2 e), so each exponential of a
-// gate difference is a single v_exp_f32; fp32 problems keep natural units in
-// fp64 (see GateT).
+// Units of the cumulative gate in the chunk-local and gradient kernels. bf16
+// problems keep it in base-2 units (G log2 e, summed from g log2 e), so each
+// exponential of a gate difference is a single v_exp_f32; fp32 problems keep
+// natural units in fp64 (see GateT).
 template <typename OpT>
 struct GateUnits {
   static constexpr float scale = 1.4426950408889634f;
