@@ -490,6 +490,20 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
 
   // ---- S5: dAqk and dAkk, lower 16x16 blocks (m rows, ns columns)
   constexpr int NPAIR = NB * (NB + 1) / 2, PPW = (NPAIR + NW - 1) / NW;
+  // Pair p of wave w is p = w + NW jp. With four row blocks and eight waves
+  // only waves 0 and 1 take two pairs; they get (0,0), (1,0) and (2,0), (3,0),
+  // whose U and W rows (block ns = 0) they load once.
+  auto s5_pair = [](int p, int& m, int& ns) {
+    if constexpr (NB == 4 && NW == 8) {
+      // m = {0,2,1,2,3,2,3,3,1,3}, ns = {0,0,1,1,1,2,2,3,0,0}, 4 bits per pair
+      m = static_cast<int>((0x3133232120ull >> (4 * p)) & 15);
+      ns = static_cast<int>((0x32211100ull >> (4 * p)) & 15);
+    } else {
+      m = 0;
+      ns = p;
+      while (ns > m) { ns -= m + 1; ++m; }
+    }
+  };
   f32x4 xq[PPW], xk[PPW];
   // GDN-2: the erase gate rows, requested now and transposed into LDS for S6
   VT braw[G2 ? VPT : 1];
@@ -509,6 +523,9 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     static_assert(PPW == 1 || PPW == 2 || PPW == 4, "pairs per wave");
     float vb[4 * PPW];
     int pm[PPW];
+    constexpr int NKV = V / KS;
+    typename M::frag fu[NKV], fw[NKV];  // U and -W rows of block ns (kept while ns repeats)
+    int ns_held = -1;
 #pragma unroll
     for (int jp = 0; jp < PPW; ++jp) {
       const int p = w + NW * jp;
@@ -517,17 +534,18 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       for (int rr = 0; rr < 4; ++rr) vb[4 * jp + rr] = 0.f;
       pm[jp] = -1;
       if (p >= NPAIR) continue;
-      int m = 0, ns = p;
-      while (ns > m) { ns -= m + 1; ++m; }
+      int m, ns;
+      s5_pair(p, m, ns);
       pm[jp] = m;
       // global operands of this pair first (U and -W rows of block ns, P^T)
-      constexpr int NKV = V / KS;
-      typename M::frag fu[NKV], fw[NKV];
       uint32_t pv[4];  // raw: converted at use
+      if (ns != ns_held) {
 #pragma unroll
-      for (int j = 0; j < NKV; ++j) {
-        fu[j] = M::load(Ug + FragMajor<OpT>::frag(ns, j, V, lane));  // both fragment-major
-        fw[j] = M::load(Wng + FragMajor<OpT>::frag(ns, j, K, lane));
+        for (int j = 0; j < NKV; ++j) {
+          fu[j] = M::load(Ug + FragMajor<OpT>::frag(ns, j, V, lane));  // both fragment-major
+          fw[j] = M::load(Wng + FragMajor<OpT>::frag(ns, j, K, lane));
+        }
+        ns_held = ns;
       }
       load4_raw<OpT>(PTg + (16 * ns + i) * C + 16 * m + 4 * g, pv);  // P[16m + 4g + rr][16ns + i]
       const f32x4 aqk = tile_nt<OpT>(zero4(), dO_s + 16 * m * LDA, LDA, Vn_s + 16 * ns * LDA, LDA, 0, V, lane);
@@ -571,8 +589,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   for (int jp = 0; jp < PPW; ++jp) {
     const int p = w + NW * jp;
     if (p >= NPAIR) break;
-    int m = 0, ns = p;
-    while (ns > m) { ns -= m + 1; ++m; }
+    int m, ns;
+    s5_pair(p, m, ns);
     const int s_ = 16 * ns + i, r0 = 16 * m + 4 * g;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
