@@ -78,9 +78,6 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Sum over the 16 lanes that share g (the lanes of one tile row group).
-__device__ __forceinline__ float sum16(float x) { return group_sum<16>(x); }
-
 // N sums at once over each aligned group of 16 lanes (N = 1, 2, 4, 8 or 16
 // values per lane): on return lane l holds its group's sum of v[l % N].
 // Partners are taken in turn across the row mirror, the half-row mirror and

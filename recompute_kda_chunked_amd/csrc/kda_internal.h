@@ -65,7 +65,8 @@ struct CarryMap {
 // the chunk index relative to the segment start. Operand element type is
 // bf16 for bf16 problems and fp32 for fp32 problems. Wn, U, qg, kgT, Aqk,
 // Aqk_lo, AqkT, kg, qgT, WnT and TT are stored fragment-major (FragMajor in
-// kda_device.h); PT and Uf are row-major. The forward layout keeps U in fp32
+// kda_device.h; qg and kg in its row-parity slot order); PT is row-major and
+// Uf in 16x16 blocks (see Uf). The forward layout keeps U in fp32
 // and Aqk as a bf16 pair (Aqk + Aqk_lo) because the output takes them
 // directly: rounding either to bf16 would add a bf16 rounding's worth of
 // error to O.
