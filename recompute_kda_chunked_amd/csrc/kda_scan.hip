@@ -151,12 +151,16 @@ __device__ __forceinline__ void load_fwd_ops(FwdOps<OpT, D, C, BV>& f, const Chu
 #pragma unroll
     for (int j = 0; j < G::NKF; ++j) f.q[j] = M::load(qg + FM::frag_p(m, j, K, lane));  // row-parity order
     const OpT* aq = static_cast<const OpT*>(ops.Aqk) + idx * C * C;
+    // Aqk[r][s] = 0 for s > r: fragments past the wave's diagonal are never
+    // used, and load the last used one again (lines already in flight, so no
+    // new misses; the loads stay unconditional)
+    const int nf = (16 * (m + 1) + G::M::KS - 1) / G::M::KS;
 #pragma unroll
-    for (int j = 0; j < G::NCF; ++j) f.a[j] = M::load(aq + FM::frag(m, j, C, lane));
+    for (int j = 0; j < G::NCF; ++j) f.a[j] = M::load(aq + FM::frag(m, j < nf ? j : nf - 1, C, lane));
     if constexpr (sizeof(OpT) == 2) {
       const OpT* al = static_cast<const OpT*>(ops.Aqk_lo) + idx * C * C;
 #pragma unroll
-      for (int j = 0; j < G::NCF; ++j) f.al[j] = M::load(al + FM::frag(m, j, C, lane));
+      for (int j = 0; j < G::NCF; ++j) f.al[j] = M::load(al + FM::frag(m, j < nf ? j : nf - 1, C, lane));
     }
   }
   if (PART < 0 || PART == 2) {
@@ -424,8 +428,9 @@ __device__ __forceinline__ void load_bwd_ops(BwdOps<TI, OpT, D, C, BV>& f, const
   if (PART < 0 || PART == 1) {
     const int m = w < G::NB ? w : G::NB - 1;  // unconditional, as in the forward
     const OpT* at = static_cast<const OpT*>(ops.AqkT) + idx * C * C;
+    const int f_lo = (16 * m) / G::M::KS;  // Aqk^T[r][s] = 0 for s < r: unused fragments re-load f_lo
 #pragma unroll
-    for (int j = 0; j < G::NCF; ++j) f.at[j] = M::load(at + FM::frag(m, j, C, lane));
+    for (int j = 0; j < G::NCF; ++j) f.at[j] = M::load(at + FM::frag(m, j < f_lo ? f_lo : j, C, lane));
     const OpT* kg = static_cast<const OpT*>(ops.kg) + idx * C * K;
 #pragma unroll
     for (int j = 0; j < G::NKF; ++j) f.kg[j] = M::load(kg + FM::frag_p(m, j, K, lane));  // row-parity order
