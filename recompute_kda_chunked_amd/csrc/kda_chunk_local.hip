@@ -310,7 +310,8 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   };
   // Aqk (forward) or Aqk^T (backward), fragment-major: the tiles of the
   // wave's pairs, and zeros in the blocks above (Aqk) or below (Aqk^T) the
-  // diagonal, which the scans read as parts of whole fragments. The forward
+  // diagonal that share a fragment with entries the scans use (the scans
+  // load no fragment that lies wholly in the zero triangle). The forward
   // layout of a bf16 problem also stores what rounding Aqk to bf16 dropped
   // (Aqk_lo), so that the output's intra-chunk product sees Aqk to about
   // 2^-17 of its value.
@@ -339,6 +340,10 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     for (int zb = w; zb < NB * (NB - 1) / 2; zb += 4) {
       int I = 1, J = zb;  // zb-th block pair with J < I
       while (J >= I) { J -= I; ++I; }
+      // only blocks inside a fragment that a scan wave loads (one that also
+      // holds its row block's triangle); the others are never read
+      const bool read = BWD ? (16 * J) / KS >= (16 * I) / KS : (16 * I) / KS < (16 * (J + 1) + KS - 1) / KS;
+      if (!read) continue;
       if (BWD) {
         store4_fm<OpT, true>(dst, 16 * I + i, 16 * J + 4 * g, C, zero4());
       } else {
