@@ -225,6 +225,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // the same fragments from global memory would pass 8x its bytes through
   // the CU's address unit. One 16-byte piece per thread.
   constexpr int NTT = C * C * (int)sizeof(OpT) / 16, TTPT = (NTT + NT - 1) / NT;
+  constexpr int TT_PPF = 64 * KPL * (int)sizeof(OpT) / 16;  // 16-byte pieces per fragment
   uint4 ttv[TTPT];
   static_assert(C <= LDA && C * LDA * (int)sizeof(OpT) % 16 == 0, "T^T fits the dKb_s region");
   uint32_t vin[TPW][4];
@@ -249,8 +250,12 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
     const OpT* TT = static_cast<const OpT*>(ops.TT) + idx * C * C;
 #pragma unroll
     for (int j = 0; j < TTPT; ++j) {
-      const int e = tid + NT * j;
-      ttv[j] = reinterpret_cast<const uint4*>(TT)[e < NTT ? e : 0];
+      // zero fragments (never written) are skipped where a fragment is one
+      // wave's pieces, so the test is uniform across the wave; otherwise
+      // (fp32) everything is copied and the zero fragments go unused
+      const int e = tid + NT * j, blk = (e < NTT ? e : 0) / TT_PPF;
+      if (TT_PPF < 64 || tt_frag_nonzero<OpT>(blk / (C / KS), blk % (C / KS)))
+        ttv[j] = reinterpret_cast<const uint4*>(TT)[e < NTT ? e : 0];
     }
     {
       const int t = w * TPW < T2 ? w * TPW : 0, mv = t / NB;
@@ -294,8 +299,9 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   for (int e = tid; e < 2 * NKB * C; e += NT) (&rowp[0][0][0])[e] = 0.f;
 #pragma unroll
   for (int j = 0; j < TTPT; ++j) {
-    const int e = tid + NT * j;
-    if (e < NTT) reinterpret_cast<uint4*>(dKb_s)[e] = ttv[j];
+    const int e = tid + NT * j, blk = e / TT_PPF;
+    if (e < NTT && (TT_PPF < 64 || tt_frag_nonzero<OpT>(blk / (C / KS), blk % (C / KS))))
+      reinterpret_cast<uint4*>(dKb_s)[e] = ttv[j];
   }
   __syncthreads();
   cumsum_rows<D, C, NT>(Gf, ptot);
@@ -331,7 +337,8 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
       f32x4 acc = zero4();
       // the whole reduction is taken (T^T[r][s] is stored as 0 for s < r)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) acc = M::mma(fa[ks], M::load(dKb_s + FM::frag(nr, ks, C, lane)), acc);
+      for (int ks = 0; ks < NKS; ++ks)
+        if (tt_frag_nonzero<OpT>(nr, ks)) acc = M::mma(fa[ks], M::load(dKb_s + FM::frag(nr, ks, C, lane)), acc);
       OpT* dst = dBv_s + r * LDA + vv;
       float part = 0.f;
       const f32x4 vv4 = unpack4<TI>(vin[jt]);

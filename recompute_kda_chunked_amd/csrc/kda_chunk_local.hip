@@ -420,12 +420,16 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     {
       if (BWD) {
         // P^T, so that the gradient kernel reads a lane's four rows of one
-        // column as one vector; each thread writes 16-byte pieces of its rows
+        // column as one vector; each thread writes 16-byte pieces of its rows.
+        // P is strictly lower triangular: 16x16 blocks of P^T below the block
+        // diagonal are zero and are not written (the gradient kernel reads
+        // only blocks (ns, m) with ns <= m).
         OpT* PT = static_cast<OpT*>(ops.PT) + idx * C * C;
         constexpr int PV = 16 / (int)sizeof(OpT);  // elements per piece
-        static_assert(C % PV == 0, "P^T rows split into 16-byte pieces");
+        static_assert(C % PV == 0 && 16 % PV == 0, "P^T rows split into 16-byte pieces");
         for (int e = tid; e < C * C / PV; e += 256) {
           const int a = e / (C / PV), b0 = (e % (C / PV)) * PV;  // P^T[a][b0 ..] = P[b0 ..][a]
+          if (a / 16 > b0 / 16) continue;
           typedef std::conditional_t<sizeof(OpT) == 2, bf16x8, f32x4> PVec;
           PVec v;
 #pragma unroll
@@ -574,11 +578,14 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     store4<OpT>(Tb + r * LDT + s, *reinterpret_cast<const f32x4*>(Ts + r * LDM + s));
   }
   if (BWD) {
-    // T^T, fragment-major, one lane slot per thread
+    // T^T, fragment-major, one lane slot per thread. T is lower triangular,
+    // so fragments wholly left of T^T's diagonal are zero; they are not
+    // written (the gradient kernel skips them: tt_frag_nonzero).
     typedef typename M::frag F;
     F* TT = reinterpret_cast<F*>(static_cast<OpT*>(ops.TT) + idx * C * C);
     for (int e = tid; e < C * C / KPL; e += 256) {
       const int blk = e >> 6, lane = e & 63;
+      if (!tt_frag_nonzero<OpT>(blk / (C / KS), blk % (C / KS))) continue;
       const int a = 16 * (blk / (C / KS)) + (lane & 15), b = KS * (blk % (C / KS)) + KPL * (lane >> 4);
       TT[e] = M::make([&](int j) { return Ts[(b + j) * LDM + a]; });
     }

@@ -324,6 +324,14 @@ __device__ __forceinline__ void load4_fm_raw(const OpT* a, int r, int s0, int S,
   }
 }
 
+// Whether fragment (row block rb, reduction piece sf) of the fragment-major
+// T^T (T lower triangular, so T^T[r][s] = 0 for s < r) holds a nonzero:
+// its last column reaches the block's first row.
+template <typename OpT>
+__device__ __forceinline__ bool tt_frag_nonzero(int rb, int sf) {
+  return Mma<OpT>::KS * (sf + 1) > 16 * rb;
+}
+
 // acc += sum_{kk in [k_lo, k_hi)} A[i][kk] * B[i'][kk] for one 16x16 tile.
 // A and B point at the first row of the tile; lda/ldb are row strides in
 // elements. k_lo and k_hi - k_lo are multiples of Mma<OpT>::KS.
