@@ -638,6 +638,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
         const auto gv = TL::frag(tile1, kk, s0 + g * KPL);
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
+          if (s0 >= 16 * (n + 1)) continue;  // T[16n + i][s] = 0 for s > 16n + 15
           const auto tb = M::load(Tb + (16 * n + i) * LDT + s0 + g * KPL);
           acc[n] = M::mma(gk, tb, acc[n]);              // W^T tile (k rows, r cols)
           if (BWD) acc2[n] = M::mma(tb, gk, acc2[n]);   // W tile (r rows, k cols)
