@@ -297,14 +297,17 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   }
   for (int e = tid; e < NW * C; e += NT) dbp[e / C][e % C] = 0.f;
   for (int e = tid; e < 2 * NKB * C; e += NT) (&rowp[0][0][0])[e] = 0.f;
-#pragma unroll
-  for (int j = 0; j < TTPT; ++j) {
-    const int e = tid + NT * j, blk = e / TT_PPF;
-    if (e < NTT && (TT_PPF < 64 || tt_frag_nonzero<OpT>(blk / (C / KS), blk % (C / KS))))
-      reinterpret_cast<uint4*>(dKb_s)[e] = ttv[j];
-  }
   __syncthreads();
-  cumsum_rows<D, C, NT>(Gf, ptot);
+  // T^T goes to LDS between the cumulative sum's barriers: its loads have had
+  // the prologue and half the sum to arrive
+  cumsum_rows<D, C, NT>(Gf, ptot, [&]() {
+#pragma unroll
+    for (int j = 0; j < TTPT; ++j) {
+      const int e = tid + NT * j, blk = e / TT_PPF;
+      if (e < NTT && (TT_PPF < 64 || tt_frag_nonzero<OpT>(blk / (C / KS), blk % (C / KS))))
+        reinterpret_cast<uint4*>(dKb_s)[e] = ttv[j];
+    }
+  });
   if constexpr (PH) {
     // every channel holds the same cumulative gate; channel 0's column of
     // G^T is stored in row order (its permutation is the identity). Read

@@ -298,8 +298,13 @@ __device__ __forceinline__ void prologue_rows(const Dims& d, const Inputs& in, i
 // In-place inclusive cumulative sum over the C rows of every channel k of
 // G(r, k), by all threads of the block (fixed order, deterministic).
 // part_tot: LDS scratch of at least (blockDim / D) * D values of G's type.
-template <int D, int C, int NT, class GRef, typename PT>
-__device__ __forceinline__ void cumsum_rows(GRef G, PT* part_tot) {
+struct NoMid {
+  __device__ __forceinline__ void operator()() const {}
+};
+// mid() runs between the sum's two barriers (work that may wait for loads
+// and must be ordered before the code after the sum).
+template <int D, int C, int NT, class GRef, typename PT, class Mid = NoMid>
+__device__ __forceinline__ void cumsum_rows(GRef G, PT* part_tot, Mid mid = Mid()) {
   constexpr int parts = NT / D;
   constexpr int rp = C / parts;
   static_assert(NT % D == 0 && C % parts == 0, "cumsum layout");
@@ -318,6 +323,7 @@ __device__ __forceinline__ void cumsum_rows(GRef G, PT* part_tot) {
   }
   part_tot[part * D + col] = run;
   __syncthreads();
+  mid();
   PT off = 0;
   for (int p = 0; p < part; ++p) off += part_tot[p * D + col];
 #pragma unroll
