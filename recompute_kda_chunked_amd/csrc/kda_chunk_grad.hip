@@ -143,7 +143,7 @@ __global__ void __launch_bounds__(D * 4 * grad_split<D>()) k_chunk_grad(Dims d, 
   // cumulative sum and of the partial reductions
   constexpr int OFF_S = 0;
   constexpr int OFF_X = (OFF_S + (int)sizeof(TG) * (NT + 64) + 15) / 16 * 16;
-  static_assert(OFF_X + C * (D + 8) * (int)sizeof(TI) <= SZU, "LDS scratch must fit");
+  static_assert(OFF_X + C * LDA * (int)sizeof(TI) <= SZU, "LDS scratch must fit");
   __shared__ __attribute__((aligned(16))) GV GT[K * LDG];
   __shared__ __attribute__((aligned(16))) TI qT[K * LDQ];
   __shared__ __attribute__((aligned(16))) TI kT[K * LDQ];
