@@ -132,7 +132,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
   // per CU).
   __shared__ __attribute__((aligned(16))) unsigned char regG[SZ_GR > SZ_T ? SZ_GR : SZ_T];
   __shared__ __attribute__((aligned(16))) unsigned char regM[SZ_R];  // P, then Tb
-  __shared__ float rq[C], rqs[C], rk[C], be[C];
+  __shared__ __attribute__((aligned(16))) float rq[C], rqs[C], rk[C], be[C];
   __shared__ GV ptot[256];  // cumulative-sum partials: (256 / D) parts of D channels
   GV* Gs = reinterpret_cast<GV*>(regG);
   OpT* tile0 = reinterpret_cast<OpT*>(regG);
@@ -243,7 +243,11 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
     int I, J;
     pair_blocks(p, I, J);
     const int ra = 16 * I + i, rb = 16 * J + i;
-    const float sq = rqs[ra], sk = rk[ra], sb = rk[rb];
+    // Row-side operands (rows ra, factors exp(G_ra - G_b) <= 1) are formed
+    // without their rows' L2-norm scales, which multiply the products
+    // instead (one per output row); column-side operands keep theirs, since
+    // their factors reach exp(75) on the diagonal blocks.
+    const float sq = rqs[ra], sb = rk[rb];
     f32x4 accP = zero4(), accQ = zero4();
     // per-head gate: the factors of rows ra and rb (every channel alike)
     float ea0 = 0.f, eb0 = 0.f;
@@ -270,7 +274,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
       // the row side of P carries the erase gate under GDN-2 (P = Akk)
       const auto fk = M::make([&](int j) {
         const float e = G2 ? sigmoidf(el(f.xe[ks], j)) : 1.f;
-        return el(f.xk[ks], j) * sk * ea[j] * e;
+        return el(f.xk[ks], j) * ea[j] * e;
       });
       if constexpr (HL) {
         // Aqk of the forward layout from bf16 pairs of both operands (hi hi,
@@ -281,7 +285,7 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
 #pragma unroll
         for (int j = 0; j < KPL; ++j) {
           bq[j] = el(f.xb[ks], j) * sb * eb[j];
-          qv[j] = el(f.xa[ks], j) * sq * ea[j];
+          qv[j] = el(f.xa[ks], j) * ea[j];
         }
         const auto fb = M::make([&](int j) { return bq[j]; });
         const auto fq = M::make([&](int j) { return qv[j]; });
@@ -295,10 +299,20 @@ __global__ void __launch_bounds__(256, 2) k_chunk_local(Dims d, Inputs in, int s
         const auto fb = M::make([&](int j) { return el(f.xb[ks], j) * sb * eb[j]; });
         accP = M::mma(fk, fb, accP);
         if (!STATE) {
-          const auto fq = M::make([&](int j) { return el(f.xa[ks], j) * sq * ea[j]; });
+          const auto fq = M::make([&](int j) { return el(f.xa[ks], j) * ea[j]; });
           accQ = BWD ? M::mma(fq, fb, accQ) : M::mma(fb, fq, accQ);
         }
       }
+    }
+    // the row scales: P's rows 16I + 4g + rr (operand A); Aqk's row-side
+    // operand is B in the forward layout (output column i: row ra) and A in
+    // the backward layout (output row 16I + 4g + rr)
+    const f32x4 sk4 = *reinterpret_cast<const f32x4*>(rk + 16 * I + 4 * g);
+    const f32x4 sq4 = *reinterpret_cast<const f32x4*>(rqs + 16 * I + 4 * g);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      accP[rr] *= sk4[rr];
+      accQ[rr] *= BWD ? sq4[rr] : sq;
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
