@@ -239,6 +239,25 @@ def test_gate_at_bound_stays_finite():
         check(got, ref, dt, label="bound " + str(dt))
 
 
+
+def test_large_qk_magnitudes():
+    # The in-kernel L2 normalisation makes the operator invariant to the scale
+    # of q and k, and the kernels form some products from unnormalised rows
+    # (the row side of the chunk-local pair products). q and k scaled by 1e4,
+    # with every second channel decaying at the -5 bound so that gate factors
+    # inside a chunk reach e^75, must stay finite and match the oracle.
+    announce("q and k scaled by 1e4, half the channels at the gate bound")
+    for dt, D in ((torch.float32, 64), (torch.bfloat16, 128)):
+        x = kda_inputs.make_inputs([200, 77], 2, D, D, dt, seed=23, device="cuda")
+        x["q"].mul_(1e4)
+        x["k"].mul_(1e4)
+        x["raw_g"][:, :, ::2] = 40.0
+        got = gpu_run(x, 64)
+        for name in ("o",) + GRADS:
+            assert torch.isfinite(got[name]).all(), (dt, name)
+        ref = oracle_run(x)
+        check(got, ref, dt, label="large q, k " + str(dt))
+
 # ------------------------------------------------------------------ structure
 
 
