@@ -2,7 +2,8 @@
 an MI355X).
 
 The GPU runs the whole workload in the launch configuration the benchmark
-times (all heads, every segment); the oracle then recomputes the heads in
+times (all heads, every segment, the forward saving the states that the
+backward's segments start from, as bench.py's step does); the oracle then recomputes the heads in
 groups (heads are independent), so that its FP64 copies of one group fit in
 host memory, and the comparison accumulates sum((x - ref)^2) and sum(ref^2)
 per tensor over the groups. The normalised L2 error of each whole tensor is
@@ -27,7 +28,8 @@ import pytest
 import torch
 
 import kda_inputs
-from test_gpu_parity import (ROW_TOL, TOL, gate_sum_scales, gpu_run, oracle_run, row_stats,
+from recompute_kda_chunked_amd import kda_backward, kda_forward
+from test_gpu_parity import (GRADS, NAMES, ROW_TOL, TOL, gate_sum_scales, oracle_run, row_stats,
                              to_np)
 
 pytestmark = pytest.mark.gpu
@@ -35,9 +37,21 @@ pytestmark = pytest.mark.gpu
 OUTS = ("o", "dq", "dk", "dv", "draw_g", "draw_beta", "dA_log", "ddt_bias")
 
 
+def bench_step(x, chunk):
+    """One forward and backward as bench.py times them: the forward saves the
+    states entering the backward's segments and the backward starts from them."""
+    args = [x[n] for n in NAMES]
+    kw = dict(cu_seqlens_host=x["cu_seqlens_host"], chunk=chunk)
+    o, _, ck = kda_forward(*args, x["cu_seqlens"], save_checkpoints=True, **kw)
+    out = {"o": o}
+    out.update(zip(GRADS, kda_backward(*args, x["dO"], x["cu_seqlens"], checkpoints=ck, **kw)))
+    torch.cuda.synchronize()
+    return out
+
+
 def compare_every_head(x, H, group, label, per_head_gate=False, dtype=torch.bfloat16):
     """Run the oracle over head groups and compare all of `got` with it."""
-    got = gpu_run(x, x["_chunk"])
+    got = bench_step(x, x["_chunk"])
     tol_o, tol_g = TOL[dtype]
     acc = {n: [0.0, 0.0, 0.0, 0] for n in OUTS}  # err^2, ref^2, worst row error, rows
     gate_rel = []  # per-head gate sums (bf16): |error| / norm of their terms
