@@ -394,16 +394,19 @@ struct ProfScope {
   hipStream_t s;
   hipEvent_t a = nullptr;
   ProfScope(int k, int64_t u, hipStream_t st) : kind(k), units(u), s(st) {
-    if (g_prof_on && hipEventCreate(&a) == hipSuccess) hipEventRecord(a, s);
+    if (g_prof_on && hipEventCreate(&a) == hipSuccess && hipEventRecord(a, s) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      a = nullptr;
+    }
   }
   void done() {
     if (!a) return;
     hipEvent_t b = nullptr;
-    if (hipEventCreate(&b) == hipSuccess) {
-      hipEventRecord(b, s);
+    if (hipEventCreate(&b) == hipSuccess && hipEventRecord(b, s) == hipSuccess) {
       g_prof.push_back({kind, units, a, b});
     } else {
-      hipEventDestroy(a);
+      if (b) (void)hipEventDestroy(b);
+      (void)hipEventDestroy(a);
     }
     a = nullptr;
   }
@@ -694,8 +697,8 @@ int kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
 
 int kda_profile_begin(void) {
   for (auto& r : g_prof) {
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_prof.clear();
   g_prof_on = true;
@@ -719,8 +722,8 @@ int kda_profile_end(int32_t* launches, double* total_ms, int64_t* units, int n) 
       if (total_ms) total_ms[r.kind] += ms;
       if (units) units[r.kind] += r.units;
     }
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_prof.clear();
   return st;

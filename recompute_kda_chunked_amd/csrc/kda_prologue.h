@@ -82,7 +82,7 @@ struct ChunkLoc {
 };
 
 template <int C>
-__device__ __forceinline__ ChunkLoc locate(const Inputs& in, int N, int c) {
+__device__ __forceinline__ ChunkLoc locate(const Inputs& in, [[maybe_unused]] int N, int c) {
   const int2 e = in.cloc[c];
   return ChunkLoc{static_cast<int64_t>(e.x), e.y};
 }
